@@ -1,0 +1,169 @@
+"""Plain float64 CPU oracle for the tied LM head + logit softcap + cross-entropy -> bits-per-byte path.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this module. The GPU library never calls it, and it shares no code with the GPU library.
+
+What it computes, and where the pages state it:
+
+* Tied LM head: the input embedding E[V, D] is reused as the output projection, so the logits are
+  z = H . E^T (trios issue #19, table of approaches, "Tied embeddings"; parameter-golf README
+  leaderboard, "Naive Baseline" row: "TiedEmbeddings"; repo-explainer page, "The Baseline Is a Map",
+  ``logits = model(batch["x"])``).
+* Logit softcap: the pages only say the logits are "softcapped" (HYDRA Golf site, stack list,
+  "fused softcapped CE kernel"; README leaderboard, PR #1787 row). Reading taken: s = c * tanh(z / c)
+  with c = 30; c = 0 means no cap (s = z).
+* Cross-entropy against the next token, in nats: lse(s) - s[target] (trios issue, "Контекст":
+  "cross-entropy loss / bits-per-byte"; repo-explainer, ``loss = criterion(logits, batch["y"])``).
+* Bits per byte: total -log2 p(target) over scored rows divided by the total UTF-8 bytes of those
+  targets, a ratio of sums (README introduction: "evaluated by compression ... tokenizer-agnostic,
+  bits per byte"; tproger article, "Правила и метрика": compression counted in bytes). A per-position
+  byte count may replace the per-vocabulary table (README leaderboard, PR #1736 row,
+  "byte-sidecar BPB accounting").
+* Scored rows: a mask selects the rows that count (README leaderboard, "Sliding Window Eval" row,
+  stride 64). Unscored rows get nats = 0 and lse = 0 and enter no sum.
+* Backward of L = g * sum_scored nats (repo-explainer, ``loss.backward()``):
+  dS = g (softmax(s) - onehot(target)), dZ = dS * ds/dz with ds/dz = 1 - tanh(z/c)^2,
+  dH = dZ . E, dE = dZ^T . H (the LM-head part of the tied embedding's gradient).
+
+Every function works on float64 arrays (bf16 inputs are widened exactly before they get here).
+Nothing is blocked, fused or reordered beyond the formulas above; numpy's matmul is the only
+library primitive used for a step.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+LN2 = float(np.log(2.0))
+
+__all__ = ["LN2", "logits", "softcap", "softcap_derivative", "log_sum_exp", "forward", "bpb",
+           "backward", "embed_grad_rows", "loss"]
+
+
+def logits(H: np.ndarray, E: np.ndarray) -> np.ndarray:
+    """z[t, v] = sum_d H[t, d] * E[v, d]: the tied head, the embedding used as output projection."""
+    return np.asarray(H, dtype=np.float64) @ np.asarray(E, dtype=np.float64).T
+
+
+def softcap(z: np.ndarray, c: float) -> np.ndarray:
+    """s = c * tanh(z / c) for c > 0; s = z when c == 0 (no cap)."""
+    if c > 0:
+        return c * np.tanh(z / c)
+    return np.array(z, dtype=np.float64, copy=True)
+
+
+def softcap_derivative(z: np.ndarray, c: float) -> np.ndarray:
+    """ds/dz = 1 - tanh(z / c)^2 for c > 0, else 1."""
+    if c > 0:
+        return 1.0 - np.tanh(z / c) ** 2
+    return np.ones_like(z, dtype=np.float64)
+
+
+def log_sum_exp(s: np.ndarray) -> np.ndarray:
+    """lse[t] = log sum_v exp(s[t, v]), shifted by the row maximum to stay finite."""
+    m = np.max(s, axis=1)
+    return m + np.log(np.sum(np.exp(s - m[:, None]), axis=1))
+
+
+def _scored(T: int, mask) -> np.ndarray:
+    if mask is None:
+        return np.ones(T, dtype=bool)
+    return np.asarray(mask).astype(bool)
+
+
+def forward(H, E, target, c: float, mask=None):
+    """Per-row (nats, lse) of the softcapped cross-entropy.
+
+    nats[t] = lse[t] - s[t, target[t]] on scored rows; 0 (and lse 0) on unscored rows.
+    A scored row whose target lies outside [0, V) gets nats = NaN.
+    """
+    H = np.asarray(H, dtype=np.float64)
+    E = np.asarray(E, dtype=np.float64)
+    target = np.asarray(target, dtype=np.int64)
+    T, V = H.shape[0], E.shape[0]
+    s = softcap(logits(H, E), c)
+    lse = log_sum_exp(s)
+    valid = (target >= 0) & (target < V)
+    s_target = np.full(T, np.nan)
+    rows = np.nonzero(valid)[0]
+    s_target[rows] = s[rows, target[rows]]
+    nats = lse - s_target
+    scored = _scored(T, mask)
+    nats = np.where(scored, nats, 0.0)
+    lse = np.where(scored, lse, 0.0)
+    return nats, lse
+
+
+def bpb(nats, target, byte_len, mask=None, byte_per_pos=None, V=None):
+    """(sum_nats, sum_bytes, n_scored, bits_per_byte) over the scored rows.
+
+    bytes[t] = byte_len[target[t]], or byte_per_pos[t] when given. A scored row whose target is
+    outside [0, V) adds no bytes (its nats are NaN already). bits_per_byte = sum_nats /
+    (ln 2 * sum_bytes), with IEEE results for empty sums (0/0 = NaN, x/0 = inf).
+    """
+    nats = np.asarray(nats, dtype=np.float64)
+    target = np.asarray(target, dtype=np.int64)
+    byte_len = np.asarray(byte_len, dtype=np.int64)
+    V = byte_len.shape[0] if V is None else int(V)
+    T = nats.shape[0]
+    scored = _scored(T, mask)
+    if byte_per_pos is not None:
+        bytes_t = np.asarray(byte_per_pos, dtype=np.int64)
+    else:
+        valid = (target >= 0) & (target < V)
+        bytes_t = np.where(valid, byte_len[np.clip(target, 0, V - 1)], 0)
+    sum_nats = float(np.sum(nats[scored]))
+    sum_bytes = int(np.sum(bytes_t[scored]))
+    n_scored = int(np.count_nonzero(scored))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        bits = np.float64(sum_nats) / (np.float64(LN2) * np.float64(sum_bytes))
+    return sum_nats, sum_bytes, n_scored, float(bits)
+
+
+def loss(H, E, target, c: float, g: float, mask=None) -> float:
+    """L = g * sum over scored rows of nats."""
+    nats, _ = forward(H, E, target, c, mask)
+    return float(g * np.sum(nats))
+
+
+def backward(H, E, target, c: float, g: float, mask=None):
+    """(dH, dE) of L = g * sum_scored nats, from the definition.
+
+    p = softmax(s) per row, dS = g * (p - onehot(target)), dZ = dS * ds/dz (zero on unscored
+    rows), dH = dZ . E, dE = dZ^T . H. dE is only the LM-head part of the tied embedding's
+    gradient; the caller adds the gradient of the input lookup.
+    """
+    H = np.asarray(H, dtype=np.float64)
+    E = np.asarray(E, dtype=np.float64)
+    target = np.asarray(target, dtype=np.int64)
+    T, V = H.shape[0], E.shape[0]
+    z = logits(H, E)
+    s = softcap(z, c)
+    p = np.exp(s - log_sum_exp(s)[:, None])
+    onehot = np.zeros((T, V))
+    onehot[np.arange(T), target] = 1.0
+    dS = g * (p - onehot)
+    dZ = dS * softcap_derivative(z, c)
+    dZ[~_scored(T, mask)] = 0.0
+    dH = dZ @ E
+    dE = dZ.T @ H
+    return dH, dE
+
+
+def embed_grad_rows(H, E, target, c: float, g: float, lse, vocab_rows, mask=None):
+    """dE[vocab_rows, :] from the same definition, given the per-row lse of the forward.
+
+    Only the logits of the requested vocabulary entries are formed, so this works at full size;
+    ``lse`` must come from :func:`forward` on the same inputs.
+    """
+    H = np.asarray(H, dtype=np.float64)
+    E = np.asarray(E, dtype=np.float64)
+    target = np.asarray(target, dtype=np.int64)
+    vocab_rows = np.asarray(vocab_rows, dtype=np.int64)
+    T = H.shape[0]
+    z = H @ E[vocab_rows].T                                  # [T, n]
+    s = softcap(z, c)
+    p = np.exp(s - np.asarray(lse, dtype=np.float64)[:, None])
+    onehot = (target[:, None] == vocab_rows[None, :]).astype(np.float64)
+    dZ = g * (p - onehot) * softcap_derivative(z, c)
+    dZ[~_scored(T, mask)] = 0.0
+    return dZ.T @ H

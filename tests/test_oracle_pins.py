@@ -1,0 +1,270 @@
+"""Pins of the float64 oracle's forward and bits-per-byte against what the definition fixes.
+
+None of these compares the oracle with itself: each check is a closed form, a worked example whose
+answer is known in closed form (tests/golden), a textbook special case computed by a library
+routine, an invariant of the definition, or an independent brute force written here with Python
+scalars.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as ora
+from lm_head_cross_pg_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(T, D, V, seed=0, hscale=1.0, escale=0.02):
+    rng = np.random.default_rng(seed)
+    H = rng.standard_normal((T, D)) * hscale
+    E = rng.standard_normal((V, D)) * escale
+    y = rng.integers(0, V, size=T)
+    return H, E, y
+
+
+# ---------------------------------------------------------------- golden worked examples
+def test_worked_example_softcap30():
+    g = _load("worked_softcap30.json")
+    H, E, y, c = np.array(g["hidden"]), np.array(g["embed"]), np.array(g["target"]), g["softcap"]
+    s = ora.softcap(ora.logits(H, E), c)
+    np.testing.assert_allclose(s[0], g["expected"]["s"], rtol=0, atol=1e-12)
+    nats, lse = ora.forward(H, E, y, c)
+    np.testing.assert_allclose(nats, g["expected"]["nats"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, g["expected"]["lse"], rtol=1e-13)
+    sn, sb, n, b = ora.bpb(nats, y, np.array(g["byte_len"]))
+    assert sb == g["expected"]["sum_bytes"] and n == g["expected"]["n_scored"]
+    assert sn == pytest.approx(g["expected"]["sum_nats"], rel=1e-13)
+    assert b == pytest.approx(g["expected"]["bpb"], rel=1e-13)
+
+
+def test_worked_example_one_bit_per_byte():
+    g = _load("worked_nocap_one_bit_per_byte.json")
+    H, E, y = np.array(g["hidden"]), np.array(g["embed"]), np.array(g["target"])
+    mask = np.array(g["mask"], dtype=np.uint8)
+    nats, lse = ora.forward(H, E, y, g["softcap"], mask)
+    np.testing.assert_allclose(nats, g["expected"]["nats"], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse, g["expected"]["lse"], rtol=1e-14, atol=1e-15)
+    sn, sb, n, b = ora.bpb(nats, y, np.array(g["byte_len"]), mask)
+    assert (sb, n) == (3, 2)
+    assert b == pytest.approx(1.0, rel=1e-14)
+
+
+def test_uniform_logits_give_ln_V():
+    g = _load("uniform_logits.json")
+    for case in g["cases"]:
+        V = case["V"]
+        H, E, y = _rand(7, 16, V, seed=V)
+        for c in (30.0, 0.0):
+            nats, lse = ora.forward(H, np.zeros_like(E), y, c)          # E = 0
+            np.testing.assert_allclose(nats, case["nats"], rtol=1e-14)
+            nats, _ = ora.forward(np.zeros_like(H), E, y, c)            # H = 0
+            np.testing.assert_allclose(nats, case["nats"], rtol=1e-14)
+
+
+def test_stride64_window_mask_matches_fixture():
+    g = _load("stride64_windows.json")
+    m = synth.stride_mask(g["T"], g["seq_len"], g["stride"])
+    assert np.nonzero(m)[0].tolist() == g["scored_rows"]
+
+
+# ---------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("V", [512, 1024, 8192])
+def test_zero_weights_bpb_closed_form(V):
+    """H = 0: every row costs log2 V bits, so BPB = log2(V) * N_scored / total bytes."""
+    T = 300
+    rng = np.random.default_rng(V)
+    y = rng.integers(0, V, size=T)
+    blen = rng.integers(1, 17, size=V)
+    mask = (rng.random(T) < 0.4).astype(np.uint8)
+    nats, _ = ora.forward(np.zeros((T, 8)), rng.standard_normal((V, 8)), y, 30.0, mask)
+    sn, sb, n, b = ora.bpb(nats, y, blen, mask)
+    assert n == int(mask.sum())
+    assert sb == int(blen[y][mask.astype(bool)].sum())
+    assert b == pytest.approx(math.log2(V) * n / sb, rel=1e-13)
+
+
+def test_vocab_of_one_costs_nothing():
+    H, E, y = _rand(5, 4, 1)
+    nats, _ = ora.forward(H, E, np.zeros(5, dtype=int), 30.0)
+    np.testing.assert_allclose(nats, 0.0, atol=1e-15)
+    assert ora.bpb(nats, np.zeros(5, dtype=int), np.array([3]))[3] == 0.0
+
+
+@pytest.mark.parametrize("c", [30.0, 2.0, 0.0])
+def test_vocab_of_two_is_softplus(c):
+    H, E, y = _rand(50, 6, 2, seed=3, hscale=20.0, escale=0.5)
+    nats, _ = ora.forward(H, E, y, c)
+    for t in range(50):
+        z = [sum(H[t, d] * E[v, d] for d in range(6)) for v in range(2)]
+        s = [c * math.tanh(zz / c) if c > 0 else zz for zz in z]
+        delta = s[1 - y[t]] - s[y[t]]
+        softplus = max(delta, 0.0) + math.log1p(math.exp(-abs(delta)))
+        assert nats[t] == pytest.approx(softplus, rel=1e-12, abs=1e-14)
+
+
+def test_no_cap_matches_library_cross_entropy():
+    """c = 0 reduces to the textbook cross-entropy; torch's float64 routine is the library check."""
+    H, E, y = _rand(40, 12, 97, seed=4, hscale=3.0, escale=1.0)
+    nats, _ = ora.forward(H, E, y, 0.0)
+    ref = torch.nn.functional.cross_entropy(torch.from_numpy(H @ E.T), torch.from_numpy(y), reduction="none")
+    np.testing.assert_allclose(nats, ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- softcap properties
+def test_softcap_bounds_odd_monotone():
+    c = 30.0
+    z = np.linspace(-18 * c, 18 * c, 200001)
+    s = ora.softcap(z, c)
+    assert np.all(np.abs(s) < c)                       # strict inside the fp64-representable range
+    np.testing.assert_array_equal(ora.softcap(-z, c), -s)
+    assert np.all(np.diff(s) >= 0)
+    big = np.array([-1e6, -1e300, 1e6, 1e300])
+    assert np.all(np.abs(ora.softcap(big, c)) <= c)
+
+
+def test_softcap_is_identity_to_second_order():
+    c = 30.0
+    z = np.array([1e-3, 0.01, 0.1, 0.5, 1.0, 3.0])
+    s = ora.softcap(z, c)
+    rel = (z - s) / z
+    np.testing.assert_allclose(rel, (z / c) ** 2 / 3, rtol=0.02)
+
+
+def test_softcap_derivative_closed_form():
+    c = 7.0
+    z = np.linspace(-40, 40, 1001)
+    d = ora.softcap_derivative(z, c)
+    s = ora.softcap(z, c)
+    np.testing.assert_allclose(d, 1 - (s / c) ** 2, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(d, 1 / np.cosh(z / c) ** 2, rtol=1e-10, atol=1e-15)
+
+
+# ---------------------------------------------------------------- brute force
+def _brute_force_nats(H, E, y, c):
+    """Softmax cross-entropy with Python floats, no max shift, no numpy."""
+    out = []
+    T, D = H.shape
+    V = E.shape[0]
+    for t in range(T):
+        s = []
+        for v in range(V):
+            z = 0.0
+            for d in range(D):
+                z += float(H[t, d]) * float(E[v, d])
+            s.append(c * math.tanh(z / c) if c > 0 else z)
+        total = sum(math.exp(x) for x in s)
+        out.append(-math.log(math.exp(s[int(y[t])]) / total))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("c", [30.0, 3.0, 0.0])
+def test_brute_force_tiny(c):
+    H, E, y = _rand(9, 5, 13, seed=11, hscale=2.0, escale=0.7)
+    nats, lse = ora.forward(H, E, y, c)
+    np.testing.assert_allclose(nats, _brute_force_nats(H, E, y, c), rtol=1e-12, atol=1e-12)
+    assert np.all(nats >= 0)
+
+
+def test_brute_force_with_mask_and_bytes():
+    H, E, y = _rand(11, 4, 9, seed=12, hscale=3.0, escale=0.5)
+    mask = np.array([1, 0, 1, 1, 0, 0, 1, 1, 1, 0, 1], dtype=np.uint8)
+    blen = np.arange(1, 10)
+    nats, _ = ora.forward(H, E, y, 30.0, mask)
+    brute = _brute_force_nats(H, E, y, 30.0)
+    total_nats, total_bytes = 0.0, 0
+    for t in range(11):
+        if mask[t]:
+            total_nats += brute[t]
+            total_bytes += int(blen[y[t]])
+        else:
+            assert nats[t] == 0.0
+    sn, sb, n, b = ora.bpb(nats, y, blen, mask)
+    assert (sb, n) == (total_bytes, 7)
+    assert sn == pytest.approx(total_nats, rel=1e-12)
+    assert b == pytest.approx(total_nats / math.log(2) / total_bytes, rel=1e-12)
+
+
+# ---------------------------------------------------------------- metamorphic
+def test_vocab_permutation_invariance():
+    H, E, y = _rand(30, 8, 40, seed=5, hscale=5.0, escale=0.5)
+    perm = np.random.default_rng(0).permutation(40)
+    inv = np.argsort(perm)
+    nats, lse = ora.forward(H, E, y, 30.0)
+    nats_p, lse_p = ora.forward(H, E[perm], inv[y], 30.0)
+    np.testing.assert_allclose(nats_p, nats, rtol=1e-12)
+    np.testing.assert_allclose(lse_p, lse, rtol=1e-12)
+
+
+def test_row_permutation_and_scale_invariance():
+    H, E, y = _rand(30, 8, 40, seed=6, hscale=5.0, escale=0.5)
+    perm = np.random.default_rng(1).permutation(30)
+    nats, _ = ora.forward(H, E, y, 30.0)
+    nats_p, _ = ora.forward(H[perm], E, y[perm], 30.0)
+    np.testing.assert_allclose(nats_p, nats[perm], rtol=1e-12)
+    nats_s, _ = ora.forward(H * 8.0, E / 8.0, y, 30.0)
+    np.testing.assert_allclose(nats_s, nats, rtol=1e-12)
+
+
+def test_bpb_byte_level_and_scaling():
+    H, E, y = _rand(64, 8, 50, seed=7, hscale=2.0, escale=0.3)
+    nats, _ = ora.forward(H, E, y, 30.0)
+    ones = np.ones(50, dtype=int)
+    assert ora.bpb(nats, y, ones)[3] == pytest.approx(nats.mean() / math.log(2), rel=1e-13)
+    blen = np.random.default_rng(2).integers(1, 9, size=50)
+    b1 = ora.bpb(nats, y, blen)[3]
+    assert ora.bpb(nats, y, 3 * blen)[3] == pytest.approx(b1 / 3, rel=1e-13)
+    sidecar = blen[y]
+    assert ora.bpb(nats, y, np.zeros(50, dtype=int), byte_per_pos=sidecar)[3] == pytest.approx(b1, rel=1e-13)
+
+
+def test_bpb_mask_equals_compacted_rows():
+    H, E, y = _rand(80, 8, 30, seed=8, hscale=2.0, escale=0.3)
+    mask = (np.random.default_rng(3).random(80) < 0.3).astype(np.uint8)
+    blen = np.random.default_rng(4).integers(1, 9, size=30)
+    nats, _ = ora.forward(H, E, y, 30.0, mask)
+    rows = np.nonzero(mask)[0]
+    nats_c, _ = ora.forward(H[rows], E, y[rows], 30.0)
+    assert ora.bpb(nats, y, blen, mask)[3] == pytest.approx(ora.bpb(nats_c, y[rows], blen)[3], rel=1e-13)
+
+
+# ---------------------------------------------------------------- degenerate and poison cases
+def test_empty_mask_and_zero_bytes():
+    H, E, y = _rand(10, 4, 6, seed=9)
+    nats, _ = ora.forward(H, E, y, 30.0, np.zeros(10, dtype=np.uint8))
+    sn, sb, n, b = ora.bpb(nats, y, np.ones(6, dtype=int), np.zeros(10, dtype=np.uint8))
+    assert (sn, sb, n) == (0.0, 0, 0) and math.isnan(b)
+    nats, _ = ora.forward(H, E, y, 30.0)
+    assert math.isinf(ora.bpb(nats, y, np.zeros(6, dtype=int))[3])
+
+
+def test_out_of_range_target_poisons():
+    H, E, y = _rand(10, 4, 6, seed=10)
+    y = y.copy()
+    y[3] = 6
+    y[5] = -1
+    nats, lse = ora.forward(H, E, y, 30.0)
+    assert math.isnan(nats[3]) and math.isnan(nats[5]) and np.all(np.isfinite(lse))
+    assert math.isnan(ora.bpb(nats, y, np.ones(6, dtype=int))[3])
+    # masked out, the bad rows do not matter
+    mask = np.ones(10, dtype=np.uint8)
+    mask[[3, 5]] = 0
+    nats, _ = ora.forward(H, E, y, 30.0, mask)
+    assert np.all(np.isfinite(nats)) and math.isfinite(ora.bpb(nats, y, np.ones(6, dtype=int), mask)[3])
+
+
+def test_sanity_mean_nats_near_lnV_plus_half_variance():
+    """Weak-logit regime of the synthetic workloads: mean nats ~ ln V + var(z)/2 (not a pin)."""
+    inp = synth.make_inputs("tiny_f32", seed=0)
+    H, E = synth.as_f64(inp["hidden"], "f32"), synth.as_f64(inp["embed"], "f32")
+    nats, _ = ora.forward(H, E, inp["target"], 30.0)
+    assert nats.mean() == pytest.approx(math.log(512) + 64 * 0.02 ** 2 / 2, abs=0.05)
