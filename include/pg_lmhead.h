@@ -1,0 +1,133 @@
+/*
+ * pg_lmhead.h - C ABI of the fused tied LM head + logit softcap cross-entropy -> bits-per-byte
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The path scores a small GPT by compression, as the Parameter Golf challenge does:
+ *   logits      z[t,v] = sum_d H[t,d] * E[v,d]      tied head: the input embedding E is the output
+ *                                                    projection (trios issue #19, approach table,
+ *                                                    "Tied embeddings"; parameter-golf README
+ *                                                    leaderboard, "Naive Baseline": TiedEmbeddings)
+ *   softcap     s = c * tanh(z / c), c = 0: s = z    ("fused softcapped CE kernel", HYDRA Golf site
+ *                                                    stack list; README leaderboard, PR #1787 row)
+ *   loss        nats[t] = logsumexp_v s[t,v] - s[t,y[t]]   (trios issue, "Контекст": cross-entropy)
+ *   metric      bpb = sum nats / (ln 2 * sum bytes(y[t])) over scored rows   (README introduction:
+ *                                                    "evaluated by compression ... bits per byte")
+ *   backward    dZ = g (softmax(s) - onehot(y)) * (1 - (s/c)^2), dH = dZ E, dE = dZ^T H
+ *                                                    (repo-explainer, "The Baseline Is a Map":
+ *                                                    loss.backward())
+ *
+ * Conventions for every entry point:
+ *   - Array pointers are DEVICE pointers (hipMalloc'ed or equivalent), row-major and contiguous,
+ *     16-byte aligned. H is [T, D], E is [V, D]; D is the fastest axis of both.
+ *   - bf16 arrays hold raw bfloat16 bit patterns (uint16). f32 arrays are IEEE binary32.
+ *   - The caller owns every buffer, including the workspace. The library allocates no device
+ *     memory, keeps no pointer after a call returns and has no mutable global state beyond a
+ *     per-device cache of the device check.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default stream) and never
+ *     synchronises the host. Buffers must stay alive until the stream's work is done.
+ *   - Arguments are validated on the host before anything is launched; a non-zero status means
+ *     nothing was enqueued. Data errors found on the device (a target outside [0, V) on a scored
+ *     row, NaN/Inf inputs) are not reported as codes: they turn the affected nats into NaN, which
+ *     propagates into the bits-per-byte.
+ *   - Unscored rows (score_mask[t] == 0) get nats = lse = 0, zero dH rows, and add nothing to any
+ *     sum. A NULL score_mask scores every row.
+ */
+#ifndef PG_LMHEAD_H
+#define PG_LMHEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pg_status;
+
+enum {
+  PG_OK = 0,
+  PG_ERR_NULL = -1,      /* a required pointer is NULL */
+  PG_ERR_SHAPE = -2,     /* T < 0, D < 1, V < 1, or a size beyond the supported range */
+  PG_ERR_DTYPE = -3,     /* unknown dtype code */
+  PG_ERR_SOFTCAP = -4,   /* softcap negative or not finite; grad_scale not finite */
+  PG_ERR_WORKSPACE = -5, /* workspace smaller than pg_workspace_bytes() asks for */
+  PG_ERR_ALIGN = -6,     /* a pointer is not 16-byte aligned */
+  PG_ERR_DEVICE = -7,    /* no HIP device, or the current device is not gfx950 */
+  PG_ERR_HIP = -8        /* a HIP runtime call or kernel launch failed */
+};
+
+enum { PG_DTYPE_BF16 = 0, PG_DTYPE_F32 = 1 }; /* dtype of H and E (they share one) */
+enum { PG_OP_FWD = 0, PG_OP_BWD = 1, PG_OP_BPB = 2 };
+
+/* Largest supported sizes: T rows up to 2^31 - 1 (each row index fits an int32), V and D up to
+ * 2^20. bf16 with D in {32, 64, 128, 256, 512} runs the MFMA kernels; any other D, and f32 inputs,
+ * run a plain vector kernel with the same results up to rounding. */
+
+/*
+ * Forward: per-row softcapped cross-entropy, without ever writing the T x V logits to memory.
+ *   hidden      [T, D] bf16 or f32 - final hidden states (input of the tied head)
+ *   embed       [V, D] same dtype  - tied embedding, used as the output projection
+ *   target      [T] int32          - next-token ids (the caller has already shifted x -> y)
+ *   score_mask  [T] uint8 or NULL  - 1 = scored row (sliding-window evaluation scores only the
+ *                                    last `stride` rows of each window: README leaderboard,
+ *                                    "Sliding Window Eval", stride 64)
+ *   softcap     c >= 0; c = 0 disables the cap
+ *   nats        [T] f32 out        - -ln p(target) per row; 0 on unscored rows
+ *   lse         [T] f32 out or NULL - logsumexp of the capped logits; 0 on unscored rows
+ *                                    (pg_lmhead_ce_bwd needs it)
+ *   workspace   device scratch of at least pg_workspace_bytes(PG_OP_FWD, T, D, V) bytes
+ */
+pg_status pg_lmhead_ce_fwd(const void* hidden, const void* embed, int32_t dtype,
+                           const int32_t* target, const uint8_t* score_mask,
+                           int64_t T, int32_t D, int32_t V, float softcap,
+                           float* nats, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of L = grad_scale * sum over scored rows of nats (mean cross-entropy: grad_scale =
+ * 1 / number of scored rows). The logits are recomputed from hidden and embed; lse must be the
+ * output of pg_lmhead_ce_fwd on the same inputs.
+ *   dhidden     [T, D] f32 out, overwritten; rows of unscored positions are zero
+ *   dembed      [V, D] f32 out, overwritten; the LM-head part of the tied embedding's gradient
+ *               only (the caller adds the gradient of the input lookup)
+ *   workspace   at least pg_workspace_bytes(PG_OP_BWD, T, D, V) bytes (holds bf16 dZ [T, V])
+ */
+pg_status pg_lmhead_ce_bwd(const void* hidden, const void* embed, int32_t dtype,
+                           const int32_t* target, const uint8_t* score_mask, const float* lse,
+                           int64_t T, int32_t D, int32_t V, float softcap, float grad_scale,
+                           float* dhidden, float* dembed,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bits per byte over the scored rows (tproger article, "Правила и метрика": the score counts
+ * compression in bytes, independent of the tokenizer).
+ *   nats          [T] f32 from pg_lmhead_ce_fwd
+ *   target        [T] int32 - used to look up byte_len; a scored row whose target is outside
+ *                 [0, V) adds no bytes (pg_lmhead_ce_fwd gives such a row NaN nats)
+ *   byte_len      [V] int32 - UTF-8 bytes of each vocabulary entry (BOS / specials = 0)
+ *   byte_per_pos  [T] int32 or NULL - per-position byte counts that replace byte_len (README
+ *                 leaderboard, PR #1736 row: "byte-sidecar BPB accounting")
+ *   out           [4] double, device: sum_nats, sum_bytes, n_scored, bits_per_byte
+ *                 (0/0 = NaN for an empty mask, x/0 = +inf for zero bytes)
+ * The sums use a fixed reduction order, so the result is bitwise reproducible.
+ */
+pg_status pg_bpb_reduce(const float* nats, const int32_t* target, const uint8_t* score_mask,
+                        const int32_t* byte_len, const int32_t* byte_per_pos,
+                        int64_t T, int32_t V, double* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes an entry point needs for these sizes (0 for invalid sizes). */
+size_t pg_workspace_bytes(int32_t op, int64_t T, int32_t D, int32_t V);
+
+/* Static, NUL-terminated description of a status code. */
+const char* pg_status_str(pg_status s);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int32_t pg_abi_version(void);
+
+#define PG_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PG_LMHEAD_H */

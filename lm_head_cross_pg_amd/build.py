@@ -1,0 +1,56 @@
+"""Build libpg_lmhead.so (the gfx950 HIP library) in place with hipcc.
+
+    python -m lm_head_cross_pg_amd.build          # or: python lm_head_cross_pg_amd/build.py
+
+The library needs only the HIP runtime; no PyTorch headers are involved.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libpg_lmhead.so")
+SOURCES = ["pg_api.hip", "pg_fwd.hip", "pg_bwd.hip", "pg_bpb.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # packed fp32 instructions stay off: the compiler still vectorises with plain ops
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument",
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libpg_lmhead.so next to this file; returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *flags(), *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(line for line in (res.stderr or "").splitlines()
+                    if "packed-fp32-ops" not in line and "is not a recognized feature" not in line)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}\n{res.stdout}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

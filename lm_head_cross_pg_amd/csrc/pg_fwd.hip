@@ -1,0 +1,549 @@
+// Forward of the fused tied LM head + logit softcap + cross-entropy for gfx950.
+//
+// What is computed (per scored row t): z = H[t] . E^T (tied head: trios issue #19, approach
+// table, "Tied embeddings"), s = c tanh(z / c) ("fused softcapped CE", HYDRA Golf stack list),
+// nats = logsumexp(s) - s[y[t]] (trios issue, "Контекст": cross-entropy). The T x V logits never
+// reach memory.
+//
+// Kernel layout (bf16, D in {32..512}):
+//   * one workgroup = 8 waves (two per SIMD) = 256 token rows; each wave keeps the bf16 hidden
+//     rows of its 32 tokens in registers as the B operand of v_mfma_f32_32x32x16_bf16 (lane l:
+//     token l % 32, half l / 32 of the hidden width);
+//   * the embedding streams through LDS in tiles of 64 vocabulary rows, double-buffered, loaded
+//     with global_load_lds_dwordx4 (no VGPR round trip) into a XOR-swizzled layout;
+//   * each 32 x 32 accumulator holds 16 vocabulary rows of one token per lane, so the softcap and
+//     the log-sum-exp run per lane with no cross-lane traffic until the very end;
+//   * for 0 < c <= 40 the log-sum-exp uses the fixed shift c (|s| <= c), so each logit costs
+//     exp2, fma, rcp, exp2 and an add: no running maximum, no rescaling;
+//   * the epilogue of one vocabulary block is issued after the MFMA chain of the next block so the
+//     two overlap;
+//   * a grid smaller than the chip (few scored rows) splits the vocabulary across workgroups and
+//     merges the partial sums in a second kernel, in a fixed order.
+#include "pg_common.h"
+#include "pg_internal.h"
+
+namespace pg {
+
+struct FwdParams {
+  const uint16_t* H;
+  const uint16_t* E;
+  const int32_t* target;
+  const int32_t* rows;    // compacted scored rows, or nullptr (row i = i)
+  const int32_t* n_dev;   // device row count, or nullptr (use n_host)
+  int64_t n_host;
+  int V;
+  int n_vtiles;
+  int splits_host;        // > 0: number of vocabulary splits; 0: derived on the device
+  Softcap sc;
+  int direct;             // 1: one split, write nats / lse directly
+  float* nats;
+  float* lse;
+  float* part_l;
+  float* part_m;
+  float* s_target;
+};
+
+__device__ __forceinline__ int device_splits(int64_t n, int n_vtiles, int grid) {
+  int rt = (int)((n + kRowsPerWG - 1) / kRowsPerWG);
+  if (rt <= 0) return 1;
+  int s = grid / rt;
+  return s < 1 ? 1 : (s > n_vtiles ? n_vtiles : s);
+}
+
+// Loads EPL consecutive bf16 values (EPL in {1, 2, 4, 8}) and widens them to float.
+template <int EPL>
+__device__ __forceinline__ void load_bf16(const uint16_t* p, float (&out)[EPL]) {
+  if constexpr (EPL == 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { out[2 * j] = __uint_as_float(w[j] << 16); out[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u); }
+  } else if constexpr (EPL == 4) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    out[0] = __uint_as_float(u.x << 16); out[1] = __uint_as_float(u.x & 0xffff0000u);
+    out[2] = __uint_as_float(u.y << 16); out[3] = __uint_as_float(u.y & 0xffff0000u);
+  } else if constexpr (EPL == 2) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+    out[0] = __uint_as_float(u << 16); out[1] = __uint_as_float(u & 0xffff0000u);
+  } else {
+    out[0] = bf16_to_f32(*p);
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Rows of the workgroup's token tile handled by one wave.
+constexpr int kFwdWaves = 8;
+constexpr int kTokPerWave = kRowsPerWG / kFwdWaves;   // 32: one MFMA column block
+
+// LDS layout of one embedding tile (kVocabTile rows). D = 512: one 1 KiB row per load
+// instruction, rows padded to 1040 bytes so that 16 lanes reading 16 consecutive rows at the same
+// column hit 16 different bank groups. Smaller D: dense rows with the 16-byte chunk index XORed by
+// a function of the row (global_load_lds writes each instruction's 1 KiB contiguously, so there is
+// no room for padding inside it).
+template <int D>
+struct TileLayout {
+  static constexpr int ROWB = 2 * D;
+  static constexpr bool PAD = (ROWB == 1024);
+  static constexpr int PITCH = PAD ? ROWB + 16 : ROWB;
+  static constexpr int TILEB = kVocabTile * PITCH;
+  static constexpr int RPB = (256 / ROWB) > 1 ? (256 / ROWB) : 1;
+  static constexpr int CPR = D / 8;
+  static constexpr int SWZ = CPR < 16 ? CPR : 16;
+  __device__ static int swz(int row) { return PAD ? 0 : (row / RPB) % SWZ; }
+};
+
+// Hint to interleave one 32-row block's MFMA chain (KS steps: one LDS read + one MFMA each) with
+// the epilogue of the previous block (about 6 VALU / transcendental instructions per logit).
+template <int KS, int VALU_PER_STEP>
+__device__ __forceinline__ void interleave_hint() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // two LDS reads ahead
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x402, VALU_PER_STEP, 0);  // VALU + transcendental
+  }
+}
+
+template <int D, bool FIXED>
+struct FwdCore {
+  static constexpr int KS = D / 16;
+  using TL = TileLayout<D>;
+  const lds_char* lds;
+  int h, col, V;
+  float alpha, invK;
+  Softcap sc;
+  bf16x8 hf[KS];
+  float lsum = 0.f;
+  float mrun = -INFINITY;
+
+  // Z^T block (32 vocabulary rows x this lane's token) from LDS buffer `buf`, rows vb*32 ...
+  __device__ __forceinline__ f32x16 chain(int buf, int vb) const {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const int row = vb * 32 + col;
+    const lds_char* rbase = lds + buf * TL::TILEB + row * TL::PITCH;
+    const int sw = TL::swz(row);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int chunk = (h * KS + ks) ^ sw;
+      const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(rbase + chunk * 16);
+      acc = mfma32x32x16(a, hf[ks], acc);
+    }
+    return acc;
+  }
+
+  // Accumulate the block's exp-sum. Register r holds vocabulary row vbase + 8 (r/4) + 4 h + r%4.
+  template <bool MASKED>
+  __device__ __forceinline__ void epilogue(const f32x16& acc, int vbase) {
+    if (FIXED) {
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float w = fexp2(capped_shifted(acc[r], alpha, invK));
+        if (MASKED) {
+          const int v = vbase + 8 * (r >> 2) + 4 * h + (r & 3);
+          part += v < V ? w : 0.f;
+        } else {
+          part += w;
+        }
+      }
+      lsum += part;
+    } else {
+      float s2[16];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = vbase + 8 * (r >> 2) + 4 * h + (r & 3);
+        s2[r] = (!MASKED || v < V) ? capped_log2(acc[r], sc) : -INFINITY;
+        bm = fmaxf(bm, s2[r]);
+      }
+      const float mn = fmaxf(mrun, bm);
+      if (mn != -INFINITY) {
+        float part = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part += fexp2(s2[r] - mn);
+        lsum = lsum * fexp2(mrun - mn) + part;
+        mrun = mn;
+      }
+    }
+  }
+};
+
+template <int D, bool FIXED>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_mfma_kernel(FwdParams p) {
+  using TL = TileLayout<D>;
+  constexpr int KS = D / 16;
+  constexpr int NI = kVocabTile * TL::ROWB / 1024;    // 1 KiB load instructions per tile
+  constexpr int EPL = D >= 64 ? D / 64 : 1;           // hidden elements per lane in the target dot
+  static_assert(kTokPerWave == 32, "one 32-token MFMA block per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TL::TILEB];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, col = lane & 31;
+
+  const int64_t n = p.n_dev ? (int64_t)(*p.n_dev) : p.n_host;
+  const int rt_count = (int)((n + kRowsPerWG - 1) / kRowsPerWG);
+  const int S = p.splits_host > 0 ? p.splits_host : device_splits(n, p.n_vtiles, gridDim.x);
+  const int id = blockIdx.x;
+  if (id >= rt_count * S) return;
+  const int rt = id / S, split = id % S;
+  const int tps = (p.n_vtiles + S - 1) / S;
+  const int t_begin = split * tps;
+  const int t_end = min(t_begin + tps, p.n_vtiles);
+  const int V = p.V;
+  const int64_t tok0 = (int64_t)rt * kRowsPerWG + wave * kTokPerWave;   // first token of this wave
+
+  // ---- target logit (split 0 only): lanes span the hidden width, 8 tokens per batch
+  float sy = 0.f;
+  if (split == 0) {
+    for (int j0 = 0; j0 < kTokPerWave; j0 += 8) {
+      float part[8];
+      int okm = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        int64_t i = tok0 + j0 + j;
+        i = i < n ? i : n - 1;
+        const int64_t r = p.rows ? (int64_t)p.rows[i] : i;
+        const int y = p.target[r];
+        const bool ok = (y >= 0) && (y < V);
+        okm |= ok ? (1 << j) : 0;
+        float hv[EPL], ev[EPL];
+        part[j] = 0.f;
+        if (D >= 64 || lane < D) {
+          load_bf16<EPL>(p.H + r * D + lane * EPL, hv);
+          load_bf16<EPL>(p.E + (int64_t)(ok ? y : 0) * D + lane * EPL, ev);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) part[j] = __builtin_fmaf(hv[e], ev[e], part[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float zy = wave_sum(part[j]);
+        if (col == j0 + j) sy = ((okm >> j) & 1) ? capped_log2(zy, p.sc) : __builtin_nanf("");
+      }
+    }
+  }
+
+  FwdCore<D, FIXED> core;
+  core.lds = (const lds_char*)smem;
+  core.h = h;
+  core.col = col;
+  core.V = V;
+  core.alpha = p.sc.alpha;
+  core.invK = p.sc.invK;
+  core.sc = p.sc;
+
+  // ---- this lane's token: hidden row half into registers (B operand of the MFMA)
+  const int64_t tok = tok0 + col;
+  const int64_t ic = tok < n ? tok : n - 1;
+  const int64_t grow = p.rows ? (int64_t)p.rows[ic] : ic;
+  {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(p.H + grow * D + h * (D / 2));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) core.hf[ks] = src[ks];
+  }
+
+  // ---- embedding tile loader: global_load_lds_dwordx4, 1 KiB per instruction
+  auto load_tile = [&](int tile, int buf) {
+    const int v0 = tile * kVocabTile;
+#pragma unroll
+    for (int j = wave; j < NI; j += kFwdWaves) {
+      const int byte = j * 1024 + lane * 16;
+      const int row = byte / TL::ROWB;
+      const int pchunk = (byte % TL::ROWB) / 16;
+      const int lchunk = pchunk ^ TL::swz(row);
+      const int v = min(v0 + row, V - 1);
+      const char* g = reinterpret_cast<const char*>(p.E + (int64_t)v * D) + lchunk * 16;
+      char* dst = smem + buf * TL::TILEB + (TL::PAD ? j * TL::PITCH : j * 1024);
+      __builtin_amdgcn_global_load_lds(g, (lds_void*)dst, 16, 0, 0);
+    }
+  };
+
+  // ---- main loop. Only the last tile of the vocabulary can be partial; it runs the masked
+  //      epilogue. In every other tile the epilogue of the previous 32-row block is interleaved
+  //      with the MFMA chain of the current one.
+  const int ntiles = t_end - t_begin;
+  const bool last_partial = (t_end == p.n_vtiles) && (V % kVocabTile != 0);
+  constexpr int VPS = 6;   // epilogue VALU/transcendental instructions per MFMA step (16 logits x 6 / 32)
+  f32x16 accp;
+  int vprev = -1;
+  if (ntiles > 0) load_tile(t_begin, 0);
+  for (int i = 0; i < ntiles; ++i) {
+    const int tile = t_begin + i;
+    const int buf = i & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (i + 1 < ntiles) load_tile(tile + 1, buf ^ 1);
+    const int vb0 = tile * kVocabTile;
+    if (last_partial && i + 1 == ntiles) {
+      const f32x16 a0 = core.chain(buf, 0);
+      if (vprev >= 0) core.template epilogue<false>(accp, vprev);
+      const f32x16 a1 = core.chain(buf, 1);
+      core.template epilogue<true>(a0, vb0);
+      core.template epilogue<true>(a1, vb0 + 32);
+      vprev = -1;
+    } else if (vprev < 0) {
+      const f32x16 a0 = core.chain(buf, 0);
+      const f32x16 a1 = core.chain(buf, 1);
+      core.template epilogue<false>(a0, vb0);
+      interleave_hint<KS, VPS>();
+      accp = a1;
+      vprev = vb0 + 32;
+    } else {
+      const f32x16 a0 = core.chain(buf, 0);
+      core.template epilogue<false>(accp, vprev);
+      interleave_hint<KS, VPS>();
+      const f32x16 a1 = core.chain(buf, 1);
+      core.template epilogue<false>(a0, vb0);
+      interleave_hint<KS, VPS>();
+      accp = a1;
+      vprev = vb0 + 32;
+    }
+  }
+  if (vprev >= 0) core.template epilogue<false>(accp, vprev);
+
+  // ---- combine the two lane halves (each holds 16 of every 32 vocabulary rows) and write out
+  {
+    float l = core.lsum, m = core.mrun;
+    const float l2 = __shfl_xor(l, 32);
+    if (FIXED) {
+      l += l2;
+    } else {
+      const float m2 = __shfl_xor(m, 32);
+      lse_merge(m, l, m2, l2);
+    }
+    if (h == 0 && tok < n) {
+      if (p.direct) {
+        const float lse2 = (FIXED ? p.sc.M : m) + flog2(l);
+        p.nats[grow] = kLn2 * (lse2 - sy);
+        if (p.lse) p.lse[grow] = kLn2 * lse2;
+      } else {
+        p.part_l[(int64_t)split * n + tok] = l;
+        if (!FIXED) p.part_m[(int64_t)split * n + tok] = m;
+        if (split == 0) p.s_target[tok] = sy;
+      }
+    }
+  }
+}
+
+// Merge the per-split partial sums of each compacted row, in split order.
+__global__ __launch_bounds__(256) void fwd_finalize_kernel(FwdParams p, int main_grid, int fixed) {
+  const int64_t n = p.n_dev ? (int64_t)(*p.n_dev) : p.n_host;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int S = p.splits_host > 0 ? p.splits_host : device_splits(n, p.n_vtiles, main_grid);
+  float lse2;
+  if (fixed) {
+    float l = 0.f;
+    for (int s = 0; s < S; ++s) l += p.part_l[(int64_t)s * n + i];
+    lse2 = p.sc.M + flog2(l);
+  } else {
+    float m = -INFINITY, l = 0.f;
+    for (int s = 0; s < S; ++s) lse_merge(m, l, p.part_m[(int64_t)s * n + i], p.part_l[(int64_t)s * n + i]);
+    lse2 = m + flog2(l);
+  }
+  const int64_t r = p.rows ? (int64_t)p.rows[i] : i;
+  p.nats[r] = kLn2 * (lse2 - p.s_target[i]);
+  if (p.lse) p.lse[r] = kLn2 * lse2;
+}
+
+// Plain vector kernel for f32 inputs and hidden widths without an MFMA instantiation: one wave
+// per row, lanes stride over the vocabulary with a running (max, sum) each, merged at the end.
+template <typename TIn>
+__device__ __forceinline__ float load_in(const TIn* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_in<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void fwd_generic_kernel(const TIn* H, const TIn* E, const int32_t* target,
+                                                          const int32_t* rows, const int32_t* n_dev,
+                                                          int64_t n_host, int D, int V, Softcap sc,
+                                                          float* nats, float* lse) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t n = n_dev ? (int64_t)(*n_dev) : n_host;
+  if (i >= n) return;
+  const int64_t r = rows ? (int64_t)rows[i] : i;
+  const TIn* hrow = H + r * D;
+  float m = -INFINITY, l = 0.f;
+  for (int v = lane; v < V; v += 64) {
+    const TIn* erow = E + (int64_t)v * D;
+    float z = 0.f;
+    for (int d = 0; d < D; ++d) z = __builtin_fmaf(load_in(hrow, d), load_in(erow, d), z);
+    lse_merge(m, l, capped_log2(z, sc), 1.0f);
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+    lse_merge(m, l, m2, l2);
+  }
+  if (lane == 0) {
+    const int y = target[r];
+    float sy = __builtin_nanf("");
+    if (y >= 0 && y < V) {
+      const TIn* erow = E + (int64_t)y * D;
+      float z = 0.f;
+      for (int d = 0; d < D; ++d) z = __builtin_fmaf(load_in(hrow, d), load_in(erow, d), z);
+      sy = capped_log2(z, sc);
+    }
+    const float lse2 = m + flog2(l);
+    nats[r] = kLn2 * (lse2 - sy);
+    if (lse) lse[r] = kLn2 * lse2;
+  }
+}
+
+// Scored-row selection: one workgroup scans the mask, writes the ascending list of scored rows and
+// their count, and zeroes the outputs of unscored rows.
+__global__ __launch_bounds__(1024) void compact_rows_kernel(const uint8_t* mask, int64_t T, int32_t* rows,
+                                                            int32_t* n_out, float* nats, float* lse) {
+  __shared__ int64_t scan[1024];
+  const int tid = threadIdx.x;
+  const int64_t chunk = (T + 1023) / 1024;
+  const int64_t b = (int64_t)tid * chunk;
+  const int64_t e = (b + chunk < T) ? b + chunk : T;
+  int64_t cnt = 0;
+  for (int64_t t = b; t < e; ++t) cnt += mask[t] != 0;
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int64_t v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int64_t pos = scan[tid] - cnt;
+  for (int64_t t = b; t < e; ++t) {
+    if (mask[t]) {
+      rows[pos++] = (int32_t)t;
+    } else {
+      if (nats) nats[t] = 0.f;
+      if (lse) lse[t] = 0.f;
+    }
+  }
+  if (tid == 1023) *n_out = (int32_t)scan[1023];
+}
+
+// ------------------------------------------------------------------------------------ host side
+
+int64_t fwd_partial_entries(int64_t T) {
+  // Launch grids never exceed max(ceil(T / 256), 1024) workgroups, and splits x compacted rows
+  // never exceed grid x 256.
+  int64_t rt = (T + kRowsPerWG - 1) / kRowsPerWG;
+  int64_t g = rt > 1024 ? rt : 1024;
+  return g * kRowsPerWG;
+}
+
+FwdWorkspace fwd_workspace(int64_t T, int32_t D, int32_t V) {
+  (void)D; (void)V;
+  FwdWorkspace L;
+  size_t o = 0;
+  L.n_rows = o; o += 256;
+  L.rows = o; o += align256((size_t)T * 4);
+  L.s_target = o; o += align256((size_t)T * 4);
+  const size_t P = (size_t)fwd_partial_entries(T);
+  L.part_l = o; o += align256(P * 4);
+  L.part_m = o; o += align256(P * 4);
+  L.total = o;
+  return L;
+}
+
+hipError_t launch_compact_rows(const uint8_t* mask, int64_t T, char* ws, const FwdWorkspace& L,
+                               float* nats, float* lse, hipStream_t st) {
+  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(1024), 0, st, mask, T,
+                     reinterpret_cast<int32_t*>(ws + L.rows), reinterpret_cast<int32_t*>(ws + L.n_rows),
+                     nats, lse);
+  return hipGetLastError();
+}
+
+template <int D, bool FIXED>
+static void launch_mfma(const FwdParams& p, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, FIXED>), dim3(grid), dim3(kFwdWaves * 64), 0, st, p);
+}
+
+template <int D>
+static void launch_mfma_d(const FwdParams& p, int grid, hipStream_t st) {
+  if (p.sc.fixed) launch_mfma<D, true>(p, grid, st);
+  else launch_mfma<D, false>(p, grid, st);
+}
+
+hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t* target,
+                      const uint8_t* mask, int64_t T, int32_t D, int32_t V, float softcap,
+                      float* nats, float* lse, char* ws, const DeviceInfo& dev, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const FwdWorkspace L = fwd_workspace(T, D, V);
+  const Softcap sc = Softcap::make(softcap);
+  const int32_t* rows = nullptr;
+  const int32_t* n_dev = nullptr;
+  if (mask) {
+    hipError_t e = launch_compact_rows(mask, T, ws, L, nats, lse, st);
+    if (e != hipSuccess) return e;
+    rows = reinterpret_cast<const int32_t*>(ws + L.rows);
+    n_dev = reinterpret_cast<const int32_t*>(ws + L.n_rows);
+  }
+
+  if (dtype != 0 || !mfma_width(D)) {
+    const int64_t blocks = (T + 3) / 4;
+    if (dtype == 0)
+      hipLaunchKernelGGL(fwd_generic_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
+                         (const uint16_t*)H, (const uint16_t*)E, target, rows, n_dev, T, D, V, sc, nats, lse);
+    else
+      hipLaunchKernelGGL(fwd_generic_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
+                         (const float*)H, (const float*)E, target, rows, n_dev, T, D, V, sc, nats, lse);
+    return hipGetLastError();
+  }
+
+  FwdParams p{};
+  p.H = (const uint16_t*)H;
+  p.E = (const uint16_t*)E;
+  p.target = target;
+  p.rows = rows;
+  p.n_dev = n_dev;
+  p.n_host = T;
+  p.V = V;
+  p.n_vtiles = (V + kVocabTile - 1) / kVocabTile;
+  p.sc = sc;
+  p.nats = nats;
+  p.lse = lse;
+  p.part_l = reinterpret_cast<float*>(ws + L.part_l);
+  p.part_m = reinterpret_cast<float*>(ws + L.part_m);
+  p.s_target = reinterpret_cast<float*>(ws + L.s_target);
+
+  const int64_t rt = (T + kRowsPerWG - 1) / kRowsPerWG;
+  const int ncu = dev.cu_count > 0 ? (dev.cu_count < 1024 ? dev.cu_count : 1024) : 256;
+  int grid;
+  if (!mask) {
+    int64_t s = ncu / rt;
+    s = s < 1 ? 1 : (s > p.n_vtiles ? p.n_vtiles : s);
+    p.splits_host = (int)s;
+    p.direct = (s == 1);
+    grid = (int)(rt * s);
+  } else {
+    p.splits_host = 0;
+    p.direct = 0;
+    grid = (int)(rt > ncu ? rt : ncu);
+  }
+
+  switch (D) {
+    case 32: launch_mfma_d<32>(p, grid, st); break;
+    case 64: launch_mfma_d<64>(p, grid, st); break;
+    case 128: launch_mfma_d<128>(p, grid, st); break;
+    case 256: launch_mfma_d<256>(p, grid, st); break;
+    default: launch_mfma_d<512>(p, grid, st); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.direct) return e;
+  const int64_t fin_blocks = (T + 255) / 256;
+  hipLaunchKernelGGL(fwd_finalize_kernel, dim3((unsigned)fin_blocks), dim3(256), 0, st, p, grid, (int)sc.fixed);
+  return hipGetLastError();
+}
+
+}  // namespace pg

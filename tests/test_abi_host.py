@@ -1,0 +1,143 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and validates arguments
+before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lm_head_cross_pg_amd import abi, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pg_lmhead.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(abi.LIB_PATH):
+        build.build()
+    return abi.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_symbols() == sorted(abi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert abi.abi_version() == 1
+    for code in range(0, -9, -1):
+        assert abi.status_str(code) and abi.status_str(code) != "unknown status"
+    assert abi.status_str(-99) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    T, D, V = 65536, 512, 8192
+    fwd = abi.workspace_bytes(abi.PG_OP_FWD, T, D, V)
+    bwd = abi.workspace_bytes(abi.PG_OP_BWD, T, D, V)
+    bpb = abi.workspace_bytes(abi.PG_OP_BPB, T, D, V)
+    assert fwd >= 2 * T * 4 and fwd < 64 << 20
+    assert bwd >= T * V * 2                       # bf16 dZ
+    assert 0 < bpb <= 1 << 20
+    assert abi.workspace_bytes(abi.PG_OP_FWD, -1, D, V) == 0
+    assert abi.workspace_bytes(abi.PG_OP_FWD, T, 0, V) == 0
+    assert abi.workspace_bytes(7, T, D, V) == 0
+    assert abi.workspace_bytes(abi.PG_OP_FWD, 0, D, V) > 0
+
+
+# fake, 16-byte aligned "device" addresses: validation never dereferences them
+P = 0x10000
+BIG = 1 << 40
+
+
+def fwd(lib, **kw):
+    a = dict(hidden=P, embed=P, dtype=0, target=P, mask=None, T=256, D=64, V=512, c=30.0,
+             nats=P, lse=P, ws=P, wsb=BIG, stream=None)
+    a.update(kw)
+    return lib.pg_lmhead_ce_fwd(a["hidden"], a["embed"], a["dtype"], a["target"], a["mask"], a["T"], a["D"],
+                                a["V"], a["c"], a["nats"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def bwd(lib, **kw):
+    a = dict(hidden=P, embed=P, dtype=0, target=P, mask=None, lse=P, T=256, D=64, V=512, c=30.0, g=1 / 256,
+             dh=P, de=P, ws=P, wsb=BIG, stream=None)
+    a.update(kw)
+    return lib.pg_lmhead_ce_bwd(a["hidden"], a["embed"], a["dtype"], a["target"], a["mask"], a["lse"], a["T"],
+                                a["D"], a["V"], a["c"], a["g"], a["dh"], a["de"], a["ws"], a["wsb"], a["stream"])
+
+
+def bpb(lib, **kw):
+    a = dict(nats=P, target=P, mask=None, blen=P, bpp=None, T=256, V=512, out=P, ws=P, wsb=BIG, stream=None)
+    a.update(kw)
+    return lib.pg_bpb_reduce(a["nats"], a["target"], a["mask"], a["blen"], a["bpp"], a["T"], a["V"], a["out"],
+                             a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("call", [fwd, bwd, bpb])
+def test_validation_codes(lib, call):
+    assert call(lib, T=-1) == -2
+    assert call(lib, V=0) == -2
+    assert call(lib, ws=None) == -1
+    assert call(lib, ws=P + 8) == -6
+    assert call(lib, wsb=16) == -5
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, hidden=None) == -1
+    assert fwd(lib, embed=None) == -1
+    assert fwd(lib, target=None) == -1
+    assert fwd(lib, nats=None) == -1
+    assert fwd(lib, D=0) == -2
+    assert fwd(lib, D=1 << 21) == -2
+    assert fwd(lib, dtype=2) == -3
+    assert fwd(lib, c=-1.0) == -4
+    assert fwd(lib, c=float("nan")) == -4
+    assert fwd(lib, c=float("inf")) == -4
+    assert fwd(lib, hidden=P + 2) == -6
+    assert fwd(lib, mask=P + 1) == -6
+    assert fwd(lib, lse=P + 4) == -6
+
+
+def test_backward_validation(lib):
+    assert bwd(lib, lse=None) == -1
+    assert bwd(lib, dh=None) == -1
+    assert bwd(lib, de=None) == -1
+    assert bwd(lib, g=float("nan")) == -4
+    assert bwd(lib, dtype=5) == -3
+    assert bwd(lib, de=P + 12) == -6
+
+
+def test_bpb_validation(lib):
+    assert bpb(lib, nats=None) == -1
+    assert bpb(lib, blen=None) == -1
+    assert bpb(lib, out=None) == -1
+    assert bpb(lib, out=P + 8) == -6
+
+
+def test_valid_arguments_reach_the_device_check(lib):
+    """With every argument valid, the only thing left to fail on a host without a gfx950 GPU is
+    the device check; nothing is enqueued."""
+    if os.environ.get("HIP_VISIBLE_DEVICES") is None and _has_gpu():
+        pytest.skip("a GPU is present; the device check would pass")
+    assert fwd(lib) == -7
+    assert bwd(lib) == -7
+    assert bpb(lib) == -7
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False

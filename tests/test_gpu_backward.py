@@ -1,0 +1,81 @@
+"""GPU parity of the backward (dH, dE) against the float64 oracle through the C ABI."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from lm_head_cross_pg_amd import abi, synth
+from oracle import oracle as ora
+from tests.gpu_helpers import GRAD_RL2, ensure_lib, host_inputs, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+
+
+def workload(name, **over):
+    return dataclasses.replace(synth.WORKLOADS[name], **over)
+
+
+def run_bwd(inp, softcap=None, mask=None, grad_scale=None):
+    T, D, V = inp["T"], inp["D"], inp["V"]
+    c = inp["softcap"] if softcap is None else softcap
+    mask = inp["mask"] if mask is None else mask
+    n_scored = T if mask is None else int(mask.sum())
+    g = (1.0 / max(n_scored, 1)) if grad_scale is None else grad_scale
+    print(f"[case] bwd {inp['workload']} seed={inp['seed']} T={T} D={D} V={V} c={c} masked={mask is not None}",
+          flush=True)
+    d = abi.to_device(inp)
+    mask_t = None if mask is None else torch.from_numpy(mask).cuda()
+    nats = torch.empty(T, device="cuda")
+    lse = torch.empty(T, device="cuda")
+    abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], mask_t, c, nats, lse)
+    dH = torch.full((T, D), float("nan"), device="cuda")
+    dE = torch.full((V, D), float("nan"), device="cuda")
+    abi.pg_lmhead_ce_bwd(d["hidden"], d["embed"], d["target"], mask_t, lse, c, g, dH, dE)
+    torch.cuda.synchronize()
+    dH, dE = dH.cpu().numpy().astype(np.float64), dE.cpu().numpy().astype(np.float64)
+    H, E = host_inputs(inp)
+    odH, odE = ora.backward(H, E, inp["target"], c, g, mask)
+    assert np.all(np.isfinite(dH)) and np.all(np.isfinite(dE))
+    assert rel_l2(dH, odH) <= GRAD_RL2, rel_l2(dH, odH)
+    assert rel_l2(dE, odE) <= GRAD_RL2, rel_l2(dE, odE)
+    if mask is not None:
+        assert np.all(dH[~mask.astype(bool)] == 0.0)
+    return dH, dE
+
+
+def test_fd_shape_f32():
+    run_bwd(synth.make_inputs("fd", 0))
+
+
+def test_fd_shape_bf16():
+    run_bwd(synth.make_inputs(workload("fd", dtype="bf16"), 0))
+
+
+@pytest.mark.parametrize("seed", [0, 42])
+def test_training_shape_small(seed):
+    run_bwd(synth.make_inputs("train_v8192", seed, T=700))
+
+
+@pytest.mark.parametrize("D,V", [(64, 1000), (128, 777), (256, 300), (48, 200)])
+def test_widths(D, V):
+    run_bwd(synth.make_inputs(workload("train_v8192", D=D, V=V, T=520, stream=70 + D), 0))
+
+
+@pytest.mark.parametrize("c", [0.0, 5.0, 50.0])
+def test_caps(c):
+    run_bwd(synth.make_inputs(workload("train_v8192", V=1500, T=400, stream=80, softcap=c), 1), softcap=c)
+
+
+def test_stress():
+    run_bwd(synth.make_inputs("stress", 0))
+
+
+def test_masked():
+    inp = synth.make_inputs("masked_stride64", 0, T=4096)
+    run_bwd(inp)

@@ -1,0 +1,199 @@
+"""GPU parity of the fused forward and the bits-per-byte reduction against the float64 oracle,
+through the C ABI, on seeded synthetic inputs."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from lm_head_cross_pg_amd import abi, synth
+from oracle import oracle as ora
+from tests.gpu_helpers import (BPB_RTOL, NATS_ATOL, ensure_lib, gpu_bpb, host_inputs,
+                               oracle_forward_chunked)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+
+
+def workload(name, **over):
+    return dataclasses.replace(synth.WORKLOADS[name], **over)
+
+
+def run(inp, softcap=None, mask=None, sample_rows=None, check_bpb=True, byte_per_pos=None):
+    """Forward + BPB on the GPU vs the oracle; returns (nats_gpu, lse_gpu)."""
+    T, D, V = inp["T"], inp["D"], inp["V"]
+    c = inp["softcap"] if softcap is None else softcap
+    mask = inp["mask"] if mask is None else mask
+    d = abi.to_device(inp)
+    mask_t = None if mask is None else torch.from_numpy(mask).cuda()
+    print(f"[case] {inp['workload']} seed={inp['seed']} T={T} D={D} V={V} c={c} masked={mask is not None}", flush=True)
+    nats_t = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+    lse_t = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+    abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], mask_t, c, nats_t, lse_t)
+    torch.cuda.synchronize()
+    nats, lse = nats_t.cpu().numpy().astype(np.float64), lse_t.cpu().numpy().astype(np.float64)
+    H, E = host_inputs(inp)
+    y = inp["target"]
+    scored = np.ones(T, bool) if mask is None else mask.astype(bool)
+    if sample_rows is None:
+        rows = np.nonzero(scored)[0]
+    else:
+        rows = np.asarray(sample_rows)
+    onats = np.zeros(T)
+    olse = np.zeros(T)
+    if len(rows):
+        onats[rows], olse[rows] = oracle_forward_chunked(H[rows], E, y[rows], c)
+    err = np.max(np.abs(nats[rows] - onats[rows])) if len(rows) else 0.0
+    assert err <= NATS_ATOL, f"max |nats - oracle| = {err}"
+    assert np.max(np.abs(lse[rows] - olse[rows]), initial=0.0) <= NATS_ATOL
+    assert np.all(nats[~scored] == 0.0) and np.all(lse[~scored] == 0.0)
+    if check_bpb:
+        bpp_t = None if byte_per_pos is None else torch.from_numpy(byte_per_pos).cuda()
+        out = gpu_bpb(nats_t, d, V, mask_t, bpp_t)
+        # the reduction itself: float64 sums of the GPU's own nats, exactly the same rows
+        assert out[2] == scored.sum()
+        assert out[0] == pytest.approx(np.sum(nats[scored]), rel=1e-12, abs=1e-9)
+        if sample_rows is None:
+            sn, sb, n, b = ora.bpb(onats, y, inp["byte_len"], mask, byte_per_pos)
+            assert out[1] == sb and out[2] == n
+            if math.isfinite(b):
+                assert abs(out[3] - b) <= BPB_RTOL * abs(b), (out[3], b)
+            else:
+                assert (math.isnan(b) and math.isnan(out[3])) or out[3] == b
+    return nats, lse
+
+
+@pytest.mark.parametrize("seed", [0, 42, 1234])
+def test_tiny_f32(seed):
+    run(synth.make_inputs("tiny_f32", seed))
+
+
+@pytest.mark.parametrize("seed", [0, 42, 1234])
+def test_baseline_vocab_full_size(seed):
+    """T = 4 x 2048, D = 512, V = 1024: vocabulary split over workgroups, every row checked."""
+    run(synth.make_inputs("fwd_v1024", seed))
+
+
+@pytest.mark.parametrize("T", [1, 255, 1000, 4097])
+def test_main_shape_ragged_rows(T):
+    run(synth.make_inputs("fwd_v8192", 0, T=T))
+
+
+@pytest.mark.parametrize("D,V", [(32, 128), (64, 1000), (128, 777), (256, 2048), (512, 100), (512, 1),
+                                 (48, 300), (512, 65)])
+def test_widths_and_ragged_vocab(D, V):
+    w = workload("fwd_v8192", D=D, V=V, T=700, stream=40 + D)
+    run(synth.make_inputs(w, 1))
+
+
+@pytest.mark.parametrize("c", [0.0, 50.0, 5.0])
+def test_other_caps(c):
+    """c = 0 (no cap) and c > 40 take the running-maximum path; c = 5 bends the logits."""
+    w = workload("fwd_v8192", T=600, V=3000, stream=50, softcap=c)
+    run(synth.make_inputs(w, 2), softcap=c)
+
+
+@pytest.mark.parametrize("seed", [0, 42])
+def test_softcap_stress(seed):
+    inp = synth.make_inputs("stress", seed)
+    nats, _ = run(inp)
+    H, E = host_inputs(inp)
+    assert np.max(np.abs(H @ E.T)) > 5 * 30.0
+
+
+def test_stress_f32_and_bf16_generic():
+    inp = synth.make_inputs(workload("stress", dtype="f32", D=40, stream=61), 0)
+    run(inp)
+
+
+@pytest.mark.parametrize("seed", [0, 42, 1234])
+def test_masked_stride64_small(seed):
+    run(synth.make_inputs("masked_stride64", seed, T=8192))
+
+
+def test_masked_stride64_full_size():
+    run(synth.make_inputs("masked_stride64", 0))
+
+
+def test_main_full_size_sampled():
+    """T = 65536, D = 512, V = 8192 in the benchmark's launch configuration: sampled rows against
+    the oracle, the whole BPB against the oracle's full forward."""
+    inp = synth.make_inputs("fwd_v8192", 0)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.choice(65536, 384, replace=False), [0, 1, 255, 256, 65535]]))
+    nats, _ = run(inp, sample_rows=rows)
+    H, E = host_inputs(inp)
+    onats, _ = oracle_forward_chunked(H, E, inp["target"], 30.0)
+    assert np.max(np.abs(nats - onats)) <= NATS_ATOL
+    b_gpu = ora.bpb(nats, inp["target"], inp["byte_len"])[3]
+    b_ora = ora.bpb(onats, inp["target"], inp["byte_len"])[3]
+    assert abs(b_gpu - b_ora) <= BPB_RTOL * b_ora
+
+
+def test_ragged_full_width_direct():
+    """65,436 rows: still one vocabulary split per workgroup (direct write), ragged last tile."""
+    inp = synth.make_inputs("fwd_v8192", 3, T=65436)
+    rows = np.array([0, 17, 30000, 65279, 65280, 65400, 65435])
+    run(inp, sample_rows=rows, check_bpb=False)
+
+
+def test_byte_sidecar():
+    inp = synth.make_inputs("fwd_v1024", 5, T=3000)
+    bpp = np.random.default_rng(1).integers(0, 9, size=3000).astype(np.int32)
+    run(inp, byte_per_pos=bpp)
+
+
+def test_empty_mask_zero_bytes_and_poison():
+    inp = synth.make_inputs("fwd_v8192", 9, T=300)
+    d = abi.to_device(inp)
+    T, V = 300, 8192
+    # empty mask: zero nats, BPB = 0/0
+    mask = torch.zeros(T, dtype=torch.uint8, device="cuda")
+    nats = torch.full((T,), 7.0, device="cuda")
+    abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], mask, 30.0, nats, None)
+    out = gpu_bpb(nats, d, V, mask)
+    assert torch.all(nats == 0).item() and out[2] == 0 and math.isnan(out[3])
+    # zero bytes everywhere: +inf
+    abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, 30.0, nats, None)
+    d0 = dict(d, byte_len=torch.zeros(V, dtype=torch.int32, device="cuda"))
+    assert math.isinf(gpu_bpb(nats, d0, V)[3])
+    # out-of-range targets and a NaN hidden row poison only their own rows
+    y = d["target"].clone()
+    y[5] = V
+    y[6] = -3
+    h = d["hidden"].clone()
+    h[9, 3] = float("nan")
+    abi.pg_lmhead_ce_fwd(h, d["embed"], y, None, 30.0, nats, None)
+    n = nats.cpu().numpy()
+    assert np.isnan(n[[5, 6, 9]]).all() and np.isfinite(np.delete(n, [5, 6, 9])).all()
+    assert math.isnan(gpu_bpb(nats, dict(d, target=y), V)[3])
+
+
+def test_zero_rows_and_zero_weights():
+    inp = synth.make_inputs("fwd_v8192", 4, T=500)
+    d = abi.to_device(inp)
+    nats = torch.zeros(0, device="cuda")
+    abi.pg_lmhead_ce_fwd(d["hidden"][:0], d["embed"], d["target"][:0], None, 30.0, nats, None)
+    # zero embedding: ln V exactly (up to float32), BPB = log2(V) N / bytes
+    nats = torch.empty(500, device="cuda")
+    abi.pg_lmhead_ce_fwd(d["hidden"], torch.zeros_like(d["embed"]), d["target"], None, 30.0, nats, None)
+    assert np.allclose(nats.cpu().numpy(), math.log(8192), atol=1e-5)
+    out = gpu_bpb(nats, d, 8192)
+    exp = math.log2(8192) * 500 / inp["byte_len"][inp["target"]].sum()
+    assert abs(out[3] - exp) <= 1e-5 * exp
+
+
+def test_bitwise_reproducible():
+    inp = synth.make_inputs("fwd_v1024", 0)
+    d = abi.to_device(inp)
+    res = []
+    for _ in range(2):
+        nats = torch.empty(inp["T"], device="cuda")
+        abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, 30.0, nats, None)
+        res.append((nats.cpu().numpy().tobytes(), gpu_bpb(nats, d, inp["V"]).tobytes()))
+    assert res[0] == res[1]
