@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the data-parallel head needs no exchange until the "
@@ -93,6 +95,14 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        src = torch.ones(1 << 27, dtype=torch.float32, device="cuda")   # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "launches": 5}))
+        return
     from lm_head_cross_pg_amd import abi, build, synth
     if not os.path.exists(abi.LIB_PATH):
         build.build()

@@ -43,28 +43,53 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // Softcap constants in base 2. With a = z * alpha, e = 2^a, r = 1 / (1 + e):
 //   tanh(z / c) = 1 - 2 r,  s * log2 e = M + K r  with M = c log2 e and K = -2 M.
 // K r is evaluated as rcp(e / K + 1 / K), i.e. one fma and one reciprocal.
+//
+// Small logits (|z| <= c / 8) use the tanh series instead, truncated after x^7:
+//   tanh(x) = x - x^3/3 + 2 x^5/15 - 17 x^7/315 + O(x^9)   (coefficients from the Bernoulli
+// numbers); at |x| <= 1/8 the first omitted term, 62 x^9/2835, is below 1.4e-9 |x|, far under float
+// rounding. In base 2: s * log2 e = z * Q(z^2), Q(u) = q0 + q1 u + q2 u^2 + q3 u^3 with
+// q0 = log2 e, q1 = -log2 e / (3 c^2), q2 = 2 log2 e / (15 c^4), q3 = -17 log2 e / (315 c^6):
+// three fma and two multiplies, no transcendental.
 struct Softcap {
   float c;        // cap (0 = none)
   float alpha;    // 2 log2 e / c
   float M;        // c log2 e
   float K;        // -2 M
   float invK;     // 1 / K
+  float invM;     // 1 / M
+  float q0, q1, q2, q3;  // series coefficients of s * log2 e in powers of z^2
+  float thr;      // series used when every |z| of a block is <= thr (c / 8; 0 = never)
   bool fixed;     // fixed log-sum-exp shift M (0 < c <= kFixedShiftMaxCap)
   __host__ static Softcap make(float cap) {
     Softcap s;
     s.c = cap;
     if (cap > 0.f) {
-      s.alpha = 2.0f * kLog2e / cap;
-      s.M = cap * kLog2e;
+      const double c = cap, l2e = 1.4426950408889634;
+      s.alpha = (float)(2.0 * l2e / c);
+      s.M = (float)(c * l2e);
       s.K = -2.0f * s.M;
       s.invK = 1.0f / s.K;
+      s.invM = 1.0f / s.M;
+      s.q0 = (float)l2e;
+      s.q1 = (float)(-l2e / (3.0 * c * c));
+      s.q2 = (float)(2.0 * l2e / (15.0 * c * c * c * c));
+      s.q3 = (float)(-17.0 * l2e / (315.0 * c * c * c * c * c * c));
+      s.thr = (cap >= 0.01f) ? cap / 8.0f : 0.0f;
       s.fixed = cap <= kFixedShiftMaxCap;
     } else {
-      s.alpha = 0.f; s.M = 0.f; s.K = 0.f; s.invK = 0.f; s.fixed = false;
+      s.alpha = 0.f; s.M = 0.f; s.K = 0.f; s.invK = 0.f; s.invM = 0.f;
+      s.q0 = s.q1 = s.q2 = s.q3 = 0.f; s.thr = 0.f; s.fixed = false;
     }
     return s;
   }
 };
+
+// s * log2 e by the series (valid for |z| <= c / 8).
+__device__ __forceinline__ float capped_log2_series(float z, const Softcap& sc) {
+  const float u = z * z;
+  const float q = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(sc.q3, u, sc.q2), u, sc.q1), u, sc.q0);
+  return z * q;
+}
 
 // (s - M) * log2 e for c > 0, i.e. K * r; overflow-safe: e -> inf gives 0 (s = c), e -> 0 gives K.
 __device__ __forceinline__ float capped_shifted(float z, float alpha, float invK) {

@@ -13,14 +13,16 @@
 //     with global_load_lds_dwordx4 (no VGPR round trip) into a XOR-swizzled layout;
 //   * each 32 x 32 accumulator holds 16 vocabulary rows of one token per lane, so the softcap and
 //     the log-sum-exp run per lane with no cross-lane traffic until the very end;
-//   * for 0 < c <= 40 the log-sum-exp uses the fixed shift c (|s| <= c), so each logit costs
-//     exp2, fma, rcp, exp2 and an add: no running maximum, no rescaling;
+//   * for 0 < c <= 40 the log-sum-exp uses the fixed shift c (|s| <= c): no running maximum, no
+//     rescaling. A block whose logits all satisfy |z| <= c/8 evaluates the cap by the tanh series
+//     (one exp2 per logit); otherwise by exp2, fma, rcp (three transcendentals per logit);
 //   * the epilogue of one vocabulary block is issued after the MFMA chain of the next block so the
 //     two overlap;
 //   * a grid smaller than the chip (few scored rows) splits the vocabulary across workgroups and
 //     merges the partial sums in a second kernel, in a fixed order.
 #include "pg_common.h"
 #include "pg_internal.h"
+#include "pg_tile.h"
 
 namespace pg {
 
@@ -50,129 +52,94 @@ __device__ __forceinline__ int device_splits(int64_t n, int n_vtiles, int grid) 
   return s < 1 ? 1 : (s > n_vtiles ? n_vtiles : s);
 }
 
-// Loads EPL consecutive bf16 values (EPL in {1, 2, 4, 8}) and widens them to float.
-template <int EPL>
-__device__ __forceinline__ void load_bf16(const uint16_t* p, float (&out)[EPL]) {
-  if constexpr (EPL == 8) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { out[2 * j] = __uint_as_float(w[j] << 16); out[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u); }
-  } else if constexpr (EPL == 4) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    out[0] = __uint_as_float(u.x << 16); out[1] = __uint_as_float(u.x & 0xffff0000u);
-    out[2] = __uint_as_float(u.y << 16); out[3] = __uint_as_float(u.y & 0xffff0000u);
-  } else if constexpr (EPL == 2) {
-    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-    out[0] = __uint_as_float(u << 16); out[1] = __uint_as_float(u & 0xffff0000u);
-  } else {
-    out[0] = bf16_to_f32(*p);
-  }
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
-// Rows of the workgroup's token tile handled by one wave.
-constexpr int kFwdWaves = 8;
-constexpr int kTokPerWave = kRowsPerWG / kFwdWaves;   // 32: one MFMA column block
-
-// LDS layout of one embedding tile (kVocabTile rows). D = 512: one 1 KiB row per load
-// instruction, rows padded to 1040 bytes so that 16 lanes reading 16 consecutive rows at the same
-// column hit 16 different bank groups. Smaller D: dense rows with the 16-byte chunk index XORed by
-// a function of the row (global_load_lds writes each instruction's 1 KiB contiguously, so there is
-// no room for padding inside it).
-template <int D>
-struct TileLayout {
-  static constexpr int ROWB = 2 * D;
-  static constexpr bool PAD = (ROWB == 1024);
-  static constexpr int PITCH = PAD ? ROWB + 16 : ROWB;
-  static constexpr int TILEB = kVocabTile * PITCH;
-  static constexpr int RPB = (256 / ROWB) > 1 ? (256 / ROWB) : 1;
-  static constexpr int CPR = D / 8;
-  static constexpr int SWZ = CPR < 16 ? CPR : 16;
-  __device__ static int swz(int row) { return PAD ? 0 : (row / RPB) % SWZ; }
-};
-
-// Hint to interleave one 32-row block's MFMA chain (KS steps: one LDS read + one MFMA each) with
-// the epilogue of the previous block (about 6 VALU / transcendental instructions per logit).
-template <int KS, int VALU_PER_STEP>
-__device__ __forceinline__ void interleave_hint() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // two LDS reads ahead
-#pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read
-    __builtin_amdgcn_sched_group_barrier(0x402, VALU_PER_STEP, 0);  // VALU + transcendental
-  }
-}
-
 template <int D, bool FIXED>
 struct FwdCore {
   static constexpr int KS = D / 16;
-  using TL = TileLayout<D>;
   const lds_char* lds;
   int h, col, V;
-  float alpha, invK;
   Softcap sc;
   bf16x8 hf[KS];
   float lsum = 0.f;
   float mrun = -INFINITY;
 
-  // Z^T block (32 vocabulary rows x this lane's token) from LDS buffer `buf`, rows vb*32 ...
-  __device__ __forceinline__ f32x16 chain(int buf, int vb) const {
-    f32x16 acc;
+  __device__ __forceinline__ f32x16 chain(int buf, int vb) const { return logit_block<D>(lds, buf, vb, h, col, hf); }
+
+  // Exp-sum of one block with the fixed shift M, by the tanh series (valid when |z| <= c/8).
+  __device__ __forceinline__ float part_series(const f32x16& acc) const {
+    float part = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    const int row = vb * 32 + col;
-    const lds_char* rbase = lds + buf * TL::TILEB + row * TL::PITCH;
-    const int sw = TL::swz(row);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int chunk = (h * KS + ks) ^ sw;
-      const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(rbase + chunk * 16);
-      acc = mfma32x32x16(a, hf[ks], acc);
+    for (int r = 0; r < 16; ++r) {
+      const float z = acc[r];
+      const float u = z * z;
+      const float q = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(sc.q3, u, sc.q2), u, sc.q1), u, sc.q0);
+      part += fexp2(__builtin_fmaf(z, q, -sc.M));
     }
-    return acc;
+    return part;
   }
 
-  // Accumulate the block's exp-sum. Register r holds vocabulary row vbase + 8 (r/4) + 4 h + r%4.
+  // Exp-sum of one block with the fixed shift M, exact softcap. Register r holds vocabulary row
+  // vbase + 8 (r/4) + 4 h + r%4; MASKED drops rows >= V.
   template <bool MASKED>
-  __device__ __forceinline__ void epilogue(const f32x16& acc, int vbase) {
-    if (FIXED) {
-      float part = 0.f;
+  __device__ __forceinline__ float part_exact(const f32x16& acc, int vbase) const {
+    float part = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float w = fexp2(capped_shifted(acc[r], alpha, invK));
-        if (MASKED) {
-          const int v = vbase + 8 * (r >> 2) + 4 * h + (r & 3);
-          part += v < V ? w : 0.f;
-        } else {
-          part += w;
-        }
-      }
-      lsum += part;
-    } else {
-      float s2[16];
-      float bm = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 16; ++r) {
+      const float w = fexp2(capped_shifted(acc[r], sc.alpha, sc.invK));
+      if (MASKED) {
         const int v = vbase + 8 * (r >> 2) + 4 * h + (r & 3);
-        s2[r] = (!MASKED || v < V) ? capped_log2(acc[r], sc) : -INFINITY;
-        bm = fmaxf(bm, s2[r]);
-      }
-      const float mn = fmaxf(mrun, bm);
-      if (mn != -INFINITY) {
-        float part = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) part += fexp2(s2[r] - mn);
-        lsum = lsum * fexp2(mrun - mn) + part;
-        mrun = mn;
+        part += v < V ? w : 0.f;
+      } else {
+        part += w;
       }
     }
+    return part;
+  }
+
+  // Running-maximum variant for c = 0 and caps above the fixed-shift range.
+  template <bool MASKED>
+  __device__ __forceinline__ void epilogue_online(const f32x16& acc, int vbase) {
+    float s2[16];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int v = vbase + 8 * (r >> 2) + 4 * h + (r & 3);
+      s2[r] = (!MASKED || v < V) ? capped_log2(acc[r], sc) : -INFINITY;
+      bm = fmaxf(bm, s2[r]);
+    }
+    const float mn = fmaxf(mrun, bm);
+    if (mn != -INFINITY) {
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part += fexp2(s2[r] - mn);
+      lsum = lsum * fexp2(mrun - mn) + part;
+      mrun = mn;
+    }
+  }
+
+  // Epilogue of a block outside the interleaved main loop (first/last/partial blocks).
+  template <bool MASKED>
+  __device__ __forceinline__ void epilogue(const f32x16& acc, int vbase) {
+    if (FIXED) lsum += part_exact<MASKED>(acc, vbase);
+    else epilogue_online<MASKED>(acc, vbase);
+  }
+
+  // MFMA chain of block (buf, vb) with the epilogue of the pending full block `prev` interleaved in
+  // one basic block. The series is computed speculatively; if any |z| of `prev` exceeds c/8 (a
+  // wave-uniform, rarely taken branch) the block's sum is recomputed with the exact softcap.
+  __device__ __forceinline__ f32x16 chain_with_epilogue(int buf, int vb, const f32x16& prev, int vprev) {
+    f32x16 a;
+    if (FIXED) {
+      a = chain(buf, vb);
+      const float part = part_series(prev);
+      const float amax = wave_absmax16(prev);
+      lsum += part;
+      interleave_hint<KS, (16 * 8 + KS - 1) / KS>();
+      if (!__all(amax <= sc.thr)) lsum += part_exact<false>(prev, vprev) - part;
+    } else {
+      a = chain(buf, vb);
+      epilogue_online<false>(prev, vprev);
+    }
+    return a;
   }
 };
 
@@ -181,7 +148,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(FwdParams p) {
   using TL = TileLayout<D>;
   constexpr int KS = D / 16;
-  constexpr int NI = kVocabTile * TL::ROWB / 1024;    // 1 KiB load instructions per tile
   constexpr int EPL = D >= 64 ? D / 64 : 1;           // hidden elements per lane in the target dot
   static_assert(kTokPerWave == 32, "one 32-token MFMA block per wave");
   __shared__ __attribute__((aligned(1024))) char smem[2 * TL::TILEB];
@@ -237,8 +203,6 @@ void fwd_mfma_kernel(FwdParams p) {
   core.h = h;
   core.col = col;
   core.V = V;
-  core.alpha = p.sc.alpha;
-  core.invK = p.sc.invK;
   core.sc = p.sc;
 
   // ---- this lane's token: hidden row half into registers (B operand of the MFMA)
@@ -251,37 +215,20 @@ void fwd_mfma_kernel(FwdParams p) {
     for (int ks = 0; ks < KS; ++ks) core.hf[ks] = src[ks];
   }
 
-  // ---- embedding tile loader: global_load_lds_dwordx4, 1 KiB per instruction
-  auto load_tile = [&](int tile, int buf) {
-    const int v0 = tile * kVocabTile;
-#pragma unroll
-    for (int j = wave; j < NI; j += kFwdWaves) {
-      const int byte = j * 1024 + lane * 16;
-      const int row = byte / TL::ROWB;
-      const int pchunk = (byte % TL::ROWB) / 16;
-      const int lchunk = pchunk ^ TL::swz(row);
-      const int v = min(v0 + row, V - 1);
-      const char* g = reinterpret_cast<const char*>(p.E + (int64_t)v * D) + lchunk * 16;
-      char* dst = smem + buf * TL::TILEB + (TL::PAD ? j * TL::PITCH : j * 1024);
-      __builtin_amdgcn_global_load_lds(g, (lds_void*)dst, 16, 0, 0);
-    }
-  };
-
   // ---- main loop. Only the last tile of the vocabulary can be partial; it runs the masked
-  //      epilogue. In every other tile the epilogue of the previous 32-row block is interleaved
-  //      with the MFMA chain of the current one.
+  //      epilogue. Elsewhere the epilogue of the previous 32-row block is interleaved with the
+  //      MFMA chain of the current one.
   const int ntiles = t_end - t_begin;
   const bool last_partial = (t_end == p.n_vtiles) && (V % kVocabTile != 0);
-  constexpr int VPS = 6;   // epilogue VALU/transcendental instructions per MFMA step (16 logits x 6 / 32)
   f32x16 accp;
   int vprev = -1;
-  if (ntiles > 0) load_tile(t_begin, 0);
+  if (ntiles > 0) load_embed_tile<D, kFwdWaves>(smem, p.E, V, t_begin, 0, wave, lane);
   for (int i = 0; i < ntiles; ++i) {
     const int tile = t_begin + i;
     const int buf = i & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (i + 1 < ntiles) load_tile(tile + 1, buf ^ 1);
+    if (i + 1 < ntiles) load_embed_tile<D, kFwdWaves>(smem, p.E, V, tile + 1, buf ^ 1, wave, lane);
     const int vb0 = tile * kVocabTile;
     if (last_partial && i + 1 == ntiles) {
       const f32x16 a0 = core.chain(buf, 0);
@@ -292,19 +239,11 @@ void fwd_mfma_kernel(FwdParams p) {
       vprev = -1;
     } else if (vprev < 0) {
       const f32x16 a0 = core.chain(buf, 0);
-      const f32x16 a1 = core.chain(buf, 1);
-      core.template epilogue<false>(a0, vb0);
-      interleave_hint<KS, VPS>();
-      accp = a1;
+      accp = core.chain_with_epilogue(buf, 1, a0, vb0);
       vprev = vb0 + 32;
     } else {
-      const f32x16 a0 = core.chain(buf, 0);
-      core.template epilogue<false>(accp, vprev);
-      interleave_hint<KS, VPS>();
-      const f32x16 a1 = core.chain(buf, 1);
-      core.template epilogue<false>(a0, vb0);
-      interleave_hint<KS, VPS>();
-      accp = a1;
+      const f32x16 a0 = core.chain_with_epilogue(buf, 0, accp, vprev);
+      accp = core.chain_with_epilogue(buf, 1, a0, vb0);
       vprev = vb0 + 32;
     }
   }

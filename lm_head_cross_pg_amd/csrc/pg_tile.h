@@ -1,0 +1,120 @@
+// Pieces shared by the forward and backward kernels that stream the tied embedding through LDS
+// against register-resident hidden rows (internal header).
+#pragma once
+#include "pg_common.h"
+
+namespace pg {
+
+// Loads EPL consecutive bf16 values (EPL in {1, 2, 4, 8}) and widens them to float.
+template <int EPL>
+__device__ __forceinline__ void load_bf16(const uint16_t* p, float (&out)[EPL]) {
+  if constexpr (EPL == 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { out[2 * j] = __uint_as_float(w[j] << 16); out[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u); }
+  } else if constexpr (EPL == 4) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    out[0] = __uint_as_float(u.x << 16); out[1] = __uint_as_float(u.x & 0xffff0000u);
+    out[2] = __uint_as_float(u.y << 16); out[3] = __uint_as_float(u.y & 0xffff0000u);
+  } else if constexpr (EPL == 2) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+    out[0] = __uint_as_float(u << 16); out[1] = __uint_as_float(u & 0xffff0000u);
+  } else {
+    out[0] = bf16_to_f32(*p);
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Rows of the workgroup's token tile handled by one wave.
+constexpr int kFwdWaves = 8;
+constexpr int kTokPerWave = kRowsPerWG / kFwdWaves;   // 32: one MFMA column block
+
+// LDS layout of one embedding tile (kVocabTile rows). D = 512: one 1 KiB row per load
+// instruction, rows padded to 1040 bytes so that 16 lanes reading 16 consecutive rows at the same
+// column hit 16 different bank groups. Smaller D: dense rows with the 16-byte chunk index XORed by
+// a function of the row (global_load_lds writes each instruction's 1 KiB contiguously, so there is
+// no room for padding inside it).
+template <int D>
+struct TileLayout {
+  static constexpr int ROWB = 2 * D;
+  static constexpr bool PAD = (ROWB == 1024);
+  static constexpr int PITCH = PAD ? ROWB + 16 : ROWB;
+  static constexpr int TILEB = kVocabTile * PITCH;
+  static constexpr int RPB = (256 / ROWB) > 1 ? (256 / ROWB) : 1;
+  static constexpr int CPR = D / 8;
+  static constexpr int SWZ = CPR < 16 ? CPR : 16;
+  __device__ static int swz(int row) { return PAD ? 0 : (row / RPB) % SWZ; }
+};
+
+// Hint to interleave one 32-row block's MFMA chain (KS steps: one LDS read + one MFMA each) with
+// the epilogue of the previous block (about 6 VALU / transcendental instructions per logit).
+template <int KS, int VALU_PER_STEP>
+__device__ __forceinline__ void interleave_hint() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // two LDS reads ahead
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x402, VALU_PER_STEP, 0);  // VALU + transcendental
+  }
+}
+
+// One embedding tile from global memory into LDS buffer `buf` with global_load_lds_dwordx4
+// (1 KiB per instruction, no VGPR round trip), spread over `nwaves` waves. Rows past the end of
+// the vocabulary repeat the last row (valid memory; their logits are masked by the caller).
+template <int D, int NWAVES>
+__device__ __forceinline__ void load_embed_tile(char* smem, const uint16_t* E, int V, int tile, int buf,
+                                                int wave, int lane) {
+  using TL = TileLayout<D>;
+  constexpr int NI = kVocabTile * TL::ROWB / 1024;
+  const int v0 = tile * kVocabTile;
+#pragma unroll
+  for (int j = wave; j < NI; j += NWAVES) {
+    const int byte = j * 1024 + lane * 16;
+    const int row = byte / TL::ROWB;
+    const int pchunk = (byte % TL::ROWB) / 16;
+    const int lchunk = pchunk ^ TL::swz(row);
+    const int v = min(v0 + row, V - 1);
+    const char* g = reinterpret_cast<const char*>(E + (int64_t)v * D) + lchunk * 16;
+    char* dst = smem + buf * TL::TILEB + (TL::PAD ? j * TL::PITCH : j * 1024);
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)dst, 16, 0, 0);
+  }
+}
+
+// Z^T block: 32 vocabulary rows (vb*32 ... of LDS buffer `buf`) against this lane's token.
+// Accumulator register r holds vocabulary row 8 (r/4) + 4 h + r%4 of the block.
+template <int D>
+__device__ __forceinline__ f32x16 logit_block(const lds_char* lds, int buf, int vb, int h, int col,
+                                              const bf16x8 (&hf)[D / 16]) {
+  using TL = TileLayout<D>;
+  constexpr int KS = D / 16;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int row = vb * 32 + col;
+  const lds_char* rbase = lds + buf * TL::TILEB + row * TL::PITCH;
+  const int sw = TL::swz(row);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int chunk = (h * KS + ks) ^ sw;
+    const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(rbase + chunk * 16);
+    acc = mfma32x32x16(a, hf[ks], acc);
+  }
+  return acc;
+}
+
+// Largest |z| of a block, over the whole wave.
+__device__ __forceinline__ float wave_absmax16(const f32x16& acc) {
+  float m = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[r]));
+  return m;
+}
+
+}  // namespace pg
