@@ -15,7 +15,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpg_lmhead.so")
-SOURCES = ["pg_api.hip", "pg_fwd.hip", "pg_bwd.hip", "pg_bpb.hip"]
+SOURCES = ["pg_api.hip", "pg_fwd.hip", "pg_bwd.hip", "pg_gemm.hip", "pg_bpb.hip"]
+# Kernels that keep MFMA accumulators in VGPRs so that the hidden-row operands can live in AGPRs.
+VGPR_ACC_SOURCES = {"pg_fwd.hip", "pg_bwd.hip"}
 ARCH = "gfx950"
 
 
@@ -28,17 +30,14 @@ def hipcc() -> str:
 
 def flags() -> list[str]:
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 instructions stay off: the compiler still vectorises with plain ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument",
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libpg_lmhead.so next to this file; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *flags(), *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,6 +47,20 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}\n{res.stdout}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libpg_lmhead.so next to this file; returns its path."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        extra = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] if src in VGPR_ACC_SOURCES else []
+        _run([hipcc(), *flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -100,10 +100,7 @@ __global__ __launch_bounds__(256) void zero_unscored_kernel(const uint8_t* mask,
 //    v_mfma_f32_32x32x16_bf16 and turns it into dZ = (p - onehot) * (1 - (s/c)^2) in the epilogue,
 //    which is interleaved with the next block's MFMA chain. dZ goes to the workspace as bf16,
 //    [rows rounded up to 256][V rounded up to 64], zero in the padding.
-// 2. gemm_bf16_kernel: C = alpha * A B on 256 x 256 tiles (4 waves of 128 x 128, 16 MFMA
-//    accumulators each), 32-deep k-chunks in a 3-stage LDS ring filled by global_load_lds. An
-//    operand stored with its k index slow (dZ^T for dE, E and H for both products) is read with
-//    ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one column: no transpose pass.
+// 2. The bf16 GEMM of pg_gemm.hip forms the two products:
 //      dH = g dZ E      A = dZ [rows][V] (k = v contiguous), B = E [V][D]
 //      dE = g dZ^T H    A = dZ read transposed, B = H rows (gathered through the scored-row list)
 //    dE splits k over several workgroups; a final kernel adds the partial tiles in a fixed order.
@@ -126,20 +123,23 @@ struct DzParams {
 template <int D, bool CAPPED>
 struct DzCore {
   static constexpr int KS = D / 16;
+  static constexpr int NB = kTokBlocks;
   const lds_char* lds;
   int h, col, V;
   Softcap sc;
-  bf16x8 hf[KS];
-  float bias;      // -lse * log2 e of this lane's row (-inf for padding rows)
-  int ytok;        // target of this lane's row (never matches for padding rows)
-  uint16_t* dzrow;
+  bf16x8 hf[NB][KS];
+  float bias[NB];      // -lse * log2 e of this lane's rows (-inf for padding rows)
+  int ytok[NB];        // targets of this lane's rows (never matching for padding rows)
+  uint16_t* dzrow[NB];
 
-  __device__ __forceinline__ f32x16 chain(int buf, int vb) const { return logit_block<D>(lds, buf, vb, h, col, hf); }
+  __device__ __forceinline__ void chain(int buf, int vb, f32x16 (&acc)[NB]) const {
+    logit_blocks<D>(lds, buf, vb, h, col, hf, acc);
+  }
 
   // mode 0: series softcap (|z| <= c/8), 1: exact softcap, 2: no cap
   template <int MODE, bool MASKED>
-  __device__ __forceinline__ void store_block(const f32x16& acc, int vbase) const {
-    const int dy = ytok - vbase;
+  __device__ __forceinline__ void store_block(const f32x16& acc, int vbase, int tb) const {
+    const int dy = ytok[tb] - vbase;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float vals[4];
@@ -152,19 +152,19 @@ struct DzCore {
         if (MODE == 0) {
           const float u = z * z;
           const float s2 = z * __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(sc.q3, u, sc.q2), u, sc.q1), u, sc.q0);
-          p = fexp2(s2 + bias);
+          p = fexp2(s2 + bias[tb]);
           const float t = s2 * sc.invM;              // s / c = tanh(z / c)
           slope = __builtin_fmaf(-t, t, 1.0f);
         } else if (MODE == 1) {
           const float rk = capped_shifted(z, sc.alpha, sc.invK);   // K r, r = 1 / (1 + e^(2z/c))
-          p = fexp2(rk + (sc.M + bias));
+          p = fexp2(rk + (sc.M + bias[tb]));
           const float rr = rk * sc.invK;
           slope = rr * __builtin_fmaf(-4.0f, rr, 4.0f);             // 4 r (1 - r) = 1 - tanh^2
         } else {
-          p = fexp2(__builtin_fmaf(z, kLog2e, bias));
+          p = fexp2(__builtin_fmaf(z, kLog2e, bias[tb]));
           slope = 1.0f;
         }
-        float g = (off == dy) ? p - 1.0f : p;
+        const float g = (off == dy) ? p - 1.0f : p;
         float val = g * slope;
         if (MASKED) val = (vbase + off < V) ? val : 0.0f;
         vals[e] = val;
@@ -173,37 +173,50 @@ struct DzCore {
       bf16x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = (__bf16)vals[e];
-      *reinterpret_cast<bf16x4*>(dzrow + vbase + 8 * q + 4 * h) = o;
+      *reinterpret_cast<bf16x4*>(dzrow[tb] + vbase + 8 * q + 4 * h) = o;
     }
   }
 
   template <bool MASKED>
-  __device__ __forceinline__ void store_exact(const f32x16& acc, int vbase) const {
-    if (CAPPED) store_block<1, MASKED>(acc, vbase);
-    else store_block<2, MASKED>(acc, vbase);
+  __device__ __forceinline__ void store_exact(const f32x16 (&acc)[NB], int vbase) const {
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) {
+      if (CAPPED) store_block<1, MASKED>(acc[tb], vbase, tb);
+      else store_block<2, MASKED>(acc[tb], vbase, tb);
+    }
   }
 
-  __device__ __forceinline__ f32x16 chain_with_store(int buf, int vb, const f32x16& prev, int vprev) const {
-    f32x16 a;
+  // MFMA chain of (buf, vb) with dZ of the pending full block `prev` formed and stored in the same
+  // basic block: series softcap first; blocks with some |z| > c/8 are redone exactly (the later
+  // store of the same lane to the same address wins).
+  __device__ __forceinline__ void chain_with_store(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
+                                                   int vprev) const {
+    chain(buf, vb, a);
     if (CAPPED) {
-      a = chain(buf, vb);
-      store_block<0, false>(prev, vprev);
-      const float amax = wave_absmax16(prev);
-      interleave_hint<KS, (16 * 13 + KS - 1) / KS>();
-      if (!__all(amax <= sc.thr)) store_block<1, false>(prev, vprev);
+      float amax = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) {
+        store_block<0, false>(prev[tb], vprev, tb);
+        amax = fmaxf(amax, wave_absmax16(prev[tb]));
+      }
+      interleave_hint2<KS, NB * 16 * 13>();
+      if (!__all(amax <= sc.thr)) {
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) store_block<1, false>(prev[tb], vprev, tb);
+      }
     } else {
-      a = chain(buf, vb);
-      store_block<2, false>(prev, vprev);
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) store_block<2, false>(prev[tb], vprev, tb);
     }
-    return a;
   }
 };
 
 template <int D, bool CAPPED>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dz_kernel(DzParams p) {
   using TL = TileLayout<D>;
   constexpr int KS = D / 16;
+  constexpr int NB = kTokBlocks;
   __shared__ __attribute__((aligned(1024))) char smem[2 * TL::TILEB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, col = lane & 31;
@@ -218,22 +231,23 @@ void bwd_dz_kernel(DzParams p) {
   core.col = col;
   core.V = V;
   core.sc = p.sc;
-  const int64_t tok = (int64_t)rt * kRowsPerWG + wave * kTokPerWave + col;
-  const bool valid = tok < n;
-  const int64_t ic = valid ? tok : n - 1;
-  const int64_t grow = p.rows ? (int64_t)p.rows[ic] : ic;
-  {
+#pragma unroll
+  for (int tb = 0; tb < NB; ++tb) {
+    const int64_t tok = (int64_t)rt * kRowsPerWG + wave * kTokPerWave + tb * 32 + col;
+    const bool valid = tok < n;
+    const int64_t ic = valid ? tok : n - 1;
+    const int64_t grow = p.rows ? (int64_t)p.rows[ic] : ic;
     const bf16x8* src = reinterpret_cast<const bf16x8*>(p.H + grow * D + h * (D / 2));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) core.hf[ks] = src[ks];
+    for (int ks = 0; ks < KS; ++ks) core.hf[tb][ks] = src[ks];
+    core.bias[tb] = valid ? -p.lse[grow] * kLog2e : -INFINITY;
+    core.ytok[tb] = valid ? p.target[grow] : -(1 << 30);
+    core.dzrow[tb] = p.dz + tok * p.ldz;
   }
-  core.bias = valid ? -p.lse[grow] * kLog2e : -INFINITY;
-  core.ytok = valid ? p.target[grow] : -(1 << 30);
-  core.dzrow = p.dz + tok * p.ldz;
 
   const int ntiles = p.n_vtiles;
   const bool last_partial = (V % kVocabTile) != 0;
-  f32x16 accp;
+  f32x16 accp[NB];
   int vprev = -1;
   load_embed_tile<D, kFwdWaves>(smem, p.E, V, 0, 0, wave, lane);
   for (int i = 0; i < ntiles; ++i) {
@@ -242,193 +256,26 @@ void bwd_dz_kernel(DzParams p) {
     __syncthreads();
     if (i + 1 < ntiles) load_embed_tile<D, kFwdWaves>(smem, p.E, V, i + 1, buf ^ 1, wave, lane);
     const int vb0 = i * kVocabTile;
+    f32x16 a0[NB];
     if (last_partial && i + 1 == ntiles) {
-      const f32x16 a0 = core.chain(buf, 0);
+      core.chain(buf, 0, a0);
       if (vprev >= 0) core.template store_exact<false>(accp, vprev);
-      const f32x16 a1 = core.chain(buf, 1);
+      f32x16 a1[NB];
+      core.chain(buf, 1, a1);
       core.template store_exact<true>(a0, vb0);
       if (vb0 + 32 < p.ldz) core.template store_exact<true>(a1, vb0 + 32);
       vprev = -1;
     } else if (vprev < 0) {
-      const f32x16 a0 = core.chain(buf, 0);
-      accp = core.chain_with_store(buf, 1, a0, vb0);
+      core.chain(buf, 0, a0);
+      core.chain_with_store(buf, 1, accp, a0, vb0);
       vprev = vb0 + 32;
     } else {
-      const f32x16 a0 = core.chain_with_store(buf, 0, accp, vprev);
-      accp = core.chain_with_store(buf, 1, a0, vb0);
+      core.chain_with_store(buf, 0, a0, accp, vprev);
+      core.chain_with_store(buf, 1, accp, a0, vb0);
       vprev = vb0 + 32;
     }
   }
   if (vprev >= 0) core.template store_exact<false>(accp, vprev);
-}
-
-// ------------------------------------------------------------------------------- bf16 GEMM
-constexpr int kGemmBM = 256, kGemmBN = 256, kGemmBK = 32, kGemmStages = 3;
-
-struct GemmParams {
-  const uint16_t* A;      // element (m, k): A_TRANS ? A[k * lda + m] : A[m * lda + k]
-  int64_t lda;
-  const uint16_t* B;      // element (k, n): B[krow(k) * ldb + n]
-  int64_t ldb;
-  const int32_t* brows;   // krow(k) = brows[k] when given, else k
-  const int32_t* n_dev;   // device count that replaces M (m_dev) or K (k_dev)
-  int m_dev, k_dev;
-  int64_t M, N, K;        // sizes (upper bounds when taken from n_dev)
-  int64_t kvalid;         // rows of B that exist (host bound; clamped below the device count)
-  float alpha;
-  float* C;
-  int64_t ldc;
-  const int32_t* crows;   // output row of m when given
-  int64_t split_stride;   // elements between the partial outputs of k splits
-};
-
-// LDS tile layouts (bytes):
-//   k-contiguous A: [256 m][32 k], 64 B rows; 16-byte chunk c of row m stored at c ^ ((m >> 2) & 3)
-//   k-slow A or B: [32 k][256 m|n], 512 B rows; chunk c of row k stored at c ^ (4 (k & 3))
-// Both keep the 16 lanes of an LDS read phase on 16 different 16-byte bank groups.
-template <bool A_TRANS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_bf16_kernel(GemmParams g) {
-  constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2, SBYTES = ABYTES + BBYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[kGemmStages * SBYTES];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  const int64_t ndev = g.n_dev ? (int64_t)(*g.n_dev) : 0;
-  const int64_t M = g.m_dev ? ndev : g.M;
-  const int64_t K = g.k_dev ? ndev : g.K;
-  const int64_t m0 = (int64_t)blockIdx.x * BM;
-  const int64_t n0 = (int64_t)blockIdx.y * BN;
-  if (m0 >= M) return;
-  const int64_t kchunks = (K + BK - 1) / BK;
-  const int nsplit = gridDim.z;
-  const int64_t cps = (kchunks + nsplit - 1) / nsplit;
-  const int64_t kc_begin = (int64_t)blockIdx.z * cps;
-  const int64_t kc_end = kc_begin + cps < kchunks ? kc_begin + cps : kchunks;
-  const int64_t nk = kc_end > kc_begin ? kc_end - kc_begin : 0;
-  const int64_t kvalid = g.k_dev ? ndev : g.kvalid;
-
-  // ---- stage loader: 32 global_load_lds_dwordx4 per stage, 8 per wave
-  auto load_stage = [&](int64_t kc, int st) {
-    char* sA = smem + st * SBYTES;
-    char* sB = sA + ABYTES;
-    const int64_t k0 = kc * BK;
-#pragma unroll
-    for (int j = wave; j < 16; j += 4) {
-      const uint16_t* src;
-      if (!A_TRANS) {
-        const int row = 16 * j + (lane >> 2);
-        const int lc = (lane & 3) ^ ((row >> 2) & 3);
-        int64_t m = m0 + row;
-        m = m < M ? m : M - 1;
-        src = g.A + m * g.lda + k0 + 8 * lc;
-      } else {
-        const int row = 2 * j + (lane >> 5);
-        const int lc = (lane & 31) ^ (4 * (row & 3));
-        int64_t col = m0 + 8 * lc;
-        col = col <= g.lda - 8 ? col : g.lda - 8;
-        src = g.A + (k0 + row) * g.lda + col;
-      }
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(sA + j * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int j = wave; j < 16; j += 4) {
-      const int row = 2 * j + (lane >> 5);
-      const int lc = (lane & 31) ^ (4 * (row & 3));
-      int64_t k = k0 + row;
-      k = k < kvalid ? k : kvalid - 1;
-      const int64_t krow = g.brows ? (int64_t)g.brows[k] : k;
-      int64_t col = n0 + 8 * lc;
-      col = col <= g.ldb - 8 ? col : g.ldb - 8;
-      __builtin_amdgcn_global_load_lds(g.B + krow * g.ldb + col, (lds_void*)(sB + j * 1024), 16, 0, 0);
-    }
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int grp = lane >> 4, li = lane & 15;
-  // transposed-read lane address inside a [32 k][256] tile: row k0 + li / 4, columns
-  // cbase + 16 (grp & 1) + 4 (li & 3) .. + 3, for k0 = 16 ks + 8 (grp >> 1) + 4 half
-  auto tr_addr = [&](int ks, int half, int cbase) -> int {
-    const int k = 16 * ks + 8 * (grp >> 1) + 4 * half + (li >> 2);
-    const int c = cbase + 16 * (grp & 1) + 4 * (li & 3);
-    return k * 512 + 16 * ((c >> 3) ^ (4 * (k & 3))) + 2 * (c & 7);
-  };
-  auto read_tr = [&](const char* tile, int ks, int cbase) -> bf16x8 {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tr_addr(ks, 0, cbase)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tr_addr(ks, 1, cbase)));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-  };
-
-  if (nk > 0) load_stage(kc_begin, 0);
-  if (nk > 1) load_stage(kc_begin + 1, 1);
-  for (int64_t it = 0; it < nk; ++it) {
-    if (it + 1 < nk) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (it + 2 < nk) load_stage(kc_begin + it + 2, (int)((it + 2) % kGemmStages));
-    const int st = (int)(it % kGemmStages);
-    const char* sA = smem + st * SBYTES;
-    const char* sB = sA + ABYTES;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        const int mb = wm * 128 + bm * 32;
-        if (!A_TRANS) {
-          const int row = mb + (lane & 31);
-          const int chunk = (2 * ks + h) ^ ((row >> 2) & 3);
-          af[bm] = *(const __attribute__((address_space(3))) bf16x8*)((const lds_char*)sA + row * 64 + chunk * 16);
-        } else {
-          af[bm] = read_tr(sA, ks, mb);
-        }
-      }
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn) bfr[bn] = read_tr(sB, ks, wn * 128 + bn * 32);
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma32x32x16(af[bm], bfr[bn], acc[bm][bn]);
-    }
-  }
-
-  // ---- epilogue: alpha * acc to C (row-scattered) or to this split's partial tile
-  float* C = g.C + (int64_t)blockIdx.z * g.split_stride;
-#pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const int64_t n = n0 + wn * 128 + bn * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 128 + bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M && n < g.N) {
-          const int64_t crow = g.crows ? (int64_t)g.crows[m] : m;
-          C[crow * g.ldc + n] = g.alpha * acc[bm][bn][r];
-        }
-      }
-    }
-}
-
-// out[i] = sum over s of part[s * stride + i], in split order.
-__global__ __launch_bounds__(256) void sum_splits_kernel(const float* part, int nsplit, int64_t stride, int64_t count,
-                                                         float* out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= count) return;
-  float s = 0.f;
-  for (int k = 0; k < nsplit; ++k) s += part[(int64_t)k * stride + i];
-  out[i] = s;
 }
 
 // ------------------------------------------------------------------------------------ host side
@@ -512,21 +359,15 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
       a.M = T; a.N = D; a.K = V; a.kvalid = V;
       a.alpha = grad_scale;
       a.C = dH; a.ldc = D; a.crows = rows; a.split_stride = 0;
-      hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3(rblk, (unsigned)((D + kGemmBN - 1) / kGemmBN), 1), dim3(256),
-                         0, st, a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      e = launch_gemm(a, false, dim3(rblk, (unsigned)((D + kGemmBN - 1) / kGemmBN), 1), st);
+      if (e != hipSuccess) return e;
     }
     // dE = g dZ^T H, k split over workgroups when the output has few tiles
     const int64_t tiles = ((int64_t)(V + kGemmBM - 1) / kGemmBM) * ((D + kGemmBN - 1) / kGemmBN);
     const int ncu = dev.cu_count > 0 ? dev.cu_count : 256;
     int64_t ks = ncu / (tiles > 0 ? tiles : 1);
     ks = ks < 1 ? 1 : (ks > kDeSplit ? kDeSplit : ks);
-    if (T == 0) {
-      const int64_t cnt = (int64_t)V * D;
-      hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st,
-                         (const float*)nullptr, 0, cnt, cnt, dE);
-      return hipGetLastError();
-    }
+    if (T == 0) return launch_sum_splits(nullptr, 0, (int64_t)V * D, (int64_t)V * D, dE, st);
     float* part = reinterpret_cast<float*>(ws + L.de_part);
     GemmParams b{};
     b.A = dz; b.lda = ((V + kVocabTile - 1) / kVocabTile) * (int64_t)kVocabTile;
@@ -536,14 +377,10 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     b.M = V; b.N = D; b.K = T; b.kvalid = T;
     b.alpha = grad_scale;
     b.C = ks > 1 ? part : dE; b.ldc = D; b.crows = nullptr; b.split_stride = (int64_t)V * D;
-    hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3((unsigned)((V + kGemmBM - 1) / kGemmBM),
-                       (unsigned)((D + kGemmBN - 1) / kGemmBN), (unsigned)ks), dim3(256), 0, st, b);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_gemm(b, true, dim3((unsigned)((V + kGemmBM - 1) / kGemmBM),
+                                             (unsigned)((D + kGemmBN - 1) / kGemmBN), (unsigned)ks), st);
     if (e != hipSuccess || ks == 1) return e;
-    const int64_t cnt = (int64_t)V * D;
-    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, part, (int)ks,
-                       cnt, cnt, dE);
-    return hipGetLastError();
+    return launch_sum_splits(part, (int)ks, (int64_t)V * D, (int64_t)V * D, dE, st);
   }
   const unsigned rblocks = (unsigned)((T + 3) / 4);
   const unsigned hblocks = (unsigned)((T * D + 255) / 256);

@@ -6,9 +6,10 @@
 // reach memory.
 //
 // Kernel layout (bf16, D in {32..512}):
-//   * one workgroup = 8 waves (two per SIMD) = 256 token rows; each wave keeps the bf16 hidden
-//     rows of its 32 tokens in registers as the B operand of v_mfma_f32_32x32x16_bf16 (lane l:
-//     token l % 32, half l / 32 of the hidden width);
+//   * one workgroup = 4 waves (one per SIMD) = 256 token rows; each wave keeps the bf16 hidden
+//     rows of its 64 tokens in registers (VGPRs and AGPRs) as the B operands of
+//     v_mfma_f32_32x32x16_bf16 (lane l: token l % 32 of each 32-token block, half l / 32 of the
+//     hidden width), so every embedding fragment read from LDS feeds two MFMAs;
 //   * the embedding streams through LDS in tiles of 64 vocabulary rows, double-buffered, loaded
 //     with global_load_lds_dwordx4 (no VGPR round trip) into a XOR-swizzled layout;
 //   * each 32 x 32 accumulator holds 16 vocabulary rows of one token per lane, so the softcap and
@@ -55,16 +56,19 @@ __device__ __forceinline__ int device_splits(int64_t n, int n_vtiles, int grid) 
 template <int D, bool FIXED>
 struct FwdCore {
   static constexpr int KS = D / 16;
+  static constexpr int NB = kTokBlocks;
   const lds_char* lds;
   int h, col, V;
   Softcap sc;
-  bf16x8 hf[KS];
-  float lsum = 0.f;
-  float mrun = -INFINITY;
+  bf16x8 hf[NB][KS];
+  float lsum[NB];
+  float mrun[NB];
 
-  __device__ __forceinline__ f32x16 chain(int buf, int vb) const { return logit_block<D>(lds, buf, vb, h, col, hf); }
+  __device__ __forceinline__ void chain(int buf, int vb, f32x16 (&acc)[NB]) const {
+    logit_blocks<D>(lds, buf, vb, h, col, hf, acc);
+  }
 
-  // Exp-sum of one block with the fixed shift M, by the tanh series (valid when |z| <= c/8).
+  // Exp-sum with the fixed shift M by the tanh series (valid when |z| <= c/8).
   __device__ __forceinline__ float part_series(const f32x16& acc) const {
     float part = 0.f;
 #pragma unroll
@@ -77,7 +81,7 @@ struct FwdCore {
     return part;
   }
 
-  // Exp-sum of one block with the fixed shift M, exact softcap. Register r holds vocabulary row
+  // Exp-sum with the fixed shift M, exact softcap. Register r holds vocabulary row
   // vbase + 8 (r/4) + 4 h + r%4; MASKED drops rows >= V.
   template <bool MASKED>
   __device__ __forceinline__ float part_exact(const f32x16& acc, int vbase) const {
@@ -97,7 +101,7 @@ struct FwdCore {
 
   // Running-maximum variant for c = 0 and caps above the fixed-shift range.
   template <bool MASKED>
-  __device__ __forceinline__ void epilogue_online(const f32x16& acc, int vbase) {
+  __device__ __forceinline__ void online(const f32x16& acc, int vbase, int tb) {
     float s2[16];
     float bm = -INFINITY;
 #pragma unroll
@@ -106,50 +110,64 @@ struct FwdCore {
       s2[r] = (!MASKED || v < V) ? capped_log2(acc[r], sc) : -INFINITY;
       bm = fmaxf(bm, s2[r]);
     }
-    const float mn = fmaxf(mrun, bm);
+    const float mn = fmaxf(mrun[tb], bm);
     if (mn != -INFINITY) {
       float part = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) part += fexp2(s2[r] - mn);
-      lsum = lsum * fexp2(mrun - mn) + part;
-      mrun = mn;
+      lsum[tb] = lsum[tb] * fexp2(mrun[tb] - mn) + part;
+      mrun[tb] = mn;
     }
   }
 
-  // Epilogue of a block outside the interleaved main loop (first/last/partial blocks).
+  // Epilogue outside the interleaved steady state (first, last and partial blocks).
   template <bool MASKED>
-  __device__ __forceinline__ void epilogue(const f32x16& acc, int vbase) {
-    if (FIXED) lsum += part_exact<MASKED>(acc, vbase);
-    else epilogue_online<MASKED>(acc, vbase);
+  __device__ __forceinline__ void epilogue(const f32x16 (&acc)[NB], int vbase) {
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) {
+      if (FIXED) lsum[tb] += part_exact<MASKED>(acc[tb], vbase);
+      else online<MASKED>(acc[tb], vbase, tb);
+    }
   }
 
-  // MFMA chain of block (buf, vb) with the epilogue of the pending full block `prev` interleaved in
-  // one basic block. The series is computed speculatively; if any |z| of `prev` exceeds c/8 (a
-  // wave-uniform, rarely taken branch) the block's sum is recomputed with the exact softcap.
-  __device__ __forceinline__ f32x16 chain_with_epilogue(int buf, int vb, const f32x16& prev, int vprev) {
-    f32x16 a;
+  // MFMA chain of block (buf, vb) with the epilogue of the pending full block `prev` in the same
+  // basic block. The series sum is computed speculatively; when some |z| of `prev` exceeds c/8 (a
+  // wave-uniform, rarely taken branch) the exact sum replaces it.
+  __device__ __forceinline__ void chain_with_epilogue(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
+                                                      int vprev) {
     if (FIXED) {
-      a = chain(buf, vb);
-      const float part = part_series(prev);
-      const float amax = wave_absmax16(prev);
-      lsum += part;
-      interleave_hint<KS, (16 * 8 + KS - 1) / KS>();
-      if (!__all(amax <= sc.thr)) lsum += part_exact<false>(prev, vprev) - part;
+      chain(buf, vb, a);
+      float part[NB];
+      float amax = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) {
+        part[tb] = part_series(prev[tb]);
+        amax = fmaxf(amax, wave_absmax16(prev[tb]));
+      }
+      interleave_hint2<KS, NB * 16 * 8>();
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) asm volatile("" ::"v"(part[tb]));   // keep the speculation here
+      if (!__all(amax <= sc.thr)) {
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) part[tb] = part_exact<false>(prev[tb], vprev);
+      }
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) lsum[tb] += part[tb];
     } else {
-      a = chain(buf, vb);
-      epilogue_online<false>(prev, vprev);
+      chain(buf, vb, a);
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) online<false>(prev[tb], vprev, tb);
     }
-    return a;
   }
 };
 
 template <int D, bool FIXED>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_mfma_kernel(FwdParams p) {
   using TL = TileLayout<D>;
   constexpr int KS = D / 16;
+  constexpr int NB = kTokBlocks;
   constexpr int EPL = D >= 64 ? D / 64 : 1;           // hidden elements per lane in the target dot
-  static_assert(kTokPerWave == 32, "one 32-token MFMA block per wave");
   __shared__ __attribute__((aligned(1024))) char smem[2 * TL::TILEB];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -167,8 +185,9 @@ void fwd_mfma_kernel(FwdParams p) {
   const int V = p.V;
   const int64_t tok0 = (int64_t)rt * kRowsPerWG + wave * kTokPerWave;   // first token of this wave
 
-  // ---- target logit (split 0 only): lanes span the hidden width, 8 tokens per batch
-  float sy = 0.f;
+  // ---- target logit (split 0 only): lanes span the hidden width, 8 tokens per batch; the lane
+  //      of token j within a 32-token block keeps it
+  float sy[NB] = {};
   if (split == 0) {
     for (int j0 = 0; j0 < kTokPerWave; j0 += 8) {
       float part[8];
@@ -193,7 +212,11 @@ void fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float zy = wave_sum(part[j]);
-        if (col == j0 + j) sy = ((okm >> j) & 1) ? capped_log2(zy, p.sc) : __builtin_nanf("");
+        const int t = j0 + j;
+        const float v = ((okm >> j) & 1) ? capped_log2(zy, p.sc) : __builtin_nanf("");
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+          if (t == tb * 32 + col) sy[tb] = v;
       }
     }
   }
@@ -205,14 +228,18 @@ void fwd_mfma_kernel(FwdParams p) {
   core.V = V;
   core.sc = p.sc;
 
-  // ---- this lane's token: hidden row half into registers (B operand of the MFMA)
-  const int64_t tok = tok0 + col;
-  const int64_t ic = tok < n ? tok : n - 1;
-  const int64_t grow = p.rows ? (int64_t)p.rows[ic] : ic;
-  {
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(p.H + grow * D + h * (D / 2));
+  // ---- this lane's tokens: hidden row halves into registers (B operands of the MFMA)
+  int64_t tok[NB], grow[NB];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) core.hf[ks] = src[ks];
+  for (int tb = 0; tb < NB; ++tb) {
+    core.lsum[tb] = 0.f;
+    core.mrun[tb] = -INFINITY;
+    tok[tb] = tok0 + tb * 32 + col;
+    const int64_t ic = tok[tb] < n ? tok[tb] : n - 1;
+    grow[tb] = p.rows ? (int64_t)p.rows[ic] : ic;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(p.H + grow[tb] * D + h * (D / 2));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) core.hf[tb][ks] = src[ks];
   }
 
   // ---- main loop. Only the last tile of the vocabulary can be partial; it runs the masked
@@ -220,7 +247,7 @@ void fwd_mfma_kernel(FwdParams p) {
   //      MFMA chain of the current one.
   const int ntiles = t_end - t_begin;
   const bool last_partial = (t_end == p.n_vtiles) && (V % kVocabTile != 0);
-  f32x16 accp;
+  f32x16 accp[NB];
   int vprev = -1;
   if (ntiles > 0) load_embed_tile<D, kFwdWaves>(smem, p.E, V, t_begin, 0, wave, lane);
   for (int i = 0; i < ntiles; ++i) {
@@ -230,28 +257,31 @@ void fwd_mfma_kernel(FwdParams p) {
     __syncthreads();
     if (i + 1 < ntiles) load_embed_tile<D, kFwdWaves>(smem, p.E, V, tile + 1, buf ^ 1, wave, lane);
     const int vb0 = tile * kVocabTile;
+    f32x16 a0[NB];
     if (last_partial && i + 1 == ntiles) {
-      const f32x16 a0 = core.chain(buf, 0);
+      core.chain(buf, 0, a0);
       if (vprev >= 0) core.template epilogue<false>(accp, vprev);
-      const f32x16 a1 = core.chain(buf, 1);
+      f32x16 a1[NB];
+      core.chain(buf, 1, a1);
       core.template epilogue<true>(a0, vb0);
       core.template epilogue<true>(a1, vb0 + 32);
       vprev = -1;
     } else if (vprev < 0) {
-      const f32x16 a0 = core.chain(buf, 0);
-      accp = core.chain_with_epilogue(buf, 1, a0, vb0);
+      core.chain(buf, 0, a0);
+      core.chain_with_epilogue(buf, 1, accp, a0, vb0);
       vprev = vb0 + 32;
     } else {
-      const f32x16 a0 = core.chain_with_epilogue(buf, 0, accp, vprev);
-      accp = core.chain_with_epilogue(buf, 1, a0, vb0);
+      core.chain_with_epilogue(buf, 0, a0, accp, vprev);
+      core.chain_with_epilogue(buf, 1, accp, a0, vb0);
       vprev = vb0 + 32;
     }
   }
   if (vprev >= 0) core.template epilogue<false>(accp, vprev);
 
   // ---- combine the two lane halves (each holds 16 of every 32 vocabulary rows) and write out
-  {
-    float l = core.lsum, m = core.mrun;
+#pragma unroll
+  for (int tb = 0; tb < NB; ++tb) {
+    float l = core.lsum[tb], m = core.mrun[tb];
     const float l2 = __shfl_xor(l, 32);
     if (FIXED) {
       l += l2;
@@ -259,15 +289,15 @@ void fwd_mfma_kernel(FwdParams p) {
       const float m2 = __shfl_xor(m, 32);
       lse_merge(m, l, m2, l2);
     }
-    if (h == 0 && tok < n) {
+    if (h == 0 && tok[tb] < n) {
       if (p.direct) {
         const float lse2 = (FIXED ? p.sc.M : m) + flog2(l);
-        p.nats[grow] = kLn2 * (lse2 - sy);
-        if (p.lse) p.lse[grow] = kLn2 * lse2;
+        p.nats[grow[tb]] = kLn2 * (lse2 - sy[tb]);
+        if (p.lse) p.lse[grow[tb]] = kLn2 * lse2;
       } else {
-        p.part_l[(int64_t)split * n + tok] = l;
-        if (!FIXED) p.part_m[(int64_t)split * n + tok] = m;
-        if (split == 0) p.s_target[tok] = sy;
+        p.part_l[(int64_t)split * n + tok[tb]] = l;
+        if (!FIXED) p.part_m[(int64_t)split * n + tok[tb]] = m;
+        if (split == 0) p.s_target[tok[tb]] = sy[tb];
       }
     }
   }

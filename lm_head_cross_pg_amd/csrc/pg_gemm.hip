@@ -1,0 +1,179 @@
+// bf16 GEMM with float32 accumulation for the two products of the backward, dH = g dZ E and
+// dE = g dZ^T H, on gfx950 (v_mfma_f32_32x32x16_bf16).
+//
+// 256 x 256 output tiles per workgroup (4 waves of 128 x 128, sixteen 32 x 32 accumulators each,
+// held in AGPRs), 32-deep k-chunks in a 3-stage LDS ring filled by global_load_lds_dwordx4. An
+// operand whose k index is the slow one in memory (dZ read as dZ^T, E and H as k x n) is fed to
+// the MFMA with ds_read_b64_tr_b16, which gives each lane 4 consecutive k of one column, so no
+// transpose pass over memory is needed.
+#include "pg_common.h"
+#include "pg_internal.h"
+
+namespace pg {
+
+
+
+// LDS tile layouts (bytes):
+//   k-contiguous A: [256 m][32 k], 64 B rows; 16-byte chunk c of row m stored at c ^ ((m >> 2) & 3)
+//   k-slow A or B: [32 k][256 m|n], 512 B rows; chunk c of row k stored at c ^ (4 (k & 3))
+// Both keep the 16 lanes of an LDS read phase on 16 different 16-byte bank groups.
+template <bool A_TRANS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_kernel(GemmParams g) {
+  constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
+  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2, SBYTES = ABYTES + BBYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[kGemmStages * SBYTES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int64_t ndev = g.n_dev ? (int64_t)(*g.n_dev) : 0;
+  const int64_t M = g.m_dev ? ndev : g.M;
+  const int64_t K = g.k_dev ? ndev : g.K;
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int64_t n0 = (int64_t)blockIdx.y * BN;
+  if (m0 >= M) return;
+  const int64_t kchunks = (K + BK - 1) / BK;
+  const int nsplit = gridDim.z;
+  const int64_t cps = (kchunks + nsplit - 1) / nsplit;
+  const int64_t kc_begin = (int64_t)blockIdx.z * cps;
+  const int64_t kc_end = kc_begin + cps < kchunks ? kc_begin + cps : kchunks;
+  const int64_t nk = kc_end > kc_begin ? kc_end - kc_begin : 0;
+  const int64_t kvalid = g.k_dev ? ndev : g.kvalid;
+
+  // ---- stage loader: 32 global_load_lds_dwordx4 per stage, 8 per wave
+  auto load_stage = [&](int64_t kc, int st) {
+    char* sA = smem + st * SBYTES;
+    char* sB = sA + ABYTES;
+    const int64_t k0 = kc * BK;
+#pragma unroll
+    for (int j = wave; j < 16; j += 4) {
+      const uint16_t* src;
+      if (!A_TRANS) {
+        const int row = 16 * j + (lane >> 2);
+        const int lc = (lane & 3) ^ ((row >> 2) & 3);
+        int64_t m = m0 + row;
+        m = m < M ? m : M - 1;
+        src = g.A + m * g.lda + k0 + 8 * lc;
+      } else {
+        const int row = 2 * j + (lane >> 5);
+        const int lc = (lane & 31) ^ (4 * (row & 3));
+        int64_t col = m0 + 8 * lc;
+        col = col <= g.lda - 8 ? col : g.lda - 8;
+        src = g.A + (k0 + row) * g.lda + col;
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(sA + j * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = wave; j < 16; j += 4) {
+      const int row = 2 * j + (lane >> 5);
+      const int lc = (lane & 31) ^ (4 * (row & 3));
+      int64_t k = k0 + row;
+      k = k < kvalid ? k : kvalid - 1;
+      const int64_t krow = g.brows ? (int64_t)g.brows[k] : k;
+      int64_t col = n0 + 8 * lc;
+      col = col <= g.ldb - 8 ? col : g.ldb - 8;
+      __builtin_amdgcn_global_load_lds(g.B + krow * g.ldb + col, (lds_void*)(sB + j * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int grp = lane >> 4, li = lane & 15;
+  // transposed-read lane address inside a [32 k][256] tile: row k0 + li / 4, columns
+  // cbase + 16 (grp & 1) + 4 (li & 3) .. + 3, for k0 = 16 ks + 8 (grp >> 1) + 4 half
+  auto tr_addr = [&](int ks, int half, int cbase) -> int {
+    const int k = 16 * ks + 8 * (grp >> 1) + 4 * half + (li >> 2);
+    const int c = cbase + 16 * (grp & 1) + 4 * (li & 3);
+    return k * 512 + 16 * ((c >> 3) ^ (4 * (k & 3))) + 2 * (c & 7);
+  };
+  auto read_tr = [&](const char* tile, int ks, int cbase) -> bf16x8 {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tr_addr(ks, 0, cbase)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tr_addr(ks, 1, cbase)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  if (nk > 0) load_stage(kc_begin, 0);
+  if (nk > 1) load_stage(kc_begin + 1, 1);
+  for (int64_t it = 0; it < nk; ++it) {
+    if (it + 1 < nk) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 2 < nk) load_stage(kc_begin + it + 2, (int)((it + 2) % kGemmStages));
+    const int st = (int)(it % kGemmStages);
+    const char* sA = smem + st * SBYTES;
+    const char* sB = sA + ABYTES;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) {
+        const int mb = wm * 128 + bm * 32;
+        if (!A_TRANS) {
+          const int row = mb + (lane & 31);
+          const int chunk = (2 * ks + h) ^ ((row >> 2) & 3);
+          af[bm] = *(const __attribute__((address_space(3))) bf16x8*)((const lds_char*)sA + row * 64 + chunk * 16);
+        } else {
+          af[bm] = read_tr(sA, ks, mb);
+        }
+      }
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) bfr[bn] = read_tr(sB, ks, wn * 128 + bn * 32);
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma32x32x16(af[bm], bfr[bn], acc[bm][bn]);
+    }
+  }
+
+  // ---- epilogue: alpha * acc to C (row-scattered) or to this split's partial tile
+  float* C = g.C + (int64_t)blockIdx.z * g.split_stride;
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      const int64_t n = n0 + wn * 128 + bn * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 128 + bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < M && n < g.N) {
+          const int64_t crow = g.crows ? (int64_t)g.crows[m] : m;
+          C[crow * g.ldc + n] = g.alpha * acc[bm][bn][r];
+        }
+      }
+    }
+}
+
+// out[i] = sum over s of part[s * stride + i], in split order.
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* part, int nsplit, int64_t stride, int64_t count,
+                                                         float* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float s = 0.f;
+  for (int k = 0; k < nsplit; ++k) s += part[(int64_t)k * stride + i];
+  out[i] = s;
+}
+
+
+hipError_t launch_gemm(const GemmParams& g, bool a_trans, dim3 grid, hipStream_t st) {
+  if (a_trans) hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, dim3(256), 0, st, g);
+  else hipLaunchKernelGGL(gemm_bf16_kernel<false>, grid, dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_splits(const float* part, int nsplit, int64_t stride, int64_t count, float* out,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, part, nsplit,
+                     stride, count, out);
+  return hipGetLastError();
+}
+
+}  // namespace pg

@@ -56,6 +56,31 @@ hipError_t launch_bpb(const float* nats, const int32_t* target, const uint8_t* m
                       const int32_t* byte_len, const int32_t* byte_per_pos, int64_t T, int32_t V,
                       double* out, char* ws, hipStream_t st);
 
+// C = alpha * A B in bf16 with float32 accumulation (pg_gemm.hip).
+constexpr int kGemmBM = 256, kGemmBN = 256, kGemmBK = 32, kGemmStages = 3;
+struct GemmParams {
+  const uint16_t* A;      // element (m, k): A_TRANS ? A[k * lda + m] : A[m * lda + k]
+  int64_t lda;
+  const uint16_t* B;      // element (k, n): B[krow(k) * ldb + n]
+  int64_t ldb;
+  const int32_t* brows;   // krow(k) = brows[k] when given, else k
+  const int32_t* n_dev;   // device count that replaces M (m_dev) or K (k_dev)
+  int m_dev, k_dev;
+  int64_t M, N, K;        // sizes (upper bounds when taken from n_dev)
+  int64_t kvalid;         // rows of B that exist (host bound; clamped below the device count)
+  float alpha;
+  float* C;
+  int64_t ldc;
+  const int32_t* crows;   // output row of m when given
+  int64_t split_stride;   // elements between the partial outputs of k splits
+};
+// a_trans: A's element (m, k) is A[k * lda + m] (else A[m * lda + k]). grid = (m tiles, n tiles,
+// k splits); with several splits, C receives one partial output per split at split_stride.
+hipError_t launch_gemm(const GemmParams& g, bool a_trans, dim3 grid, hipStream_t st);
+// out[i] = sum over s < nsplit of part[s * stride + i], in split order (nsplit = 0 writes zeros).
+hipError_t launch_sum_splits(const float* part, int nsplit, int64_t stride, int64_t count, float* out,
+                             hipStream_t st);
+
 // True when the bf16 MFMA kernels cover this hidden width.
 inline bool mfma_width(int32_t D) {
   return D == 32 || D == 64 || D == 128 || D == 256 || D == 512;

@@ -31,9 +31,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Rows of the workgroup's token tile handled by one wave.
-constexpr int kFwdWaves = 8;
-constexpr int kTokPerWave = kRowsPerWG / kFwdWaves;   // 32: one MFMA column block
+// Rows of the workgroup's token tile handled by one wave: two 32-token MFMA column blocks, so
+// every embedding fragment read from LDS feeds two MFMAs (one wave per SIMD, hidden rows of 64
+// tokens held in VGPRs and AGPRs).
+constexpr int kFwdWaves = 4;
+constexpr int kTokPerWave = kRowsPerWG / kFwdWaves;   // 64
+constexpr int kTokBlocks = kTokPerWave / 32;          // 2
 
 // LDS layout of one embedding tile (kVocabTile rows). D = 512: one 1 KiB row per load
 // instruction, rows padded to 1040 bytes so that 16 lanes reading 16 consecutive rows at the same
@@ -87,16 +90,37 @@ __device__ __forceinline__ void load_embed_tile(char* smem, const uint16_t* E, i
   }
 }
 
-// Z^T block: 32 vocabulary rows (vb*32 ... of LDS buffer `buf`) against this lane's token.
-// Accumulator register r holds vocabulary row 8 (r/4) + 4 h + r%4 of the block.
+// v_mfma_f32_32x32x16_bf16 with the B operand (hidden rows) read straight from AGPRs and the
+// accumulator in VGPRs. Written as inline assembly because the compiler otherwise copies AGPR
+// operands back into VGPRs before every MFMA. Hazards the compiler cannot see here are covered
+// by hand: the first MFMA of a chain takes an inline-constant zero accumulator (no VALU write
+// before an MFMA read), a chain of MFMAs on one accumulator is a same-size srcC/vdst overlap
+// (no wait states), and mfma_drain() keeps VALU readers of the result 24 wait states away.
+// One embedding fragment against both token blocks: the two MFMAs stay adjacent so that the
+// two accumulation chains alternate in the matrix pipeline.
+__device__ __forceinline__ void mfma_pair_b_agpr(f32x16& c0, f32x16& c1, const bf16x8& a, const bf16x8& b0,
+                                                 const bf16x8& b1) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\tv_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
+      : "+v"(c0), "+v"(c1) : "v"(a), "a"(b0), "a"(b1));
+}
+__device__ __forceinline__ void mfma_pair_b_agpr_first(f32x16& c0, f32x16& c1, const bf16x8& a, const bf16x8& b0,
+                                                       const bf16x8& b1) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %2, %3, 0\n\tv_mfma_f32_32x32x16_bf16 %1, %2, %4, 0"
+      : "=&v"(c0), "=&v"(c1) : "v"(a), "a"(b0), "a"(b1));
+}
+__device__ __forceinline__ void mfma_drain(f32x16& a0, f32x16& a1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
+}
+
+// Z^T blocks: 32 vocabulary rows (vb*32 ... of LDS buffer `buf`) against this lane's two tokens.
+// Accumulator register r holds vocabulary row 8 (r/4) + 4 h + r%4 of the block; each embedding
+// fragment read from LDS feeds one MFMA per token block.
 template <int D>
-__device__ __forceinline__ f32x16 logit_block(const lds_char* lds, int buf, int vb, int h, int col,
-                                              const bf16x8 (&hf)[D / 16]) {
+__device__ __forceinline__ void logit_blocks(const lds_char* lds, int buf, int vb, int h, int col,
+                                             const bf16x8 (&hf)[kTokBlocks][D / 16], f32x16 (&acc)[kTokBlocks]) {
   using TL = TileLayout<D>;
   constexpr int KS = D / 16;
-  f32x16 acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  static_assert(kTokBlocks == 2, "two token blocks per wave");
   const int row = vb * 32 + col;
   const lds_char* rbase = lds + buf * TL::TILEB + row * TL::PITCH;
   const int sw = TL::swz(row);
@@ -104,9 +128,26 @@ __device__ __forceinline__ f32x16 logit_block(const lds_char* lds, int buf, int 
   for (int ks = 0; ks < KS; ++ks) {
     const int chunk = (h * KS + ks) ^ sw;
     const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(rbase + chunk * 16);
-    acc = mfma32x32x16(a, hf[ks], acc);
+    if (ks == 0) mfma_pair_b_agpr_first(acc[0], acc[1], a, hf[0][ks], hf[1][ks]);
+    else mfma_pair_b_agpr(acc[0], acc[1], a, hf[0][ks], hf[1][ks]);
   }
-  return acc;
+  mfma_drain(acc[0], acc[1]);
+}
+
+// Interleave hint for a chain of KS steps (one LDS read + kTokBlocks MFMAs each) overlapped with
+// VALU_TOTAL VALU / transcendental instructions of an epilogue.
+template <int KS, int VALU_TOTAL>
+__device__ __forceinline__ void interleave_hint2() {
+  constexpr int per = (VALU_TOTAL + KS - 1) / KS;
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, per / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, per - per / 2, 0);
+  }
 }
 
 // Largest |z| of a block, over the whole wave.
