@@ -86,6 +86,16 @@ __global__ __launch_bounds__(256) void de_generic_kernel(const uint16_t* dz, con
   dE[v * D + d] = g * acc;
 }
 
+// Hc[i] = H[rows[i]] for the compacted scored rows (16 bytes per thread).
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* H, const int32_t* rows, const int32_t* n_dev,
+                                                          int64_t T, int D, uint16_t* Hc) {
+  const int64_t cpr = D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = idx / cpr, c = idx % cpr;
+  if (i >= T || i >= (int64_t)(*n_dev)) return;
+  reinterpret_cast<uint4*>(Hc + i * D)[c] = reinterpret_cast<const uint4*>(H + (int64_t)rows[i] * D)[c];
+}
+
 // Zero the dH rows of unscored positions.
 __global__ __launch_bounds__(256) void zero_unscored_kernel(const uint8_t* mask, int64_t T, int D, float* dH) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -120,10 +130,9 @@ struct DzParams {
   uint16_t* dz;
 };
 
-template <int D, bool CAPPED>
+template <int D, bool CAPPED, int NB>
 struct DzCore {
   static constexpr int KS = D / 16;
-  static constexpr int NB = kTokBlocks;
   const lds_char* lds;
   int h, col, V;
   Softcap sc;
@@ -133,7 +142,7 @@ struct DzCore {
   uint16_t* dzrow[NB];
 
   __device__ __forceinline__ void chain(int buf, int vb, f32x16 (&acc)[NB]) const {
-    logit_blocks<D>(lds, buf, vb, h, col, hf, acc);
+    logit_blocks<D, NB>(lds, buf, vb, h, col, hf, acc);
   }
 
   // mode 0: series softcap (|z| <= c/8), 1: exact softcap, 2: no cap
@@ -211,12 +220,13 @@ struct DzCore {
   }
 };
 
-template <int D, bool CAPPED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, bool CAPPED, int NB>
+__global__ __launch_bounds__(WaveShape<NB>::kThreads) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
 void bwd_dz_kernel(DzParams p) {
   using TL = TileLayout<D>;
   constexpr int KS = D / 16;
-  constexpr int NB = kTokBlocks;
+  constexpr int kTokPerWave = WaveShape<NB>::kTok;
+  constexpr int kFwdWaves = WaveShape<NB>::kWaves;
   __shared__ __attribute__((aligned(1024))) char smem[2 * TL::TILEB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, col = lane & 31;
@@ -225,7 +235,7 @@ void bwd_dz_kernel(DzParams p) {
   if ((int64_t)rt * kRowsPerWG >= n) return;
   const int V = p.V;
 
-  DzCore<D, CAPPED> core;
+  DzCore<D, CAPPED, NB> core;
   core.lds = (const lds_char*)smem;
   core.h = h;
   core.col = col;
@@ -281,13 +291,17 @@ void bwd_dz_kernel(DzParams p) {
 // ------------------------------------------------------------------------------------ host side
 
 constexpr int kDeSplit = 4;
+// 32-token MFMA column blocks per wave in the dZ kernel (see WaveShape).
+constexpr int kDzTokBlocks = 2;
 
 template <int D>
 static void launch_dz(const DzParams& q, unsigned blocks, hipStream_t st) {
   if (q.sc.c > 0.f)
-    hipLaunchKernelGGL((bwd_dz_kernel<D, true>), dim3(blocks), dim3(kFwdWaves * 64), 0, st, q);
+    hipLaunchKernelGGL((bwd_dz_kernel<D, true, kDzTokBlocks>), dim3(blocks), dim3(WaveShape<kDzTokBlocks>::kThreads), 0,
+                       st, q);
   else
-    hipLaunchKernelGGL((bwd_dz_kernel<D, false>), dim3(blocks), dim3(kFwdWaves * 64), 0, st, q);
+    hipLaunchKernelGGL((bwd_dz_kernel<D, false, kDzTokBlocks>), dim3(blocks), dim3(WaveShape<kDzTokBlocks>::kThreads), 0,
+                       st, q);
 }
 
 BwdWorkspace bwd_workspace(int64_t T, int32_t D, int32_t V) {
@@ -299,6 +313,7 @@ BwdWorkspace bwd_workspace(int64_t T, int32_t D, int32_t V) {
   const size_t ldz = (size_t)((V + kVocabTile - 1) / kVocabTile) * kVocabTile;
   L.dz = o; o += align256(rows_pad * ldz * 2);
   L.de_part = o; o += align256((size_t)kDeSplit * (size_t)V * (size_t)D * 4);
+  L.hc = o; o += align256((size_t)T * (size_t)D * 2);
   L.total = o;
   return L;
 }
@@ -354,12 +369,11 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
       GemmParams a{};
       a.A = dz; a.lda = q.ldz;
       a.B = (const uint16_t*)E; a.ldb = D;
-      a.brows = nullptr;
       a.n_dev = n_dev; a.m_dev = n_dev != nullptr; a.k_dev = 0;
       a.M = T; a.N = D; a.K = V; a.kvalid = V;
       a.alpha = grad_scale;
       a.C = dH; a.ldc = D; a.crows = rows; a.split_stride = 0;
-      e = launch_gemm(a, false, dim3(rblk, (unsigned)((D + kGemmBN - 1) / kGemmBN), 1), st);
+      e = launch_gemm(a, false, dim3((unsigned)((T + kGemmBM - 1) / kGemmBM), (unsigned)((D + kGemmBN - 1) / kGemmBN), 1), st);
       if (e != hipSuccess) return e;
     }
     // dE = g dZ^T H, k split over workgroups when the output has few tiles
@@ -372,7 +386,14 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     GemmParams b{};
     b.A = dz; b.lda = ((V + kVocabTile - 1) / kVocabTile) * (int64_t)kVocabTile;
     b.B = (const uint16_t*)H; b.ldb = D;
-    b.brows = rows;
+    if (rows) {   // masked: the scored hidden rows, compacted, so that k runs over them directly
+      uint16_t* hc = reinterpret_cast<uint16_t*>(ws + L.hc);
+      const int64_t cnt = T * (D / 8);
+      hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, (const uint16_t*)H,
+                         rows, n_dev, T, D, hc);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      b.B = hc;
+    }
     b.n_dev = n_dev; b.m_dev = 0; b.k_dev = n_dev != nullptr;
     b.M = V; b.N = D; b.K = T; b.kvalid = T;
     b.alpha = grad_scale;

@@ -53,10 +53,18 @@ __device__ __forceinline__ int device_splits(int64_t n, int n_vtiles, int grid) 
   return s < 1 ? 1 : (s > n_vtiles ? n_vtiles : s);
 }
 
-template <int D, bool FIXED>
+// LDS fragment reads issued this many MFMA steps ahead of their use.
+constexpr int kPrefetch = 4;
+
+#ifndef PG_FWD_TOK_BLOCKS
+#define PG_FWD_TOK_BLOCKS 1
+#endif
+// 32-token MFMA column blocks per wave in the forward (see WaveShape).
+constexpr int kFwdTokBlocks = PG_FWD_TOK_BLOCKS;
+
+template <int D, bool FIXED, int NB>
 struct FwdCore {
   static constexpr int KS = D / 16;
-  static constexpr int NB = kTokBlocks;
   const lds_char* lds;
   int h, col, V;
   Softcap sc;
@@ -65,7 +73,7 @@ struct FwdCore {
   float mrun[NB];
 
   __device__ __forceinline__ void chain(int buf, int vb, f32x16 (&acc)[NB]) const {
-    logit_blocks<D>(lds, buf, vb, h, col, hf, acc);
+    logit_blocks<D, NB>(lds, buf, vb, h, col, hf, acc);
   }
 
   // Exp-sum with the fixed shift M by the tanh series (valid when |z| <= c/8).
@@ -130,43 +138,85 @@ struct FwdCore {
     }
   }
 
-  // MFMA chain of block (buf, vb) with the epilogue of the pending full block `prev` in the same
-  // basic block. The series sum is computed speculatively; when some |z| of `prev` exceeds c/8 (a
-  // wave-uniform, rarely taken branch) the exact sum replaces it.
+  // MFMA chain of block (buf, vb) with the epilogue of the pending full block `prev`, software
+  // pipelined by hand (one wave per SIMD leaves no other wave to hide latencies): k-step k issues
+  // the LDS read of step k + kPrefetch, the MFMA pair of step k and stage s of the series epilogue
+  // of element group k - s, so that dependent VALU operations sit one MFMA pair apart. Scheduling
+  // barriers keep each step's instructions together. The series sum is speculative: when some
+  // |z| of `prev` exceeds c/8 (a wave-uniform, rarely taken branch) the exact sum replaces it.
   __device__ __forceinline__ void chain_with_epilogue(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
                                                       int vprev) {
-    if (FIXED) {
-      chain(buf, vb, a);
-      float part[NB];
-      float amax = 0.f;
-#pragma unroll
-      for (int tb = 0; tb < NB; ++tb) {
-        part[tb] = part_series(prev[tb]);
-        amax = fmaxf(amax, wave_absmax16(prev[tb]));
-      }
-      interleave_hint2<KS, NB * 16 * 8>();
-#pragma unroll
-      for (int tb = 0; tb < NB; ++tb) asm volatile("" ::"v"(part[tb]));   // keep the speculation here
-      if (!__all(amax <= sc.thr)) {
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb) part[tb] = part_exact<false>(prev[tb], vprev);
-      }
-#pragma unroll
-      for (int tb = 0; tb < NB; ++tb) lsum[tb] += part[tb];
-    } else {
+    if (!FIXED) {
       chain(buf, vb, a);
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) online<false>(prev[tb], vprev, tb);
+      return;
     }
+    using TL = TileLayout<D>;
+    constexpr int NE = NB * 16;                     // logits of `prev` per lane
+    constexpr int EPC = (NE + KS - 1) / KS;         // elements per group
+    constexpr int NG = (NE + EPC - 1) / EPC;        // element groups
+    constexpr int NST = 7;                          // epilogue stages
+    constexpr int NSTEP = (NG + NST - 1) > KS ? (NG + NST - 1) : KS;
+    constexpr int PF = kPrefetch < KS ? kPrefetch : KS;
+    const int row = vb * 32 + col;
+    const lds_char* rbase = lds + buf * TL::TILEB + row * TL::PITCH;
+    const int sw = TL::swz(row);
+    auto frag = [&](int ks) -> bf16x8 {
+      return *(const __attribute__((address_space(3))) bf16x8*)(rbase + ((h * KS + ks) ^ sw) * 16);
+    };
+    bf16x8 fr[KS];
+    float u[NE], q[NE];
+    float part[NB] = {};
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < PF; ++k) fr[k] = frag(k);
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+      if (k + PF < KS) fr[k + PF] = frag(k + PF);
+      if (k < KS) {
+        lds_wait_upto((k + PF < KS ? k + PF : KS - 1) - k);
+        mfma_step<NB, KS>(a, fr[k], hf, k);
+      }
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int g = k - st;
+        if (g < 0 || g >= NG) continue;
+#pragma unroll
+        for (int e = g * EPC; e < (g + 1) * EPC && e < NE; ++e) {
+          const float z = prev[e / 16][e % 16];
+          switch (st) {
+            case 0: u[e] = z * z; amax = fmaxf(amax, fabsf(z)); break;
+            case 1: q[e] = __builtin_fmaf(sc.q3, u[e], sc.q2); break;
+            case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q1); break;
+            case 3: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
+            case 4: q[e] = __builtin_fmaf(z, q[e], -sc.M); break;
+            case 5: q[e] = fexp2(q[e]); break;
+            default: part[e / 16] += q[e]; break;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_finish<NB>(a);
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) asm volatile("" ::"v"(part[tb]));   // keep the speculation in the pipeline
+    if (!__all(amax <= sc.thr)) {
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) part[tb] = part_exact<false>(prev[tb], vprev);
+    }
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) lsum[tb] += part[tb];
   }
 };
 
-template <int D, bool FIXED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, bool FIXED, int NB>
+__global__ __launch_bounds__(WaveShape<NB>::kThreads) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
 void fwd_mfma_kernel(FwdParams p) {
   using TL = TileLayout<D>;
   constexpr int KS = D / 16;
-  constexpr int NB = kTokBlocks;
+  constexpr int kTokPerWave = WaveShape<NB>::kTok;
+  constexpr int kFwdWaves = WaveShape<NB>::kWaves;
   constexpr int EPL = D >= 64 ? D / 64 : 1;           // hidden elements per lane in the target dot
   __shared__ __attribute__((aligned(1024))) char smem[2 * TL::TILEB];
 
@@ -221,7 +271,7 @@ void fwd_mfma_kernel(FwdParams p) {
     }
   }
 
-  FwdCore<D, FIXED> core;
+  FwdCore<D, FIXED, NB> core;
   core.lds = (const lds_char*)smem;
   core.h = h;
   core.col = col;
@@ -435,7 +485,8 @@ hipError_t launch_compact_rows(const uint8_t* mask, int64_t T, char* ws, const F
 
 template <int D, bool FIXED>
 static void launch_mfma(const FwdParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, FIXED>), dim3(grid), dim3(kFwdWaves * 64), 0, st, p);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, FIXED, kFwdTokBlocks>), dim3(grid), dim3(WaveShape<kFwdTokBlocks>::kThreads),
+                     0, st, p);
 }
 
 template <int D>

@@ -1,7 +1,7 @@
 // bf16 GEMM with float32 accumulation for the two products of the backward, dH = g dZ E and
 // dE = g dZ^T H, on gfx950 (v_mfma_f32_32x32x16_bf16).
 //
-// 256 x 256 output tiles per workgroup (4 waves of 128 x 128, sixteen 32 x 32 accumulators each,
+// 128 x 512 output tiles per workgroup (4 waves of 128 x 128, sixteen 32 x 32 accumulators each,
 // held in AGPRs), 32-deep k-chunks in a 3-stage LDS ring filled by global_load_lds_dwordx4. An
 // operand whose k index is the slow one in memory (dZ read as dZ^T, E and H as k x n) is fed to
 // the MFMA with ds_read_b64_tr_b16, which gives each lane 4 consecutive k of one column, so no
@@ -13,19 +13,23 @@ namespace pg {
 
 
 
-// LDS tile layouts (bytes):
-//   k-contiguous A: [256 m][32 k], 64 B rows; 16-byte chunk c of row m stored at c ^ ((m >> 2) & 3)
-//   k-slow A or B: [32 k][256 m|n], 512 B rows; chunk c of row k stored at c ^ (4 (k & 3))
-// Both keep the 16 lanes of an LDS read phase on 16 different 16-byte bank groups.
+// LDS tile layouts (bytes), 16-byte chunk index XORed so that the 16 lanes of an LDS read phase
+// hit 16 different 16-byte bank groups:
+//   k-contiguous A: [128 m][32 k], 64 B rows; chunk c of row m stored at c ^ ((m >> 2) & 3)
+//   k-slow A:       [32 k][128 m], 256 B rows; chunk c of row k stored at c ^ (4 (k & 3))
+//   B:              [32 k][512 n], 1 KiB rows; chunk c of row k stored at c ^ (4 (k & 3))
+// A workgroup owns a 128 x 512 output tile (the whole hidden width), so dZ is read from memory once.
 template <bool A_TRANS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(GemmParams g) {
   constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
   constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2, SBYTES = ABYTES + BBYTES;
+  constexpr int A_LOADS = ABYTES / 1024, B_LOADS = BBYTES / 1024;   // 1 KiB load instructions
+  constexpr int LOADS_PER_WAVE = (A_LOADS + B_LOADS) / 4;
+  static_assert(BM == 128 && BN == 512 && BK == 32, "tile shape assumed by the layouts below");
   __shared__ __attribute__((aligned(1024))) char smem[kGemmStages * SBYTES];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
 
   const int64_t ndev = g.n_dev ? (int64_t)(*g.n_dev) : 0;
   const int64_t M = g.m_dev ? ndev : g.M;
@@ -41,13 +45,13 @@ void gemm_bf16_kernel(GemmParams g) {
   const int64_t nk = kc_end > kc_begin ? kc_end - kc_begin : 0;
   const int64_t kvalid = g.k_dev ? ndev : g.kvalid;
 
-  // ---- stage loader: 32 global_load_lds_dwordx4 per stage, 8 per wave
+  // ---- stage loader: each wave issues LOADS_PER_WAVE global_load_lds_dwordx4
   auto load_stage = [&](int64_t kc, int st) {
     char* sA = smem + st * SBYTES;
     char* sB = sA + ABYTES;
     const int64_t k0 = kc * BK;
 #pragma unroll
-    for (int j = wave; j < 16; j += 4) {
+    for (int j = wave; j < A_LOADS; j += 4) {
       const uint16_t* src;
       if (!A_TRANS) {
         const int row = 16 * j + (lane >> 2);
@@ -56,8 +60,8 @@ void gemm_bf16_kernel(GemmParams g) {
         m = m < M ? m : M - 1;
         src = g.A + m * g.lda + k0 + 8 * lc;
       } else {
-        const int row = 2 * j + (lane >> 5);
-        const int lc = (lane & 31) ^ (4 * (row & 3));
+        const int row = 4 * j + (lane >> 4);
+        const int lc = (lane & 15) ^ (4 * (row & 3));
         int64_t col = m0 + 8 * lc;
         col = col <= g.lda - 8 ? col : g.lda - 8;
         src = g.A + (k0 + row) * g.lda + col;
@@ -65,15 +69,14 @@ void gemm_bf16_kernel(GemmParams g) {
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(sA + j * 1024), 16, 0, 0);
     }
 #pragma unroll
-    for (int j = wave; j < 16; j += 4) {
-      const int row = 2 * j + (lane >> 5);
-      const int lc = (lane & 31) ^ (4 * (row & 3));
+    for (int j = wave; j < B_LOADS; j += 4) {
+      const int row = j;
+      const int lc = lane ^ (4 * (row & 3));
       int64_t k = k0 + row;
       k = k < kvalid ? k : kvalid - 1;
-      const int64_t krow = g.brows ? (int64_t)g.brows[k] : k;
       int64_t col = n0 + 8 * lc;
       col = col <= g.ldb - 8 ? col : g.ldb - 8;
-      __builtin_amdgcn_global_load_lds(g.B + krow * g.ldb + col, (lds_void*)(sB + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(g.B + k * g.ldb + col, (lds_void*)(sB + j * 1024), 16, 0, 0);
     }
   };
 
@@ -86,27 +89,30 @@ void gemm_bf16_kernel(GemmParams g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int grp = lane >> 4, li = lane & 15;
-  // transposed-read lane address inside a [32 k][256] tile: row k0 + li / 4, columns
-  // cbase + 16 (grp & 1) + 4 (li & 3) .. + 3, for k0 = 16 ks + 8 (grp >> 1) + 4 half
-  auto tr_addr = [&](int ks, int half, int cbase) -> int {
-    const int k = 16 * ks + 8 * (grp >> 1) + 4 * half + (li >> 2);
-    const int c = cbase + 16 * (grp & 1) + 4 * (li & 3);
-    return k * 512 + 16 * ((c >> 3) ^ (4 * (k & 3))) + 2 * (c & 7);
-  };
-  auto read_tr = [&](const char* tile, int ks, int cbase) -> bf16x8 {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tr_addr(ks, 0, cbase)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + tr_addr(ks, 1, cbase)));
+  // transposed read: lanes of group grp take rows k0 + li / 4 and columns cbase + 16 (grp & 1) +
+  // 4 (li & 3) .. + 3, for k0 = 16 ks + 8 (grp >> 1) + 4 half; lane i of the group receives 4
+  // consecutive k of column cbase + 16 (grp & 1) + i
+  auto read_tr = [&](const char* tile, int pitch, int ks, int cbase) -> bf16x8 {
+    i16x4 part[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int k = 16 * ks + 8 * (grp >> 1) + 4 * half + (li >> 2);
+      const int c = cbase + 16 * (grp & 1) + 4 * (li & 3);
+      const int addr = k * pitch + 16 * ((c >> 3) ^ (4 * (k & 3))) + 2 * (c & 7);
+      part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + addr));
+    }
     typedef short i16x8 __attribute__((ext_vector_type(8)));
-    i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    i16x8 v = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
     return __builtin_bit_cast(bf16x8, v);
   };
 
   if (nk > 0) load_stage(kc_begin, 0);
   if (nk > 1) load_stage(kc_begin + 1, 1);
   for (int64_t it = 0; it < nk; ++it) {
-    if (it + 1 < nk) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    // this wave's loads of stage `it` are done when at most one stage (the next) is in flight
+    if (it + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_WAVE) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();   // every wave's loads of stage `it` landed; stage it-1 is free
     if (it + 2 < nk) load_stage(kc_begin + it + 2, (int)((it + 2) % kGemmStages));
     const int st = (int)(it % kGemmStages);
     const char* sA = smem + st * SBYTES;
@@ -116,17 +122,16 @@ void gemm_bf16_kernel(GemmParams g) {
       bf16x8 af[4], bfr[4];
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm) {
-        const int mb = wm * 128 + bm * 32;
         if (!A_TRANS) {
-          const int row = mb + (lane & 31);
+          const int row = bm * 32 + (lane & 31);
           const int chunk = (2 * ks + h) ^ ((row >> 2) & 3);
           af[bm] = *(const __attribute__((address_space(3))) bf16x8*)((const lds_char*)sA + row * 64 + chunk * 16);
         } else {
-          af[bm] = read_tr(sA, ks, mb);
+          af[bm] = read_tr(sA, BM * 2, ks, bm * 32);
         }
       }
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn) bfr[bn] = read_tr(sB, ks, wn * 128 + bn * 32);
+      for (int bn = 0; bn < 4; ++bn) bfr[bn] = read_tr(sB, BN * 2, ks, wave * 128 + bn * 32);
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
@@ -140,10 +145,10 @@ void gemm_bf16_kernel(GemmParams g) {
   for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
     for (int bn = 0; bn < 4; ++bn) {
-      const int64_t n = n0 + wn * 128 + bn * 32 + (lane & 31);
+      const int64_t n = n0 + wave * 128 + bn * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 128 + bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t m = m0 + bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < M && n < g.N) {
           const int64_t crow = g.crows ? (int64_t)g.crows[m] : m;
           C[crow * g.ldc + n] = g.alpha * acc[bm][bn][r];

@@ -22,6 +22,7 @@ struct BwdWorkspace {
   size_t n_rows;   // int32
   size_t rows;     // int32[T]
   size_t dz;       // bf16[T, V]: dZ without the grad_scale factor
+  size_t hc;       // bf16[T, D]: hidden rows of the scored positions, compacted (masked calls)
   size_t de_part;  // f32[KSPLIT, V, D]: split-K partials of dE
   size_t total;
 };
@@ -57,13 +58,12 @@ hipError_t launch_bpb(const float* nats, const int32_t* target, const uint8_t* m
                       double* out, char* ws, hipStream_t st);
 
 // C = alpha * A B in bf16 with float32 accumulation (pg_gemm.hip).
-constexpr int kGemmBM = 256, kGemmBN = 256, kGemmBK = 32, kGemmStages = 3;
+constexpr int kGemmBM = 128, kGemmBN = 512, kGemmBK = 32, kGemmStages = 3;
 struct GemmParams {
   const uint16_t* A;      // element (m, k): A_TRANS ? A[k * lda + m] : A[m * lda + k]
   int64_t lda;
-  const uint16_t* B;      // element (k, n): B[krow(k) * ldb + n]
+  const uint16_t* B;      // element (k, n): B[k * ldb + n]
   int64_t ldb;
-  const int32_t* brows;   // krow(k) = brows[k] when given, else k
   const int32_t* n_dev;   // device count that replaces M (m_dev) or K (k_dev)
   int m_dev, k_dev;
   int64_t M, N, K;        // sizes (upper bounds when taken from n_dev)

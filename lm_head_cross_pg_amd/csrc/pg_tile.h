@@ -31,12 +31,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Rows of the workgroup's token tile handled by one wave: two 32-token MFMA column blocks, so
-// every embedding fragment read from LDS feeds two MFMAs (one wave per SIMD, hidden rows of 64
-// tokens held in VGPRs and AGPRs).
-constexpr int kFwdWaves = 4;
-constexpr int kTokPerWave = kRowsPerWG / kFwdWaves;   // 64
-constexpr int kTokBlocks = kTokPerWave / 32;          // 2
+// Shape of the token tile: NB 32-token MFMA column blocks per wave, 256 rows per workgroup.
+//   NB = 1: 8 waves (two per SIMD), hidden rows of 32 tokens in VGPRs; every embedding fragment
+//           read from LDS feeds one MFMA.
+//   NB = 2: 4 waves (one per SIMD), hidden rows of 64 tokens in AGPRs; every fragment feeds two.
+template <int NB>
+struct WaveShape {
+  static constexpr int kWaves = 8 / NB;
+  static constexpr int kTok = 32 * NB;
+  static constexpr int kThreads = 64 * kWaves;
+};
 
 // LDS layout of one embedding tile (kVocabTile rows). D = 512: one 1 KiB row per load
 // instruction, rows padded to 1040 bytes so that 16 lanes reading 16 consecutive rows at the same
@@ -112,15 +116,47 @@ __device__ __forceinline__ void mfma_drain(f32x16& a0, f32x16& a1) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
 }
 
-// Z^T blocks: 32 vocabulary rows (vb*32 ... of LDS buffer `buf`) against this lane's two tokens.
-// Accumulator register r holds vocabulary row 8 (r/4) + 4 h + r%4 of the block; each embedding
-// fragment read from LDS feeds one MFMA per token block.
-template <int D>
+// Wait until at most n LDS operations of this wave are outstanding (n <= 4). LDS reads return
+// in order, so with n younger reads in flight the oldest one has landed.
+__device__ __forceinline__ void lds_wait_upto(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt lgkmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt lgkmcnt(3)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory"); break;
+  }
+}
+
+// One MFMA step of the chain: the embedding fragment `a` against every token block.
+template <int NB, int KS>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[NB], const bf16x8& a, const bf16x8 (&hf)[NB][KS], int ks) {
+  if constexpr (NB == 2) {
+    if (ks == 0) mfma_pair_b_agpr_first(acc[0], acc[1], a, hf[0][ks], hf[1][ks]);
+    else mfma_pair_b_agpr(acc[0], acc[1], a, hf[0][ks], hf[1][ks]);
+  } else {
+    if (ks == 0) {
+      const f32x16 zero = {};
+      acc[0] = mfma32x32x16(a, hf[0][ks], zero);
+    } else {
+      acc[0] = mfma32x32x16(a, hf[0][ks], acc[0]);
+    }
+  }
+}
+
+// End of a chain: the assembly form needs its wait states before VALU readers by hand.
+template <int NB>
+__device__ __forceinline__ void mfma_finish(f32x16 (&acc)[NB]) {
+  if constexpr (NB == 2) mfma_drain(acc[0], acc[1]);
+}
+
+// Z^T blocks: 32 vocabulary rows (vb*32 ... of LDS buffer `buf`) against this lane's NB tokens.
+// Accumulator register r holds vocabulary row 8 (r/4) + 4 h + r%4 of the block.
+template <int D, int NB>
 __device__ __forceinline__ void logit_blocks(const lds_char* lds, int buf, int vb, int h, int col,
-                                             const bf16x8 (&hf)[kTokBlocks][D / 16], f32x16 (&acc)[kTokBlocks]) {
+                                             const bf16x8 (&hf)[NB][D / 16], f32x16 (&acc)[NB]) {
   using TL = TileLayout<D>;
   constexpr int KS = D / 16;
-  static_assert(kTokBlocks == 2, "two token blocks per wave");
   const int row = vb * 32 + col;
   const lds_char* rbase = lds + buf * TL::TILEB + row * TL::PITCH;
   const int sw = TL::swz(row);
@@ -128,10 +164,9 @@ __device__ __forceinline__ void logit_blocks(const lds_char* lds, int buf, int v
   for (int ks = 0; ks < KS; ++ks) {
     const int chunk = (h * KS + ks) ^ sw;
     const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(rbase + chunk * 16);
-    if (ks == 0) mfma_pair_b_agpr_first(acc[0], acc[1], a, hf[0][ks], hf[1][ks]);
-    else mfma_pair_b_agpr(acc[0], acc[1], a, hf[0][ks], hf[1][ks]);
+    mfma_step<NB, KS>(acc, a, hf, ks);
   }
-  mfma_drain(acc[0], acc[1]);
+  mfma_finish<NB>(acc);
 }
 
 // Interleave hint for a chain of KS steps (one LDS read + kTokBlocks MFMAs each) overlapped with
