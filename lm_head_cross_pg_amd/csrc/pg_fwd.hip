@@ -175,7 +175,7 @@ struct FwdCore {
     for (int k = 0; k < NSTEP; ++k) {
       if (k + PF < KS) fr[k + PF] = frag(k + PF);
       if (k < KS) {
-        lds_wait_upto((k + PF < KS ? k + PF : KS - 1) - k);
+        if (NB == 2) lds_wait_upto((k + PF < KS ? k + PF : KS - 1) - k);
         mfma_step<NB, KS>(a, fr[k], hf, k);
       }
 #pragma unroll

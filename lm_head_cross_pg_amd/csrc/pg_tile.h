@@ -72,6 +72,25 @@ __device__ __forceinline__ void interleave_hint() {
   }
 }
 
+// One 16-byte-per-lane LDS DMA (global_load_lds_dwordx4: lane i's 16 bytes land at lds_base + 16 i)
+// issued as assembly. Issued through the builtin, a DMA still in flight makes the compiler wait for
+// every outstanding LDS read (lgkmcnt(0)) before each MFMA operand is used, which cancels the read
+// prefetch of the MFMA chains; here the compiler does not see it, so completion is the caller's
+// business: an explicit s_waitcnt vmcnt before the barrier that publishes the tile. M0 (the LDS base
+// of the DMA) is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(const void* gptr, const lds_char* lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base))
+      : "memory");
+}
+
 // One embedding tile from global memory into LDS buffer `buf` with global_load_lds_dwordx4
 // (1 KiB per instruction, no VGPR round trip), spread over `nwaves` waves. Rows past the end of
 // the vocabulary repeat the last row (valid memory; their logits are masked by the caller).
@@ -90,7 +109,7 @@ __device__ __forceinline__ void load_embed_tile(char* smem, const uint16_t* E, i
     const int v = min(v0 + row, V - 1);
     const char* g = reinterpret_cast<const char*>(E + (int64_t)v * D) + lchunk * 16;
     char* dst = smem + buf * TL::TILEB + (TL::PAD ? j * TL::PITCH : j * 1024);
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)dst, 16, 0, 0);
+    lds_dma16(g, (const lds_char*)dst);
   }
 }
 
