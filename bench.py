@@ -1,6 +1,8 @@
 """Benchmark of the fused tied LM head + softcap cross-entropy -> bits-per-byte path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-train] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-train] [--no-cpu] [--cold]
+    python bench.py --calibrate-copy              # plain 512 MiB copy, for HBM counter scaling
+    python bench.py --summarize-counters DIR      # rocprofv3 counter CSVs -> profiles/ summaries
 
 A step is one pass of the scoring path over one synthetic batch shaped like the challenge's main
 evaluation (T = 32 x 2048 rows, D = 512, V = 8192 BPE entries, bf16, softcap 30, every row scored):
@@ -30,7 +32,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_mfma_T65536_D512_V8192_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "lm_head_cross_pg_amd", "csrc", f) for f in ("pg_fwd.hip", "pg_common.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "lm_head_cross_pg_amd", "csrc", f)
+                  for f in ("pg_fwd.hip", "pg_common.h", "pg_tile.h")]
+FWD_KERNEL = "fwd_mfma_kernel<512, true"
+COPY_BYTES = 1 << 29          # --calibrate-copy moves 512 MiB each way per launch
 
 
 def kernel_source_hash() -> str:
@@ -54,6 +59,99 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
+def _counter_rows(d):
+    """Rows of every rocprofv3 *_counter_collection.csv below directory d."""
+    import csv
+    rows = []
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                with open(os.path.join(root, f)) as fh:
+                    rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, name_part, counter):
+    """Mean over dispatches of kernels whose name contains name_part of one counter (summed over
+    the per-agent rows of a dispatch)."""
+    per = {}
+    for r in rows:
+        if name_part.lower() in r["Kernel_Name"].lower() and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return (sum(per.values()) / len(per), len(per)) if per else (None, 0)
+
+
+def summarize_counters(d):
+    """Turn the counter runs under d (fetch/, write/, calib_fetch/, calib_write/, mfma/, each a
+    rocprofv3 --pmc output directory) into the traffic file read by the roofline report and a
+    short markdown summary next to it."""
+    out = {"kernel": FWD_KERNEL + ">", "workload": "fwd_v8192 T=65536 D=512 V=8192",
+           "kernel_source_sha256_16": kernel_source_hash()}
+    cf, _ = _per_dispatch(_counter_rows(os.path.join(d, "calib_fetch")), "copy", "FETCH_SIZE")
+    cw, _ = _per_dispatch(_counter_rows(os.path.join(d, "calib_write")), "copy", "WRITE_SIZE")
+    ff, nf = _per_dispatch(_counter_rows(os.path.join(d, "fetch")), FWD_KERNEL, "FETCH_SIZE")
+    fw, nw = _per_dispatch(_counter_rows(os.path.join(d, "write")), FWD_KERNEL, "WRITE_SIZE")
+    lines = ["# HBM traffic of the fused forward (T=65536, D=512, V=8192)", ""]
+    if None in (cf, cw, ff, fw):
+        raise SystemExit("missing counter runs under " + d)
+    kf, kw = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
+    fetch_b, write_b = ff * 1024.0 * kf, fw * 1024.0 * kw
+    out.update({"copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_scale": kf, "write_scale": kw,
+                "fetch_kib_per_launch": ff, "write_kib_per_launch": fw, "launches": [nf, nw],
+                "fetch_bytes": fetch_b, "write_bytes": write_b, "bytes_per_launch": fetch_b + write_b})
+    lines += ["| quantity | value |", "|---|---|",
+              f"| copy kernel, 512 MiB each way: FETCH_SIZE | {cf:.0f} KiB (scale {kf:.3f}) |",
+              f"| copy kernel: WRITE_SIZE | {cw:.0f} KiB (scale {kw:.3f}) |",
+              f"| forward FETCH_SIZE per launch ({nf} launches) | {ff:.0f} KiB -> {fetch_b / 2**20:.1f} MiB |",
+              f"| forward WRITE_SIZE per launch ({nw} launches) | {fw:.0f} KiB -> {write_b / 2**20:.2f} MiB |",
+              f"| compulsory (H 64 MiB + E 8 MiB + targets 256 KiB; nats + lse 512 KiB) | 72.25 MiB read, 0.5 MiB written |"]
+    mrows = _counter_rows(os.path.join(d, "mfma"))
+    if mrows:
+        busy, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_VALU_MFMA_BUSY_CYCLES")
+        gui, _ = _per_dispatch(mrows, FWD_KERNEL, "GRBM_GUI_ACTIVE")
+        mops, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        valu, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_INSTS_VALU")
+        lds, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_INSTS_LDS")
+        conf, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_LDS_BANK_CONFLICT")
+        if busy and gui:
+            # GRBM_GUI_ACTIVE comes back summed over the 8 XCDs; per XCD it is the kernel's cycles
+            cyc = gui / 8.0
+            durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in mrows
+                    if FWD_KERNEL in r["Kernel_Name"] and r["Counter_Name"] == "GRBM_GUI_ACTIVE"]
+            dur_ns = sum(durs) / len(durs)
+            out["mfma_busy_pct"] = 100.0 * busy / (cyc * 1024)
+            out["clock_ghz"] = cyc / dur_ns
+            lines.append(f"| MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) | "
+                         f"{out['mfma_busy_pct']:.1f} % |")
+            lines.append(f"| mean shader clock during the launch (GRBM_GUI_ACTIVE / 8 / duration) | "
+                         f"{out['clock_ghz']:.2f} GHz over {dur_ns / 1e3:.1f} us |")
+        if mops:
+            out["mfma_flop"] = mops * 512
+            lines.append(f"| bf16 MFMA FLOP (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) | {mops * 512:.4g} "
+                         f"(algorithmic 2TDV = {2.0 * 65536 * 512 * 8192:.4g}) |")
+        for nm, v in (("SQ_INSTS_VALU", valu), ("SQ_INSTS_LDS", lds), ("SQ_LDS_BANK_CONFLICT", conf)):
+            if v is not None:
+                out[nm] = v
+                lines.append(f"| {nm} per launch | {v:.4g} |")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    md = TRAFFIC_FILE.replace("_traffic.json", "_counters.md")
+    lines += ["", "Commands (from the repository root, cd /tmp first as rocprofv3 wants a writable cwd):", "",
+              "```",
+              "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -- python3 bench.py --steps 3 --warmup 1 --no-train --no-cpu",
+              "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -- python3 bench.py --steps 3 --warmup 1 --no-train --no-cpu",
+              "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/calib_fetch -- python3 bench.py --calibrate-copy",
+              "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/calib_write -- python3 bench.py --calibrate-copy",
+              "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU "
+              "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT --output-format csv -d <dir>/mfma -- python3 bench.py --steps 3 --warmup 1 --no-train --no-cpu",
+              "python3 bench.py --summarize-counters <dir>",
+              "```", ""]
+    with open(md, "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps(out))
+
+
 def cpu_baseline(inp, seconds: float = 12.0):
     """The float64 oracle on the first rows of the same workload, in chunks, until `seconds`."""
     from oracle import oracle as ora
@@ -65,16 +163,17 @@ def cpu_baseline(inp, seconds: float = 12.0):
         threads = os.cpu_count() or 1
     E = synth.as_f64(inp["embed"], inp["dtype"])
     y = inp["target"]
-    rows, chunk = 0, 1024
+    rows, chunk, T = 0, 1024, inp["T"]
     t0 = time.perf_counter()
-    while rows < inp["T"] and time.perf_counter() - t0 < seconds:
-        H = synth.as_f64(inp["hidden"][rows:rows + chunk], inp["dtype"])
-        ora.forward(H, E, y[rows:rows + chunk], inp["softcap"])
+    while time.perf_counter() - t0 < seconds:
+        r0 = rows % T
+        H = synth.as_f64(inp["hidden"][r0:r0 + chunk], inp["dtype"])
+        ora.forward(H, E, y[r0:r0 + chunk], inp["softcap"])
         rows += H.shape[0]
     dt = time.perf_counter() - t0
     return {"value": rows / dt, "unit": "scored tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows} of {inp['T']} rows of the same workload, float64 forward "
-                      f"(numpy matmul + tanh/exp/log), {dt:.1f} s wall"}
+            "sample": f"{rows} rows ({rows / T:.2f} passes over the {T} rows of the same workload, in "
+                      f"{chunk}-row chunks), float64 forward (numpy matmul + tanh/exp/log), {dt:.1f} s wall"}
 
 
 def main():
@@ -87,7 +186,14 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 1 GiB scratch tensor between timed forward launches (cold L2/MALL)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="summarise rocprofv3 counter runs under DIR into profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the data-parallel head needs no exchange until the "
               "final three-scalar sum, and this build runs on a single MI355X (use --gpus 1).",
@@ -133,12 +239,16 @@ def main():
 
     # per-launch time of the fused forward kernel, HIP events on the stream it runs on
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if args.cold else None
     for a, b in ev:
+        if scratch is not None:
+            scratch.fill_(1.0)
         a.record()
         abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, c, nats, lse, ws_fwd)
         b.record()
     torch.cuda.synchronize()
-    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    launch = np.array([a.elapsed_time(b) for a, b in ev])
+    fwd_ms = float(np.mean(launch))
     flop_fwd = 2.0 * T * D * V
     achieved = flop_fwd / (fwd_ms * 1e-3) / 1e12
 
@@ -159,6 +269,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "fwd_mfma_kernel<512,true>", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(), "launch_ms": fwd_ms,
+                     "launch_ms_p10_p50_p90": [float(np.percentile(launch, q)) for q in (10, 50, 90)],
+                     "l2_mall": "cold (1 GiB written between launches)" if args.cold else "warm",
                      "algorithmic": "2*T*D*V = %.4g FLOP per launch" % flop_fwd},
     }
 
