@@ -108,11 +108,13 @@ __global__ __launch_bounds__(256) void zero_unscored_kernel(const uint8_t* mask,
 // 1. bwd_dz_kernel: the forward's structure (8 waves x 32 tokens per workgroup, hidden rows in
 //    registers, the embedding streamed through LDS) recomputes each 32 x 32 logit block with
 //    v_mfma_f32_32x32x16_bf16 and turns it into dZ = (p - onehot) * (1 - (s/c)^2) in the epilogue,
-//    which is interleaved with the next block's MFMA chain. dZ goes to the workspace as bf16,
-//    [rows rounded up to 256][V rounded up to 64], zero in the padding.
-// 2. The bf16 GEMM of pg_gemm.hip forms the two products:
-//      dH = g dZ E      A = dZ [rows][V] (k = v contiguous), B = E [V][D]
-//      dE = g dZ^T H    A = dZ read transposed, B = H rows (gathered through the scored-row list)
+//    which is interleaved with the next block's MFMA chain. dZ goes to the workspace as bf16 in
+//    32 x 32 blocks laid out like the MFMA accumulator (described in pg_internal.h), so that
+//    every lane stores 32 contiguous bytes and each block is one contiguous 2 KiB run; zero in
+//    the padding rows and columns.
+// 2. The bf16 GEMM of pg_gemm.hip forms the two products from those blocks:
+//      dH = g dZ E      A = dZ blocks, B = E [V][D]
+//      dE = g dZ^T H    A = dZ blocks read transposed, B = H rows (compacted when masked)
 //    dE splits k over several workgroups; a final kernel adds the partial tiles in a fixed order.
 
 struct DzParams {
@@ -125,7 +127,7 @@ struct DzParams {
   int64_t n_host;
   int V;
   int n_vtiles;
-  int64_t ldz;
+  int64_t ldz;            // vocabulary extent of dZ (V rounded up to 64)
   Softcap sc;
   uint16_t* dz;
 };
@@ -139,51 +141,53 @@ struct DzCore {
   bf16x8 hf[NB][KS];
   float bias[NB];      // -lse * log2 e of this lane's rows (-inf for padding rows)
   int ytok[NB];        // targets of this lane's rows (never matching for padding rows)
-  uint16_t* dzrow[NB];
+  uint16_t* dzblk[NB]; // this lane's 16 elements of block (token block, vocabulary block 0)
 
   __device__ __forceinline__ void chain(int buf, int vb, f32x16 (&acc)[NB]) const {
     logit_blocks<D, NB>(lds, buf, vb, h, col, hf, acc);
+  }
+
+  // Eight dZ values of this lane (accumulator registers 8 j8 .. 8 j8 + 7 of the block whose
+  // vocabulary rows start at vbase) as one 16-byte store into the block layout.
+  __device__ __forceinline__ void store8(const float* vals, int vbase, int tb, int j8) const {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)vals[e];
+    *reinterpret_cast<bf16x8*>(dzblk[tb] + (int64_t)(vbase >> 5) * 1024 + 8 * j8) = o;
   }
 
   // mode 0: series softcap (|z| <= c/8), 1: exact softcap, 2: no cap
   template <int MODE, bool MASKED>
   __device__ __forceinline__ void store_block(const f32x16& acc, int vbase, int tb) const {
     const int dy = ytok[tb] - vbase;
+    float vals[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float vals[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * q + e;
-        const int off = 8 * q + 4 * h + e;
-        const float z = acc[r];
-        float p, slope;
-        if (MODE == 0) {
-          const float u = z * z;
-          const float s2 = z * __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(sc.q3, u, sc.q2), u, sc.q1), u, sc.q0);
-          p = fexp2(s2 + bias[tb]);
-          const float t = s2 * sc.invM;              // s / c = tanh(z / c)
-          slope = __builtin_fmaf(-t, t, 1.0f);
-        } else if (MODE == 1) {
-          const float rk = capped_shifted(z, sc.alpha, sc.invK);   // K r, r = 1 / (1 + e^(2z/c))
-          p = fexp2(rk + (sc.M + bias[tb]));
-          const float rr = rk * sc.invK;
-          slope = rr * __builtin_fmaf(-4.0f, rr, 4.0f);             // 4 r (1 - r) = 1 - tanh^2
-        } else {
-          p = fexp2(__builtin_fmaf(z, kLog2e, bias[tb]));
-          slope = 1.0f;
-        }
-        const float g = (off == dy) ? p - 1.0f : p;
-        float val = g * slope;
-        if (MASKED) val = (vbase + off < V) ? val : 0.0f;
-        vals[e] = val;
+    for (int r = 0; r < 16; ++r) {
+      const int off = 8 * (r >> 2) + 4 * h + (r & 3);
+      const float z = acc[r];
+      float p, slope;
+      if (MODE == 0) {
+        const float u = z * z;
+        const float s2 = z * __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(sc.q3, u, sc.q2), u, sc.q1), u, sc.q0);
+        p = fexp2(s2 + bias[tb]);
+        const float t = s2 * sc.invM;              // s / c = tanh(z / c)
+        slope = __builtin_fmaf(-t, t, 1.0f);
+      } else if (MODE == 1) {
+        const float rk = capped_shifted(z, sc.alpha, sc.invK);   // K r, r = 1 / (1 + e^(2z/c))
+        p = fexp2(rk + (sc.M + bias[tb]));
+        const float rr = rk * sc.invK;
+        slope = rr * __builtin_fmaf(-4.0f, rr, 4.0f);             // 4 r (1 - r) = 1 - tanh^2
+      } else {
+        p = fexp2(__builtin_fmaf(z, kLog2e, bias[tb]));
+        slope = 1.0f;
       }
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (__bf16)vals[e];
-      *reinterpret_cast<bf16x4*>(dzrow[tb] + vbase + 8 * q + 4 * h) = o;
+      const float g = (off == dy) ? p - 1.0f : p;
+      float val = g * slope;
+      if (MASKED) val = (vbase + off < V) ? val : 0.0f;
+      vals[r] = val;
     }
+    store8(vals, vbase, tb, 0);
+    store8(vals + 8, vbase, tb, 1);
   }
 
   template <bool MASKED>
@@ -196,26 +200,92 @@ struct DzCore {
   }
 
   // MFMA chain of (buf, vb) with dZ of the pending full block `prev` formed and stored in the same
-  // basic block: series softcap first; blocks with some |z| > c/8 are redone exactly (the later
-  // store of the same lane to the same address wins).
+  // basic block, software pipelined by hand: k-step k issues the LDS read of a later step, the MFMA
+  // step k and stage s of the epilogue of element group k - s, so that the dependent operations of
+  // one logit sit an MFMA step apart and independent logits fill the gaps (with one wave per SIMD
+  // nothing else would). The softcap is the tanh series; a block with some |z| > c/8 (a
+  // wave-uniform, rarely taken branch) is redone exactly (the later store of the same lane to the
+  // same address wins).
   __device__ __forceinline__ void chain_with_store(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
-                                                   int vprev) const {
-    chain(buf, vb, a);
-    if (CAPPED) {
+                                                   int vprev) {
+    constexpr int NST = 10;                                  // epilogue stages
+    if (!CAPPED || KS < 2 * NST) {                           // short chains: no room to pipeline
+      chain(buf, vb, a);
+      if (!CAPPED) {
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) store_block<2, false>(prev[tb], vprev, tb);
+        return;
+      }
       float amax = 0.f;
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) {
         store_block<0, false>(prev[tb], vprev, tb);
         amax = fmaxf(amax, wave_absmax16(prev[tb]));
       }
-      interleave_hint2<KS, NB * 16 * 13>();
       if (!__all(amax <= sc.thr)) {
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) store_block<1, false>(prev[tb], vprev, tb);
       }
-    } else {
+      return;
+    }
+    using TL = TileLayout<D>;
+    constexpr int NE = NB * 16;                              // logits of `prev` per lane
+    // elements per group (a power of two, so a group of eight stored together is never split), small
+    // enough that every group finishes its last stage by step KS - 1 where possible
+    constexpr int EPC0 = (NE + (KS - NST)) / (KS - NST + 1);
+    constexpr int EPC = EPC0 <= 1 ? 1 : EPC0 <= 2 ? 2 : EPC0 <= 4 ? 4 : EPC0 <= 8 ? 8 : 16;
+    constexpr int NG = (NE + EPC - 1) / EPC;
+    constexpr int NSTEP = (NG + NST - 1) > KS ? (NG + NST - 1) : KS;
+    constexpr int PF = 4 < KS ? 4 : KS;
+    const int row = vb * 32 + col;
+    const lds_char* rbase = lds + buf * TL::TILEB + row * TL::PITCH;
+    const int sw = TL::swz(row);
+    auto frag = [&](int ks) -> bf16x8 {
+      return *(const __attribute__((address_space(3))) bf16x8*)(rbase + ((h * KS + ks) ^ sw) * 16);
+    };
+    bf16x8 fr[KS];
+    float u[NE], q[NE], t[NE], v[NE];
+    float amax = 0.f;
+    int dy[NB];
 #pragma unroll
-      for (int tb = 0; tb < NB; ++tb) store_block<2, false>(prev[tb], vprev, tb);
+    for (int tb = 0; tb < NB; ++tb) dy[tb] = ytok[tb] - vprev;
+#pragma unroll
+    for (int k = 0; k < PF; ++k) fr[k] = frag(k);
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+      if (k + PF < KS) fr[k + PF] = frag(k + PF);
+      if (k < KS) mfma_step<NB, KS>(a, fr[k], hf, k);
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int g = k - st;
+        if (g < 0 || g >= NG) continue;
+#pragma unroll
+        for (int e = g * EPC; e < (g + 1) * EPC && e < NE; ++e) {
+          const int tb = e / 16, r = e % 16;
+          const float z = prev[tb][r];
+          const int off = 8 * (r >> 2) + 4 * h + (r & 3);
+          switch (st) {
+            case 0: u[e] = z * z; amax = fmaxf(amax, fabsf(z)); break;
+            case 1: q[e] = __builtin_fmaf(sc.q3, u[e], sc.q2); break;
+            case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q1); break;
+            case 3: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
+            case 4: q[e] = z * q[e]; break;                                 // s log2 e
+            case 5: t[e] = q[e] * sc.invM; q[e] = q[e] + bias[tb]; break;  // s / c; log2 p
+            case 6: q[e] = fexp2(q[e]); t[e] = __builtin_fmaf(-t[e], t[e], 1.0f); break;
+            case 7: v[e] = (off == dy[tb]) ? q[e] - 1.0f : q[e]; break;
+            case 8: v[e] = v[e] * t[e]; break;
+            default:
+              if ((r & 7) == 7) store8(&v[e - 7], vprev, tb, r >> 3);   // eight values: one 16-byte store
+              break;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_finish<NB>(a);
+    if (!__all(amax <= sc.thr)) {
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) store_block<1, false>(prev[tb], vprev, tb);
     }
   }
 };
@@ -252,7 +322,7 @@ void bwd_dz_kernel(DzParams p) {
     for (int ks = 0; ks < KS; ++ks) core.hf[tb][ks] = src[ks];
     core.bias[tb] = valid ? -p.lse[grow] * kLog2e : -INFINITY;
     core.ytok[tb] = valid ? p.target[grow] : -(1 << 30);
-    core.dzrow[tb] = p.dz + tok * p.ldz;
+    core.dzblk[tb] = p.dz + ((tok >> 5) * (p.ldz >> 5)) * 1024 + lane * 16;
   }
 
   const int ntiles = p.n_vtiles;
@@ -367,7 +437,7 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
 
       // dH = g dZ E
       GemmParams a{};
-      a.A = dz; a.lda = q.ldz;
+      a.A = dz; a.lda = q.ldz / 32;
       a.B = (const uint16_t*)E; a.ldb = D;
       a.n_dev = n_dev; a.m_dev = n_dev != nullptr; a.k_dev = 0;
       a.M = T; a.N = D; a.K = V; a.kvalid = V;
@@ -384,7 +454,7 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     if (T == 0) return launch_sum_splits(nullptr, 0, (int64_t)V * D, (int64_t)V * D, dE, st);
     float* part = reinterpret_cast<float*>(ws + L.de_part);
     GemmParams b{};
-    b.A = dz; b.lda = ((V + kVocabTile - 1) / kVocabTile) * (int64_t)kVocabTile;
+    b.A = dz; b.lda = ((V + kVocabTile - 1) / kVocabTile) * (int64_t)kVocabTile / 32;
     b.B = (const uint16_t*)H; b.ldb = D;
     if (rows) {   // masked: the scored hidden rows, compacted, so that k runs over them directly
       uint16_t* hc = reinterpret_cast<uint16_t*>(ws + L.hc);

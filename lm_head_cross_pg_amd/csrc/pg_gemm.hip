@@ -2,22 +2,27 @@
 // dE = g dZ^T H, on gfx950 (v_mfma_f32_32x32x16_bf16).
 //
 // 128 x 512 output tiles per workgroup (4 waves of 128 x 128, sixteen 32 x 32 accumulators each,
-// held in AGPRs), 32-deep k-chunks in a 3-stage LDS ring filled by global_load_lds_dwordx4. An
-// operand whose k index is the slow one in memory (dZ read as dZ^T, E and H as k x n) is fed to
-// the MFMA with ds_read_b64_tr_b16, which gives each lane 4 consecutive k of one column, so no
-// transpose pass over memory is needed.
+// held in AGPRs), 32-deep k-chunks in a 3-stage LDS ring filled by global_load_lds_dwordx4.
+// A is dZ in its 32 x 32 block layout (described in pg_internal.h); each stage's A tile is four
+// whole blocks, i.e. four contiguous 2 KiB runs. The other operand (E for dH, H for dE) is k x n
+// row-major and is fed to the MFMA with ds_read_b64_tr_b16, which gives each lane 4 consecutive k
+// of one column, so no transpose pass over memory is needed; for dE the A operand is read the same
+// way from the blocks.
 #include "pg_common.h"
 #include "pg_internal.h"
+#include "pg_tile.h"
 
 namespace pg {
 
+// LDS tile layouts (bytes), 16-byte chunk indices permuted so that the 16 lanes of an LDS read
+// phase hit 16 different 16-byte bank groups:
+//   A: four dZ blocks of 2 KiB; chunk c of a block stored at chunk a_swz(c)
+//   B: [32 k][512 n], 1 KiB rows; chunk c of row k stored at c ^ (4 (k & 3))
+// a_swz flips chunk bit 0 when bit 4 is set (the plain 16-byte reads of dH, which stride two
+// chunks per lane) and bit 3 when bit 6 is set (the transposed reads of dE, which pair chunks 64
+// apart); it is its own inverse.
+__device__ __forceinline__ int a_swz(int c) { return c ^ ((c >> 4) & 1) ^ (((c >> 6) & 1) << 3); }
 
-
-// LDS tile layouts (bytes), 16-byte chunk index XORed so that the 16 lanes of an LDS read phase
-// hit 16 different 16-byte bank groups:
-//   k-contiguous A: [128 m][32 k], 64 B rows; chunk c of row m stored at c ^ ((m >> 2) & 3)
-//   k-slow A:       [32 k][128 m], 256 B rows; chunk c of row k stored at c ^ (4 (k & 3))
-//   B:              [32 k][512 n], 1 KiB rows; chunk c of row k stored at c ^ (4 (k & 3))
 // A workgroup owns a 128 x 512 output tile (the whole hidden width), so dZ is read from memory once.
 template <bool A_TRANS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -52,21 +57,20 @@ void gemm_bf16_kernel(GemmParams g) {
     const int64_t k0 = kc * BK;
 #pragma unroll
     for (int j = wave; j < A_LOADS; j += 4) {
-      const uint16_t* src;
-      if (!A_TRANS) {
-        const int row = 16 * j + (lane >> 2);
-        const int lc = (lane & 3) ^ ((row >> 2) & 3);
-        int64_t m = m0 + row;
-        m = m < M ? m : M - 1;
-        src = g.A + m * g.lda + k0 + 8 * lc;
-      } else {
-        const int row = 4 * j + (lane >> 4);
-        const int lc = (lane & 15) ^ (4 * (row & 3));
-        int64_t col = m0 + 8 * lc;
-        col = col <= g.lda - 8 ? col : g.lda - 8;
-        src = g.A + (k0 + row) * g.lda + col;
+      // instruction j: half (j & 1) of block bm = j / 2 of the stage
+      const int bm = j >> 1;
+      int64_t bt, bv;
+      if (!A_TRANS) {                   // dH: m = token, k = vocabulary
+        bt = (m0 >> 5) + bm;
+        bv = k0 >> 5;
+      } else {                          // dE: m = vocabulary, k = token
+        bt = k0 >> 5;
+        bv = (m0 >> 5) + bm;
+        bv = bv < g.lda ? bv : g.lda - 1;
       }
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(sA + j * 1024), 16, 0, 0);
+      const int chunk = a_swz(64 * (j & 1) + lane);
+      const uint16_t* src = g.A + (bt * g.lda + bv) * 1024 + chunk * 8;
+      lds_dma16(src, (const lds_char*)(sA + j * 1024));
     }
 #pragma unroll
     for (int j = wave; j < B_LOADS; j += 4) {
@@ -76,7 +80,7 @@ void gemm_bf16_kernel(GemmParams g) {
       k = k < kvalid ? k : kvalid - 1;
       int64_t col = n0 + 8 * lc;
       col = col <= g.ldb - 8 ? col : g.ldb - 8;
-      __builtin_amdgcn_global_load_lds(g.B + k * g.ldb + col, (lds_void*)(sB + j * 1024), 16, 0, 0);
+      lds_dma16(g.B + k * g.ldb + col, (const lds_char*)(sB + j * 1024));
     }
   };
 
@@ -92,11 +96,13 @@ void gemm_bf16_kernel(GemmParams g) {
   // transposed read: lanes of group grp take rows k0 + li / 4 and columns cbase + 16 (grp & 1) +
   // 4 (li & 3) .. + 3, for k0 = 16 ks + 8 (grp >> 1) + 4 half; lane i of the group receives 4
   // consecutive k of column cbase + 16 (grp & 1) + i
-  auto read_tr = [&](const char* tile, int pitch, int ks, int cbase) -> bf16x8 {
+  // With INTERLEAVED k order, half `half` of lane l's eight values covers rows 16 ks + 8 half +
+  // 4 (l / 32) .. + 3 instead of 16 ks + 8 (l / 32) + 4 half .. + 3 (the order the dZ blocks hold).
+  auto read_tr = [&](const char* tile, int pitch, int ks, int cbase, bool interleaved) -> bf16x8 {
     i16x4 part[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int k = 16 * ks + 8 * (grp >> 1) + 4 * half + (li >> 2);
+      const int k = 16 * ks + (interleaved ? 8 * half + 4 * (grp >> 1) : 8 * (grp >> 1) + 4 * half) + (li >> 2);
       const int c = cbase + 16 * (grp & 1) + 4 * (li & 3);
       const int addr = k * pitch + 16 * ((c >> 3) ^ (4 * (k & 3))) + 2 * (c & 7);
       part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + addr));
@@ -104,6 +110,35 @@ void gemm_bf16_kernel(GemmParams g) {
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     i16x8 v = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
     return __builtin_bit_cast(bf16x8, v);
+  };
+
+  // Fragments of one 16-deep k step: the 4 A blocks of this wave and its 4 B blocks.
+  auto load_frags = [&](const char* sA, const char* sB, int ks, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm) {
+      const char* blk = sA + bm * 2048;
+      if (!A_TRANS) {
+        // lane l holds row l % 32 of the block in its own 32 bytes: the 16 at chunk 2 l + ks are
+        // vocabulary rows 16 ks + 8 (j / 4) + 4 (l / 32) + j % 4, j = 0..7
+        af[bm] = *(const __attribute__((address_space(3))) bf16x8*)((const lds_char*)blk + a_swz(2 * lane + ks) * 16);
+      } else {
+        // transposed read: lane l receives vocabulary row l % 32 at tokens 16 ks + 8 (l / 32) + j;
+        // the lanes of a 16-lane group address 4 tokens x 4 runs of 4 vocabulary rows
+        i16x4 part[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int t = 16 * ks + 8 * (grp >> 1) + 4 * half + (li >> 2);
+          const int cg = li & 3;
+          const int c = 2 * (t + 32 * (cg & 1)) + (grp & 1);
+          part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(blk + a_swz(c) * 16 + 8 * (cg >> 1)));
+        }
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        i16x8 v = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
+        af[bm] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) bfr[bn] = read_tr(sB, BN * 2, ks, wave * 128 + bn * 32, !A_TRANS);
   };
 
   if (nk > 0) load_stage(kc_begin, 0);
@@ -117,26 +152,20 @@ void gemm_bf16_kernel(GemmParams g) {
     const int st = (int)(it % kGemmStages);
     const char* sA = smem + st * SBYTES;
     const char* sB = sA + ABYTES;
+    // every fragment of the stage is requested before the first MFMA; the compiler's waits then
+    // release each MFMA as soon as its own two fragments have arrived
+    bf16x8 af[BK / 16][4], bfr[BK / 16][4];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) load_frags(sA, sB, ks, af[ks], bfr[ks]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        if (!A_TRANS) {
-          const int row = bm * 32 + (lane & 31);
-          const int chunk = (2 * ks + h) ^ ((row >> 2) & 3);
-          af[bm] = *(const __attribute__((address_space(3))) bf16x8*)((const lds_char*)sA + row * 64 + chunk * 16);
-        } else {
-          af[bm] = read_tr(sA, BM * 2, ks, bm * 32);
-        }
-      }
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn) bfr[bn] = read_tr(sB, BN * 2, ks, wave * 128 + bn * 32);
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma32x32x16(af[bm], bfr[bn], acc[bm][bn]);
+        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma32x32x16(af[ks][bm], bfr[ks][bn], acc[bm][bn]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue: alpha * acc to C (row-scattered) or to this split's partial tile

@@ -21,7 +21,7 @@ int64_t fwd_partial_entries(int64_t T);
 struct BwdWorkspace {
   size_t n_rows;   // int32
   size_t rows;     // int32[T]
-  size_t dz;       // bf16[T, V]: dZ without the grad_scale factor
+  size_t dz;       // bf16 dZ without the grad_scale factor, block layout, T rounded up to 256, V to 64
   size_t hc;       // bf16[T, D]: hidden rows of the scored positions, compacted (masked calls)
   size_t de_part;  // f32[KSPLIT, V, D]: split-K partials of dE
   size_t total;
@@ -57,11 +57,18 @@ hipError_t launch_bpb(const float* nats, const int32_t* target, const uint8_t* m
                       const int32_t* byte_len, const int32_t* byte_per_pos, int64_t T, int32_t V,
                       double* out, char* ws, hipStream_t st);
 
+// dZ block layout (the backward's workspace). dZ[t][v] is stored in 32 x 32 blocks laid out like
+// the accumulator of v_mfma_f32_32x32x16_bf16: block (bt, bv) holds tokens 32 bt .. 32 bt + 31 and
+// vocabulary rows 32 bv .. 32 bv + 31 as 1024 bf16 at offset (bt * nvb + bv) * 1024, nvb = number
+// of vocabulary blocks; inside a block, element (t, v) sits at 16 L + r with
+//   L = t + 32 ((v >> 2) & 1)   (the lane that computed it),  r = 4 (v >> 3) + (v & 3).
+// Each lane of the dZ kernel thus writes 32 contiguous bytes and each block is one 2 KiB run.
+
 // C = alpha * A B in bf16 with float32 accumulation (pg_gemm.hip).
 constexpr int kGemmBM = 128, kGemmBN = 512, kGemmBK = 32, kGemmStages = 3;
 struct GemmParams {
-  const uint16_t* A;      // element (m, k): A_TRANS ? A[k * lda + m] : A[m * lda + k]
-  int64_t lda;
+  const uint16_t* A;      // dZ blocks; element (m, k) = dZ[m][k], or dZ[k][m] when A_TRANS
+  int64_t lda;            // vocabulary blocks per token block (nvb)
   const uint16_t* B;      // element (k, n): B[k * ldb + n]
   int64_t ldb;
   const int32_t* n_dev;   // device count that replaces M (m_dev) or K (k_dev)
@@ -74,8 +81,8 @@ struct GemmParams {
   const int32_t* crows;   // output row of m when given
   int64_t split_stride;   // elements between the partial outputs of k splits
 };
-// a_trans: A's element (m, k) is A[k * lda + m] (else A[m * lda + k]). grid = (m tiles, n tiles,
-// k splits); with several splits, C receives one partial output per split at split_stride.
+// a_trans: A's element (m, k) is dZ[k][m] (else dZ[m][k]). grid = (m tiles, n tiles, k splits);
+// with several splits, C receives one partial output per split at split_stride.
 hipError_t launch_gemm(const GemmParams& g, bool a_trans, dim3 grid, hipStream_t st);
 // out[i] = sum over s < nsplit of part[s * stride + i], in split order (nsplit = 0 writes zeros).
 hipError_t launch_sum_splits(const float* part, int nsplit, int64_t stride, int64_t count, float* out,
