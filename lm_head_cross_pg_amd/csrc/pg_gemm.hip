@@ -50,14 +50,16 @@ void gemm_bf16_kernel(GemmParams g) {
   const int64_t nk = kc_end > kc_begin ? kc_end - kc_begin : 0;
   const int64_t kvalid = g.k_dev ? ndev : g.kvalid;
 
-  // ---- stage loader: each wave issues LOADS_PER_WAVE global_load_lds_dwordx4
-  auto load_stage = [&](int64_t kc, int st) {
+  // ---- stage loader: each wave issues LOADS_PER_WAVE global_load_lds_dwordx4; load_one(kc, st, i)
+  //      issues this wave's i-th, so that the loads of a stage can be spread over the MFMAs of the
+  //      previous one (issued in a burst they stall the wave for longer than the MFMAs take)
+  static_assert(A_LOADS % 4 == 0 && B_LOADS % 4 == 0, "loads split evenly over the 4 waves");
+  auto load_one = [&](int64_t kc, int st, int i) {
     char* sA = smem + st * SBYTES;
     char* sB = sA + ABYTES;
     const int64_t k0 = kc * BK;
-#pragma unroll
-    for (int j = wave; j < A_LOADS; j += 4) {
-      // instruction j: half (j & 1) of block bm = j / 2 of the stage
+    if (i < A_LOADS / 4) {
+      const int j = wave + 4 * i;       // half (j & 1) of block bm = j / 2 of the stage
       const int bm = j >> 1;
       int64_t bt, bv;
       if (!A_TRANS) {                   // dH: m = token, k = vocabulary
@@ -71,17 +73,19 @@ void gemm_bf16_kernel(GemmParams g) {
       const int chunk = a_swz(64 * (j & 1) + lane);
       const uint16_t* src = g.A + (bt * g.lda + bv) * 1024 + chunk * 8;
       lds_dma16(src, (const lds_char*)(sA + j * 1024));
-    }
-#pragma unroll
-    for (int j = wave; j < B_LOADS; j += 4) {
-      const int row = j;
-      const int lc = lane ^ (4 * (row & 3));
-      int64_t k = k0 + row;
+    } else {
+      const int j = wave + 4 * (i - A_LOADS / 4);   // row j of the B tile
+      const int lc = lane ^ (4 * (j & 3));
+      int64_t k = k0 + j;
       k = k < kvalid ? k : kvalid - 1;
       int64_t col = n0 + 8 * lc;
       col = col <= g.ldb - 8 ? col : g.ldb - 8;
       lds_dma16(g.B + k * g.ldb + col, (const lds_char*)(sB + j * 1024));
     }
+  };
+  auto load_stage = [&](int64_t kc, int st) {
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) load_one(kc, st, i);
   };
 
   f32x16 acc[4][4];
@@ -148,7 +152,6 @@ void gemm_bf16_kernel(GemmParams g) {
     if (it + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_WAVE) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();   // every wave's loads of stage `it` landed; stage it-1 is free
-    if (it + 2 < nk) load_stage(kc_begin + it + 2, (int)((it + 2) % kGemmStages));
     const int st = (int)(it % kGemmStages);
     const char* sA = smem + st * SBYTES;
     const char* sB = sA + ABYTES;
@@ -158,14 +161,21 @@ void gemm_bf16_kernel(GemmParams g) {
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) load_frags(sA, sB, ks, af[ks], bfr[ks]);
     __builtin_amdgcn_sched_barrier(0);
+    // the MFMAs of this stage with the loads of stage it + 2 (into the buffer stage it - 1 used)
+    // issued between them, one every MFMA_PER_LOAD MFMAs
+    constexpr int NMFMA = (BK / 16) * 16;
+    constexpr int MFMA_PER_LOAD = NMFMA / LOADS_PER_WAVE;
+    const bool prefetch = it + 2 < nk;
+    const int64_t kc_pf = kc_begin + it + 2;
+    const int st_pf = (int)((it + 2) % kGemmStages);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-        for (int bn = 0; bn < 4; ++bn) acc[bm][bn] = mfma32x32x16(af[ks][bm], bfr[ks][bn], acc[bm][bn]);
+    for (int mi = 0; mi < NMFMA; ++mi) {
+      const int ks = mi >> 4, bm = (mi >> 2) & 3, bn = mi & 3;
+      acc[bm][bn] = mfma32x32x16(af[ks][bm], bfr[ks][bn], acc[bm][bn]);
+      if (mi % MFMA_PER_LOAD == 0 && mi / MFMA_PER_LOAD < LOADS_PER_WAVE && prefetch)
+        load_one(kc_pf, st_pf, mi / MFMA_PER_LOAD);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue: alpha * acc to C (row-scattered) or to this split's partial tile
