@@ -99,6 +99,28 @@ pg_status pg_lmhead_ce_bwd(const void* hidden, const void* embed, int32_t dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Asymmetric softcap variants: s = cap_pos * tanh(z / cap_pos) for z >= 0 and
+ * s = cap_neg * tanh(z / cap_neg) for z < 0 (ds/dz = 1 - (s / cap)^2 on each side; a cap of 0 leaves
+ * that side uncapped). The pages name an "AsymLogit" change to the head (HYDRA Golf site,
+ * leaderboard table, entries #1 and #4; README leaderboard, PR #2135 and PR #1945 rows) without
+ * defining it; separate caps for positive and negative logits is the reading taken here. With
+ * cap_pos == cap_neg these equal pg_lmhead_ce_fwd / pg_lmhead_ce_bwd. Arguments, workspace sizes
+ * and errors are those of the symmetric entry points; either cap negative or not finite gives
+ * PG_ERR_SOFTCAP.
+ */
+pg_status pg_lmhead_ce_fwd_asym(const void* hidden, const void* embed, int32_t dtype,
+                                const int32_t* target, const uint8_t* score_mask,
+                                int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
+                                float* nats, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+pg_status pg_lmhead_ce_bwd_asym(const void* hidden, const void* embed, int32_t dtype,
+                                const int32_t* target, const uint8_t* score_mask, const float* lse,
+                                int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg, float grad_scale,
+                                float* dhidden, float* dembed,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bits per byte over the scored rows (tproger article, "Правила и метрика": the score counts
  * compression in bytes, independent of the tokenizer).
  *   nats          [T] f32 from pg_lmhead_ce_fwd

@@ -25,8 +25,8 @@ STATUS_NAMES = {0: "PG_OK", -1: "PG_ERR_NULL", -2: "PG_ERR_SHAPE", -3: "PG_ERR_D
                 -5: "PG_ERR_WORKSPACE", -6: "PG_ERR_ALIGN", -7: "PG_ERR_DEVICE", -8: "PG_ERR_HIP"}
 
 # every symbol the header declares
-EXPORTS = ("pg_lmhead_ce_fwd", "pg_lmhead_ce_bwd", "pg_bpb_reduce", "pg_workspace_bytes",
-           "pg_status_str", "pg_abi_version")
+EXPORTS = ("pg_lmhead_ce_fwd", "pg_lmhead_ce_bwd", "pg_lmhead_ce_fwd_asym", "pg_lmhead_ce_bwd_asym",
+           "pg_bpb_reduce", "pg_workspace_bytes", "pg_status_str", "pg_abi_version")
 
 
 class PgError(RuntimeError):
@@ -51,6 +51,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pg_lmhead_ce_fwd.restype = i32
     lib.pg_lmhead_ce_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i32, i32, f32, f32, vp, vp, vp, sz, vp]
     lib.pg_lmhead_ce_bwd.restype = i32
+    lib.pg_lmhead_ce_fwd_asym.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, f32, f32, vp, vp, vp, sz, vp]
+    lib.pg_lmhead_ce_fwd_asym.restype = i32
+    lib.pg_lmhead_ce_bwd_asym.argtypes = [vp, vp, i32, vp, vp, vp, i64, i32, i32, f32, f32, f32, vp, vp, vp, sz, vp]
+    lib.pg_lmhead_ce_bwd_asym.restype = i32
     lib.pg_bpb_reduce.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, sz, vp]
     lib.pg_bpb_reduce.restype = i32
     lib.pg_workspace_bytes.argtypes = [i32, i64, i32, i32]
@@ -134,6 +138,33 @@ def pg_lmhead_ce_bwd(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Te
                                  _ptr(lse), T, D, V, float(softcap), float(grad_scale), _ptr(dhidden),
                                  _ptr(dembed), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "pg_lmhead_ce_bwd")
+
+
+def pg_lmhead_ce_fwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Tensor,
+                          score_mask: Optional[torch.Tensor], cap_pos: float, cap_neg: float,
+                          nats: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    T, D = hidden.shape
+    V = embed.shape[0]
+    ws = _workspace(PG_OP_FWD, T, D, V, embed, workspace)
+    st = load().pg_lmhead_ce_fwd_asym(_ptr(hidden), _ptr(embed), _dtype_code(hidden), _ptr(target),
+                                      _ptr(score_mask), T, D, V, float(cap_pos), float(cap_neg), _ptr(nats),
+                                      _ptr(lse), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "pg_lmhead_ce_fwd_asym")
+
+
+def pg_lmhead_ce_bwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Tensor,
+                          score_mask: Optional[torch.Tensor], lse: torch.Tensor, cap_pos: float, cap_neg: float,
+                          grad_scale: float, dhidden: torch.Tensor, dembed: torch.Tensor,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    T, D = hidden.shape
+    V = embed.shape[0]
+    ws = _workspace(PG_OP_BWD, T, D, V, embed, workspace)
+    st = load().pg_lmhead_ce_bwd_asym(_ptr(hidden), _ptr(embed), _dtype_code(hidden), _ptr(target),
+                                      _ptr(score_mask), _ptr(lse), T, D, V, float(cap_pos), float(cap_neg),
+                                      float(grad_scale), _ptr(dhidden), _ptr(dembed), _ptr(ws), ws.numel(),
+                                      _stream(stream))
+    _check(st, "pg_lmhead_ce_bwd_asym")
 
 
 def pg_bpb_reduce(nats: torch.Tensor, target: torch.Tensor, score_mask: Optional[torch.Tensor],

@@ -84,39 +84,36 @@ size_t pg_workspace_bytes(int32_t op, int64_t T, int32_t D, int32_t V) {
   }
 }
 
-pg_status pg_lmhead_ce_fwd(const void* hidden, const void* embed, int32_t dtype,
-                           const int32_t* target, const uint8_t* score_mask,
-                           int64_t T, int32_t D, int32_t V, float softcap,
-                           float* nats, float* lse,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+static pg_status fwd_impl(const void* hidden, const void* embed, int32_t dtype, const int32_t* target,
+                          const uint8_t* score_mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
+                          float* nats, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   pg_status s;
   if ((s = check_shape(T, D, V)) != PG_OK) return s;
   if (T > 0 && (!hidden || !target || !nats)) return PG_ERR_NULL;
   if (!embed || !workspace) return PG_ERR_NULL;
   if (dtype != PG_DTYPE_BF16 && dtype != PG_DTYPE_F32) return PG_ERR_DTYPE;
-  if ((s = check_softcap(softcap)) != PG_OK) return s;
+  if ((s = check_softcap(cap_pos)) != PG_OK || (s = check_softcap(cap_neg)) != PG_OK) return s;
   if (misaligned(hidden) || misaligned(embed) || misaligned(target) || misaligned(score_mask) ||
       misaligned(nats) || misaligned(lse) || misaligned(workspace))
     return PG_ERR_ALIGN;
   if (workspace_bytes < pg_workspace_bytes(PG_OP_FWD, T, D, V)) return PG_ERR_WORKSPACE;
   pg::DeviceInfo dev{};
   if ((s = device_check(dev)) != PG_OK) return s;
-  hipError_t e = pg::launch_fwd(hidden, embed, dtype, target, score_mask, T, D, V, softcap, nats, lse,
+  hipError_t e = pg::launch_fwd(hidden, embed, dtype, target, score_mask, T, D, V, cap_pos, cap_neg, nats, lse,
                                 static_cast<char*>(workspace), dev, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PG_OK : PG_ERR_HIP;
 }
 
-pg_status pg_lmhead_ce_bwd(const void* hidden, const void* embed, int32_t dtype,
-                           const int32_t* target, const uint8_t* score_mask, const float* lse,
-                           int64_t T, int32_t D, int32_t V, float softcap, float grad_scale,
-                           float* dhidden, float* dembed,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+static pg_status bwd_impl(const void* hidden, const void* embed, int32_t dtype, const int32_t* target,
+                          const uint8_t* score_mask, const float* lse, int64_t T, int32_t D, int32_t V,
+                          float cap_pos, float cap_neg, float grad_scale, float* dhidden, float* dembed,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   pg_status s;
   if ((s = check_shape(T, D, V)) != PG_OK) return s;
   if (T > 0 && (!hidden || !target || !lse || !dhidden)) return PG_ERR_NULL;
   if (!embed || !dembed || !workspace) return PG_ERR_NULL;
   if (dtype != PG_DTYPE_BF16 && dtype != PG_DTYPE_F32) return PG_ERR_DTYPE;
-  if ((s = check_softcap(softcap)) != PG_OK) return s;
+  if ((s = check_softcap(cap_pos)) != PG_OK || (s = check_softcap(cap_neg)) != PG_OK) return s;
   if (!std::isfinite(grad_scale)) return PG_ERR_SOFTCAP;
   if (misaligned(hidden) || misaligned(embed) || misaligned(target) || misaligned(score_mask) ||
       misaligned(lse) || misaligned(dhidden) || misaligned(dembed) || misaligned(workspace))
@@ -124,10 +121,46 @@ pg_status pg_lmhead_ce_bwd(const void* hidden, const void* embed, int32_t dtype,
   if (workspace_bytes < pg_workspace_bytes(PG_OP_BWD, T, D, V)) return PG_ERR_WORKSPACE;
   pg::DeviceInfo dev{};
   if ((s = device_check(dev)) != PG_OK) return s;
-  hipError_t e = pg::launch_bwd(hidden, embed, dtype, target, score_mask, lse, T, D, V, softcap, grad_scale,
-                                dhidden, dembed, static_cast<char*>(workspace), dev,
+  hipError_t e = pg::launch_bwd(hidden, embed, dtype, target, score_mask, lse, T, D, V, cap_pos, cap_neg,
+                                grad_scale, dhidden, dembed, static_cast<char*>(workspace), dev,
                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PG_OK : PG_ERR_HIP;
+}
+
+pg_status pg_lmhead_ce_fwd(const void* hidden, const void* embed, int32_t dtype,
+                           const int32_t* target, const uint8_t* score_mask,
+                           int64_t T, int32_t D, int32_t V, float softcap,
+                           float* nats, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(hidden, embed, dtype, target, score_mask, T, D, V, softcap, softcap, nats, lse, workspace,
+                  workspace_bytes, stream);
+}
+
+pg_status pg_lmhead_ce_bwd(const void* hidden, const void* embed, int32_t dtype,
+                           const int32_t* target, const uint8_t* score_mask, const float* lse,
+                           int64_t T, int32_t D, int32_t V, float softcap, float grad_scale,
+                           float* dhidden, float* dembed,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(hidden, embed, dtype, target, score_mask, lse, T, D, V, softcap, softcap, grad_scale, dhidden,
+                  dembed, workspace, workspace_bytes, stream);
+}
+
+pg_status pg_lmhead_ce_fwd_asym(const void* hidden, const void* embed, int32_t dtype,
+                                const int32_t* target, const uint8_t* score_mask,
+                                int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
+                                float* nats, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(hidden, embed, dtype, target, score_mask, T, D, V, cap_pos, cap_neg, nats, lse, workspace,
+                  workspace_bytes, stream);
+}
+
+pg_status pg_lmhead_ce_bwd_asym(const void* hidden, const void* embed, int32_t dtype,
+                                const int32_t* target, const uint8_t* score_mask, const float* lse,
+                                int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg, float grad_scale,
+                                float* dhidden, float* dembed,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(hidden, embed, dtype, target, score_mask, lse, T, D, V, cap_pos, cap_neg, grad_scale, dhidden,
+                  dembed, workspace, workspace_bytes, stream);
 }
 
 pg_status pg_bpb_reduce(const float* nats, const int32_t* target, const uint8_t* score_mask,

@@ -37,16 +37,9 @@ __global__ __launch_bounds__(256) void dz_generic_kernel(const TIn* H, const TIn
     const TIn* erow = E + (int64_t)v * D;
     float z = 0.f;
     for (int d = 0; d < D; ++d) z = __builtin_fmaf(bload(hrow, d), bload(erow, d), z);
-    float p, slope;
-    if (sc.c > 0.f) {
-      const float rk = capped_shifted(z, sc.alpha, sc.invK);   // K r
-      p = fexp2(sc.M + rk - lse2);
-      const float rr = rk * sc.invK;                            // r = 1 / (1 + e^(2z/c))
-      slope = 4.0f * rr * (1.0f - rr);                          // 1 - tanh^2 = 4 r (1 - r)
-    } else {
-      p = fexp2(z * kLog2e - lse2);
-      slope = 1.0f;
-    }
+    float s2, slope;
+    capped_log2_slope(z, sc, s2, slope);                        // s log2 e, 1 - (s / c)^2
+    const float p = fexp2(s2 - lse2);
     const float g = (v == y) ? p - 1.0f : p;
     dz[i * V + v] = f32_to_bf16(g * slope);
   }
@@ -173,10 +166,9 @@ struct DzCore {
         const float t = s2 * sc.invM;              // s / c = tanh(z / c)
         slope = __builtin_fmaf(-t, t, 1.0f);
       } else if (MODE == 1) {
-        const float rk = capped_shifted(z, sc.alpha, sc.invK);   // K r, r = 1 / (1 + e^(2z/c))
-        p = fexp2(rk + (sc.M + bias[tb]));
-        const float rr = rk * sc.invK;
-        slope = rr * __builtin_fmaf(-4.0f, rr, 4.0f);             // 4 r (1 - r) = 1 - tanh^2
+        float s2;
+        capped_log2_slope(z, sc, s2, slope);                     // either cap form, exact
+        p = fexp2(s2 + bias[tb]);
       } else {
         p = fexp2(__builtin_fmaf(z, kLog2e, bias[tb]));
         slope = 1.0f;
@@ -209,6 +201,12 @@ struct DzCore {
   __device__ __forceinline__ void chain_with_store(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
                                                    int vprev) {
     constexpr int NST = 10;                                  // epilogue stages
+    if (CAPPED && sc.asym) {                                 // asymmetric caps: exact form only
+      chain(buf, vb, a);
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) store_block<1, false>(prev[tb], vprev, tb);
+      return;
+    }
     if (!CAPPED || KS < 2 * NST) {                           // short chains: no room to pipeline
       chain(buf, vb, a);
       if (!CAPPED) {
@@ -366,7 +364,7 @@ constexpr int kDzTokBlocks = 2;
 
 template <int D>
 static void launch_dz(const DzParams& q, unsigned blocks, hipStream_t st) {
-  if (q.sc.c > 0.f)
+  if (q.sc.capped())
     hipLaunchKernelGGL((bwd_dz_kernel<D, true, kDzTokBlocks>), dim3(blocks), dim3(WaveShape<kDzTokBlocks>::kThreads), 0,
                        st, q);
   else
@@ -390,10 +388,10 @@ BwdWorkspace bwd_workspace(int64_t T, int32_t D, int32_t V) {
 
 hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t* target,
                       const uint8_t* mask, const float* lse, int64_t T, int32_t D, int32_t V,
-                      float softcap, float grad_scale, float* dH, float* dE, char* ws,
+                      float cap_pos, float cap_neg, float grad_scale, float* dH, float* dE, char* ws,
                       const DeviceInfo& dev, hipStream_t st) {
   const BwdWorkspace L = bwd_workspace(T, D, V);
-  const Softcap sc = Softcap::make(softcap);
+  const Softcap sc = Softcap::make(cap_pos, cap_neg);
   const int32_t* rows = nullptr;
   const int32_t* n_dev = nullptr;
   if (mask && T > 0) {

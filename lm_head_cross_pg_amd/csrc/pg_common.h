@@ -50,8 +50,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // rounding. In base 2: s * log2 e = z * Q(z^2), Q(u) = q0 + q1 u + q2 u^2 + q3 u^3 with
 // q0 = log2 e, q1 = -log2 e / (3 c^2), q2 = 2 log2 e / (15 c^4), q3 = -17 log2 e / (315 c^6):
 // three fma and two multiplies, no transcendental.
+//
+// Asymmetric caps: c (the fields above) applies to z >= 0 and cn to z < 0, each side with its own
+// constants; 0 leaves that side uncapped. The series fast path is not used then (thr = 0), and the
+// fixed log-sum-exp shift is M = c log2 e, the largest possible s * log2 e.
 struct Softcap {
-  float c;        // cap (0 = none)
+  float c;        // cap (0 = none); the cap of z >= 0 when asym
   float alpha;    // 2 log2 e / c
   float M;        // c log2 e
   float K;        // -2 M
@@ -59,12 +63,17 @@ struct Softcap {
   float invM;     // 1 / M
   float q0, q1, q2, q3;  // series coefficients of s * log2 e in powers of z^2
   float thr;      // series used when every |z| of a block is <= thr (c / 8; 0 = never)
-  bool fixed;     // fixed log-sum-exp shift M (0 < c <= kFixedShiftMaxCap)
-  __host__ static Softcap make(float cap) {
-    Softcap s;
+  bool fixed;     // fixed log-sum-exp shift M (every side capped, caps <= kFixedShiftMaxCap)
+  bool asym;      // separate cap cn for z < 0
+  float cn, alpha_n, M_n, invK_n;   // the z < 0 side (asym only)
+  __host__ static Softcap make(float cap) { return make(cap, cap); }
+  __host__ static Softcap make(float cap, float cap_neg) {
+    Softcap s{};
+    const double l2e = 1.4426950408889634;
     s.c = cap;
+    s.asym = cap != cap_neg;
     if (cap > 0.f) {
-      const double c = cap, l2e = 1.4426950408889634;
+      const double c = cap;
       s.alpha = (float)(2.0 * l2e / c);
       s.M = (float)(c * l2e);
       s.K = -2.0f * s.M;
@@ -74,14 +83,20 @@ struct Softcap {
       s.q1 = (float)(-l2e / (3.0 * c * c));
       s.q2 = (float)(2.0 * l2e / (15.0 * c * c * c * c));
       s.q3 = (float)(-17.0 * l2e / (315.0 * c * c * c * c * c * c));
-      s.thr = (cap >= 0.01f) ? cap / 8.0f : 0.0f;
-      s.fixed = cap <= kFixedShiftMaxCap;
-    } else {
-      s.alpha = 0.f; s.M = 0.f; s.K = 0.f; s.invK = 0.f; s.invM = 0.f;
-      s.q0 = s.q1 = s.q2 = s.q3 = 0.f; s.thr = 0.f; s.fixed = false;
+      s.thr = (cap >= 0.01f && !s.asym) ? cap / 8.0f : 0.0f;
     }
+    if (s.asym && cap_neg > 0.f) {
+      s.cn = cap_neg;
+      s.alpha_n = (float)(2.0 * l2e / cap_neg);
+      s.M_n = (float)(cap_neg * l2e);
+      s.invK_n = 1.0f / (-2.0f * s.M_n);
+    }
+    s.fixed = cap > 0.f && cap <= kFixedShiftMaxCap &&
+              (!s.asym || (cap_neg > 0.f && cap_neg <= kFixedShiftMaxCap));
     return s;
   }
+  // some side of the cap is active
+  __host__ __device__ bool capped() const { return c > 0.f || (asym && cn > 0.f); }
 };
 
 // s * log2 e by the series (valid for |z| <= c / 8).
@@ -97,10 +112,38 @@ __device__ __forceinline__ float capped_shifted(float z, float alpha, float invK
   return frcp(__builtin_fmaf(e, invK, invK));
 }
 
+// s * log2 e and ds/dz = 1 - (s / c_side)^2 for either cap form (exact, no series).
+__device__ __forceinline__ void capped_log2_slope(float z, const Softcap& sc, float& s2, float& slope) {
+  const bool neg = sc.asym && z < 0.f;
+  const float c = neg ? sc.cn : sc.c;
+  if (c > 0.f) {
+    const float invK = neg ? sc.invK_n : sc.invK;
+    const float rk = capped_shifted(z, neg ? sc.alpha_n : sc.alpha, invK);   // K r
+    s2 = (neg ? sc.M_n : sc.M) + rk;
+    const float rr = rk * invK;
+    slope = rr * __builtin_fmaf(-4.0f, rr, 4.0f);                            // 4 r (1 - r)
+  } else {
+    s2 = z * kLog2e;
+    slope = 1.0f;
+  }
+}
+
 // Capped logit in base 2 (s * log2 e).
 __device__ __forceinline__ float capped_log2(float z, const Softcap& sc) {
-  if (sc.c > 0.f) return sc.M + capped_shifted(z, sc.alpha, sc.invK);
-  return z * kLog2e;
+  if (!sc.asym) {
+    if (sc.c > 0.f) return sc.M + capped_shifted(z, sc.alpha, sc.invK);
+    return z * kLog2e;
+  }
+  float s2, slope;
+  capped_log2_slope(z, sc, s2, slope);
+  return s2;
+}
+
+// (s * log2 e) - M for the fixed-shift log-sum-exp (sc.fixed: every side capped).
+__device__ __forceinline__ float capped_shifted_sc(float z, const Softcap& sc) {
+  if (!sc.asym) return capped_shifted(z, sc.alpha, sc.invK);
+  return z < 0.f ? (sc.M_n - sc.M) + capped_shifted(z, sc.alpha_n, sc.invK_n)
+                 : capped_shifted(z, sc.alpha, sc.invK);
 }
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {

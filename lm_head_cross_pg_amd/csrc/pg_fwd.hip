@@ -96,7 +96,7 @@ struct FwdCore {
     float part = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float w = fexp2(capped_shifted(acc[r], sc.alpha, sc.invK));
+      const float w = fexp2(capped_shifted_sc(acc[r], sc));
       if (MASKED) {
         const int v = vbase + 8 * (r >> 2) + 4 * h + (r & 3);
         part += v < V ? w : 0.f;
@@ -146,10 +146,13 @@ struct FwdCore {
   // |z| of `prev` exceeds c/8 (a wave-uniform, rarely taken branch) the exact sum replaces it.
   __device__ __forceinline__ void chain_with_epilogue(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
                                                       int vprev) {
-    if (!FIXED) {
+    if (!FIXED || sc.asym) {   // running maximum, or asymmetric caps (exact form only)
       chain(buf, vb, a);
 #pragma unroll
-      for (int tb = 0; tb < NB; ++tb) online<false>(prev[tb], vprev, tb);
+      for (int tb = 0; tb < NB; ++tb) {
+        if (FIXED) lsum[tb] += part_exact<false>(prev[tb], vprev);
+        else online<false>(prev[tb], vprev, tb);
+      }
       return;
     }
     using TL = TileLayout<D>;
@@ -496,11 +499,11 @@ static void launch_mfma_d(const FwdParams& p, int grid, hipStream_t st) {
 }
 
 hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t* target,
-                      const uint8_t* mask, int64_t T, int32_t D, int32_t V, float softcap,
+                      const uint8_t* mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
                       float* nats, float* lse, char* ws, const DeviceInfo& dev, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const FwdWorkspace L = fwd_workspace(T, D, V);
-  const Softcap sc = Softcap::make(softcap);
+  const Softcap sc = Softcap::make(cap_pos, cap_neg);
   const int32_t* rows = nullptr;
   const int32_t* n_dev = nullptr;
   if (mask) {

@@ -39,17 +39,18 @@ struct DeviceInfo {
   int cu_count;
 };
 
-// Forward launchers (pg_fwd.hip). `ws` is the workspace base.
+// Forward launchers (pg_fwd.hip). `ws` is the workspace base. Caps: z >= 0 uses cap_pos, z < 0
+// cap_neg (equal for the symmetric softcap); 0 = uncapped side.
 hipError_t launch_compact_rows(const uint8_t* mask, int64_t T, char* ws, const FwdWorkspace& L,
                                float* nats, float* lse, hipStream_t st);
 hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t* target,
-                      const uint8_t* mask, int64_t T, int32_t D, int32_t V, float softcap,
+                      const uint8_t* mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
                       float* nats, float* lse, char* ws, const DeviceInfo& dev, hipStream_t st);
 
 // Backward launcher (pg_bwd.hip).
 hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t* target,
                       const uint8_t* mask, const float* lse, int64_t T, int32_t D, int32_t V,
-                      float softcap, float grad_scale, float* dH, float* dE, char* ws,
+                      float cap_pos, float cap_neg, float grad_scale, float* dH, float* dE, char* ws,
                       const DeviceInfo& dev, hipStream_t st);
 
 // Bits-per-byte launcher (pg_bpb.hip).

@@ -12,6 +12,11 @@ What it computes, and where the pages state it:
 * Logit softcap: the pages only say the logits are "softcapped" (HYDRA Golf site, stack list,
   "fused softcapped CE kernel"; README leaderboard, PR #1787 row). Reading taken: s = c * tanh(z / c)
   with c = 30; c = 0 means no cap (s = z).
+* Asymmetric softcap: the pages name an "AsymLogit" head change (HYDRA Golf site, leaderboard
+  table, entries #1 and #4; README leaderboard, PR #2135 and PR #1945 rows) without defining it.
+  Reading taken: separate caps for positive and negative logits, s = c_pos tanh(z / c_pos) for
+  z >= 0 and c_neg tanh(z / c_neg) for z < 0; every function taking a cap c accepts the pair
+  (c_pos, c_neg) in its place.
 * Cross-entropy against the next token, in nats: lse(s) - s[target] (trios issue, "Контекст":
   "cross-entropy loss / bits-per-byte"; repo-explainer, ``loss = criterion(logits, batch["y"])``).
 * Bits per byte: total -log2 p(target) over scored rows divided by the total UTF-8 bytes of those
@@ -44,18 +49,46 @@ def logits(H: np.ndarray, E: np.ndarray) -> np.ndarray:
     return np.asarray(H, dtype=np.float64) @ np.asarray(E, dtype=np.float64).T
 
 
-def softcap(z: np.ndarray, c: float) -> np.ndarray:
-    """s = c * tanh(z / c) for c > 0; s = z when c == 0 (no cap)."""
+def _caps(c):
+    """(cap of z >= 0, cap of z < 0). A single number caps both sides alike; a pair (c_pos, c_neg)
+    is the asymmetric softcap."""
+    if isinstance(c, (tuple, list)):
+        return float(c[0]), float(c[1])
+    return float(c), float(c)
+
+
+def _cap_side(z: np.ndarray, c: float) -> np.ndarray:
     if c > 0:
         return c * np.tanh(z / c)
     return np.array(z, dtype=np.float64, copy=True)
 
 
-def softcap_derivative(z: np.ndarray, c: float) -> np.ndarray:
-    """ds/dz = 1 - tanh(z / c)^2 for c > 0, else 1."""
+def _cap_side_derivative(z: np.ndarray, c: float) -> np.ndarray:
     if c > 0:
         return 1.0 - np.tanh(z / c) ** 2
     return np.ones_like(z, dtype=np.float64)
+
+
+def softcap(z: np.ndarray, c) -> np.ndarray:
+    """s = c * tanh(z / c) for c > 0; s = z when c == 0 (no cap).
+
+    With c = (c_pos, c_neg): s = c_pos tanh(z / c_pos) for z >= 0 and c_neg tanh(z / c_neg) for
+    z < 0 (each side uncapped when its cap is 0).
+    """
+    cp, cn = _caps(c)
+    z = np.asarray(z, dtype=np.float64)
+    if cp == cn:
+        return _cap_side(z, cp)
+    return np.where(z >= 0, _cap_side(z, cp), _cap_side(z, cn))
+
+
+def softcap_derivative(z: np.ndarray, c) -> np.ndarray:
+    """ds/dz = 1 - tanh(z / c)^2 for c > 0, else 1; per side for c = (c_pos, c_neg)."""
+    cp, cn = _caps(c)
+    z = np.asarray(z, dtype=np.float64)
+    if cp == cn:
+        return _cap_side_derivative(z, cp)
+    return np.where(z >= 0, _cap_side_derivative(z, cp), _cap_side_derivative(z, cn))
 
 
 def log_sum_exp(s: np.ndarray) -> np.ndarray:

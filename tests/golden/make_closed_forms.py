@@ -34,6 +34,29 @@ def worked_softcap30():
     }
 
 
+def worked_asym():
+    s = [18.0, -8.0, 0.0, -3640.0 / 365.0]
+    lse = 18.0 + math.log1p(math.exp(-26.0) + math.exp(-18.0) + math.exp(s[3] - 18.0))
+    nats = [lse - v for v in s]
+    return {
+        "what": "worked example of the asymmetric softcap (cap 30 for z >= 0, cap 10 for z < 0), closed form",
+        "source": ("definition only: the pages name an 'AsymLogit' head change (HYDRA Golf site leaderboard table, "
+                   "entries #1 and #4; README leaderboard, PR #2135 and PR #1945 rows) without defining it; the reading "
+                   "taken is s = c_pos tanh(z / c_pos) for z >= 0 and c_neg tanh(z / c_neg) for z < 0."),
+        "derivation": ("H = [[1]] x4, E = [[30 ln 2], [-10 ln 3], [0], [-30 ln 3]], caps (30, 10). "
+                       "z/c = ln 2 (positive side), -ln 3, 0, -3 ln 3 (negative side); tanh(k ln 3) = (3^(2k) - 1)/(3^(2k) + 1), "
+                       "so s = [30 * 3/5, -10 * 4/5, 0, -10 * 728/730] = [18, -8, 0, -3640/365]. "
+                       "lse = 18 + log1p(e^-26 + e^-18 + e^(s3 - 18)); targets [0, 1, 2, 3]; byte_len [1, 1, 2, 3]."),
+        "caps": [30.0, 10.0],
+        "hidden": [[1.0], [1.0], [1.0], [1.0]],
+        "embed": [[30.0 * math.log(2.0)], [-10.0 * math.log(3.0)], [0.0], [-30.0 * math.log(3.0)]],
+        "target": [0, 1, 2, 3],
+        "byte_len": [1, 1, 2, 3],
+        "expected": {"s": s, "lse": [lse] * 4, "nats": nats, "sum_nats": sum(nats), "sum_bytes": 7,
+                     "n_scored": 4, "bpb": sum(nats) / (LN2 * 7)},
+    }
+
+
 def worked_nocap():
     return {
         "what": "worked example without a cap: one bit and two bits of surprise over three bytes gives 1 bit per byte",
@@ -76,6 +99,7 @@ def uniform():
 if __name__ == "__main__":
     for name, obj in [("worked_softcap30.json", worked_softcap30()),
                       ("worked_nocap_one_bit_per_byte.json", worked_nocap()),
+                      ("worked_asym_softcap_30_10.json", worked_asym()),
                       ("stride64_windows.json", stride64()), ("uniform_logits.json", uniform())]:
         with open(os.path.join(HERE, name), "w") as f:
             json.dump(obj, f, indent=1)

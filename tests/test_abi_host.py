@@ -77,6 +77,23 @@ def bwd(lib, **kw):
                                 a["D"], a["V"], a["c"], a["g"], a["dh"], a["de"], a["ws"], a["wsb"], a["stream"])
 
 
+def fwd_asym(lib, **kw):
+    a = dict(hidden=P, embed=P, dtype=0, target=P, mask=None, T=256, D=64, V=512, cp=30.0, cn=10.0,
+             nats=P, lse=P, ws=P, wsb=BIG, stream=None)
+    a.update(kw)
+    return lib.pg_lmhead_ce_fwd_asym(a["hidden"], a["embed"], a["dtype"], a["target"], a["mask"], a["T"], a["D"],
+                                     a["V"], a["cp"], a["cn"], a["nats"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def bwd_asym(lib, **kw):
+    a = dict(hidden=P, embed=P, dtype=0, target=P, mask=None, lse=P, T=256, D=64, V=512, cp=30.0, cn=10.0,
+             g=1 / 256, dh=P, de=P, ws=P, wsb=BIG, stream=None)
+    a.update(kw)
+    return lib.pg_lmhead_ce_bwd_asym(a["hidden"], a["embed"], a["dtype"], a["target"], a["mask"], a["lse"],
+                                     a["T"], a["D"], a["V"], a["cp"], a["cn"], a["g"], a["dh"], a["de"], a["ws"],
+                                     a["wsb"], a["stream"])
+
+
 def bpb(lib, **kw):
     a = dict(nats=P, target=P, mask=None, blen=P, bpp=None, T=256, V=512, out=P, ws=P, wsb=BIG, stream=None)
     a.update(kw)
@@ -84,7 +101,7 @@ def bpb(lib, **kw):
                              a["ws"], a["wsb"], a["stream"])
 
 
-@pytest.mark.parametrize("call", [fwd, bwd, bpb])
+@pytest.mark.parametrize("call", [fwd, bwd, fwd_asym, bwd_asym, bpb])
 def test_validation_codes(lib, call):
     assert call(lib, T=-1) == -2
     assert call(lib, V=0) == -2
@@ -118,6 +135,16 @@ def test_backward_validation(lib):
     assert bwd(lib, de=P + 12) == -6
 
 
+@pytest.mark.parametrize("call", [fwd_asym, bwd_asym])
+def test_asymmetric_cap_validation(lib, call):
+    assert call(lib, cp=-1.0) == -4
+    assert call(lib, cn=-0.5) == -4
+    assert call(lib, cn=float("nan")) == -4
+    assert call(lib, cp=float("inf")) == -4
+    assert call(lib, hidden=None) == -1
+    assert call(lib, dtype=3) == -3
+
+
 def test_bpb_validation(lib):
     assert bpb(lib, nats=None) == -1
     assert bpb(lib, blen=None) == -1
@@ -132,6 +159,8 @@ def test_valid_arguments_reach_the_device_check(lib):
         pytest.skip("a GPU is present; the device check would pass")
     assert fwd(lib) == -7
     assert bwd(lib) == -7
+    assert fwd_asym(lib) == -7
+    assert bwd_asym(lib) == -7
     assert bpb(lib) == -7
 
 

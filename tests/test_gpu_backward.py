@@ -33,10 +33,14 @@ def run_bwd(inp, softcap=None, mask=None, grad_scale=None):
     mask_t = None if mask is None else torch.from_numpy(mask).cuda()
     nats = torch.empty(T, device="cuda")
     lse = torch.empty(T, device="cuda")
-    abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], mask_t, c, nats, lse)
     dH = torch.full((T, D), float("nan"), device="cuda")
     dE = torch.full((V, D), float("nan"), device="cuda")
-    abi.pg_lmhead_ce_bwd(d["hidden"], d["embed"], d["target"], mask_t, lse, c, g, dH, dE)
+    if isinstance(c, tuple):
+        abi.pg_lmhead_ce_fwd_asym(d["hidden"], d["embed"], d["target"], mask_t, c[0], c[1], nats, lse)
+        abi.pg_lmhead_ce_bwd_asym(d["hidden"], d["embed"], d["target"], mask_t, lse, c[0], c[1], g, dH, dE)
+    else:
+        abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], mask_t, c, nats, lse)
+        abi.pg_lmhead_ce_bwd(d["hidden"], d["embed"], d["target"], mask_t, lse, c, g, dH, dE)
     torch.cuda.synchronize()
     dH, dE = dH.cpu().numpy().astype(np.float64), dE.cpu().numpy().astype(np.float64)
     H, E = host_inputs(inp)
@@ -114,3 +118,15 @@ def test_training_full_size_sampled():
     assert rel_l2(dE[vrows], odE) <= GRAD_RL2, rel_l2(dE[vrows], odE)
     a, b = np.sum(dH * H), np.sum(dE * E)
     assert abs(a - b) <= 1e-2 * abs(b), (a, b)
+
+
+@pytest.mark.parametrize("caps", [(30.0, 10.0), (10.0, 30.0), (30.0, 0.0), (0.0, 20.0)])
+def test_asymmetric_caps(caps):
+    """Gradients with separate caps for z >= 0 and z < 0; logits reach both caps' curvature."""
+    w = workload("train_v8192", T=520, V=1500, stream=99, hidden_scale=40.0)
+    run_bwd(synth.make_inputs(w, 1), softcap=caps)
+
+
+def test_asymmetric_caps_generic_and_masked():
+    run_bwd(synth.make_inputs(workload("fd", stream=100), 0), softcap=(3.0, 1.0))
+    run_bwd(synth.make_inputs("masked_stride64", 0, T=4096), softcap=(30.0, 15.0))

@@ -34,7 +34,10 @@ def run(inp, softcap=None, mask=None, sample_rows=None, check_bpb=True, byte_per
     print(f"[case] {inp['workload']} seed={inp['seed']} T={T} D={D} V={V} c={c} masked={mask is not None}", flush=True)
     nats_t = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
     lse_t = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
-    abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], mask_t, c, nats_t, lse_t)
+    if isinstance(c, tuple):
+        abi.pg_lmhead_ce_fwd_asym(d["hidden"], d["embed"], d["target"], mask_t, c[0], c[1], nats_t, lse_t)
+    else:
+        abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], mask_t, c, nats_t, lse_t)
     torch.cuda.synchronize()
     nats, lse = nats_t.cpu().numpy().astype(np.float64), lse_t.cpu().numpy().astype(np.float64)
     H, E = host_inputs(inp)
@@ -201,3 +204,48 @@ def test_bitwise_reproducible():
         abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, 30.0, nats, None)
         res.append((nats.cpu().numpy().tobytes(), gpu_bpb(nats, d, inp["V"]).tobytes()))
     assert res[0] == res[1]
+
+
+# ---------------------------------------------------------------- asymmetric softcap
+@pytest.mark.parametrize("caps", [(30.0, 10.0), (10.0, 30.0), (30.0, 0.0), (0.0, 20.0), (8.0, 40.0)])
+def test_asymmetric_caps(caps):
+    """Separate caps for z >= 0 and z < 0 (fixed-shift path when both sides are capped at <= 40,
+    running maximum otherwise), logits spread over both caps' curvature."""
+    w = workload("fwd_v8192", T=700, V=1500, stream=95, hidden_scale=40.0)
+    inp = synth.make_inputs(w, 3)
+    run(inp, softcap=caps)
+    H, E = host_inputs(inp)
+    z = H @ E.T
+    assert z.max() > 30.0 and z.min() < -30.0
+
+
+def test_asymmetric_equal_caps_are_the_symmetric_path():
+    inp = synth.make_inputs(workload("fwd_v8192", T=1000, V=2048, stream=96), 0)
+    d = abi.to_device(inp)
+    a = torch.empty(inp["T"], device="cuda")
+    b = torch.empty(inp["T"], device="cuda")
+    abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, 30.0, a, None)
+    abi.pg_lmhead_ce_fwd_asym(d["hidden"], d["embed"], d["target"], None, 30.0, 30.0, b, None)
+    assert torch.equal(a, b)
+
+
+def test_asymmetric_generic_widths():
+    """f32 inputs and a width without an MFMA kernel take the vector path."""
+    run(synth.make_inputs(workload("stress", dtype="f32", D=40, stream=97), 0), softcap=(30.0, 10.0))
+    run(synth.make_inputs(workload("stress", D=48, stream=98), 0), softcap=(12.0, 30.0))
+
+
+def test_asymmetric_main_full_size_sampled():
+    """The main workload (T = 65536, D = 512, V = 8192) with caps (30, 20): sampled rows and the
+    whole bits per byte against the oracle."""
+    inp = synth.make_inputs("fwd_v8192", 0)
+    caps = (30.0, 20.0)
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([rng.choice(65536, 256, replace=False), [0, 65535]]))
+    nats, _ = run(inp, softcap=caps, sample_rows=rows)
+    H, E = host_inputs(inp)
+    onats, _ = oracle_forward_chunked(H, E, inp["target"], caps)
+    assert np.max(np.abs(nats - onats)) <= NATS_ATOL
+    b_gpu = ora.bpb(nats, inp["target"], inp["byte_len"])[3]
+    b_ora = ora.bpb(onats, inp["target"], inp["byte_len"])[3]
+    assert abs(b_gpu - b_ora) <= BPB_RTOL * b_ora

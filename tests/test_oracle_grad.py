@@ -122,3 +122,36 @@ def test_embed_grad_rows_matches_full_backward():
     rows = np.array([0, 3, 19, 7])
     np.testing.assert_allclose(ora.embed_grad_rows(H, E, y, c, g, lse, rows, mask), dE[rows],
                                rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("caps", [(2.0, 5.0), (5.0, 0.0), (0.0, 3.0)])
+def test_finite_differences_asymmetric_caps(caps):
+    """Separate caps for z >= 0 and z < 0, with logits spanning both sides' curvature."""
+    rng = np.random.default_rng(26)
+    H = rng.standard_normal((6, 4)) * 3.0
+    E = rng.standard_normal((9, 4)) * 1.0
+    y = rng.integers(0, 9, size=6)
+    mask = np.array([1, 0, 1, 1, 1, 0], dtype=np.uint8)
+    g = 1.0 / mask.sum()
+    z = H @ E.T
+    assert np.max(z) > 4.0 and np.min(z) < -4.0
+    dH, dE = ora.backward(H, E, y, caps, g, mask)
+    fdH, fdE = _fd_grads(H, E, y, caps, g, mask)
+    _check(dH, fdH, 1e-6)
+    _check(dE, fdE, 1e-6)
+
+
+def test_asymmetric_caps_match_torch_autograd():
+    rng = np.random.default_rng(27)
+    H = rng.standard_normal((13, 5)) * 6.0
+    E = rng.standard_normal((10, 5)) * 1.0
+    y = rng.integers(0, 10, size=13)
+    cp, cn = 4.0, 9.0
+    Ht = torch.tensor(H, requires_grad=True)
+    Et = torch.tensor(E, requires_grad=True)
+    z = Ht @ Et.T
+    s = torch.where(z >= 0, cp * torch.tanh(z / cp), cn * torch.tanh(z / cn))
+    torch.nn.functional.cross_entropy(s, torch.tensor(y), reduction="sum").backward()
+    dH, dE = ora.backward(H, E, y, (cp, cn), 1.0)
+    np.testing.assert_allclose(dH, Ht.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dE, Et.grad.numpy(), rtol=1e-11, atol=1e-13)

@@ -268,3 +268,40 @@ def test_sanity_mean_nats_near_lnV_plus_half_variance():
     H, E = synth.as_f64(inp["hidden"], "f32"), synth.as_f64(inp["embed"], "f32")
     nats, _ = ora.forward(H, E, inp["target"], 30.0)
     assert nats.mean() == pytest.approx(math.log(512) + 64 * 0.02 ** 2 / 2, abs=0.05)
+
+
+# ---------------------------------------------------------------- asymmetric softcap
+def test_worked_example_asymmetric_caps():
+    g = _load("worked_asym_softcap_30_10.json")
+    H, E, y = np.array(g["hidden"]), np.array(g["embed"]), np.array(g["target"])
+    caps = tuple(g["caps"])
+    s = ora.softcap(ora.logits(H, E), caps)
+    np.testing.assert_allclose(s[0], g["expected"]["s"], rtol=0, atol=1e-12)
+    nats, lse = ora.forward(H, E, y, caps)
+    np.testing.assert_allclose(nats, g["expected"]["nats"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, g["expected"]["lse"], rtol=1e-13)
+    sn, sb, n, b = ora.bpb(nats, y, np.array(g["byte_len"]))
+    assert (sb, n) == (7, 4)
+    assert b == pytest.approx(g["expected"]["bpb"], rel=1e-13)
+
+
+def test_asymmetric_caps_reduce_swap_and_bound():
+    rng = np.random.default_rng(31)
+    z = rng.standard_normal(4000) * 40.0
+    # equal caps are the symmetric softcap, to the bit
+    np.testing.assert_array_equal(ora.softcap(z, (12.0, 12.0)), ora.softcap(z, 12.0))
+    np.testing.assert_array_equal(ora.softcap_derivative(z, (12.0, 12.0)), ora.softcap_derivative(z, 12.0))
+    # mirroring the logits swaps the caps: s(-z; a, b) = -s(z; b, a)
+    np.testing.assert_allclose(ora.softcap(-z, (30.0, 7.0)), -ora.softcap(z, (7.0, 30.0)), rtol=0, atol=0)
+    # range (-c_neg, c_pos) and each side's own slope
+    s = ora.softcap(z, (30.0, 7.0))
+    assert np.all(s <= 30.0) and np.all(s >= -7.0)
+    inner = (z < 18 * 30.0) & (z > -18 * 7.0)      # tanh stays below 1 in float64 up to |x| ~ 19
+    assert np.all(s[inner] < 30.0) and np.all(s[inner] > -7.0)
+    pos, neg = z >= 0, z < 0
+    np.testing.assert_array_equal(s[pos], 30.0 * np.tanh(z[pos] / 30.0))
+    np.testing.assert_array_equal(s[neg], 7.0 * np.tanh(z[neg] / 7.0))
+    # one side uncapped
+    s0 = ora.softcap(z, (0.0, 7.0))
+    np.testing.assert_array_equal(s0[pos], z[pos])
+    assert np.all(s0[neg] >= -7.0)
