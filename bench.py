@@ -292,6 +292,35 @@ def main():
         "frac": flop_fwd / (asym_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bpb": float(out[3].item()),
         "note": "fused forward with separate caps for z >= 0 and z < 0 (exact softcap in the epilogue)"}
 
+    # the quantised tied head: per-row int8 embedding (quantised once), scored through the fused path
+    q8 = torch.empty((V, D), dtype=torch.int8, device="cuda")
+    sc8 = torch.empty(V, dtype=torch.float32, device="cuda")
+    ws_q8 = torch.empty(abi.workspace_bytes(abi.PG_OP_FWD_Q8, T, D, V), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        abi.pg_quantize_q8(d["embed"], q8, sc8)
+        abi.pg_lmhead_ce_fwd_q8(d["hidden"], q8, sc8, d["target"], None, c, nats, lse, ws_q8)
+    ev_q = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+    for a, b in ev_q:
+        a.record()
+        abi.pg_quantize_q8(d["embed"], q8, sc8)
+        b.record()
+    ev_f = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev_f:
+        a.record()
+        abi.pg_lmhead_ce_fwd_q8(d["hidden"], q8, sc8, d["target"], None, c, nats, lse, ws_q8)
+        b.record()
+    torch.cuda.synchronize()
+    quant_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_q]))
+    q8_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_f]))
+    abi.pg_bpb_reduce(nats, d["target"], None, d["byte_len"], None, V, out, ws_bpb)
+    quant_bytes = V * D * 2 + V * D + V * 4          # read bf16 E, write int8 q and float32 scales
+    result["q8_head"] = {
+        "format": "per-row symmetric int8, float32 scales; head computes on bf16(q * scale)",
+        "quantize_us": quant_ms * 1e3, "quantize_gbps": quant_bytes / (quant_ms * 1e-3) / 1e9,
+        "launch_ms": q8_ms, "tokens_per_s": T / (q8_ms * 1e-3),
+        "frac": flop_fwd / (q8_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bpb": float(out[3].item()),
+        "note": "launch = dequantise (8 MiB bf16 written) + fused forward"}
+
     if not args.no_train:
         tin = synth.make_inputs("train_v8192", args.seed)
         td = abi.to_device(tin)

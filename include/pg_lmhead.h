@@ -57,7 +57,7 @@ enum {
 };
 
 enum { PG_DTYPE_BF16 = 0, PG_DTYPE_F32 = 1 }; /* dtype of H and E (they share one) */
-enum { PG_OP_FWD = 0, PG_OP_BWD = 1, PG_OP_BPB = 2 };
+enum { PG_OP_FWD = 0, PG_OP_BWD = 1, PG_OP_BPB = 2, PG_OP_FWD_Q8 = 3 };
 
 /* Largest supported sizes: T rows up to 2^31 - 1 (each row index fits an int32), V and D up to
  * 2^20. bf16 with D in {32, 64, 128, 256, 512} runs the MFMA kernels; any other D, and f32 inputs,
@@ -119,6 +119,31 @@ pg_status pg_lmhead_ce_bwd_asym(const void* hidden, const void* embed, int32_t d
                                 int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg, float grad_scale,
                                 float* dhidden, float* dembed,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Quantised tied head. The model is quantised to fit the artifact (trios issue #19, approach
+ * table, "Квантование": INT4/INT8; README leaderboard, GPTQ and LQER rows), and the tied embedding
+ * then serves as both input lookup and output head. The pages define no format; this library uses
+ * per-row symmetric int8:
+ *   scale[v] = max_d |E[v,d]| / 127                      (float32, correctly rounded)
+ *   q[v,d]   = round_half_even(E[v,d] / scale[v])         (int8 in [-127, 127]; 0 if scale is 0)
+ *   E'[v,d]  = bf16_round_half_even(float32(q[v,d]) * scale[v])   (what the head computes with)
+ * D must be a multiple of 8 (PG_ERR_SHAPE otherwise).
+ *
+ * pg_quantize_q8: embed [V, D] (bf16 or f32, dtype as above) -> embed_q8 [V, D] int8 and
+ *   embed_scale [V] f32, all device arrays. Needs no workspace.
+ * pg_lmhead_ce_fwd_q8: the forward of pg_lmhead_ce_fwd (bf16 hidden) with the head E' rebuilt
+ *   from (embed_q8, embed_scale) into the workspace, which must hold
+ *   pg_workspace_bytes(PG_OP_FWD_Q8, T, D, V) bytes. nats and lse as for pg_lmhead_ce_fwd.
+ */
+pg_status pg_quantize_q8(const void* embed, int32_t dtype, int32_t V, int32_t D, int8_t* embed_q8,
+                         float* embed_scale, void* stream);
+
+pg_status pg_lmhead_ce_fwd_q8(const void* hidden, const int8_t* embed_q8, const float* embed_scale,
+                              const int32_t* target, const uint8_t* score_mask,
+                              int64_t T, int32_t D, int32_t V, float softcap,
+                              float* nats, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bits per byte over the scored rows (tproger article, "Правила и метрика": the score counts

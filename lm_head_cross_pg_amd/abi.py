@@ -20,13 +20,14 @@ LIB_PATH = os.path.join(HERE, "libpg_lmhead.so")
 PG_OK = 0
 PG_DTYPE_BF16 = 0
 PG_DTYPE_F32 = 1
-PG_OP_FWD, PG_OP_BWD, PG_OP_BPB = 0, 1, 2
+PG_OP_FWD, PG_OP_BWD, PG_OP_BPB, PG_OP_FWD_Q8 = 0, 1, 2, 3
 STATUS_NAMES = {0: "PG_OK", -1: "PG_ERR_NULL", -2: "PG_ERR_SHAPE", -3: "PG_ERR_DTYPE", -4: "PG_ERR_SOFTCAP",
                 -5: "PG_ERR_WORKSPACE", -6: "PG_ERR_ALIGN", -7: "PG_ERR_DEVICE", -8: "PG_ERR_HIP"}
 
 # every symbol the header declares
 EXPORTS = ("pg_lmhead_ce_fwd", "pg_lmhead_ce_bwd", "pg_lmhead_ce_fwd_asym", "pg_lmhead_ce_bwd_asym",
-           "pg_bpb_reduce", "pg_workspace_bytes", "pg_status_str", "pg_abi_version")
+           "pg_quantize_q8", "pg_lmhead_ce_fwd_q8", "pg_bpb_reduce", "pg_workspace_bytes", "pg_status_str",
+           "pg_abi_version")
 
 
 class PgError(RuntimeError):
@@ -55,6 +56,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pg_lmhead_ce_fwd_asym.restype = i32
     lib.pg_lmhead_ce_bwd_asym.argtypes = [vp, vp, i32, vp, vp, vp, i64, i32, i32, f32, f32, f32, vp, vp, vp, sz, vp]
     lib.pg_lmhead_ce_bwd_asym.restype = i32
+    lib.pg_quantize_q8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    lib.pg_quantize_q8.restype = i32
+    lib.pg_lmhead_ce_fwd_q8.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, f32, vp, vp, vp, sz, vp]
+    lib.pg_lmhead_ce_fwd_q8.restype = i32
     lib.pg_bpb_reduce.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, sz, vp]
     lib.pg_bpb_reduce.restype = i32
     lib.pg_workspace_bytes.argtypes = [i32, i64, i32, i32]
@@ -165,6 +170,26 @@ def pg_lmhead_ce_bwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: tor
                                       float(grad_scale), _ptr(dhidden), _ptr(dembed), _ptr(ws), ws.numel(),
                                       _stream(stream))
     _check(st, "pg_lmhead_ce_bwd_asym")
+
+
+def pg_quantize_q8(embed: torch.Tensor, embed_q8: torch.Tensor, embed_scale: torch.Tensor, stream=None) -> None:
+    V, D = embed.shape
+    st = load().pg_quantize_q8(_ptr(embed), _dtype_code(embed), V, D, _ptr(embed_q8), _ptr(embed_scale),
+                               _stream(stream))
+    _check(st, "pg_quantize_q8")
+
+
+def pg_lmhead_ce_fwd_q8(hidden: torch.Tensor, embed_q8: torch.Tensor, embed_scale: torch.Tensor,
+                        target: torch.Tensor, score_mask: Optional[torch.Tensor], softcap: float,
+                        nats: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    T, D = hidden.shape
+    V = embed_q8.shape[0]
+    ws = _workspace(PG_OP_FWD_Q8, T, D, V, embed_q8, workspace)
+    st = load().pg_lmhead_ce_fwd_q8(_ptr(hidden), _ptr(embed_q8), _ptr(embed_scale), _ptr(target),
+                                    _ptr(score_mask), T, D, V, float(softcap), _ptr(nats), _ptr(lse), _ptr(ws),
+                                    ws.numel(), _stream(stream))
+    _check(st, "pg_lmhead_ce_fwd_q8")
 
 
 def pg_bpb_reduce(nats: torch.Tensor, target: torch.Tensor, score_mask: Optional[torch.Tensor],

@@ -80,6 +80,9 @@ size_t pg_workspace_bytes(int32_t op, int64_t T, int32_t D, int32_t V) {
     case PG_OP_FWD: return pg::fwd_workspace(T, D, V).total;
     case PG_OP_BWD: return pg::bwd_workspace(T, D, V).total;
     case PG_OP_BPB: return pg::bpb_workspace(T).total;
+    case PG_OP_FWD_Q8:
+      if (D % 8 != 0) return 0;
+      return pg::align256((size_t)V * (size_t)D * 2) + pg::fwd_workspace(T, D, V).total;
     default: return 0;
   }
 }
@@ -161,6 +164,47 @@ pg_status pg_lmhead_ce_bwd_asym(const void* hidden, const void* embed, int32_t d
                                 void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(hidden, embed, dtype, target, score_mask, lse, T, D, V, cap_pos, cap_neg, grad_scale, dhidden,
                   dembed, workspace, workspace_bytes, stream);
+}
+
+pg_status pg_quantize_q8(const void* embed, int32_t dtype, int32_t V, int32_t D, int8_t* embed_q8,
+                         float* embed_scale, void* stream) {
+  pg_status s;
+  if ((s = check_shape(0, D, V)) != PG_OK) return s;
+  if (D % 8 != 0) return PG_ERR_SHAPE;
+  if (!embed || !embed_q8 || !embed_scale) return PG_ERR_NULL;
+  if (dtype != PG_DTYPE_BF16 && dtype != PG_DTYPE_F32) return PG_ERR_DTYPE;
+  if (misaligned(embed) || misaligned(embed_q8) || misaligned(embed_scale)) return PG_ERR_ALIGN;
+  pg::DeviceInfo dev{};
+  if ((s = device_check(dev)) != PG_OK) return s;
+  hipError_t e = pg::launch_quantize(embed, dtype, V, D, embed_q8, embed_scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PG_OK : PG_ERR_HIP;
+}
+
+pg_status pg_lmhead_ce_fwd_q8(const void* hidden, const int8_t* embed_q8, const float* embed_scale,
+                              const int32_t* target, const uint8_t* score_mask,
+                              int64_t T, int32_t D, int32_t V, float softcap,
+                              float* nats, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  pg_status s;
+  if ((s = check_shape(T, D, V)) != PG_OK) return s;
+  if (D % 8 != 0) return PG_ERR_SHAPE;
+  if (T > 0 && (!hidden || !target || !nats)) return PG_ERR_NULL;
+  if (!embed_q8 || !embed_scale || !workspace) return PG_ERR_NULL;
+  if ((s = check_softcap(softcap)) != PG_OK) return s;
+  if (misaligned(hidden) || misaligned(embed_q8) || misaligned(embed_scale) || misaligned(target) ||
+      misaligned(score_mask) || misaligned(nats) || misaligned(lse) || misaligned(workspace))
+    return PG_ERR_ALIGN;
+  if (workspace_bytes < pg_workspace_bytes(PG_OP_FWD_Q8, T, D, V)) return PG_ERR_WORKSPACE;
+  pg::DeviceInfo dev{};
+  if ((s = device_check(dev)) != PG_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* deq = reinterpret_cast<uint16_t*>(ws);
+  hipError_t e = pg::launch_dequantize(embed_q8, embed_scale, V, D, deq, st);
+  if (e == hipSuccess)
+    e = pg::launch_fwd(hidden, deq, PG_DTYPE_BF16, target, score_mask, T, D, V, softcap, softcap, nats, lse,
+                       ws + pg::align256((size_t)V * (size_t)D * 2), dev, st);
+  return e == hipSuccess ? PG_OK : PG_ERR_HIP;
 }
 
 pg_status pg_bpb_reduce(const float* nats, const int32_t* target, const uint8_t* score_mask,

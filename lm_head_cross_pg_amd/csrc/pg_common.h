@@ -32,6 +32,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
+__device__ __forceinline__ float load_value(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_value(const uint16_t* p, int64_t i) { return __uint_as_float(((uint32_t)p[i]) << 16); }
+
 // Round-to-nearest-even float -> bf16 bit pattern (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);

@@ -53,6 +53,11 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
                       float cap_pos, float cap_neg, float grad_scale, float* dH, float* dE, char* ws,
                       const DeviceInfo& dev, hipStream_t st);
 
+// Per-row int8 embedding (pg_quant.hip): quantiser and dequantiser to bf16.
+hipError_t launch_quantize(const void* E, int32_t dtype, int32_t V, int32_t D, int8_t* q, float* scale,
+                           hipStream_t st);
+hipError_t launch_dequantize(const int8_t* q, const float* scale, int32_t V, int32_t D, uint16_t* E, hipStream_t st);
+
 // Bits-per-byte launcher (pg_bpb.hip).
 hipError_t launch_bpb(const float* nats, const int32_t* target, const uint8_t* mask,
                       const int32_t* byte_len, const int32_t* byte_per_pos, int64_t T, int32_t V,

@@ -17,6 +17,11 @@ What it computes, and where the pages state it:
   Reading taken: separate caps for positive and negative logits, s = c_pos tanh(z / c_pos) for
   z >= 0 and c_neg tanh(z / c_neg) for z < 0; every function taking a cap c accepts the pair
   (c_pos, c_neg) in its place.
+* Quantised tied head: the model is quantised to fit the artifact (trios issue #19, approach table,
+  "Квантование": INT4/INT8; README leaderboard, GPTQ and LQER rows); no format is given, so per-row
+  symmetric int8 with float32
+  scales is the reading taken, and the head computes on the bfloat16 rounding of q * scale
+  (quantize_rows_q8, dequantize_rows_q8, forward_q8).
 * Cross-entropy against the next token, in nats: lse(s) - s[target] (trios issue, "Контекст":
   "cross-entropy loss / bits-per-byte"; repo-explainer, ``loss = criterion(logits, batch["y"])``).
 * Bits per byte: total -log2 p(target) over scored rows divided by the total UTF-8 bytes of those
@@ -41,7 +46,7 @@ import numpy as np
 LN2 = float(np.log(2.0))
 
 __all__ = ["LN2", "logits", "softcap", "softcap_derivative", "log_sum_exp", "forward", "bpb",
-           "backward", "embed_grad_rows", "loss"]
+           "backward", "embed_grad_rows", "loss", "quantize_rows_q8", "dequantize_rows_q8", "forward_q8"]
 
 
 def logits(H: np.ndarray, E: np.ndarray) -> np.ndarray:
@@ -150,6 +155,41 @@ def bpb(nats, target, byte_len, mask=None, byte_per_pos=None, V=None):
     with np.errstate(divide="ignore", invalid="ignore"):
         bits = np.float64(sum_nats) / (np.float64(LN2) * np.float64(sum_bytes))
     return sum_nats, sum_bytes, n_scored, float(bits)
+
+
+def _bf16_round(x32: np.ndarray) -> np.ndarray:
+    """float32 values -> nearest bfloat16 (ties to even), returned as float64."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def quantize_rows_q8(E):
+    """Per-row symmetric int8 form of the tied embedding, (q [V, D] int8, scale [V] float32).
+
+    The pages quantise the model to fit the artifact (trios issue #19, approach table,
+    "Квантование": INT4/INT8; tproger article on int6/int5/ternary weights; README leaderboard,
+    GPTQ and LQER rows) but define no format; the reading taken here, in float32 arithmetic:
+    scale[v] = max_d |E[v, d]| / 127, q[v, d] = round_half_even(E[v, d] / scale[v]) clipped to
+    [-127, 127], and q = 0 on a row whose scale is 0.
+    """
+    E32 = np.asarray(E, dtype=np.float32)
+    scale = (np.max(np.abs(E32), axis=1) / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    r = np.rint(E32 / safe[:, None])
+    r = np.where(scale[:, None] > 0, r, 0.0)
+    return np.clip(r, -127, 127).astype(np.int8), scale
+
+
+def dequantize_rows_q8(q, scale) -> np.ndarray:
+    """E'[v, d] = bfloat16(float32(q[v, d]) * scale[v]), the embedding the quantised head uses."""
+    prod = np.asarray(q, dtype=np.float32) * np.asarray(scale, dtype=np.float32)[:, None]
+    return _bf16_round(prod)
+
+
+def forward_q8(H, q, scale, target, c, mask=None):
+    """Forward of the quantised tied head: :func:`forward` on the dequantised embedding."""
+    return forward(H, dequantize_rows_q8(q, scale), target, c, mask)
 
 
 def loss(H, E, target, c: float, g: float, mask=None) -> float:

@@ -94,6 +94,20 @@ def bwd_asym(lib, **kw):
                                      a["wsb"], a["stream"])
 
 
+def quant(lib, **kw):
+    a = dict(embed=P, dtype=0, V=512, D=64, q=P, scale=P, stream=None)
+    a.update(kw)
+    return lib.pg_quantize_q8(a["embed"], a["dtype"], a["V"], a["D"], a["q"], a["scale"], a["stream"])
+
+
+def fwd_q8(lib, **kw):
+    a = dict(hidden=P, q=P, scale=P, target=P, mask=None, T=256, D=64, V=512, c=30.0, nats=P, lse=P, ws=P,
+             wsb=BIG, stream=None)
+    a.update(kw)
+    return lib.pg_lmhead_ce_fwd_q8(a["hidden"], a["q"], a["scale"], a["target"], a["mask"], a["T"], a["D"],
+                                   a["V"], a["c"], a["nats"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
 def bpb(lib, **kw):
     a = dict(nats=P, target=P, mask=None, blen=P, bpp=None, T=256, V=512, out=P, ws=P, wsb=BIG, stream=None)
     a.update(kw)
@@ -101,7 +115,7 @@ def bpb(lib, **kw):
                              a["ws"], a["wsb"], a["stream"])
 
 
-@pytest.mark.parametrize("call", [fwd, bwd, fwd_asym, bwd_asym, bpb])
+@pytest.mark.parametrize("call", [fwd, bwd, fwd_asym, bwd_asym, fwd_q8, bpb])
 def test_validation_codes(lib, call):
     assert call(lib, T=-1) == -2
     assert call(lib, V=0) == -2
@@ -145,6 +159,24 @@ def test_asymmetric_cap_validation(lib, call):
     assert call(lib, dtype=3) == -3
 
 
+def test_quantised_head_validation(lib):
+    assert quant(lib, D=60) == -2                 # D must be a multiple of 8
+    assert quant(lib, V=0) == -2
+    assert quant(lib, embed=None) == -1
+    assert quant(lib, q=None) == -1
+    assert quant(lib, scale=None) == -1
+    assert quant(lib, dtype=4) == -3
+    assert quant(lib, q=P + 4) == -6
+    assert fwd_q8(lib, D=36) == -2
+    assert fwd_q8(lib, scale=None) == -1
+    assert fwd_q8(lib, c=-3.0) == -4
+    assert fwd_q8(lib, q=P + 8) == -6
+    need = abi.workspace_bytes(abi.PG_OP_FWD_Q8, 256, 64, 512)
+    assert need >= abi.workspace_bytes(abi.PG_OP_FWD, 256, 64, 512) + 512 * 64 * 2
+    assert fwd_q8(lib, wsb=need - 1) == -5
+    assert abi.workspace_bytes(abi.PG_OP_FWD_Q8, 256, 60, 512) == 0
+
+
 def test_bpb_validation(lib):
     assert bpb(lib, nats=None) == -1
     assert bpb(lib, blen=None) == -1
@@ -161,6 +193,8 @@ def test_valid_arguments_reach_the_device_check(lib):
     assert bwd(lib) == -7
     assert fwd_asym(lib) == -7
     assert bwd_asym(lib) == -7
+    assert quant(lib) == -7
+    assert fwd_q8(lib) == -7
     assert bpb(lib) == -7
 
 

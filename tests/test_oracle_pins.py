@@ -305,3 +305,46 @@ def test_asymmetric_caps_reduce_swap_and_bound():
     s0 = ora.softcap(z, (0.0, 7.0))
     np.testing.assert_array_equal(s0[pos], z[pos])
     assert np.all(s0[neg] >= -7.0)
+
+
+# ---------------------------------------------------------------- quantised tied head
+def test_q8_exact_grid_round_trips():
+    """Rows that are integer multiples k * 2^e of a power of two, with max |k| = 127, quantise to
+    exactly (k, 2^e) and dequantise back to themselves (|k| <= 127 fits bfloat16's significand)."""
+    rng = np.random.default_rng(41)
+    V, D = 37, 24
+    k = rng.integers(-127, 128, size=(V, D))
+    k[:, 3] = np.where(rng.random(V) < 0.5, 127, -127)       # every row reaches |k| = 127
+    e = rng.integers(-20, 5, size=V)
+    scale = np.ldexp(1.0, e)
+    E = k * scale[:, None]
+    q, s = ora.quantize_rows_q8(E)
+    np.testing.assert_array_equal(q, k)
+    np.testing.assert_array_equal(s, scale.astype(np.float32))
+    np.testing.assert_array_equal(ora.dequantize_rows_q8(q, s), E)
+
+
+def test_q8_zero_rows_sign_and_power_of_two_scaling():
+    rng = np.random.default_rng(42)
+    E = rng.standard_normal((20, 16)).astype(np.float32) * 0.02
+    E[5] = 0.0
+    q, s = ora.quantize_rows_q8(E)
+    assert s[5] == 0.0 and np.all(q[5] == 0) and np.all(ora.dequantize_rows_q8(q, s)[5] == 0.0)
+    qn, sn = ora.quantize_rows_q8(-E)
+    np.testing.assert_array_equal(qn, -q)
+    np.testing.assert_array_equal(sn, s)
+    q4, s4 = ora.quantize_rows_q8(E * np.float32(4.0))
+    np.testing.assert_array_equal(q4, q)
+    np.testing.assert_array_equal(s4, s * np.float32(4.0))
+    assert np.all(np.abs(q) <= 127) and np.all(np.max(np.abs(q), axis=1)[s > 0] == 127)
+
+
+def test_q8_round_trip_error_bound():
+    """|E' - E| <= scale / 2 (the int8 rounding) plus the bfloat16 rounding of q * scale."""
+    rng = np.random.default_rng(43)
+    E = (rng.standard_normal((64, 512)) * 0.02).astype(np.float32).astype(np.float64)
+    q, s = ora.quantize_rows_q8(E)
+    Ed = ora.dequantize_rows_q8(q, s)
+    bound = s[:, None].astype(np.float64) * (0.5 + 1e-6) + np.abs(Ed) * 2.0 ** -8
+    assert np.all(np.abs(Ed - E) <= bound)
+    assert np.max(np.abs(Ed - E) / s[:, None]) > 0.45        # the bound is nearly reached
