@@ -128,7 +128,12 @@ struct DzParams {
 template <int D, bool CAPPED, int NB>
 struct DzCore {
   static constexpr int KS = D / 16;
+  static constexpr int kWaves = WaveShape<NB>::kWaves;
+  static constexpr int kLoads = embed_loads_per_wave<D, kWaves>();
   const lds_char* lds;
+  char* smem;
+  const uint16_t* E;
+  int wave, lane;
   int h, col, V;
   Softcap sc;
   bf16x8 hf[NB][KS];
@@ -161,7 +166,7 @@ struct DzCore {
       float p, slope;
       if (MODE == 0) {
         const float u = z * z;
-        const float s2 = z * __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(sc.q3, u, sc.q2), u, sc.q1), u, sc.q0);
+        const float s2 = z * __builtin_fmaf(__builtin_fmaf(sc.q2, u, sc.q1), u, sc.q0);
         p = fexp2(s2 + bias[tb]);
         const float t = s2 * sc.invM;              // s / c = tanh(z / c)
         slope = __builtin_fmaf(-t, t, 1.0f);
@@ -198,16 +203,25 @@ struct DzCore {
   // nothing else would). The softcap is the tanh series; a block with some |z| > c/8 (a
   // wave-uniform, rarely taken branch) is redone exactly (the later store of the same lane to the
   // same address wins).
+  // With LOAD the chain also issues this wave's pieces of the load of embedding tile load_tile into
+  // LDS buffer load_buf, spread over its steps (a burst of them would stall the MFMAs).
+  template <bool LOAD>
   __device__ __forceinline__ void chain_with_store(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
-                                                   int vprev) {
-    constexpr int NST = 10;                                  // epilogue stages
+                                                   int vprev, int load_tile = 0, int load_buf = 0) {
+    auto load_all = [&]() {
+      if (LOAD)
+        for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, i);
+    };
+    constexpr int NST = 9;                                   // epilogue stages
     if (CAPPED && sc.asym) {                                 // asymmetric caps: exact form only
+      load_all();
       chain(buf, vb, a);
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) store_block<1, false>(prev[tb], vprev, tb);
       return;
     }
     if (!CAPPED || KS < 2 * NST) {                           // short chains: no room to pipeline
+      load_all();
       chain(buf, vb, a);
       if (!CAPPED) {
 #pragma unroll
@@ -230,7 +244,8 @@ struct DzCore {
     constexpr int NE = NB * 16;                              // logits of `prev` per lane
     // elements per group (a power of two, so a group of eight stored together is never split), small
     // enough that every group finishes its last stage by step KS - 1 where possible
-    constexpr int EPC0 = (NE + (KS - NST)) / (KS - NST + 1);
+    constexpr int SPAN = KS - NST + 1 > 0 ? KS - NST + 1 : 1;   // (short chains returned above)
+    constexpr int EPC0 = (NE + SPAN - 1) / SPAN;
     constexpr int EPC = EPC0 <= 1 ? 1 : EPC0 <= 2 ? 2 : EPC0 <= 4 ? 4 : EPC0 <= 8 ? 8 : 16;
     constexpr int NG = (NE + EPC - 1) / EPC;
     constexpr int NSTEP = (NG + NST - 1) > KS ? (NG + NST - 1) : KS;
@@ -249,9 +264,12 @@ struct DzCore {
     for (int tb = 0; tb < NB; ++tb) dy[tb] = ytok[tb] - vprev;
 #pragma unroll
     for (int k = 0; k < PF; ++k) fr[k] = frag(k);
+    constexpr int LOAD_EVERY = (KS / kLoads) < 4 ? ((KS / kLoads) < 1 ? 1 : KS / kLoads) : 4;
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
       if (k + PF < KS) fr[k + PF] = frag(k + PF);
+      if (LOAD && k % LOAD_EVERY == 0 && k / LOAD_EVERY < kLoads)
+        load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);
       if (k < KS) mfma_step<NB, KS>(a, fr[k], hf, k);
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
@@ -264,14 +282,13 @@ struct DzCore {
           const int off = 8 * (r >> 2) + 4 * h + (r & 3);
           switch (st) {
             case 0: u[e] = z * z; amax = fmaxf(amax, fabsf(z)); break;
-            case 1: q[e] = __builtin_fmaf(sc.q3, u[e], sc.q2); break;
-            case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q1); break;
-            case 3: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
-            case 4: q[e] = z * q[e]; break;                                 // s log2 e
-            case 5: t[e] = q[e] * sc.invM; q[e] = q[e] + bias[tb]; break;  // s / c; log2 p
-            case 6: q[e] = fexp2(q[e]); t[e] = __builtin_fmaf(-t[e], t[e], 1.0f); break;
-            case 7: v[e] = (off == dy[tb]) ? q[e] - 1.0f : q[e]; break;
-            case 8: v[e] = v[e] * t[e]; break;
+            case 1: q[e] = __builtin_fmaf(sc.q2, u[e], sc.q1); break;
+            case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
+            case 3: q[e] = z * q[e]; break;                                 // s log2 e
+            case 4: t[e] = q[e] * sc.invM; q[e] = q[e] + bias[tb]; break;  // s / c; log2 p
+            case 5: q[e] = fexp2(q[e]); t[e] = __builtin_fmaf(-t[e], t[e], 1.0f); break;
+            case 6: v[e] = (off == dy[tb]) ? q[e] - 1.0f : q[e]; break;
+            case 7: v[e] = v[e] * t[e]; break;
             default:
               if ((r & 7) == 7) store8(&v[e - 7], vprev, tb, r >> 3);   // eight values: one 16-byte store
               break;
@@ -305,6 +322,10 @@ void bwd_dz_kernel(DzParams p) {
 
   DzCore<D, CAPPED, NB> core;
   core.lds = (const lds_char*)smem;
+  core.smem = smem;
+  core.E = p.E;
+  core.wave = wave;
+  core.lane = lane;
   core.h = h;
   core.col = col;
   core.V = V;
@@ -332,7 +353,10 @@ void bwd_dz_kernel(DzParams p) {
     const int buf = i & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (i + 1 < ntiles) load_embed_tile<D, kFwdWaves>(smem, p.E, V, i + 1, buf ^ 1, wave, lane);
+    const bool next = i + 1 < ntiles;
+    // the steady state spreads the next tile's load over its first chain; elsewhere it goes first
+    const bool steady = !(last_partial && i + 1 == ntiles) && vprev >= 0;
+    if (next && !steady) load_embed_tile<D, kFwdWaves>(smem, p.E, V, i + 1, buf ^ 1, wave, lane);
     const int vb0 = i * kVocabTile;
     f32x16 a0[NB];
     if (last_partial && i + 1 == ntiles) {
@@ -345,11 +369,12 @@ void bwd_dz_kernel(DzParams p) {
       vprev = -1;
     } else if (vprev < 0) {
       core.chain(buf, 0, a0);
-      core.chain_with_store(buf, 1, accp, a0, vb0);
+      core.template chain_with_store<false>(buf, 1, accp, a0, vb0);
       vprev = vb0 + 32;
     } else {
-      core.chain_with_store(buf, 0, a0, accp, vprev);
-      core.chain_with_store(buf, 1, accp, a0, vb0);
+      if (next) core.template chain_with_store<true>(buf, 0, a0, accp, vprev, i + 1, buf ^ 1);
+      else core.template chain_with_store<false>(buf, 0, a0, accp, vprev);
+      core.template chain_with_store<false>(buf, 1, accp, a0, vb0);
       vprev = vb0 + 32;
     }
   }

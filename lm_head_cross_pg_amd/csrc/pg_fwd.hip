@@ -65,7 +65,12 @@ constexpr int kFwdTokBlocks = PG_FWD_TOK_BLOCKS;
 template <int D, bool FIXED, int NB>
 struct FwdCore {
   static constexpr int KS = D / 16;
+  static constexpr int kWaves = WaveShape<NB>::kWaves;
+  static constexpr int kLoads = embed_loads_per_wave<D, kWaves>();
   const lds_char* lds;
+  char* smem;
+  const uint16_t* E;
+  int wave, lane;
   int h, col, V;
   Softcap sc;
   bf16x8 hf[NB][KS];
@@ -83,7 +88,7 @@ struct FwdCore {
     for (int r = 0; r < 16; ++r) {
       const float z = acc[r];
       const float u = z * z;
-      const float q = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(sc.q3, u, sc.q2), u, sc.q1), u, sc.q0);
+      const float q = __builtin_fmaf(__builtin_fmaf(sc.q2, u, sc.q1), u, sc.q0);
       part += fexp2(__builtin_fmaf(z, q, -sc.M));
     }
     return part;
@@ -144,10 +149,32 @@ struct FwdCore {
   // of element group k - s, so that dependent VALU operations sit one MFMA pair apart. Scheduling
   // barriers keep each step's instructions together. The series sum is speculative: when some
   // |z| of `prev` exceeds c/8 (a wave-uniform, rarely taken branch) the exact sum replaces it.
+  // With LOAD the chain also issues this wave's pieces of the load of embedding tile load_tile
+  // into LDS buffer load_buf, spread over its steps.
+  //
+  // Wave priority falls as the wave moves through the tile (3, 2 over the two halves of block 0;
+  // 1, 0 over block 1). The two waves of a SIMD compete for one matrix pipe, and the arbiter favours
+  // the older wave at equal priority: without this the older wave finishes its tile first and
+  // waits at the barrier while the younger one finishes alone, a phase in which one wave cannot
+  // keep the matrix pipe busy. With it the wave that is behind wins the ties, and both reach the
+  // barrier close together.
+  __device__ __forceinline__ static void stage_priority(int vb, bool second_half) {
+    if (vb == 0) {
+      if (second_half) __builtin_amdgcn_s_setprio(2); else __builtin_amdgcn_s_setprio(3);
+    } else {
+      if (second_half) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
+    }
+  }
+
+  template <bool LOAD>
   __device__ __forceinline__ void chain_with_epilogue(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
-                                                      int vprev) {
+                                                      int vprev, int load_tile = 0, int load_buf = 0) {
     if (!FIXED || sc.asym) {   // running maximum, or asymmetric caps (exact form only)
+      if (LOAD)
+        for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, i);
+      stage_priority(vb, false);
       chain(buf, vb, a);
+      stage_priority(vb, true);
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) {
         if (FIXED) lsum[tb] += part_exact<false>(prev[tb], vprev);
@@ -159,7 +186,7 @@ struct FwdCore {
     constexpr int NE = NB * 16;                     // logits of `prev` per lane
     constexpr int EPC = (NE + KS - 1) / KS;         // elements per group
     constexpr int NG = (NE + EPC - 1) / EPC;        // element groups
-    constexpr int NST = 7;                          // epilogue stages
+    constexpr int NST = 6;                          // epilogue stages
     constexpr int NSTEP = (NG + NST - 1) > KS ? (NG + NST - 1) : KS;
     constexpr int PF = kPrefetch < KS ? kPrefetch : KS;
     const int row = vb * 32 + col;
@@ -174,9 +201,14 @@ struct FwdCore {
     float amax = 0.f;
 #pragma unroll
     for (int k = 0; k < PF; ++k) fr[k] = frag(k);
+    constexpr int LOAD_EVERY = (KS / kLoads) < 4 ? ((KS / kLoads) < 1 ? 1 : KS / kLoads) : 4;
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
+      if (k == 0) stage_priority(vb, false);
+      if (k == KS / 2) stage_priority(vb, true);
       if (k + PF < KS) fr[k + PF] = frag(k + PF);
+      if (LOAD && k % LOAD_EVERY == 0 && k / LOAD_EVERY < kLoads)
+        load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);
       if (k < KS) {
         if (NB == 2) lds_wait_upto((k + PF < KS ? k + PF : KS - 1) - k);
         mfma_step<NB, KS>(a, fr[k], hf, k);
@@ -190,11 +222,10 @@ struct FwdCore {
           const float z = prev[e / 16][e % 16];
           switch (st) {
             case 0: u[e] = z * z; amax = fmaxf(amax, fabsf(z)); break;
-            case 1: q[e] = __builtin_fmaf(sc.q3, u[e], sc.q2); break;
-            case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q1); break;
-            case 3: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
-            case 4: q[e] = __builtin_fmaf(z, q[e], -sc.M); break;
-            case 5: q[e] = fexp2(q[e]); break;
+            case 1: q[e] = __builtin_fmaf(sc.q2, u[e], sc.q1); break;
+            case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
+            case 3: q[e] = __builtin_fmaf(z, q[e], -sc.M); break;
+            case 4: q[e] = fexp2(q[e]); break;
             default: part[e / 16] += q[e]; break;
           }
         }
@@ -276,6 +307,10 @@ void fwd_mfma_kernel(FwdParams p) {
 
   FwdCore<D, FIXED, NB> core;
   core.lds = (const lds_char*)smem;
+  core.smem = smem;
+  core.E = p.E;
+  core.wave = wave;
+  core.lane = lane;
   core.h = h;
   core.col = col;
   core.V = V;
@@ -308,9 +343,12 @@ void fwd_mfma_kernel(FwdParams p) {
     const int buf = i & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (i + 1 < ntiles) load_embed_tile<D, kFwdWaves>(smem, p.E, V, tile + 1, buf ^ 1, wave, lane);
+    const bool next = i + 1 < ntiles;
     const int vb0 = tile * kVocabTile;
     f32x16 a0[NB];
+    // the steady state spreads the next tile's load over the first chain; elsewhere it goes first
+    const bool steady = !(last_partial && i + 1 == ntiles) && vprev >= 0;
+    if (next && !steady) load_embed_tile<D, kFwdWaves>(smem, p.E, V, tile + 1, buf ^ 1, wave, lane);
     if (last_partial && i + 1 == ntiles) {
       core.chain(buf, 0, a0);
       if (vprev >= 0) core.template epilogue<false>(accp, vprev);
@@ -321,11 +359,12 @@ void fwd_mfma_kernel(FwdParams p) {
       vprev = -1;
     } else if (vprev < 0) {
       core.chain(buf, 0, a0);
-      core.chain_with_epilogue(buf, 1, accp, a0, vb0);
+      core.template chain_with_epilogue<false>(buf, 1, accp, a0, vb0);
       vprev = vb0 + 32;
     } else {
-      core.chain_with_epilogue(buf, 0, a0, accp, vprev);
-      core.chain_with_epilogue(buf, 1, accp, a0, vb0);
+      if (next) core.template chain_with_epilogue<true>(buf, 0, a0, accp, vprev, tile + 1, buf ^ 1);
+      else core.template chain_with_epilogue<false>(buf, 0, a0, accp, vprev);
+      core.template chain_with_epilogue<false>(buf, 1, accp, a0, vb0);
       vprev = vb0 + 32;
     }
   }

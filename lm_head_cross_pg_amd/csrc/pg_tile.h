@@ -113,6 +113,32 @@ __device__ __forceinline__ void load_embed_tile(char* smem, const uint16_t* E, i
   }
 }
 
+// The same tile load split into per-wave pieces, so that the loads can be spread over the MFMA
+// chain that runs meanwhile (a burst of 1 KiB LDS DMAs right after a barrier stalls every wave on
+// issue, and with it the MFMAs): embed_loads_per_wave<D, NWAVES>() pieces, piece i issued by
+// load_embed_piece.
+template <int D, int NWAVES>
+__host__ __device__ constexpr int embed_loads_per_wave() {
+  return (kVocabTile * TileLayout<D>::ROWB / 1024 + NWAVES - 1) / NWAVES;
+}
+template <int D, int NWAVES>
+__device__ __forceinline__ void load_embed_piece(char* smem, const uint16_t* E, int V, int tile, int buf, int wave,
+                                                 int lane, int i) {
+  using TL = TileLayout<D>;
+  constexpr int NI = kVocabTile * TL::ROWB / 1024;
+  const int j = wave + i * NWAVES;
+  if (NI % NWAVES != 0 && j >= NI) return;
+  const int v0 = tile * kVocabTile;
+  const int byte = j * 1024 + lane * 16;
+  const int row = byte / TL::ROWB;
+  const int pchunk = (byte % TL::ROWB) / 16;
+  const int lchunk = pchunk ^ TL::swz(row);
+  const int v = min(v0 + row, V - 1);
+  const char* g = reinterpret_cast<const char*>(E + (int64_t)v * D) + lchunk * 16;
+  char* dst = smem + buf * TL::TILEB + (TL::PAD ? j * TL::PITCH : j * 1024);
+  lds_dma16(g, (const lds_char*)dst);
+}
+
 // v_mfma_f32_32x32x16_bf16 with the B operand (hidden rows) read straight from AGPRs and the
 // accumulator in VGPRs. Written as inline assembly because the compiler otherwise copies AGPR
 // operands back into VGPRs before every MFMA. Hazards the compiler cannot see here are covered
