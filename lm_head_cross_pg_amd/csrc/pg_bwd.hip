@@ -461,16 +461,17 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
       // dH = g dZ E
       GemmParams a{};
       a.A = dz; a.lda = q.ldz / 32;
+      a.a_mblocks = (int64_t)rblk * (kRowsPerWG / 32);   // token blocks of the padded dZ rows
       a.B = (const uint16_t*)E; a.ldb = D;
       a.n_dev = n_dev; a.m_dev = n_dev != nullptr; a.k_dev = 0;
       a.M = T; a.N = D; a.K = V; a.kvalid = V;
       a.alpha = grad_scale;
       a.C = dH; a.ldc = D; a.crows = rows; a.split_stride = 0;
-      e = launch_gemm(a, false, dim3((unsigned)((T + kGemmBM - 1) / kGemmBM), (unsigned)((D + kGemmBN - 1) / kGemmBN), 1), st);
+      e = launch_gemm(a, false, dim3((unsigned)((T + kGemmBMdH - 1) / kGemmBMdH), (unsigned)((D + kGemmBN - 1) / kGemmBN), 1), st);
       if (e != hipSuccess) return e;
     }
     // dE = g dZ^T H, k split over workgroups when the output has few tiles
-    const int64_t tiles = ((int64_t)(V + kGemmBM - 1) / kGemmBM) * ((D + kGemmBN - 1) / kGemmBN);
+    const int64_t tiles = ((int64_t)(V + kGemmBMdE - 1) / kGemmBMdE) * ((D + kGemmBN - 1) / kGemmBN);
     const int ncu = dev.cu_count > 0 ? dev.cu_count : 256;
     int64_t ks = ncu / (tiles > 0 ? tiles : 1);
     ks = ks < 1 ? 1 : (ks > kDeSplit ? kDeSplit : ks);
@@ -478,6 +479,7 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     float* part = reinterpret_cast<float*>(ws + L.de_part);
     GemmParams b{};
     b.A = dz; b.lda = ((V + kVocabTile - 1) / kVocabTile) * (int64_t)kVocabTile / 32;
+    b.a_mblocks = b.lda;                                 // vocabulary blocks of the padded dZ columns
     b.B = (const uint16_t*)H; b.ldb = D;
     if (rows) {   // masked: the scored hidden rows, compacted, so that k runs over them directly
       uint16_t* hc = reinterpret_cast<uint16_t*>(ws + L.hc);
@@ -491,7 +493,7 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     b.M = V; b.N = D; b.K = T; b.kvalid = T;
     b.alpha = grad_scale;
     b.C = ks > 1 ? part : dE; b.ldc = D; b.crows = nullptr; b.split_stride = (int64_t)V * D;
-    hipError_t e = launch_gemm(b, true, dim3((unsigned)((V + kGemmBM - 1) / kGemmBM),
+    hipError_t e = launch_gemm(b, true, dim3((unsigned)((V + kGemmBMdE - 1) / kGemmBMdE),
                                              (unsigned)((D + kGemmBN - 1) / kGemmBN), (unsigned)ks), st);
     if (e != hipSuccess || ks == 1) return e;
     return launch_sum_splits(part, (int)ks, (int64_t)V * D, (int64_t)V * D, dE, st);

@@ -1,10 +1,21 @@
 // bf16 GEMM with float32 accumulation for the two products of the backward, dH = g dZ E and
 // dE = g dZ^T H, on gfx950 (v_mfma_f32_32x32x16_bf16).
 //
-// 128 x 512 output tiles per workgroup (4 waves of 128 x 128, sixteen 32 x 32 accumulators each,
-// held in AGPRs), 32-deep k-chunks in a 3-stage LDS ring filled by global_load_lds_dwordx4.
-// A is dZ in its 32 x 32 block layout (described in pg_internal.h); each stage's A tile is four
-// whole blocks, i.e. four contiguous 2 KiB runs. The other operand (E for dH, H for dE) is k x n
+// A workgroup owns a BM x 512 output tile (BM = 64 MB, MB = 2 or 3) and runs 8 waves,
+// two per SIMD, in a 2 x 4 grid; each wave accumulates (32 MB) x 128 of the tile in 4 MB 32 x 32
+// accumulators. k advances in 32-deep chunks through a 3-stage LDS ring filled by
+// global_load_lds_dwordx4.
+//
+// Why this shape: the operand streams mix a unique stream from HBM (dZ) with a stream that every
+// workgroup shares from L2 (E or H). A CU returns vector-memory data in issue order, so the HBM
+// latency paces the shared stream too, and the CU sustains about 28 B/clk of this mix. A 192 x 512
+// tile needs 44 KiB per 6.3 MFLOP chunk (29 B/clk at the full matrix rate), a 128 x 512 tile
+// 40 KiB per 4.2 MFLOP (40 B/clk); which one is faster overall depends on how the tiles fill the
+// CUs. Two waves per SIMD keep the matrix pipe busy while the other wave of the SIMD is held up
+// issuing a load.
+//
+// A is dZ in its 32 x 32 block layout (described in pg_internal.h); each stage's A tile is BM / 32
+// whole blocks, i.e. contiguous 2 KiB runs. The other operand (E for dH, H for dE) is k x n
 // row-major and is fed to the MFMA with ds_read_b64_tr_b16, which gives each lane 4 consecutive k
 // of one column, so no transpose pass over memory is needed; for dE the A operand is read the same
 // way from the blocks.
@@ -23,18 +34,23 @@ namespace pg {
 // apart); it is its own inverse.
 __device__ __forceinline__ int a_swz(int c) { return c ^ ((c >> 4) & 1) ^ (((c >> 6) & 1) << 3); }
 
-// A workgroup owns a 128 x 512 output tile (the whole hidden width), so dZ is read from memory once.
-template <bool A_TRANS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// The tile covers the whole hidden width (512), so dZ is read from memory once.
+template <bool A_TRANS, int MB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_kernel(GemmParams g) {
-  constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
+  constexpr int BM = 64 * MB, BN = kGemmBN, BK = kGemmBK;
+  constexpr int NW = 8;
   constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2, SBYTES = ABYTES + BBYTES;
   constexpr int A_LOADS = ABYTES / 1024, B_LOADS = BBYTES / 1024;   // 1 KiB load instructions
-  constexpr int LOADS_PER_WAVE = (A_LOADS + B_LOADS) / 4;
-  static_assert(BM == 128 && BN == 512 && BK == 32, "tile shape assumed by the layouts below");
+  constexpr int NL = A_LOADS + B_LOADS;
+  constexpr int LPW = (NL + NW - 1) / NW;                           // loads per wave (the first NL % NW waves)
+  static_assert(BN == 512 && BK == 32 && (MB == 2 || MB == 3), "tile shape assumed by the layouts below");
+  static_assert(kGemmStages * SBYTES <= 160 * 1024, "LDS ring");
   __shared__ __attribute__((aligned(1024))) char smem[kGemmStages * SBYTES];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
   const int h = lane >> 5;
+  const int wm = wave >> 2, wn = wave & 3;   // this wave's rows wm * 32 MB .., columns wn * 128 ..
 
   const int64_t ndev = g.n_dev ? (int64_t)(*g.n_dev) : 0;
   const int64_t M = g.m_dev ? ndev : g.M;
@@ -50,31 +66,32 @@ void gemm_bf16_kernel(GemmParams g) {
   const int64_t nk = kc_end > kc_begin ? kc_end - kc_begin : 0;
   const int64_t kvalid = g.k_dev ? ndev : g.kvalid;
 
-  // ---- stage loader: each wave issues LOADS_PER_WAVE global_load_lds_dwordx4; load_one(kc, st, i)
-  //      issues this wave's i-th, so that the loads of a stage can be spread over the MFMAs of the
-  //      previous one (issued in a burst they stall the wave for longer than the MFMAs take)
-  static_assert(A_LOADS % 4 == 0 && B_LOADS % 4 == 0, "loads split evenly over the 4 waves");
+  // ---- stage loader: load q = wave + NW i of the stage's NL; A blocks first (two 1 KiB halves
+  //      each), then the 32 rows of B. load_one(kc, st, i) issues this wave's i-th, so that the
+  //      loads of a stage can be spread over the MFMAs of the previous one.
   auto load_one = [&](int64_t kc, int st, int i) {
+    const int q = wave + NW * i;
+    if (NL % NW != 0 && q >= NL) return;
     char* sA = smem + st * SBYTES;
     char* sB = sA + ABYTES;
     const int64_t k0 = kc * BK;
-    if (i < A_LOADS / 4) {
-      const int j = wave + 4 * i;       // half (j & 1) of block bm = j / 2 of the stage
-      const int bm = j >> 1;
+    if (q < A_LOADS) {
+      const int bm = q >> 1;             // half (q & 1) of block bm of the stage
       int64_t bt, bv;
-      if (!A_TRANS) {                   // dH: m = token, k = vocabulary
+      if (!A_TRANS) {                    // dH: m = token, k = vocabulary
         bt = (m0 >> 5) + bm;
+        bt = bt < g.a_mblocks ? bt : g.a_mblocks - 1;
         bv = k0 >> 5;
-      } else {                          // dE: m = vocabulary, k = token
+      } else {                           // dE: m = vocabulary, k = token
         bt = k0 >> 5;
         bv = (m0 >> 5) + bm;
-        bv = bv < g.lda ? bv : g.lda - 1;
+        bv = bv < g.a_mblocks ? bv : g.a_mblocks - 1;
       }
-      const int chunk = a_swz(64 * (j & 1) + lane);
+      const int chunk = a_swz(64 * (q & 1) + lane);
       const uint16_t* src = g.A + (bt * g.lda + bv) * 1024 + chunk * 8;
-      lds_dma16(src, (const lds_char*)(sA + j * 1024));
+      lds_dma16(src, (const lds_char*)(sA + q * 1024));
     } else {
-      const int j = wave + 4 * (i - A_LOADS / 4);   // row j of the B tile
+      const int j = q - A_LOADS;         // row j of the B tile
       const int lc = lane ^ (4 * (j & 3));
       int64_t k = k0 + j;
       k = k < kvalid ? k : kvalid - 1;
@@ -85,12 +102,12 @@ void gemm_bf16_kernel(GemmParams g) {
   };
   auto load_stage = [&](int64_t kc, int st) {
 #pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i) load_one(kc, st, i);
+    for (int i = 0; i < LPW; ++i) load_one(kc, st, i);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[MB][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -116,11 +133,12 @@ void gemm_bf16_kernel(GemmParams g) {
     return __builtin_bit_cast(bf16x8, v);
   };
 
-  // Fragments of one 16-deep k step: the 4 A blocks of this wave and its 4 B blocks.
-  auto load_frags = [&](const char* sA, const char* sB, int ks, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+  // Fragments of one 16-deep k step: this wave's MB A blocks (all at once) and its 4 B blocks
+  // (one at a time).
+  auto load_afrags = [&](const char* sA, int ks, bf16x8 (&af)[MB]) {
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm) {
-      const char* blk = sA + bm * 2048;
+    for (int bm = 0; bm < MB; ++bm) {
+      const char* blk = sA + (wm * MB + bm) * 2048;
       if (!A_TRANS) {
         // lane l holds row l % 32 of the block in its own 32 bytes: the 16 at chunk 2 l + ks are
         // vocabulary rows 16 ks + 8 (j / 4) + 4 (l / 32) + j % 4, j = 0..7
@@ -141,53 +159,70 @@ void gemm_bf16_kernel(GemmParams g) {
         af[bm] = __builtin_bit_cast(bf16x8, v);
       }
     }
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) bfr[bn] = read_tr(sB, BN * 2, ks, wave * 128 + bn * 32, !A_TRANS);
+  };
+  auto load_bfrag = [&](const char* sB, int ks, int bn) -> bf16x8 {
+    return read_tr(sB, BN * 2, ks, wn * 128 + bn * 32, !A_TRANS);
   };
 
   if (nk > 0) load_stage(kc_begin, 0);
   if (nk > 1) load_stage(kc_begin + 1, 1);
   for (int64_t it = 0; it < nk; ++it) {
-    // this wave's loads of stage `it` are done when at most one stage (the next) is in flight
-    if (it + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_WAVE) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // this wave's loads of stage `it` are done when at most one stage (the next) is in flight:
+    // LPW loads for the first NL % NW waves, LPW - 1 for the others
+    if (it + 1 < nk) {
+      if (NL % NW == 0 || wave < NL % NW) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW - 1) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __builtin_amdgcn_s_barrier();   // every wave's loads of stage `it` landed; stage it-1 is free
     const int st = (int)(it % kGemmStages);
     const char* sA = smem + st * SBYTES;
     const char* sB = sA + ABYTES;
-    // every fragment of the stage is requested before the first MFMA; the compiler's waits then
-    // release each MFMA as soon as its own two fragments have arrived
-    bf16x8 af[BK / 16][4], bfr[BK / 16][4];
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) load_frags(sA, sB, ks, af[ks], bfr[ks]);
-    __builtin_amdgcn_sched_barrier(0);
-    // the MFMAs of this stage with the loads of stage it + 2 (into the buffer stage it - 1 used)
-    // issued between them, one every MFMA_PER_LOAD MFMAs
-    constexpr int NMFMA = (BK / 16) * 16;
-    constexpr int MFMA_PER_LOAD = NMFMA / LOADS_PER_WAVE;
+    // The MFMAs of this stage, one 16-deep step at a time and one B block at a time (the next B
+    // fragment is read while the MB MFMAs of the current one run), with the loads of stage it + 2
+    // (into the buffer stage it - 1 used) issued between them. Wave priority drops from 3 to 1 halfway
+    // through the stage: the two waves of a SIMD share one matrix pipe, and at equal priority the
+    // older one would run ahead and leave the other to finish the stage alone.
+    constexpr int NMFMA = (BK / 16) * MB * 4;
+    constexpr int MFMA_PER_LOAD = NMFMA / LPW;
     const bool prefetch = it + 2 < nk;
     const int64_t kc_pf = kc_begin + it + 2;
     const int st_pf = (int)((it + 2) % kGemmStages);
+    __builtin_amdgcn_s_setprio(3);
 #pragma unroll
-    for (int mi = 0; mi < NMFMA; ++mi) {
-      const int ks = mi >> 4, bm = (mi >> 2) & 3, bn = mi & 3;
-      acc[bm][bn] = mfma32x32x16(af[ks][bm], bfr[ks][bn], acc[bm][bn]);
-      if (mi % MFMA_PER_LOAD == 0 && mi / MFMA_PER_LOAD < LOADS_PER_WAVE && prefetch)
-        load_one(kc_pf, st_pf, mi / MFMA_PER_LOAD);
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[MB], bcur, bnext;
+      load_afrags(sA, ks, af);
+      bcur = load_bfrag(sB, ks, 0);
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) {
+        if (bn + 1 < 4) bnext = load_bfrag(sB, ks, bn + 1);
+#pragma unroll
+        for (int bm = 0; bm < MB; ++bm) {
+          const int mi = (ks * 4 + bn) * MB + bm;
+          acc[bm][bn] = mfma32x32x16(af[bm], bcur, acc[bm][bn]);
+          if (mi % MFMA_PER_LOAD == 0 && mi / MFMA_PER_LOAD < LPW && prefetch) load_one(kc_pf, st_pf, mi / MFMA_PER_LOAD);
+          if (mi == NMFMA / 2) __builtin_amdgcn_s_setprio(1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        bcur = bnext;
+      }
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 
   // ---- epilogue: alpha * acc to C (row-scattered) or to this split's partial tile
   float* C = g.C + (int64_t)blockIdx.z * g.split_stride;
 #pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
+  for (int bm = 0; bm < MB; ++bm)
 #pragma unroll
     for (int bn = 0; bn < 4; ++bn) {
-      const int64_t n = n0 + wave * 128 + bn * 32 + (lane & 31);
+      const int64_t n = n0 + wn * 128 + bn * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + bm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t m = m0 + (wm * MB + bm) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < M && n < g.N) {
           const int64_t crow = g.crows ? (int64_t)g.crows[m] : m;
           C[crow * g.ldc + n] = g.alpha * acc[bm][bn][r];
@@ -208,8 +243,8 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* part, int 
 
 
 hipError_t launch_gemm(const GemmParams& g, bool a_trans, dim3 grid, hipStream_t st) {
-  if (a_trans) hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, dim3(256), 0, st, g);
-  else hipLaunchKernelGGL(gemm_bf16_kernel<false>, grid, dim3(256), 0, st, g);
+  if (a_trans) hipLaunchKernelGGL((gemm_bf16_kernel<true, kGemmMBdE>), grid, dim3(512), 0, st, g);
+  else hipLaunchKernelGGL((gemm_bf16_kernel<false, kGemmMBdH>), grid, dim3(512), 0, st, g);
   return hipGetLastError();
 }
 

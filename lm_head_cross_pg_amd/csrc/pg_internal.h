@@ -71,10 +71,17 @@ hipError_t launch_bpb(const float* nats, const int32_t* target, const uint8_t* m
 // Each lane of the dZ kernel thus writes 32 contiguous bytes and each block is one 2 KiB run.
 
 // C = alpha * A B in bf16 with float32 accumulation (pg_gemm.hip).
-constexpr int kGemmBM = 128, kGemmBN = 512, kGemmBK = 32, kGemmStages = 3;
+constexpr int kGemmBN = 512, kGemmBK = 32, kGemmStages = 3;
+// 32-row m blocks per wave (the workgroup's tile is 64 MB rows): dH (m = tokens) and dE
+// (m = vocabulary rows, k split over workgroups). MB = 3 feeds the matrix pipes better per CU,
+// but at T = 65536 its 342 tiles leave most of 256 CUs idle in a second round; MB = 2 gives
+// 512 tiles (two full rounds) and measures faster.
+constexpr int kGemmMBdH = 2, kGemmMBdE = 2;
+constexpr int kGemmBMdH = 64 * kGemmMBdH, kGemmBMdE = 64 * kGemmMBdE;
 struct GemmParams {
   const uint16_t* A;      // dZ blocks; element (m, k) = dZ[m][k], or dZ[k][m] when A_TRANS
   int64_t lda;            // vocabulary blocks per token block (nvb)
+  int64_t a_mblocks;      // 32-blocks of A along m that exist in memory (reads past them are clamped)
   const uint16_t* B;      // element (k, n): B[k * ldb + n]
   int64_t ldb;
   const int32_t* n_dev;   // device count that replaces M (m_dev) or K (k_dev)
