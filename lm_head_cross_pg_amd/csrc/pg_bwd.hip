@@ -215,14 +215,18 @@ struct DzCore {
     constexpr int NST = 9;                                   // epilogue stages
     if (CAPPED && sc.asym) {                                 // asymmetric caps: exact form only
       load_all();
+      tile_stage_priority(vb, false);
       chain(buf, vb, a);
+      tile_stage_priority(vb, true);
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) store_block<1, false>(prev[tb], vprev, tb);
       return;
     }
     if (!CAPPED || KS < 2 * NST) {                           // short chains: no room to pipeline
       load_all();
+      tile_stage_priority(vb, false);
       chain(buf, vb, a);
+      tile_stage_priority(vb, true);
       if (!CAPPED) {
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) store_block<2, false>(prev[tb], vprev, tb);
@@ -267,6 +271,8 @@ struct DzCore {
     constexpr int LOAD_EVERY = (KS / kLoads) < 4 ? ((KS / kLoads) < 1 ? 1 : KS / kLoads) : 4;
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
+      if (k == 0) tile_stage_priority(vb, false);
+      if (k == KS / 2) tile_stage_priority(vb, true);
       if (k + PF < KS) fr[k + PF] = frag(k + PF);
       if (LOAD && k % LOAD_EVERY == 0 && k / LOAD_EVERY < kLoads)
         load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);
@@ -384,17 +390,19 @@ void bwd_dz_kernel(DzParams p) {
 // ------------------------------------------------------------------------------------ host side
 
 constexpr int kDeSplit = 4;
-// 32-token MFMA column blocks per wave in the dZ kernel (see WaveShape).
-constexpr int kDzTokBlocks = 2;
+// 32-token MFMA column blocks per wave in the dZ kernel (see WaveShape): one (two waves per SIMD,
+// which keep the matrix pipe busier than one wave with two blocks: 605 vs 750 us at D = 512,
+// V = 8192, T = 65536), except at D = 256, where that shape runs out of registers.
+template <int D>
+constexpr int dz_tok_blocks() { return D == 256 ? 2 : 1; }
 
 template <int D>
 static void launch_dz(const DzParams& q, unsigned blocks, hipStream_t st) {
+  constexpr int NB = dz_tok_blocks<D>();
   if (q.sc.capped())
-    hipLaunchKernelGGL((bwd_dz_kernel<D, true, kDzTokBlocks>), dim3(blocks), dim3(WaveShape<kDzTokBlocks>::kThreads), 0,
-                       st, q);
+    hipLaunchKernelGGL((bwd_dz_kernel<D, true, NB>), dim3(blocks), dim3(WaveShape<NB>::kThreads), 0, st, q);
   else
-    hipLaunchKernelGGL((bwd_dz_kernel<D, false, kDzTokBlocks>), dim3(blocks), dim3(WaveShape<kDzTokBlocks>::kThreads), 0,
-                       st, q);
+    hipLaunchKernelGGL((bwd_dz_kernel<D, false, NB>), dim3(blocks), dim3(WaveShape<NB>::kThreads), 0, st, q);
 }
 
 BwdWorkspace bwd_workspace(int64_t T, int32_t D, int32_t V) {

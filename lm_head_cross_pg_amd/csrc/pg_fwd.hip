@@ -150,31 +150,17 @@ struct FwdCore {
   // barriers keep each step's instructions together. The series sum is speculative: when some
   // |z| of `prev` exceeds c/8 (a wave-uniform, rarely taken branch) the exact sum replaces it.
   // With LOAD the chain also issues this wave's pieces of the load of embedding tile load_tile
-  // into LDS buffer load_buf, spread over its steps.
-  //
-  // Wave priority falls as the wave moves through the tile (3, 2 over the two halves of block 0;
-  // 1, 0 over block 1). The two waves of a SIMD compete for one matrix pipe, and the arbiter favours
-  // the older wave at equal priority: without this the older wave finishes its tile first and
-  // waits at the barrier while the younger one finishes alone, a phase in which one wave cannot
-  // keep the matrix pipe busy. With it the wave that is behind wins the ties, and both reach the
-  // barrier close together.
-  __device__ __forceinline__ static void stage_priority(int vb, bool second_half) {
-    if (vb == 0) {
-      if (second_half) __builtin_amdgcn_s_setprio(2); else __builtin_amdgcn_s_setprio(3);
-    } else {
-      if (second_half) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
-    }
-  }
-
+  // into LDS buffer load_buf, spread over its steps. Wave priority is staged over the tile by
+  // tile_stage_priority.
   template <bool LOAD>
   __device__ __forceinline__ void chain_with_epilogue(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
                                                       int vprev, int load_tile = 0, int load_buf = 0) {
     if (!FIXED || sc.asym) {   // running maximum, or asymmetric caps (exact form only)
       if (LOAD)
         for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, i);
-      stage_priority(vb, false);
+      tile_stage_priority(vb, false);
       chain(buf, vb, a);
-      stage_priority(vb, true);
+      tile_stage_priority(vb, true);
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) {
         if (FIXED) lsum[tb] += part_exact<false>(prev[tb], vprev);
@@ -204,8 +190,8 @@ struct FwdCore {
     constexpr int LOAD_EVERY = (KS / kLoads) < 4 ? ((KS / kLoads) < 1 ? 1 : KS / kLoads) : 4;
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
-      if (k == 0) stage_priority(vb, false);
-      if (k == KS / 2) stage_priority(vb, true);
+      if (k == 0) tile_stage_priority(vb, false);
+      if (k == KS / 2) tile_stage_priority(vb, true);
       if (k + PF < KS) fr[k + PF] = frag(k + PF);
       if (LOAD && k % LOAD_EVERY == 0 && k / LOAD_EVERY < kLoads)
         load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);

@@ -161,6 +161,20 @@ __device__ __forceinline__ void mfma_drain(f32x16& a0, f32x16& a1) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
 }
 
+// Wave priority for the chains of a two-block vocabulary tile: it falls as the wave moves through
+// the tile (3, 2 over the two halves of block 0; 1, 0 over block 1). When two waves of a SIMD
+// share one matrix pipe the arbiter favours the older wave at equal priority: without this the
+// older wave finishes its tile first and waits at the barrier while the younger one finishes
+// alone, a phase in which one wave cannot keep the matrix pipe busy. With it the wave that is
+// behind wins the ties, and both reach the barrier close together.
+__device__ __forceinline__ void tile_stage_priority(int vb, bool second_half) {
+  if (vb == 0) {
+    if (second_half) __builtin_amdgcn_s_setprio(2); else __builtin_amdgcn_s_setprio(3);
+  } else {
+    if (second_half) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
+  }
+}
+
 // Wait until at most n LDS operations of this wave are outstanding (n <= 4). LDS reads return
 // in order, so with n younger reads in flight the oldest one has landed.
 __device__ __forceinline__ void lds_wait_upto(int n) {
