@@ -62,7 +62,9 @@ constexpr int kPrefetch = 4;
 // 32-token MFMA column blocks per wave in the forward (see WaveShape).
 constexpr int kFwdTokBlocks = PG_FWD_TOK_BLOCKS;
 
-template <int D, bool FIXED, int NB>
+// ASYM: separate caps for z >= 0 and z < 0 (the epilogue takes the exact form only); a template
+// parameter so that it compiles to a kernel of its own.
+template <int D, bool FIXED, int NB, bool ASYM>
 struct FwdCore {
   static constexpr int KS = D / 16;
   static constexpr int kWaves = WaveShape<NB>::kWaves;
@@ -155,7 +157,7 @@ struct FwdCore {
   template <bool LOAD>
   __device__ __forceinline__ void chain_with_epilogue(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
                                                       int vprev, int load_tile = 0, int load_buf = 0) {
-    if (!FIXED || sc.asym) {   // running maximum, or asymmetric caps (exact form only)
+    if (!FIXED || ASYM) {   // running maximum, or asymmetric caps (exact form only)
       if (LOAD)
         for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, i);
       tile_stage_priority(vb, false);
@@ -230,7 +232,7 @@ struct FwdCore {
   }
 };
 
-template <int D, bool FIXED, int NB>
+template <int D, bool FIXED, int NB, bool ASYM>
 __global__ __launch_bounds__(WaveShape<NB>::kThreads) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
 void fwd_mfma_kernel(FwdParams p) {
   using TL = TileLayout<D>;
@@ -291,7 +293,7 @@ void fwd_mfma_kernel(FwdParams p) {
     }
   }
 
-  FwdCore<D, FIXED, NB> core;
+  FwdCore<D, FIXED, NB, ASYM> core;
   core.lds = (const lds_char*)smem;
   core.smem = smem;
   core.E = p.E;
@@ -511,16 +513,21 @@ hipError_t launch_compact_rows(const uint8_t* mask, int64_t T, char* ws, const F
   return hipGetLastError();
 }
 
-template <int D, bool FIXED>
+template <int D, bool FIXED, bool ASYM>
 static void launch_mfma(const FwdParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, FIXED, kFwdTokBlocks>), dim3(grid), dim3(WaveShape<kFwdTokBlocks>::kThreads),
-                     0, st, p);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, FIXED, kFwdTokBlocks, ASYM>), dim3(grid),
+                     dim3(WaveShape<kFwdTokBlocks>::kThreads), 0, st, p);
 }
 
 template <int D>
 static void launch_mfma_d(const FwdParams& p, int grid, hipStream_t st) {
-  if (p.sc.fixed) launch_mfma<D, true>(p, grid, st);
-  else launch_mfma<D, false>(p, grid, st);
+  if (p.sc.asym) {
+    if (p.sc.fixed) launch_mfma<D, true, true>(p, grid, st);
+    else launch_mfma<D, false, true>(p, grid, st);
+  } else {
+    if (p.sc.fixed) launch_mfma<D, true, false>(p, grid, st);
+    else launch_mfma<D, false, false>(p, grid, st);
+  }
 }
 
 hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t* target,
