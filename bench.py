@@ -292,6 +292,26 @@ def main():
         "frac": flop_fwd / (asym_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bpb": float(out[3].item()),
         "note": "fused forward with separate caps for z >= 0 and z < 0 (exact softcap in the epilogue)"}
 
+    # the same head on logits of a trained model's magnitude: hidden x 8 (exact in bf16) gives z with
+    # standard deviation ~3.6, so almost every 32 x 32 block has some |z| > c/8 and the epilogue
+    # takes the exact softcap (exp2, fma, rcp, exp2 per logit) instead of the series
+    hid8 = d["hidden"] * 8
+    for _ in range(3):
+        abi.pg_lmhead_ce_fwd(hid8, d["embed"], d["target"], None, c, nats, lse, ws_fwd)
+    ev_l = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev_l:
+        a.record()
+        abi.pg_lmhead_ce_fwd(hid8, d["embed"], d["target"], None, c, nats, lse, ws_fwd)
+        b.record()
+    torch.cuda.synchronize()
+    big_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_l]))
+    abi.pg_bpb_reduce(nats, d["target"], None, d["byte_len"], None, V, out, ws_bpb)
+    result["large_logits"] = {
+        "hidden_scale": 8, "launch_ms": big_ms, "tokens_per_s": T / (big_ms * 1e-3),
+        "frac": flop_fwd / (big_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bpb": float(out[3].item()),
+        "note": "same forward, hidden x 8 (z std ~3.6): the epilogue takes the exact softcap in almost every block"}
+    del hid8
+
     # the quantised tied head: per-row int8 embedding (quantised once), scored through the fused path
     q8 = torch.empty((V, D), dtype=torch.int8, device="cuda")
     sc8 = torch.empty(V, dtype=torch.float32, device="cuda")

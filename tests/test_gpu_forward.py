@@ -142,6 +142,16 @@ def test_main_full_size_sampled():
     assert abs(b_gpu - b_ora) <= BPB_RTOL * b_ora
 
 
+def test_large_logits_exact_path():
+    """D = 512, V = 8192, c = 30 with hidden x 8: z has standard deviation ~3.6, so every 32 x 32
+    block holds some |z| > c/8 and the epilogue takes the exact softcap instead of the series."""
+    inp = synth.make_inputs(workload("fwd_v8192", T=4096, stream=97, hidden_scale=8.0), 0)
+    H, E = host_inputs(inp)
+    z = H[:64] @ E.T
+    assert np.mean(np.abs(z) > 30.0 / 8) > 0.2
+    run(inp)
+
+
 def test_ragged_full_width_direct():
     """65,436 rows: still one vocabulary split per workgroup (direct write), ragged last tile."""
     inp = synth.make_inputs("fwd_v8192", 3, T=65436)
