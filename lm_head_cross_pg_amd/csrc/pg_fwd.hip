@@ -78,6 +78,7 @@ struct FwdCore {
   bf16x8 hf[NB][KS];
   float lsum[NB];
   float mrun[NB];
+  int exact_left;   // blocks still to take the exact form before the series is tried again (uniform)
 
   __device__ __forceinline__ void chain(int buf, int vb, f32x16 (&acc)[NB]) const {
     logit_blocks<D, NB>(lds, buf, vb, h, col, hf, acc);
@@ -145,36 +146,20 @@ struct FwdCore {
     }
   }
 
-  // MFMA chain of block (buf, vb) with the epilogue of the pending full block `prev`, software
-  // pipelined by hand (one wave per SIMD leaves no other wave to hide latencies): k-step k issues
-  // the LDS read of step k + kPrefetch, the MFMA pair of step k and stage s of the series epilogue
-  // of element group k - s, so that dependent VALU operations sit one MFMA pair apart. Scheduling
-  // barriers keep each step's instructions together. The series sum is speculative: when some
-  // |z| of `prev` exceeds c/8 (a wave-uniform, rarely taken branch) the exact sum replaces it.
-  // With LOAD the chain also issues this wave's pieces of the load of embedding tile load_tile
-  // into LDS buffer load_buf, spread over its steps. Wave priority is staged over the tile by
-  // tile_stage_priority.
-  template <bool LOAD>
-  __device__ __forceinline__ void chain_with_epilogue(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
-                                                      int vprev, int load_tile = 0, int load_buf = 0) {
-    if (!FIXED || ASYM) {   // running maximum, or asymmetric caps (exact form only)
-      if (LOAD)
-        for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, i);
-      tile_stage_priority(vb, false);
-      chain(buf, vb, a);
-      tile_stage_priority(vb, true);
-#pragma unroll
-      for (int tb = 0; tb < NB; ++tb) {
-        if (FIXED) lsum[tb] += part_exact<false>(prev[tb], vprev);
-        else online<false>(prev[tb], vprev, tb);
-      }
-      return;
-    }
+  // MFMA chain of block (buf, vb) with NST-stage per-logit work on the pending full block `prev`,
+  // software pipelined by hand: k-step k issues the LDS read of step k + kPrefetch, the MFMA of
+  // step k and stage s of element group k - s (stage(s, e, z) for the logits z = prev[e / 16][e % 16]
+  // of the group), so that dependent VALU operations sit one MFMA step apart. Scheduling barriers
+  // keep each step's instructions together. With LOAD the chain also issues this wave's pieces of
+  // the load of embedding tile load_tile into LDS buffer load_buf, spread over its steps. Wave
+  // priority is staged over the tile by tile_stage_priority.
+  template <bool LOAD, int NST, typename Stage>
+  __device__ __forceinline__ void pipelined(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB], int load_tile,
+                                            int load_buf, Stage&& stage) {
     using TL = TileLayout<D>;
     constexpr int NE = NB * 16;                     // logits of `prev` per lane
     constexpr int EPC = (NE + KS - 1) / KS;         // elements per group
     constexpr int NG = (NE + EPC - 1) / EPC;        // element groups
-    constexpr int NST = 6;                          // epilogue stages
     constexpr int NSTEP = (NG + NST - 1) > KS ? (NG + NST - 1) : KS;
     constexpr int PF = kPrefetch < KS ? kPrefetch : KS;
     const int row = vb * 32 + col;
@@ -184,9 +169,6 @@ struct FwdCore {
       return *(const __attribute__((address_space(3))) bf16x8*)(rbase + ((h * KS + ks) ^ sw) * 16);
     };
     bf16x8 fr[KS];
-    float u[NE], q[NE];
-    float part[NB] = {};
-    float amax = 0.f;
 #pragma unroll
     for (int k = 0; k < PF; ++k) fr[k] = frag(k);
     constexpr int LOAD_EVERY = (KS / kLoads) < 4 ? ((KS / kLoads) < 1 ? 1 : KS / kLoads) : 4;
@@ -206,26 +188,74 @@ struct FwdCore {
         const int g = k - st;
         if (g < 0 || g >= NG) continue;
 #pragma unroll
-        for (int e = g * EPC; e < (g + 1) * EPC && e < NE; ++e) {
-          const float z = prev[e / 16][e % 16];
-          switch (st) {
-            case 0: u[e] = z * z; amax = fmaxf(amax, fabsf(z)); break;
-            case 1: q[e] = __builtin_fmaf(sc.q2, u[e], sc.q1); break;
-            case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
-            case 3: q[e] = __builtin_fmaf(z, q[e], -sc.M); break;
-            case 4: q[e] = fexp2(q[e]); break;
-            default: part[e / 16] += q[e]; break;
-          }
-        }
+        for (int e = g * EPC; e < (g + 1) * EPC && e < NE; ++e) stage(st, e, prev[e / 16][e % 16]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     mfma_finish<NB>(a);
+  }
+
+  // MFMA chain of block (buf, vb) with the exp-sum of the pending full block `prev` (fixed shift).
+  // Two forms, both pipelined into the chain:
+  //   series (|z| <= c/8): u = z^2, q = Q(u), 2^(z q - M), sum: five VALU and one exp2 per logit. It
+  //     is speculative: when some |z| of `prev` exceeds c/8 (a wave-uniform branch) the exact sum
+  //     replaces it after the chain, and the next blocks take the exact form directly;
+  //   exact: 2^(z alpha), fma, rcp, 2^(K r), sum: three transcendentals per logit, any z; the only
+  //     form of the asymmetric caps (each side with its own constants).
+  // After a series miss the exact form runs for kExactRun blocks, then the series is tried again, so
+  // inputs whose logits are mostly large pay the speculation once per kExactRun blocks.
+  static constexpr int kExactRun = 16;
+  template <bool LOAD>
+  __device__ __forceinline__ void chain_with_epilogue(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
+                                                      int vprev, int load_tile = 0, int load_buf = 0) {
+    constexpr int NE = NB * 16;
+    if (!FIXED) {   // running maximum (c = 0 or caps above the fixed-shift range)
+      if (LOAD)
+        for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, i);
+      tile_stage_priority(vb, false);
+      chain(buf, vb, a);
+      tile_stage_priority(vb, true);
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) online<false>(prev[tb], vprev, tb);
+      return;
+    }
+    float part[NB] = {};
+    float q[NE];
+    if (ASYM || exact_left > 0) {
+      pipelined<LOAD, 6>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
+        const bool neg = ASYM && z < 0.f;
+        switch (st) {
+          case 0: q[e] = z * (neg ? sc.alpha_n : sc.alpha); break;
+          case 1: q[e] = fexp2(q[e]); break;
+          case 2: { const float ik = neg ? sc.invK_n : sc.invK; q[e] = __builtin_fmaf(q[e], ik, ik); break; }
+          case 3: q[e] = frcp(q[e]); break;                                  // K r = (s - c) log2 e
+          case 4: q[e] = fexp2(ASYM ? q[e] + (neg ? sc.M_n - sc.M : 0.f) : q[e]); break;
+          default: part[e / 16] += q[e]; break;
+        }
+      });
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) lsum[tb] += part[tb];
+      if (!ASYM) --exact_left;
+      return;
+    }
+    float u[NE];
+    float amax = 0.f;
+    pipelined<LOAD, 6>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
+      switch (st) {
+        case 0: u[e] = z * z; amax = fmaxf(amax, fabsf(z)); break;
+        case 1: q[e] = __builtin_fmaf(sc.q2, u[e], sc.q1); break;
+        case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
+        case 3: q[e] = __builtin_fmaf(z, q[e], -sc.M); break;
+        case 4: q[e] = fexp2(q[e]); break;
+        default: part[e / 16] += q[e]; break;
+      }
+    });
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) asm volatile("" ::"v"(part[tb]));   // keep the speculation in the pipeline
     if (!__all(amax <= sc.thr)) {
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) part[tb] = part_exact<false>(prev[tb], vprev);
+      exact_left = kExactRun;
     }
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) lsum[tb] += part[tb];
@@ -303,6 +333,7 @@ void fwd_mfma_kernel(FwdParams p) {
   core.col = col;
   core.V = V;
   core.sc = p.sc;
+  core.exact_left = 0;
 
   // ---- this lane's tokens: hidden row halves into registers (B operands of the MFMA)
   int64_t tok[NB], grow[NB];
