@@ -101,7 +101,11 @@ __global__ __launch_bounds__(256) void zero_unscored_kernel(const uint8_t* mask,
 // 1. bwd_dz_kernel: the forward's structure (8 waves x 32 tokens per workgroup, hidden rows in
 //    registers, the embedding streamed through LDS) recomputes each 32 x 32 logit block with
 //    v_mfma_f32_32x32x16_bf16 and turns it into dZ = (p - onehot) * (1 - (s/c)^2) in the epilogue,
-//    which is interleaved with the next block's MFMA chain. dZ goes to the workspace as bf16 in
+//    which is interleaved with the next block's MFMA chain. The epilogue always takes the exact
+//    softcap (three transcendentals per logit): unlike the forward's speculative series, its cost
+//    does not depend on the size of the logits (at D = 512, V = 8192, T = 65536: 680 us at the
+//    initialisation scale, 675 us at a trained model's, against 634 and 1005 us for the series
+//    with an exact redo of the blocks it cannot take). dZ goes to the workspace as bf16 in
 //    32 x 32 blocks laid out like the MFMA accumulator (described in pg_internal.h), so that
 //    every lane stores 32 contiguous bytes and each block is one contiguous 2 KiB run; zero in
 //    the padding rows and columns.
@@ -125,7 +129,8 @@ struct DzParams {
   uint16_t* dz;
 };
 
-template <int D, bool CAPPED, int NB>
+// ASYM: separate caps for z >= 0 and z < 0 (exact form only), compiled as a kernel of its own.
+template <int D, bool CAPPED, int NB, bool ASYM>
 struct DzCore {
   static constexpr int KS = D / 16;
   static constexpr int kWaves = WaveShape<NB>::kWaves;
@@ -154,7 +159,7 @@ struct DzCore {
     *reinterpret_cast<bf16x8*>(dzblk[tb] + (int64_t)(vbase >> 5) * 1024 + 8 * j8) = o;
   }
 
-  // mode 0: series softcap (|z| <= c/8), 1: exact softcap, 2: no cap
+  // dZ of one block, not pipelined. MODE 1: exact softcap (either cap form), 2: no cap.
   template <int MODE, bool MASKED>
   __device__ __forceinline__ void store_block(const f32x16& acc, int vbase, int tb) const {
     const int dy = ytok[tb] - vbase;
@@ -164,13 +169,7 @@ struct DzCore {
       const int off = 8 * (r >> 2) + 4 * h + (r & 3);
       const float z = acc[r];
       float p, slope;
-      if (MODE == 0) {
-        const float u = z * z;
-        const float s2 = z * __builtin_fmaf(__builtin_fmaf(sc.q2, u, sc.q1), u, sc.q0);
-        p = fexp2(s2 + bias[tb]);
-        const float t = s2 * sc.invM;              // s / c = tanh(z / c)
-        slope = __builtin_fmaf(-t, t, 1.0f);
-      } else if (MODE == 1) {
+      if (MODE == 1) {
         float s2;
         capped_log2_slope(z, sc, s2, slope);                     // either cap form, exact
         p = fexp2(s2 + bias[tb]);
@@ -196,59 +195,23 @@ struct DzCore {
     }
   }
 
-  // MFMA chain of (buf, vb) with dZ of the pending full block `prev` formed and stored in the same
-  // basic block, software pipelined by hand: k-step k issues the LDS read of a later step, the MFMA
-  // step k and stage s of the epilogue of element group k - s, so that the dependent operations of
-  // one logit sit an MFMA step apart and independent logits fill the gaps (with one wave per SIMD
-  // nothing else would). The softcap is the tanh series; a block with some |z| > c/8 (a
-  // wave-uniform, rarely taken branch) is redone exactly (the later store of the same lane to the
-  // same address wins).
-  // With LOAD the chain also issues this wave's pieces of the load of embedding tile load_tile into
-  // LDS buffer load_buf, spread over its steps (a burst of them would stall the MFMAs).
-  template <bool LOAD>
-  __device__ __forceinline__ void chain_with_store(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
-                                                   int vprev, int load_tile = 0, int load_buf = 0) {
-    auto load_all = [&]() {
-      if (LOAD)
-        for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, i);
-    };
-    constexpr int NST = 9;                                   // epilogue stages
-    if (CAPPED && sc.asym) {                                 // asymmetric caps: exact form only
-      load_all();
-      tile_stage_priority(vb, false);
-      chain(buf, vb, a);
-      tile_stage_priority(vb, true);
-#pragma unroll
-      for (int tb = 0; tb < NB; ++tb) store_block<1, false>(prev[tb], vprev, tb);
-      return;
-    }
-    if (!CAPPED || KS < 2 * NST) {                           // short chains: no room to pipeline
-      load_all();
-      tile_stage_priority(vb, false);
-      chain(buf, vb, a);
-      tile_stage_priority(vb, true);
-      if (!CAPPED) {
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb) store_block<2, false>(prev[tb], vprev, tb);
-        return;
-      }
-      float amax = 0.f;
-#pragma unroll
-      for (int tb = 0; tb < NB; ++tb) {
-        store_block<0, false>(prev[tb], vprev, tb);
-        amax = fmaxf(amax, wave_absmax16(prev[tb]));
-      }
-      if (!__all(amax <= sc.thr)) {
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb) store_block<1, false>(prev[tb], vprev, tb);
-      }
-      return;
-    }
+  // MFMA chain of (buf, vb) with NST-stage per-logit work on the pending full block `prev`, software
+  // pipelined by hand: k-step k issues the LDS read of a later step, the MFMA of step k and stage s
+  // of element group k - s (stage(s, e, z) for the logits z = prev[e / 16][e % 16] of the group), so
+  // that the dependent operations of one logit sit an MFMA step apart and independent logits fill
+  // the gaps. With LOAD the chain also issues this wave's pieces of the load of embedding tile
+  // load_tile into LDS buffer load_buf, spread over its steps (a burst of them would stall the
+  // MFMAs). Wave priority is staged over the tile by tile_stage_priority.
+  static constexpr int kNST = 9;   // epilogue stages
+  template <bool LOAD, typename Stage>
+  __device__ __forceinline__ void pipelined(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB], int load_tile,
+                                            int load_buf, Stage&& stage) {
     using TL = TileLayout<D>;
+    constexpr int NST = kNST;
     constexpr int NE = NB * 16;                              // logits of `prev` per lane
     // elements per group (a power of two, so a group of eight stored together is never split), small
     // enough that every group finishes its last stage by step KS - 1 where possible
-    constexpr int SPAN = KS - NST + 1 > 0 ? KS - NST + 1 : 1;   // (short chains returned above)
+    constexpr int SPAN = KS - NST + 1 > 0 ? KS - NST + 1 : 1;   // (short chains do not come here)
     constexpr int EPC0 = (NE + SPAN - 1) / SPAN;
     constexpr int EPC = EPC0 <= 1 ? 1 : EPC0 <= 2 ? 2 : EPC0 <= 4 ? 4 : EPC0 <= 8 ? 8 : 16;
     constexpr int NG = (NE + EPC - 1) / EPC;
@@ -261,11 +224,6 @@ struct DzCore {
       return *(const __attribute__((address_space(3))) bf16x8*)(rbase + ((h * KS + ks) ^ sw) * 16);
     };
     bf16x8 fr[KS];
-    float u[NE], q[NE], t[NE], v[NE];
-    float amax = 0.f;
-    int dy[NB];
-#pragma unroll
-    for (int tb = 0; tb < NB; ++tb) dy[tb] = ytok[tb] - vprev;
 #pragma unroll
     for (int k = 0; k < PF; ++k) fr[k] = frag(k);
     constexpr int LOAD_EVERY = (KS / kLoads) < 4 ? ((KS / kLoads) < 1 ? 1 : KS / kLoads) : 4;
@@ -282,36 +240,61 @@ struct DzCore {
         const int g = k - st;
         if (g < 0 || g >= NG) continue;
 #pragma unroll
-        for (int e = g * EPC; e < (g + 1) * EPC && e < NE; ++e) {
-          const int tb = e / 16, r = e % 16;
-          const float z = prev[tb][r];
-          const int off = 8 * (r >> 2) + 4 * h + (r & 3);
-          switch (st) {
-            case 0: u[e] = z * z; amax = fmaxf(amax, fabsf(z)); break;
-            case 1: q[e] = __builtin_fmaf(sc.q2, u[e], sc.q1); break;
-            case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
-            case 3: q[e] = z * q[e]; break;                                 // s log2 e
-            case 4: t[e] = q[e] * sc.invM; q[e] = q[e] + bias[tb]; break;  // s / c; log2 p
-            case 5: q[e] = fexp2(q[e]); t[e] = __builtin_fmaf(-t[e], t[e], 1.0f); break;
-            case 6: v[e] = (off == dy[tb]) ? q[e] - 1.0f : q[e]; break;
-            case 7: v[e] = v[e] * t[e]; break;
-            default:
-              if ((r & 7) == 7) store8(&v[e - 7], vprev, tb, r >> 3);   // eight values: one 16-byte store
-              break;
-          }
-        }
+        for (int e = g * EPC; e < (g + 1) * EPC && e < NE; ++e) stage(st, e, prev[e / 16][e % 16]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     mfma_finish<NB>(a);
-    if (!__all(amax <= sc.thr)) {
+  }
+
+  // MFMA chain of (buf, vb) with dZ of the pending full block `prev` formed and stored, pipelined
+  // into the chain: K r = rcp(2^(z alpha) / K + 1 / K), log2 p = M + K r - lse log2 e,
+  // slope 4 r (1 - r) (each side of asymmetric caps with its own constants). Short chains, no cap,
+  // and asymmetric caps with one side uncapped form dZ after the chain instead.
+  template <bool LOAD>
+  __device__ __forceinline__ void chain_with_store(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
+                                                   int vprev, int load_tile = 0, int load_buf = 0) {
+    if (!CAPPED || KS < 2 * kNST || (ASYM && !(sc.c > 0.f && sc.cn > 0.f))) {   // not pipelined
+      if (LOAD)
+        for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, i);
+      tile_stage_priority(vb, false);
+      chain(buf, vb, a);
+      tile_stage_priority(vb, true);
 #pragma unroll
-      for (int tb = 0; tb < NB; ++tb) store_block<1, false>(prev[tb], vprev, tb);
+      for (int tb = 0; tb < NB; ++tb) {
+        if (CAPPED) store_block<1, false>(prev[tb], vprev, tb);
+        else store_block<2, false>(prev[tb], vprev, tb);
+      }
+      return;
     }
+    constexpr int NE = NB * 16;
+    float q[NE], t[NE], v[NE];
+    int dy[NB];
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) dy[tb] = ytok[tb] - vprev;
+    pipelined<LOAD>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
+      const int tb = e / 16, r = e % 16;
+      const int off = 8 * (r >> 2) + 4 * h + (r & 3);
+      const bool neg = ASYM && z < 0.f;
+      switch (st) {
+        case 0: q[e] = z * (neg ? sc.alpha_n : sc.alpha); break;
+        case 1: q[e] = fexp2(q[e]); break;
+        case 2: { const float ik = neg ? sc.invK_n : sc.invK; q[e] = __builtin_fmaf(q[e], ik, ik); break; }
+        case 3: q[e] = frcp(q[e]); break;                                               // K r
+        case 4: t[e] = q[e] * (neg ? sc.invK_n : sc.invK);                              // r
+                q[e] = q[e] + ((neg ? sc.M_n : sc.M) + bias[tb]); break;                // log2 p
+        case 5: q[e] = fexp2(q[e]); t[e] = t[e] * __builtin_fmaf(-4.0f, t[e], 4.0f); break;   // p; 4 r (1 - r)
+        case 6: v[e] = (off == dy[tb]) ? q[e] - 1.0f : q[e]; break;
+        case 7: v[e] = v[e] * t[e]; break;
+        default:
+          if ((r & 7) == 7) store8(&v[e - 7], vprev, tb, r >> 3);   // eight values: one 16-byte store
+          break;
+      }
+    });
   }
 };
 
-template <int D, bool CAPPED, int NB>
+template <int D, bool CAPPED, int NB, bool ASYM>
 __global__ __launch_bounds__(WaveShape<NB>::kThreads) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
 void bwd_dz_kernel(DzParams p) {
   using TL = TileLayout<D>;
@@ -326,7 +309,7 @@ void bwd_dz_kernel(DzParams p) {
   if ((int64_t)rt * kRowsPerWG >= n) return;
   const int V = p.V;
 
-  DzCore<D, CAPPED, NB> core;
+  DzCore<D, CAPPED, NB, ASYM> core;
   core.lds = (const lds_char*)smem;
   core.smem = smem;
   core.E = p.E;
@@ -399,10 +382,12 @@ constexpr int dz_tok_blocks() { return D == 256 ? 2 : 1; }
 template <int D>
 static void launch_dz(const DzParams& q, unsigned blocks, hipStream_t st) {
   constexpr int NB = dz_tok_blocks<D>();
-  if (q.sc.capped())
-    hipLaunchKernelGGL((bwd_dz_kernel<D, true, NB>), dim3(blocks), dim3(WaveShape<NB>::kThreads), 0, st, q);
+  if (q.sc.asym)
+    hipLaunchKernelGGL((bwd_dz_kernel<D, true, NB, true>), dim3(blocks), dim3(WaveShape<NB>::kThreads), 0, st, q);
+  else if (q.sc.capped())
+    hipLaunchKernelGGL((bwd_dz_kernel<D, true, NB, false>), dim3(blocks), dim3(WaveShape<NB>::kThreads), 0, st, q);
   else
-    hipLaunchKernelGGL((bwd_dz_kernel<D, false, NB>), dim3(blocks), dim3(WaveShape<NB>::kThreads), 0, st, q);
+    hipLaunchKernelGGL((bwd_dz_kernel<D, false, NB, false>), dim3(blocks), dim3(WaveShape<NB>::kThreads), 0, st, q);
 }
 
 BwdWorkspace bwd_workspace(int64_t T, int32_t D, int32_t V) {
