@@ -152,6 +152,22 @@ def test_large_logits_exact_path():
     run(inp)
 
 
+def test_series_and_exact_blocks_mixed():
+    """Most blocks take the tanh series; the embedding rows of a few vocabulary tiles are scaled by
+    32 (exact in bf16) so that their blocks miss it. The forward then switches to the exact form
+    for a run of blocks and back to the series; every row is checked against the oracle."""
+    inp = synth.make_inputs(workload("fwd_v8192", T=2048, stream=98), 0)
+    E = synth.as_f64(inp["embed"], inp["dtype"]).copy()
+    for tile in (3, 40, 41, 100):
+        E[tile * 64:(tile + 1) * 64] *= 32.0
+    inp = dict(inp, embed=synth.bf16_bits(E.astype(np.float32)))
+    H, E2 = host_inputs(inp)
+    assert np.array_equal(E2, E)
+    z = H[:32] @ E2[3 * 64:4 * 64].T
+    assert np.max(np.abs(z)) > 30.0 / 8
+    run(inp)
+
+
 def test_ragged_full_width_direct():
     """65,436 rows: still one vocabulary split per workgroup (direct write), ragged last tile."""
     inp = synth.make_inputs("fwd_v8192", 3, T=65436)
