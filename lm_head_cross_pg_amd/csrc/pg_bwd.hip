@@ -473,6 +473,7 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     GemmParams b{};
     b.A = dz; b.lda = ((V + kVocabTile - 1) / kVocabTile) * (int64_t)kVocabTile / 32;
     b.a_mblocks = b.lda;                                 // vocabulary blocks of the padded dZ columns
+    b.k_blocks = (int64_t)((T + kRowsPerWG - 1) / kRowsPerWG) * (kRowsPerWG / 32);   // token blocks of dZ
     b.B = (const uint16_t*)H; b.ldb = D;
     if (rows) {   // masked: the scored hidden rows, compacted, so that k runs over them directly
       uint16_t* hc = reinterpret_cast<uint16_t*>(ws + L.hc);

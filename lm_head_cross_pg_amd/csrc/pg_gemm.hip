@@ -1,18 +1,20 @@
 // bf16 GEMM with float32 accumulation for the two products of the backward, dH = g dZ E and
 // dE = g dZ^T H, on gfx950 (v_mfma_f32_32x32x16_bf16).
 //
-// A workgroup owns a BM x 512 output tile (BM = 64 MB, MB = 2 or 3) and runs 8 waves,
-// two per SIMD, in a 2 x 4 grid; each wave accumulates (32 MB) x 128 of the tile in 4 MB 32 x 32
-// accumulators. k advances in 32-deep chunks through a 3-stage LDS ring filled by
-// global_load_lds_dwordx4.
+// A workgroup owns a 128 x 512 output tile (BM = 64 MB, MB = 2) and runs 8 waves, two per SIMD,
+// in a 2 x 4 grid; each wave accumulates 64 x 128 of the tile in eight 32 x 32 accumulators. k
+// advances in 32-deep chunks; B and A are filled by global_load_lds_dwordx4 into LDS rings of 3 and
+// 4 slots.
 //
 // Why this shape: the operand streams mix a unique stream from HBM (dZ) with a stream that every
 // workgroup shares from L2 (E or H). A CU returns vector-memory data in issue order, so the HBM
-// latency paces the shared stream too, and the CU sustains about 28 B/clk of this mix. A 192 x 512
-// tile needs 44 KiB per 6.3 MFLOP chunk (29 B/clk at the full matrix rate), a 128 x 512 tile
-// 40 KiB per 4.2 MFLOP (40 B/clk); which one is faster overall depends on how the tiles fill the
-// CUs. Two waves per SIMD keep the matrix pipe busy while the other wave of the SIMD is held up
-// issuing a load.
+// latency paces the shared stream too, and the CU sustains about 28 B/clk of this mix. Each stage
+// therefore issues the B loads of stage s + 2 first and the A load of stage s + 3 after them: a B
+// load waits only for A loads issued a stage or more before it, and every load has three stage
+// periods to land (A needs the extra ring slot). A 128 x 512 tile needs 40 KiB per 4.2 MFLOP
+// chunk; a 192 x 512 one would need less per MFLOP, but at T = 65536 its 342 tiles do not fill
+// 256 CUs evenly. Two waves per SIMD keep the matrix pipe busy while the other wave of the SIMD is
+// held up issuing a load.
 //
 // A is dZ in its 32 x 32 block layout (described in pg_internal.h); each stage's A tile is BM / 32
 // whole blocks, i.e. contiguous 2 KiB runs. The other operand (E for dH, H for dE) is k x n
@@ -40,13 +42,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_kernel(GemmParams g) {
   constexpr int BM = 64 * MB, BN = kGemmBN, BK = kGemmBK;
   constexpr int NW = 8;
-  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2, SBYTES = ABYTES + BBYTES;
+  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;
   constexpr int A_LOADS = ABYTES / 1024, B_LOADS = BBYTES / 1024;   // 1 KiB load instructions
   constexpr int NL = A_LOADS + B_LOADS;
   constexpr int LPW = (NL + NW - 1) / NW;                           // loads per wave (the first NL % NW waves)
-  static_assert(BN == 512 && BK == 32 && (MB == 2 || MB == 3), "tile shape assumed by the layouts below");
-  static_assert(kGemmStages * SBYTES <= 160 * 1024, "LDS ring");
-  __shared__ __attribute__((aligned(1024))) char smem[kGemmStages * SBYTES];
+  static_assert(BN == 512 && BK == 32 && MB == 2, "tile shape assumed by the layouts below (one A load per wave)");
+  // B: ring of kGemmStages slots; A: ring of AST slots, one stage deeper, so that each stage's A
+  // load can be issued after its B loads and a stage earlier
+  constexpr int AST = kGemmStages + 1;
+  static_assert(kGemmStages * BBYTES + AST * ABYTES <= 160 * 1024, "LDS rings");
+  __shared__ __attribute__((aligned(1024))) char smem[kGemmStages * BBYTES + AST * ABYTES];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
   const int h = lane >> 5;
@@ -66,14 +71,18 @@ void gemm_bf16_kernel(GemmParams g) {
   const int64_t nk = kc_end > kc_begin ? kc_end - kc_begin : 0;
   const int64_t kvalid = g.k_dev ? ndev : g.kvalid;
 
-  // ---- stage loader: load q = wave + NW i of the stage's NL; A blocks first (two 1 KiB halves
-  //      each), then the 32 rows of B. load_one(kc, st, i) issues this wave's i-th, so that the
-  //      loads of a stage can be spread over the MFMAs of the previous one.
-  auto load_one = [&](int64_t kc, int st, int i) {
-    const int q = wave + NW * i;
-    if (NL % NW != 0 && q >= NL) return;
-    char* sA = smem + st * SBYTES;
-    char* sB = sA + ABYTES;
+  // ---- the load group of stage kc: this wave's B rows of stage kc (i < B_LOADS / NW: rows
+  //      wave + NW i), then its A chunk of stage kc + 1 (i = B_LOADS / NW: half (wave & 1) of A
+  //      block wave / 2). load_one(kc, i) issues the i-th, so that a group can be spread over the
+  //      MFMAs of the stage two before it.
+  auto load_one = [&](int64_t kc, int i) {
+    const int bpw = B_LOADS / NW;
+    const int64_t rel = kc - kc_begin;
+    int q;
+    if (i < bpw) { q = A_LOADS + wave + NW * i; }
+    else { q = wave; kc = kc + 1; }
+    char* sA = smem + kGemmStages * BBYTES + (int)((rel + (i < bpw ? 0 : 1)) % AST) * ABYTES;
+    char* sB = smem + (int)(rel % kGemmStages) * BBYTES;
     const int64_t k0 = kc * BK;
     if (q < A_LOADS) {
       const int bm = q >> 1;             // half (q & 1) of block bm of the stage
@@ -82,8 +91,10 @@ void gemm_bf16_kernel(GemmParams g) {
         bt = (m0 >> 5) + bm;
         bt = bt < g.a_mblocks ? bt : g.a_mblocks - 1;
         bv = k0 >> 5;
+        bv = bv < g.lda ? bv : g.lda - 1;
       } else {                           // dE: m = vocabulary, k = token
         bt = k0 >> 5;
+        bt = bt < g.k_blocks ? bt : g.k_blocks - 1;
         bv = (m0 >> 5) + bm;
         bv = bv < g.a_mblocks ? bv : g.a_mblocks - 1;
       }
@@ -100,9 +111,9 @@ void gemm_bf16_kernel(GemmParams g) {
       lds_dma16(g.B + k * g.ldb + col, (const lds_char*)(sB + j * 1024));
     }
   };
-  auto load_stage = [&](int64_t kc, int st) {
+  auto load_stage = [&](int64_t kc) {
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) load_one(kc, st, i);
+    for (int i = 0; i < LPW; ++i) load_one(kc, i);
   };
 
   f32x16 acc[MB][4];
@@ -164,21 +175,19 @@ void gemm_bf16_kernel(GemmParams g) {
     return read_tr(sB, BN * 2, ks, wn * 128 + bn * 32, !A_TRANS);
   };
 
-  if (nk > 0) load_stage(kc_begin, 0);
-  if (nk > 1) load_stage(kc_begin + 1, 1);
+  // A chunk of stage 0, then the groups of stages 0 and 1; every stage's group is issued (with
+  // clamped addresses past the end), so the waits below are constant
+  if (nk > 0) {
+    load_one(kc_begin - 1, B_LOADS / NW);
+    load_stage(kc_begin);
+    load_stage(kc_begin + 1);
+  }
   for (int64_t it = 0; it < nk; ++it) {
-    // this wave's loads of stage `it` are done when at most one stage (the next) is in flight:
-    // LPW loads for the first NL % NW waves, LPW - 1 for the others
-    if (it + 1 < nk) {
-      if (NL % NW == 0 || wave < NL % NW) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW - 1) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __builtin_amdgcn_s_barrier();   // every wave's loads of stage `it` landed; stage it-1 is free
-    const int st = (int)(it % kGemmStages);
-    const char* sA = smem + st * SBYTES;
-    const char* sB = sA + ABYTES;
+    // B(it) and A(it) landed: issued after B(it)'s last load are A(it + 1) and the group of it + 1
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW + 1) : "memory");
+    __builtin_amdgcn_s_barrier();
+    const char* sA = smem + kGemmStages * BBYTES + (int)(it % AST) * ABYTES;
+    const char* sB = smem + (int)(it % kGemmStages) * BBYTES;
     // The MFMAs of this stage, one 16-deep step at a time and one B block at a time (the next B
     // fragment is read while the MB MFMAs of the current one run), with the loads of stage it + 2
     // (into the buffer stage it - 1 used) issued between them. Wave priority drops from 3 to 1 halfway
@@ -186,9 +195,7 @@ void gemm_bf16_kernel(GemmParams g) {
     // older one would run ahead and leave the other to finish the stage alone.
     constexpr int NMFMA = (BK / 16) * MB * 4;
     constexpr int MFMA_PER_LOAD = NMFMA / LPW;
-    const bool prefetch = it + 2 < nk;
     const int64_t kc_pf = kc_begin + it + 2;
-    const int st_pf = (int)((it + 2) % kGemmStages);
     __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
@@ -203,7 +210,7 @@ void gemm_bf16_kernel(GemmParams g) {
         for (int bm = 0; bm < MB; ++bm) {
           const int mi = (ks * 4 + bn) * MB + bm;
           acc[bm][bn] = mfma32x32x16(af[bm], bcur, acc[bm][bn]);
-          if (mi % MFMA_PER_LOAD == 0 && mi / MFMA_PER_LOAD < LPW && prefetch) load_one(kc_pf, st_pf, mi / MFMA_PER_LOAD);
+          if (mi % MFMA_PER_LOAD == 0 && mi / MFMA_PER_LOAD < LPW) load_one(kc_pf, mi / MFMA_PER_LOAD);
           if (mi == NMFMA / 2) __builtin_amdgcn_s_setprio(1);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -212,6 +219,7 @@ void gemm_bf16_kernel(GemmParams g) {
     }
   }
   __builtin_amdgcn_s_setprio(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the clamped loads past the end landed
 
   // ---- epilogue: alpha * acc to C (row-scattered) or to this split's partial tile
   float* C = g.C + (int64_t)blockIdx.z * g.split_stride;

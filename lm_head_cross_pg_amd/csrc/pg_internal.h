@@ -82,6 +82,7 @@ struct GemmParams {
   const uint16_t* A;      // dZ blocks; element (m, k) = dZ[m][k], or dZ[k][m] when A_TRANS
   int64_t lda;            // vocabulary blocks per token block (nvb)
   int64_t a_mblocks;      // 32-blocks of A along m that exist in memory (reads past them are clamped)
+  int64_t k_blocks;       // A_TRANS: 32-blocks of A along k (token blocks) that exist in memory
   const uint16_t* B;      // element (k, n): B[k * ldb + n]
   int64_t ldb;
   const int32_t* n_dev;   // device count that replaces M (m_dev) or K (k_dev)
