@@ -460,11 +460,12 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
       a.M = T; a.N = D; a.K = V; a.kvalid = V;
       a.alpha = grad_scale;
       a.C = dH; a.ldc = D; a.crows = rows; a.split_stride = 0;
-      e = launch_gemm(a, false, dim3((unsigned)((T + kGemmBMdH - 1) / kGemmBMdH), (unsigned)((D + kGemmBN - 1) / kGemmBN), 1), st);
+      e = launch_gemm(a, false, 1, st);
       if (e != hipSuccess) return e;
     }
     // dE = g dZ^T H, k split over workgroups when the output has few tiles
-    const int64_t tiles = ((int64_t)(V + kGemmBMdE - 1) / kGemmBMdE) * ((D + kGemmBN - 1) / kGemmBN);
+    const int64_t tiles = ((int64_t)(V + gemm_tile_m(true) - 1) / gemm_tile_m(true)) *
+                          ((D + gemm_tile_n(true) - 1) / gemm_tile_n(true));
     const int ncu = dev.cu_count > 0 ? dev.cu_count : 256;
     int64_t ks = ncu / (tiles > 0 ? tiles : 1);
     ks = ks < 1 ? 1 : (ks > kDeSplit ? kDeSplit : ks);
@@ -487,8 +488,7 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     b.M = V; b.N = D; b.K = T; b.kvalid = T;
     b.alpha = grad_scale;
     b.C = ks > 1 ? part : dE; b.ldc = D; b.crows = nullptr; b.split_stride = (int64_t)V * D;
-    hipError_t e = launch_gemm(b, true, dim3((unsigned)((V + kGemmBMdE - 1) / kGemmBMdE),
-                                             (unsigned)((D + kGemmBN - 1) / kGemmBN), (unsigned)ks), st);
+    hipError_t e = launch_gemm(b, true, (int)ks, st);
     if (e != hipSuccess || ks == 1) return e;
     return launch_sum_splits(part, (int)ks, (int64_t)V * D, (int64_t)V * D, dE, st);
   }

@@ -70,14 +70,8 @@ hipError_t launch_bpb(const float* nats, const int32_t* target, const uint8_t* m
 //   L = t + 32 ((v >> 2) & 1)   (the lane that computed it),  r = 4 (v >> 3) + (v & 3).
 // Each lane of the dZ kernel thus writes 32 contiguous bytes and each block is one 2 KiB run.
 
-// C = alpha * A B in bf16 with float32 accumulation (pg_gemm.hip).
-constexpr int kGemmBN = 512, kGemmBK = 32, kGemmStages = 3;
-// 32-row m blocks per wave (the workgroup's tile is 64 MB rows): dH (m = tokens) and dE
-// (m = vocabulary rows, k split over workgroups). MB = 3 feeds the matrix pipes better per CU,
-// but at T = 65536 its 342 tiles leave most of 256 CUs idle in a second round; MB = 2 gives
-// 512 tiles (two full rounds) and measures faster.
-constexpr int kGemmMBdH = 2, kGemmMBdE = 2;
-constexpr int kGemmBMdH = 64 * kGemmMBdH, kGemmBMdE = 64 * kGemmMBdE;
+// C = alpha * A B in bf16 with float32 accumulation (pg_gemm.hip), k in 32-deep chunks.
+constexpr int kGemmBK = 32;
 struct GemmParams {
   const uint16_t* A;      // dZ blocks; element (m, k) = dZ[m][k], or dZ[k][m] when A_TRANS
   int64_t lda;            // vocabulary blocks per token block (nvb)
@@ -95,9 +89,13 @@ struct GemmParams {
   const int32_t* crows;   // output row of m when given
   int64_t split_stride;   // elements between the partial outputs of k splits
 };
-// a_trans: A's element (m, k) is dZ[k][m] (else dZ[m][k]). grid = (m tiles, n tiles, k splits);
-// with several splits, C receives one partial output per split at split_stride.
-hipError_t launch_gemm(const GemmParams& g, bool a_trans, dim3 grid, hipStream_t st);
+// a_trans: A's element (m, k) is dZ[k][m] (else dZ[m][k]). k is split over ksplit workgroups per
+// output tile; with several splits, C receives one partial output per split at split_stride.
+// M and N are the host bounds that size the grid.
+hipError_t launch_gemm(const GemmParams& g, bool a_trans, int ksplit, hipStream_t st);
+// Output tile of each product (rows x columns).
+int gemm_tile_m(bool a_trans);
+int gemm_tile_n(bool a_trans);
 // out[i] = sum over s < nsplit of part[s * stride + i], in split order (nsplit = 0 writes zeros).
 hipError_t launch_sum_splits(const float* part, int nsplit, int64_t stride, int64_t count, float* out,
                              hipStream_t st);
