@@ -262,6 +262,13 @@ struct FwdCore {
   }
 };
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Elements 2 j and 2 j + 1 of v.
+__device__ __forceinline__ bf16x2 bf16_pair(const bf16x8& v, int j) {
+  bf16x2 r = {v[2 * j], v[2 * j + 1]};
+  return r;
+}
+
 template <int D, bool FIXED, int NB, bool ASYM>
 __global__ __launch_bounds__(WaveShape<NB>::kThreads) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
 void fwd_mfma_kernel(FwdParams p) {
@@ -269,7 +276,6 @@ void fwd_mfma_kernel(FwdParams p) {
   constexpr int KS = D / 16;
   constexpr int kTokPerWave = WaveShape<NB>::kTok;
   constexpr int kFwdWaves = WaveShape<NB>::kWaves;
-  constexpr int EPL = D >= 64 ? D / 64 : 1;           // hidden elements per lane in the target dot
   __shared__ __attribute__((aligned(1024))) char smem[2 * TL::TILEB];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -287,42 +293,6 @@ void fwd_mfma_kernel(FwdParams p) {
   const int V = p.V;
   const int64_t tok0 = (int64_t)rt * kRowsPerWG + wave * kTokPerWave;   // first token of this wave
 
-  // ---- target logit (split 0 only): lanes span the hidden width, 8 tokens per batch; the lane
-  //      of token j within a 32-token block keeps it
-  float sy[NB] = {};
-  if (split == 0) {
-    for (int j0 = 0; j0 < kTokPerWave; j0 += 8) {
-      float part[8];
-      int okm = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        int64_t i = tok0 + j0 + j;
-        i = i < n ? i : n - 1;
-        const int64_t r = p.rows ? (int64_t)p.rows[i] : i;
-        const int y = p.target[r];
-        const bool ok = (y >= 0) && (y < V);
-        okm |= ok ? (1 << j) : 0;
-        float hv[EPL], ev[EPL];
-        part[j] = 0.f;
-        if (D >= 64 || lane < D) {
-          load_bf16<EPL>(p.H + r * D + lane * EPL, hv);
-          load_bf16<EPL>(p.E + (int64_t)(ok ? y : 0) * D + lane * EPL, ev);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) part[j] = __builtin_fmaf(hv[e], ev[e], part[j]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float zy = wave_sum(part[j]);
-        const int t = j0 + j;
-        const float v = ((okm >> j) & 1) ? capped_log2(zy, p.sc) : __builtin_nanf("");
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb)
-          if (t == tb * 32 + col) sy[tb] = v;
-      }
-    }
-  }
-
   FwdCore<D, FIXED, NB, ASYM> core;
   core.lds = (const lds_char*)smem;
   core.smem = smem;
@@ -334,6 +304,10 @@ void fwd_mfma_kernel(FwdParams p) {
   core.V = V;
   core.sc = p.sc;
   core.exact_left = 0;
+
+  // ---- the first embedding tile goes out first, so that its latency overlaps the prologue
+  const int ntiles = t_end - t_begin;
+  if (ntiles > 0) load_embed_tile<D, kFwdWaves>(smem, p.E, V, t_begin, 0, wave, lane);
 
   // ---- this lane's tokens: hidden row halves into registers (B operands of the MFMA)
   int64_t tok[NB], grow[NB];
@@ -349,14 +323,41 @@ void fwd_mfma_kernel(FwdParams p) {
     for (int ks = 0; ks < KS; ++ks) core.hf[tb][ks] = src[ks];
   }
 
+  // ---- target logit (split 0 only). Lanes l and l + 32 hold the two halves of the hidden row of
+  //      token l % 32; each dots its half with the same half of E[y] (bf16 pairs, float32
+  //      accumulation, loads in batches of up to 16 x 16 bytes) and the two halves are added.
+  float sy[NB] = {};
+  if (split == 0) {
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) {
+      const int y = p.target[grow[tb]];
+      const bool ok = (y >= 0) && (y < V);
+      const bf16x8* er = reinterpret_cast<const bf16x8*>(p.E + (int64_t)(ok ? y : 0) * D + h * (D / 2));
+      constexpr int BATCH = KS < 16 ? KS : 16;
+      float acc4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < KS; k0 += BATCH) {
+        bf16x8 ev[BATCH];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) ev[k] = er[k0 + k];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc4[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16_pair(core.hf[tb][k0 + k], j), bf16_pair(ev[k], j), acc4[j], false);
+      }
+      float zy = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+      zy += __shfl_xor(zy, 32);
+      sy[tb] = ok ? capped_log2(zy, p.sc) : __builtin_nanf("");
+    }
+  }
+
   // ---- main loop. Only the last tile of the vocabulary can be partial; it runs the masked
   //      epilogue. Elsewhere the epilogue of the previous 32-row block is interleaved with the
   //      MFMA chain of the current one.
-  const int ntiles = t_end - t_begin;
   const bool last_partial = (t_end == p.n_vtiles) && (V % kVocabTile != 0);
   f32x16 accp[NB];
   int vprev = -1;
-  if (ntiles > 0) load_embed_tile<D, kFwdWaves>(smem, p.E, V, t_begin, 0, wave, lane);
   for (int i = 0; i < ntiles; ++i) {
     const int tile = t_begin + i;
     const int buf = i & 1;

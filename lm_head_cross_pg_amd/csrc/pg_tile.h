@@ -5,32 +5,6 @@
 
 namespace pg {
 
-// Loads EPL consecutive bf16 values (EPL in {1, 2, 4, 8}) and widens them to float.
-template <int EPL>
-__device__ __forceinline__ void load_bf16(const uint16_t* p, float (&out)[EPL]) {
-  if constexpr (EPL == 8) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { out[2 * j] = __uint_as_float(w[j] << 16); out[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u); }
-  } else if constexpr (EPL == 4) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    out[0] = __uint_as_float(u.x << 16); out[1] = __uint_as_float(u.x & 0xffff0000u);
-    out[2] = __uint_as_float(u.y << 16); out[3] = __uint_as_float(u.y & 0xffff0000u);
-  } else if constexpr (EPL == 2) {
-    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-    out[0] = __uint_as_float(u << 16); out[1] = __uint_as_float(u & 0xffff0000u);
-  } else {
-    out[0] = bf16_to_f32(*p);
-  }
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
 // Shape of the token tile: NB 32-token MFMA column blocks per wave, 256 rows per workgroup.
 //   NB = 1: 8 waves (two per SIMD), hidden rows of 32 tokens in VGPRs; every embedding fragment
 //           read from LDS feeds one MFMA.
