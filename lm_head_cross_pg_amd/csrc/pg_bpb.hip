@@ -14,7 +14,7 @@ namespace pg {
 
 constexpr int kBpbThreads = 256;
 constexpr int kBpbMaxBlocks = 1024;
-constexpr int64_t kBpbRowsPerBlockMin = 2048;
+constexpr int64_t kBpbRowsPerBlockMin = kBpbThreads;   // one row per thread up to 256 Ki rows
 
 struct BpbPartial {
   double nats;
@@ -22,26 +22,35 @@ struct BpbPartial {
   long long count;
 };
 
-__device__ void block_reduce(BpbPartial& v, BpbPartial* sh) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = kBpbThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) {
-      sh[tid].nats += sh[tid + off].nats;
-      sh[tid].bytes += sh[tid + off].bytes;
-      sh[tid].count += sh[tid + off].count;
-    }
-    __syncthreads();
+// Workgroup sum in a fixed order: a butterfly within each wave, then the four wave sums in wave
+// order. Thread 0 returns the result.
+__device__ BpbPartial block_reduce(BpbPartial v) {
+  __shared__ BpbPartial sh[kBpbThreads / 64];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    v.nats += __shfl_xor(v.nats, off);
+    v.bytes += __shfl_xor(v.bytes, off);
+    v.count += __shfl_xor(v.count, off);
   }
-  v = sh[0];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    v = sh[0];
+#pragma unroll
+    for (int w = 1; w < kBpbThreads / 64; ++w) {
+      v.nats += sh[w].nats;
+      v.bytes += sh[w].bytes;
+      v.count += sh[w].count;
+    }
+  }
+  return v;
 }
 
 __global__ __launch_bounds__(kBpbThreads) void bpb_partial_kernel(const float* nats, const int32_t* target,
                                                                   const uint8_t* mask, const int32_t* byte_len,
                                                                   const int32_t* byte_per_pos, int64_t T, int V,
                                                                   int64_t rows_per_block, BpbPartial* part) {
-  __shared__ BpbPartial sh[kBpbThreads];
   const int64_t b = (int64_t)blockIdx.x * rows_per_block;
   const int64_t e = (b + rows_per_block < T) ? b + rows_per_block : T;
   BpbPartial acc{0.0, 0, 0};
@@ -56,19 +65,18 @@ __global__ __launch_bounds__(kBpbThreads) void bpb_partial_kernel(const float* n
       if (y >= 0 && y < V) acc.bytes += byte_len[y];   // out of range: no bytes (its nats are NaN)
     }
   }
-  block_reduce(acc, sh);
+  acc = block_reduce(acc);
   if (threadIdx.x == 0) part[blockIdx.x] = acc;
 }
 
 __global__ __launch_bounds__(kBpbThreads) void bpb_final_kernel(const BpbPartial* part, int nblocks, double* out) {
-  __shared__ BpbPartial sh[kBpbThreads];
   BpbPartial acc{0.0, 0, 0};
   for (int i = threadIdx.x; i < nblocks; i += kBpbThreads) {
     acc.nats += part[i].nats;
     acc.bytes += part[i].bytes;
     acc.count += part[i].count;
   }
-  block_reduce(acc, sh);
+  acc = block_reduce(acc);
   if (threadIdx.x == 0) {
     double sum_nats = acc.nats;
     double sum_bytes = (double)acc.bytes;
