@@ -274,6 +274,20 @@ def main():
                      "algorithmic": "2*T*D*V = %.4g FLOP per launch" % flop_fwd},
     }
 
+    # the bits-per-byte reduction alone (reads nats, target and the byte length of each target)
+    ev_b = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev_b:
+        a.record()
+        abi.pg_bpb_reduce(nats, d["target"], None, d["byte_len"], None, V, out, ws_bpb)
+        b.record()
+    torch.cuda.synchronize()
+    bpb_launch = np.array([a.elapsed_time(b) for a, b in ev_b]) * 1e3
+    result["bpb_reduce"] = {
+        "launch_us": float(np.mean(bpb_launch)),
+        "launch_us_p10_p50_p90": [float(np.percentile(bpb_launch, q)) for q in (10, 50, 90)],
+        "bytes": T * 12,
+        "note": "two launches (per-workgroup partials, fixed-order final); 12 B per row: nats, target, byte length"}
+
     # the asymmetric softcap (separate caps for z >= 0 and z < 0) on the same workload
     caps = (30.0, 20.0)
     for _ in range(3):

@@ -152,7 +152,7 @@ struct FwdCore {
   // of the group), so that dependent VALU operations sit one MFMA step apart. Scheduling barriers
   // keep each step's instructions together. With LOAD the chain also issues this wave's pieces of
   // the load of embedding tile load_tile into LDS buffer load_buf, spread over its steps. Wave
-  // priority is staged over the tile by tile_stage_priority.
+  // priority is staged over the tile by tile_step_priority.
   template <bool LOAD, int NST, typename Stage>
   __device__ __forceinline__ void pipelined(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB], int load_tile,
                                             int load_buf, Stage&& stage) {
@@ -174,8 +174,7 @@ struct FwdCore {
     constexpr int LOAD_EVERY = (KS / kLoads) < 4 ? ((KS / kLoads) < 1 ? 1 : KS / kLoads) : 4;
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
-      if (k == 0) tile_stage_priority(vb, false);
-      if (k == KS / 2) tile_stage_priority(vb, true);
+      if (k < KS) tile_step_priority<KS>(vb, k);
       if (k + PF < KS) fr[k + PF] = frag(k + PF);
       if (LOAD && k % LOAD_EVERY == 0 && k / LOAD_EVERY < kLoads)
         load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);
