@@ -221,6 +221,31 @@ def test_zero_rows_and_zero_weights():
     assert abs(out[3] - exp) <= 1e-5 * exp
 
 
+@pytest.mark.parametrize("T", [1, 255, 256, 257, 262144, 262145, 1000003])
+def test_bpb_reduction_row_counts(T):
+    """The reduction alone over row counts around its workgroup sizes (256 rows per workgroup up
+    to 1024 workgroups, then several rows per thread), with a mask, a few targets outside the
+    vocabulary and a byte sidecar, against the oracle's ratio of sums."""
+    V = 8192
+    rng = np.random.default_rng([7, T])
+    nats = rng.uniform(0.0, 12.0, size=T).astype(np.float32)
+    y = rng.integers(-2, V + 2, size=T).astype(np.int32)
+    blen = rng.integers(0, 17, size=V).astype(np.int32)
+    mask = (rng.random(T) < 0.7).astype(np.uint8)
+    bpp = rng.integers(0, 9, size=T).astype(np.int32)
+    print(f"[case] bpb T={T}", flush=True)
+    d = {"target": torch.from_numpy(y).cuda(), "byte_len": torch.from_numpy(blen).cuda()}
+    nats_t = torch.from_numpy(nats).cuda()
+    for m, side in ((None, None), (mask, None), (mask, bpp)):
+        m_t = None if m is None else torch.from_numpy(m).cuda()
+        s_t = None if side is None else torch.from_numpy(side).cuda()
+        out = gpu_bpb(nats_t, d, V, m_t, s_t)
+        sn, sb, n, b = ora.bpb(nats.astype(np.float64), y, blen, m, side, V=V)
+        assert out[1] == sb and out[2] == n
+        assert out[0] == pytest.approx(sn, rel=1e-12)
+        assert out[3] == pytest.approx(b, rel=1e-12)
+
+
 def test_bitwise_reproducible():
     inp = synth.make_inputs("fwd_v1024", 0)
     d = abi.to_device(inp)
