@@ -120,6 +120,38 @@ def test_training_full_size_sampled():
     assert abs(a - b) <= 1e-2 * abs(b), (a, b)
 
 
+def test_dz_beyond_2_31_elements():
+    """T = 300,007 rows at V = 8192: dZ holds 2.46e9 elements (4.9 GB), so its block offsets and
+    the GEMMs' reads of it pass 2^31. D = 32 keeps the oracle's full forward cheap. Sampled dH and
+    dE rows against the oracle, plus <dH, H> = <dE, E> over everything."""
+    from tests.gpu_helpers import oracle_forward_chunked
+    inp = synth.make_inputs(workload("train_v8192", T=300007, D=32, stream=60, hidden_scale=8.0), 0)
+    T, D, V, c = inp["T"], inp["D"], inp["V"], inp["softcap"]
+    print(f"[case] bwd T={T} D={D} V={V}", flush=True)
+    g = 1.0 / T
+    d = abi.to_device(inp)
+    nats = torch.empty(T, device="cuda")
+    lse = torch.empty(T, device="cuda")
+    abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, c, nats, lse)
+    dH = torch.empty((T, D), device="cuda")
+    dE = torch.empty((V, D), device="cuda")
+    abi.pg_lmhead_ce_bwd(d["hidden"], d["embed"], d["target"], None, lse, c, g, dH, dE)
+    torch.cuda.synchronize()
+    dH, dE = dH.cpu().numpy().astype(np.float64), dE.cpu().numpy().astype(np.float64)
+    H, E = host_inputs(inp)
+    y = inp["target"]
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([rng.choice(T, 256, replace=False), [0, 262143, 262144, T - 1]]))
+    odH, _ = ora.backward(H[rows], E, y[rows], c, g)
+    assert rel_l2(dH[rows], odH) <= GRAD_RL2, rel_l2(dH[rows], odH)
+    _, olse = oracle_forward_chunked(H, E, y, c)
+    vrows = np.unique(np.concatenate([[0, 1, 2, 100, V - 1], rng.choice(V, 59, replace=False)]))
+    odE = ora.embed_grad_rows(H, E, y, c, g, olse, vrows)
+    assert rel_l2(dE[vrows], odE) <= GRAD_RL2, rel_l2(dE[vrows], odE)
+    a, b = np.sum(dH * H), np.sum(dE * E)
+    assert abs(a - b) <= 1e-2 * abs(b), (a, b)
+
+
 @pytest.mark.parametrize("caps", [(30.0, 10.0), (10.0, 30.0), (30.0, 0.0), (0.0, 20.0)])
 def test_asymmetric_caps(caps):
     """Gradients with separate caps for z >= 0 and z < 0; logits reach both caps' curvature."""
