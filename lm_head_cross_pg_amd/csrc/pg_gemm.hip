@@ -39,7 +39,7 @@ __device__ __forceinline__ int a_swz(int c) { return c ^ ((c >> 4) & 1) ^ (((c >
 
 // Tile shape: each wave accumulates WM x WN blocks of 32 x 32; the 8 waves form a WGM x (8 / WGM)
 // grid, so the workgroup tile is BM x BN = (32 WM WGM) x (32 WN (8 / WGM)).
-template <bool A_TRANS, int WM, int WN, int WGM, int NS>
+template <int WM, int WN, int WGM>
 struct GemmShape {
   static constexpr int NW = 8, WGN = NW / WGM;
   static constexpr int BM = 32 * WM * WGM, BN = 32 * WN * WGN, BK = kGemmBK;
@@ -48,7 +48,7 @@ struct GemmShape {
 template <bool A_TRANS, int WM, int WN, int WGM, int NS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_kernel(GemmParams g) {
-  using S = GemmShape<A_TRANS, WM, WN, WGM, NS>;
+  using S = GemmShape<WM, WN, WGM>;
   constexpr int BM = S::BM, BN = S::BN, BK = S::BK, NW = S::NW;
   constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;
   constexpr int A_LOADS = ABYTES / 1024, B_LOADS = BBYTES / 1024;   // 1 KiB load instructions
@@ -89,7 +89,7 @@ void gemm_bf16_kernel(GemmParams g) {
   // ---- the load group of stage kc: this wave's B loads of stage kc (i < BPW: load wave + NW i,
   //      rows RPL (wave + NW i) ..), then its A loads of stage kc + 1 (i >= BPW: load
   //      wave + NW (i - BPW), half of an A block). load_one(kc, i) issues the i-th, so that a group
-  //      can be spread over the MFMAs of the stage two before it.
+  //      can be spread over the MFMAs of stage kc - (NS - 1).
   auto load_one = [&](int64_t kc, int i) {
     const int64_t rel = kc - kc_begin;
     if (i >= BPW) {
@@ -188,7 +188,7 @@ void gemm_bf16_kernel(GemmParams g) {
     return read_tr(sB, BN * 2, ks, wn * (32 * WN) + bn * 32, !A_TRANS);
   };
 
-  // A loads of stage 0, then the groups of stages 0 and 1; every stage's group is issued (with
+  // A loads of stage 0, then the groups of stages 0 .. NS - 2; every stage's group is issued (with
   // clamped addresses past the end), so the waits below are constant
   if (nk > 0) {
 #pragma unroll
@@ -197,14 +197,15 @@ void gemm_bf16_kernel(GemmParams g) {
     for (int d = 0; d < NS - 1; ++d) load_stage(kc_begin + d);
   }
   for (int64_t it = 0; it < nk; ++it) {
-    // B(it) and A(it) landed: issued after B(it)'s last load are A(it + 1) and the group of it + 1
+    // B(it) and A(it) landed: issued after B(it)'s last load are A(it + 1) and the groups of
+    // it + 1 .. it + NS - 2
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APW + (NS - 2) * LPW) : "memory");
     __builtin_amdgcn_s_barrier();
     const char* sA = smem + NS * BBYTES + (int)(it % AST) * ABYTES;
     const char* sB = smem + (int)(it % NS) * BBYTES;
     // The MFMAs of this stage, one 16-deep step at a time and one B block at a time (the next B
     // fragment is read while the WM MFMAs of the current one run), with the loads of the group of
-    // it + 2 (into the slots that stage it - 1 used) issued between them. Wave priority drops from 3
+    // it + NS - 1 (into the slots that stage it - 1 used) issued between them. Wave priority drops from 3
     // to 1 halfway through the stage: the two waves of a SIMD share one matrix pipe, and at equal
     // priority the older one would run ahead and leave the other to finish the stage alone.
     constexpr int NMFMA = (BK / 16) * WM * WN;
@@ -265,8 +266,8 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* part, int 
 
 
 // dH: 256 x 256 tiles, 4-slot B ring; dE: 256 x 256 tiles, 3-slot B ring (measured best for each).
-using DhShape = GemmShape<false, 4, 2, 2, 4>;
-using DeShape = GemmShape<true, 4, 2, 2, 3>;
+using DhShape = GemmShape<4, 2, 2>;
+using DeShape = GemmShape<4, 2, 2>;
 int gemm_tile_m(bool a_trans) { return a_trans ? DeShape::BM : DhShape::BM; }
 int gemm_tile_n(bool a_trans) { return a_trans ? DeShape::BN : DhShape::BN; }
 
