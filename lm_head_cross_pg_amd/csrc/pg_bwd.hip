@@ -197,9 +197,10 @@ struct DzCore {
 
   // MFMA chain of (buf, vb) with NST-stage per-logit work on the pending full block `prev`, software
   // pipelined by hand: k-step k issues the LDS read of a later step, the MFMA of step k and stage s
-  // of element group k - s (stage(s, e, z) for the logits z = prev[e / 16][e % 16] of the group), so
-  // that the dependent operations of one logit sit an MFMA step apart and independent logits fill
-  // the gaps. With LOAD the chain also issues this wave's pieces of the load of embedding tile
+  // of the element group that started s steps earlier (stage(s, e, z) for the logits
+  // z = prev[e / 16][e % 16] of the group; group starts spread over every step that lets a group
+  // finish within the chain), so that the dependent operations of one logit sit an MFMA step apart
+  // and independent logits fill the gaps. With LOAD the chain also issues this wave's pieces of the load of embedding tile
   // load_tile into LDS buffer load_buf, spread over its steps (a burst of them would stall the
   // MFMAs). Wave priority is staged over the tile by tile_step_priority.
   static constexpr int kNST = 9;   // epilogue stages
@@ -215,7 +216,8 @@ struct DzCore {
     constexpr int EPC0 = (NE + SPAN - 1) / SPAN;
     constexpr int EPC = EPC0 <= 1 ? 1 : EPC0 <= 2 ? 2 : EPC0 <= 4 ? 4 : EPC0 <= 8 ? 8 : 16;
     constexpr int NG = (NE + EPC - 1) / EPC;
-    constexpr int NSTEP = (NG + NST - 1) > KS ? (NG + NST - 1) : KS;
+    constexpr int SPAN_G = KS - NST + 1 > NG ? KS - NST + 1 : NG;   // steps on which a group can start
+    constexpr int NSTEP = (SPAN_G + NST - 1) > KS ? (SPAN_G + NST - 1) : KS;
     constexpr int PF = 4 < KS ? 4 : KS;
     const int row = vb * 32 + col;
     const lds_char* rbase = lds + buf * TL::TILEB + row * TL::PITCH;
@@ -236,8 +238,12 @@ struct DzCore {
       if (k < KS) mfma_step<NB, KS>(a, fr[k], hf, k);
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
-        const int g = k - st;
-        if (g < 0 || g >= NG) continue;
+        // group g starts at step (g SPAN_G) / NG: the starts spread over every step that still lets
+        // its last stage finish within the chain, one group per step at most
+        const int s0 = k - st;
+        if (s0 < 0 || s0 >= SPAN_G) continue;
+        const int g = (s0 * NG + SPAN_G - 1) / SPAN_G;
+        if (g >= NG || (g * SPAN_G) / NG != s0) continue;
 #pragma unroll
         for (int e = g * EPC; e < (g + 1) * EPC && e < NE; ++e) stage(st, e, prev[e / 16][e % 16]);
       }
