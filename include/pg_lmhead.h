@@ -57,7 +57,7 @@ enum {
 };
 
 enum { PG_DTYPE_BF16 = 0, PG_DTYPE_F32 = 1 }; /* dtype of H and E (they share one) */
-enum { PG_OP_FWD = 0, PG_OP_BWD = 1, PG_OP_BPB = 2, PG_OP_FWD_Q8 = 3 };
+enum { PG_OP_FWD = 0, PG_OP_BWD = 1, PG_OP_BPB = 2, PG_OP_FWD_Q8 = 3, PG_OP_FWD_BWD = 4 };
 
 /* Largest supported sizes: T rows up to 2^31 - 1 (each row index fits an int32), V and D up to
  * 2^20. bf16 with D in {32, 64, 128, 256, 512} runs the MFMA kernels; any other D, and f32 inputs,
@@ -97,6 +97,25 @@ pg_status pg_lmhead_ce_bwd(const void* hidden, const void* embed, int32_t dtype,
                            int64_t T, int32_t D, int32_t V, float softcap, float grad_scale,
                            float* dhidden, float* dembed,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forward and backward in one call: the outputs of pg_lmhead_ce_fwd (nats, lse) and of
+ * pg_lmhead_ce_bwd (dhidden, dembed) for the same arguments, the training step of the head
+ * (repo-explainer, baseline listing: loss = criterion(logits, y), then loss.backward()). For bf16
+ * with D in {32, 64, 128, 256, 512} and 0 < softcap <= 40 the logits are computed once: the forward
+ * also stores the gradient of every logit with the fixed shift of its log-sum-exp in place of the
+ * not yet known lse, and the row factor that corrects it is applied when lse is known (in the dH
+ * product, and to the hidden rows that feed dE, rounded to bf16 there). Any other input runs
+ * pg_lmhead_ce_fwd then pg_lmhead_ce_bwd. Results agree with those two calls up to rounding.
+ *   lse         [T] f32 out, required here
+ *   workspace   at least pg_workspace_bytes(PG_OP_FWD_BWD, T, D, V) bytes
+ * Other arguments and errors as for the two calls.
+ */
+pg_status pg_lmhead_ce_fwd_bwd(const void* hidden, const void* embed, int32_t dtype,
+                               const int32_t* target, const uint8_t* score_mask,
+                               int64_t T, int32_t D, int32_t V, float softcap, float grad_scale,
+                               float* nats, float* lse, float* dhidden, float* dembed,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Asymmetric softcap variants: s = cap_pos * tanh(z / cap_pos) for z >= 0 and

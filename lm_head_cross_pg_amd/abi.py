@@ -20,12 +20,12 @@ LIB_PATH = os.path.join(HERE, "libpg_lmhead.so")
 PG_OK = 0
 PG_DTYPE_BF16 = 0
 PG_DTYPE_F32 = 1
-PG_OP_FWD, PG_OP_BWD, PG_OP_BPB, PG_OP_FWD_Q8 = 0, 1, 2, 3
+PG_OP_FWD, PG_OP_BWD, PG_OP_BPB, PG_OP_FWD_Q8, PG_OP_FWD_BWD = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "PG_OK", -1: "PG_ERR_NULL", -2: "PG_ERR_SHAPE", -3: "PG_ERR_DTYPE", -4: "PG_ERR_SOFTCAP",
                 -5: "PG_ERR_WORKSPACE", -6: "PG_ERR_ALIGN", -7: "PG_ERR_DEVICE", -8: "PG_ERR_HIP"}
 
 # every symbol the header declares
-EXPORTS = ("pg_lmhead_ce_fwd", "pg_lmhead_ce_bwd", "pg_lmhead_ce_fwd_asym", "pg_lmhead_ce_bwd_asym",
+EXPORTS = ("pg_lmhead_ce_fwd", "pg_lmhead_ce_bwd", "pg_lmhead_ce_fwd_bwd", "pg_lmhead_ce_fwd_asym", "pg_lmhead_ce_bwd_asym",
            "pg_quantize_q8", "pg_lmhead_ce_fwd_q8", "pg_bpb_reduce", "pg_workspace_bytes", "pg_status_str",
            "pg_abi_version")
 
@@ -52,6 +52,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pg_lmhead_ce_fwd.restype = i32
     lib.pg_lmhead_ce_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i32, i32, f32, f32, vp, vp, vp, sz, vp]
     lib.pg_lmhead_ce_bwd.restype = i32
+    lib.pg_lmhead_ce_fwd_bwd.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, f32, f32, vp, vp, vp, vp, vp, sz, vp]
+    lib.pg_lmhead_ce_fwd_bwd.restype = i32
     lib.pg_lmhead_ce_fwd_asym.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, f32, f32, vp, vp, vp, sz, vp]
     lib.pg_lmhead_ce_fwd_asym.restype = i32
     lib.pg_lmhead_ce_bwd_asym.argtypes = [vp, vp, i32, vp, vp, vp, i64, i32, i32, f32, f32, f32, vp, vp, vp, sz, vp]
@@ -143,6 +145,19 @@ def pg_lmhead_ce_bwd(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Te
                                  _ptr(lse), T, D, V, float(softcap), float(grad_scale), _ptr(dhidden),
                                  _ptr(dembed), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "pg_lmhead_ce_bwd")
+
+
+def pg_lmhead_ce_fwd_bwd(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Tensor,
+                         score_mask: Optional[torch.Tensor], softcap: float, grad_scale: float,
+                         nats: torch.Tensor, lse: torch.Tensor, dhidden: torch.Tensor, dembed: torch.Tensor,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    T, D = hidden.shape
+    V = embed.shape[0]
+    ws = _workspace(PG_OP_FWD_BWD, T, D, V, embed, workspace)
+    st = load().pg_lmhead_ce_fwd_bwd(_ptr(hidden), _ptr(embed), _dtype_code(hidden), _ptr(target), _ptr(score_mask),
+                                     T, D, V, float(softcap), float(grad_scale), _ptr(nats), _ptr(lse),
+                                     _ptr(dhidden), _ptr(dembed), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "pg_lmhead_ce_fwd_bwd")
 
 
 def pg_lmhead_ce_fwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Tensor,

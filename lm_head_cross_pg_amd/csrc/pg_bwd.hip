@@ -375,6 +375,61 @@ void bwd_dz_kernel(DzParams p) {
   if (vprev >= 0) core.template store_exact<false>(accp, vprev);
 }
 
+// The step from the forward's unnormalised dZ to what the two GEMMs read, one wave per compacted
+// row i. The forward stored d = 2^t t (t - K) for every logit (t = s log2 e - M), and g dZ of a
+// non-target element is f d with the row's factor f = g 2^(M - lse log2 e) (-1 / M^2). This kernel
+// writes f (the dH product scales its output rows by it), the hidden row times f in bf16 (the B
+// operand of dE, whose sum runs over rows), and the target element as (p_y - 1) slope_y / (f / g),
+// from the row's nats and lse (p_y = e^-nats; s_y log2 e = (lse - nats) log2 e). Rows from the last
+// scored row to the end of its 256-row tile are cleared: the forward wrote them from duplicated
+// hidden rows, and the dE sum runs over them.
+__global__ __launch_bounds__(256) void train_prep_kernel(const uint16_t* H, const int32_t* target, const float* nats,
+                                                         const float* lse, const int32_t* rows, const int32_t* n_dev,
+                                                         int64_t n_host, int D, int V, int64_t nvb, Softcap sc,
+                                                         float g, uint16_t* dz, uint16_t* hs, float* row_scale) {
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t n = n_dev ? (int64_t)(*n_dev) : n_host;
+  const int64_t npad = (n + kRowsPerWG - 1) / kRowsPerWG * kRowsPerWG;
+  if (i >= npad) return;
+  uint16_t* zblk = dz + (i >> 5) * nvb * 1024;   // vocabulary block 0 of the row's token block
+  const int l0 = (int)(i & 31);                  // the row's two 16-element runs: lanes l0, l0 + 32
+  if (i >= n) {
+    bf16x8 zero;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zero[e] = (__bf16)0.f;
+    for (int64_t bv = lane; bv < nvb; bv += 64) {
+      bf16x8* a = reinterpret_cast<bf16x8*>(zblk + bv * 1024 + 16 * l0);
+      bf16x8* b = reinterpret_cast<bf16x8*>(zblk + bv * 1024 + 16 * (l0 + 32));
+      a[0] = zero; a[1] = zero; b[0] = zero; b[1] = zero;
+    }
+    return;
+  }
+  const int64_t r = rows ? (int64_t)rows[i] : i;
+  const float lse2 = lse[r] * kLog2e;
+  const float f = g * fexp2(sc.M - lse2) * (-sc.invM * sc.invM);
+  if (lane == 0) row_scale[i] = f;
+  for (int d0 = lane * 8; d0 < D; d0 += 512) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(H + r * D + d0);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)(f * (float)x[e]);
+    *reinterpret_cast<bf16x8*>(hs + i * D + d0) = o;
+  }
+  if (lane == 0) {
+    const int y = target[r];
+    if (y >= 0 && y < V) {
+      const float nl2 = nats[r] * kLog2e;
+      const float w = (lse2 - nl2) * sc.invM;                    // s_y / c
+      const float val = (fexp2(-nl2) - 1.f) * (1.f - w * w);     // (p_y - 1) slope_y
+      const float stored = val * (-sc.M * sc.M) * fexp2(lse2 - sc.M);
+      const int L = l0 + 32 * ((y >> 2) & 1);
+      zblk[(int64_t)(y >> 5) * 1024 + 16 * L + 4 * ((y & 31) >> 3) + (y & 3)] =
+          __builtin_bit_cast(uint16_t, (__bf16)stored);
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------ host side
 
 constexpr int kDeSplit = 4;
@@ -520,6 +575,80 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     hipLaunchKernelGGL(de_generic_kernel<float>, dim3(eblocks), dim3(256), 0, st, dz, (const float*)H,
                        rows, n_dev, T, D, V, grad_scale, dE);
   return hipGetLastError();
+}
+
+TrainWorkspace train_workspace(int64_t T, int32_t D, int32_t V) {
+  TrainWorkspace W;
+  size_t o = 0;
+  W.fwd = o; o += align256(fwd_workspace(T, D, V).total);
+  W.bwd = o; o += align256(bwd_workspace(T, D, V).total);
+  W.row_scale = o; o += align256((size_t)T * 4);
+  W.total = o;
+  return W;
+}
+
+hipError_t launch_train(const void* H, const void* E, int32_t dtype, const int32_t* target,
+                        const uint8_t* mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
+                        float grad_scale, float* nats, float* lse, float* dH, float* dE, char* ws,
+                        const DeviceInfo& dev, hipStream_t st) {
+  const TrainWorkspace W = train_workspace(T, D, V);
+  const bool fused = T > 0 && fwd_writes_dz(dtype, D, cap_pos, cap_neg);
+  const BwdWorkspace L = bwd_workspace(T, D, V);
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + W.bwd + L.dz);
+  hipError_t e = launch_fwd(H, E, dtype, target, mask, T, D, V, cap_pos, cap_neg, nats, lse, ws + W.fwd, dev, st,
+                            fused ? dz : nullptr);
+  if (e != hipSuccess) return e;
+  if (!fused)
+    return launch_bwd(H, E, dtype, target, mask, lse, T, D, V, cap_pos, cap_neg, grad_scale, dH, dE, ws + W.bwd,
+                      dev, st);
+
+  const Softcap sc = Softcap::make(cap_pos, cap_neg);
+  const FwdWorkspace F = fwd_workspace(T, D, V);
+  const int32_t* rows = mask ? reinterpret_cast<const int32_t*>(ws + W.fwd + F.rows) : nullptr;
+  const int32_t* n_dev = mask ? reinterpret_cast<const int32_t*>(ws + W.fwd + F.n_rows) : nullptr;
+  if (mask) {
+    const int64_t tot = T * D;
+    hipLaunchKernelGGL(zero_unscored_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, mask, T, D, dH);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t ldz = (int64_t)((V + kVocabTile - 1) / kVocabTile) * kVocabTile;
+  const int64_t rblk = (T + kRowsPerWG - 1) / kRowsPerWG;
+  uint16_t* hs = reinterpret_cast<uint16_t*>(ws + W.bwd + L.hc);
+  float* row_scale = reinterpret_cast<float*>(ws + W.row_scale);
+  hipLaunchKernelGGL(train_prep_kernel, dim3((unsigned)(rblk * kRowsPerWG / 4)), dim3(256), 0, st,
+                     (const uint16_t*)H, target, nats, lse, rows, n_dev, T, D, V, ldz / 32, sc, grad_scale, dz, hs,
+                     row_scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  // dH = f dZ' E, row by row
+  GemmParams a{};
+  a.A = dz; a.lda = ldz / 32;
+  a.a_mblocks = rblk * (kRowsPerWG / 32);
+  a.B = (const uint16_t*)E; a.ldb = D;
+  a.n_dev = n_dev; a.m_dev = n_dev != nullptr; a.k_dev = 0;
+  a.M = T; a.N = D; a.K = V; a.kvalid = V;
+  a.alpha = 1.f;
+  a.C = dH; a.ldc = D; a.crows = rows; a.split_stride = 0; a.row_scale = row_scale;
+  if ((e = launch_gemm(a, false, 1, st)) != hipSuccess) return e;
+
+  // dE = dZ'^T (f H): the row factors sit in the scaled hidden rows
+  const int64_t tiles = ((int64_t)(V + gemm_tile_m(true) - 1) / gemm_tile_m(true)) *
+                        ((D + gemm_tile_n(true) - 1) / gemm_tile_n(true));
+  const int ncu = dev.cu_count > 0 ? dev.cu_count : 256;
+  int64_t ks = ncu / (tiles > 0 ? tiles : 1);
+  ks = ks < 1 ? 1 : (ks > kDeSplit ? kDeSplit : ks);
+  float* part = reinterpret_cast<float*>(ws + W.bwd + L.de_part);
+  GemmParams b{};
+  b.A = dz; b.lda = ldz / 32;
+  b.a_mblocks = b.lda;
+  b.k_blocks = rblk * (kRowsPerWG / 32);
+  b.B = hs; b.ldb = D;
+  b.n_dev = n_dev; b.m_dev = 0; b.k_dev = n_dev != nullptr;
+  b.M = V; b.N = D; b.K = T; b.kvalid = T;
+  b.alpha = 1.f;
+  b.C = ks > 1 ? part : dE; b.ldc = D; b.crows = nullptr; b.split_stride = (int64_t)V * D;
+  if ((e = launch_gemm(b, true, (int)ks, st)) != hipSuccess || ks == 1) return e;
+  return launch_sum_splits(part, (int)ks, (int64_t)V * D, (int64_t)V * D, dE, st);
 }
 
 }  // namespace pg

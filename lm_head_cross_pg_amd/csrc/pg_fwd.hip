@@ -44,6 +44,8 @@ struct FwdParams {
   float* part_l;
   float* part_m;
   float* s_target;
+  uint16_t* dz;           // unnormalised dZ blocks (the kernels that write them), else unused
+  int64_t ldz;            // vocabulary rows of dz (V rounded up to the tile)
 };
 
 __device__ __forceinline__ int device_splits(int64_t n, int n_vtiles, int grid) {
@@ -64,8 +66,15 @@ constexpr int kFwdTokBlocks = PG_FWD_TOK_BLOCKS;
 
 // ASYM: separate caps for z >= 0 and z < 0 (the epilogue takes the exact form only); a template
 // parameter so that it compiles to a kernel of its own.
-template <int D, bool FIXED, int NB, bool ASYM>
+// DZ (fixed shift, one cap): the epilogue also stores, for every logit, the unnormalised gradient
+//   d = 2^t t (t - K),  t = s log2 e - M  (the exponent it sums),  K = -2 M,
+// in the dZ block layout. Since s / c = 1 + t / M, the softcap's slope is 1 - (s / c)^2 =
+// -t (t - K) / M^2, so the normalised dZ of a row is d 2^(M - lse log2 e) (-1 / M^2) - [v = y] slope,
+// a per-row factor applied after this kernel, where lse is known (the target element is rewritten
+// then as well).
+template <int D, bool FIXED, int NB, bool ASYM, bool DZ = false>
 struct FwdCore {
+  static_assert(!DZ || (FIXED && !ASYM), "unnormalised dZ needs the fixed shift and one cap");
   static constexpr int KS = D / 16;
   static constexpr int kWaves = WaveShape<NB>::kWaves;
   static constexpr int kLoads = embed_loads_per_wave<D, kWaves>();
@@ -79,6 +88,31 @@ struct FwdCore {
   float lsum[NB];
   float mrun[NB];
   int exact_left;   // blocks still to take the exact form before the series is tried again (uniform)
+  uint16_t* dzblk[NB];   // DZ: this lane's 16 elements of block (its token block, vocabulary block 0)
+
+  // DZ: eight values of this lane (accumulator registers 8 j8 .. 8 j8 + 7 of the block whose
+  // vocabulary rows start at vbase) as one 16-byte store into the block layout.
+  __device__ __forceinline__ void store8(const float* vals, int vbase, int tb, int j8) const {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)vals[e];
+    *reinterpret_cast<bf16x8*>(dzblk[tb] + (int64_t)(vbase >> 5) * 1024 + 8 * j8) = o;
+  }
+
+  // DZ, not pipelined: the exact exponent t of each logit, d = 2^t t (t - K); MASKED stores 0 for
+  // rows >= V.
+  template <bool MASKED>
+  __device__ __forceinline__ void dz_exact(const f32x16& acc, int vbase, int tb) const {
+    float d[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float t = capped_shifted_sc(acc[r], sc);
+      d[r] = fexp2(t) * (t * (t - sc.K));
+      if (MASKED) d[r] = (vbase + 8 * (r >> 2) + 4 * h + (r & 3)) < V ? d[r] : 0.f;
+    }
+    store8(d, vbase, tb, 0);
+    store8(d + 8, vbase, tb, 1);
+  }
 
   __device__ __forceinline__ void chain(int buf, int vb, f32x16 (&acc)[NB]) const {
     logit_blocks<D, NB>(lds, buf, vb, h, col, hf, acc);
@@ -143,6 +177,7 @@ struct FwdCore {
     for (int tb = 0; tb < NB; ++tb) {
       if (FIXED) lsum[tb] += part_exact<MASKED>(acc[tb], vbase);
       else online<MASKED>(acc[tb], vbase, tb);
+      if (DZ) dz_exact<MASKED>(acc[tb], vbase, tb);
     }
   }
 
@@ -228,16 +263,28 @@ struct FwdCore {
     }
     float part[NB] = {};
     float q[NE];
+    float w[DZ ? NE : 1];   // DZ: t (t - K), then the stored value
+    // DZ adds a stage: 4 also forms t (t - K), 5 multiplies it by 2^t, 6 stores eight at a time
+    constexpr int NST = DZ ? 7 : 6;
     if (ASYM || exact_left > 0) {
-      pipelined<LOAD, 6>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
+      pipelined<LOAD, NST>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
         const bool neg = ASYM && z < 0.f;
         switch (st) {
           case 0: q[e] = z * (neg ? sc.alpha_n : sc.alpha); break;
           case 1: q[e] = fexp2(q[e]); break;
           case 2: { const float ik = neg ? sc.invK_n : sc.invK; q[e] = __builtin_fmaf(q[e], ik, ik); break; }
           case 3: q[e] = frcp(q[e]); break;                                  // K r = (s - c) log2 e
-          case 4: q[e] = fexp2(ASYM ? q[e] + (neg ? sc.M_n - sc.M : 0.f) : q[e]); break;
-          default: part[e / 16] += q[e]; break;
+          case 4:
+            if (DZ) w[e] = q[e] * (q[e] - sc.K);
+            q[e] = fexp2(ASYM ? q[e] + (neg ? sc.M_n - sc.M : 0.f) : q[e]);
+            break;
+          case 5:
+            part[e / 16] += q[e];
+            if (DZ) w[e] = w[e] * q[e];
+            break;
+          default:
+            if (DZ && (e & 7) == 7) store8(&w[e - 7], vprev, e / 16, (e & 15) >> 3);
+            break;
         }
       });
 #pragma unroll
@@ -247,21 +294,33 @@ struct FwdCore {
     }
     float u[NE];
     float amax = 0.f;
-    pipelined<LOAD, 6>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
+    pipelined<LOAD, NST>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
       switch (st) {
         case 0: u[e] = z * z; amax = fmaxf(amax, fabsf(z)); break;
         case 1: q[e] = __builtin_fmaf(sc.q2, u[e], sc.q1); break;
         case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
         case 3: q[e] = __builtin_fmaf(z, q[e], -sc.M); break;
-        case 4: q[e] = fexp2(q[e]); break;
-        default: part[e / 16] += q[e]; break;
+        case 4:
+          if (DZ) w[e] = q[e] * (q[e] - sc.K);
+          q[e] = fexp2(q[e]);
+          break;
+        case 5:
+          part[e / 16] += q[e];
+          if (DZ) w[e] = w[e] * q[e];
+          break;
+        default:
+          if (DZ && (e & 7) == 7) store8(&w[e - 7], vprev, e / 16, (e & 15) >> 3);
+          break;
       }
     });
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) asm volatile("" ::"v"(part[tb]));   // keep the speculation in the pipeline
-    if (!__all(amax <= sc.thr)) {
+    if (!__all(amax <= sc.thr)) {   // the exact sums replace the series; DZ stores again
 #pragma unroll
-      for (int tb = 0; tb < NB; ++tb) part[tb] = part_exact<false>(prev[tb], vprev);
+      for (int tb = 0; tb < NB; ++tb) {
+        part[tb] = part_exact<false>(prev[tb], vprev);
+        if (DZ) dz_exact<false>(prev[tb], vprev, tb);
+      }
       exact_left = kExactRun;
     }
 #pragma unroll
@@ -276,7 +335,7 @@ __device__ __forceinline__ bf16x2 bf16_pair(const bf16x8& v, int j) {
   return r;
 }
 
-template <int D, bool FIXED, int NB, bool ASYM>
+template <int D, bool FIXED, int NB, bool ASYM, bool DZ = false>
 __global__ __launch_bounds__(WaveShape<NB>::kThreads) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
 void fwd_mfma_kernel(FwdParams p) {
   using TL = TileLayout<D>;
@@ -300,7 +359,7 @@ void fwd_mfma_kernel(FwdParams p) {
   const int V = p.V;
   const int64_t tok0 = (int64_t)rt * kRowsPerWG + wave * kTokPerWave;   // first token of this wave
 
-  FwdCore<D, FIXED, NB, ASYM> core;
+  FwdCore<D, FIXED, NB, ASYM, DZ> core;
   core.lds = (const lds_char*)smem;
   core.smem = smem;
   core.E = p.E;
@@ -328,6 +387,7 @@ void fwd_mfma_kernel(FwdParams p) {
     const bf16x8* src = reinterpret_cast<const bf16x8*>(p.H + grow[tb] * D + h * (D / 2));
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) core.hf[tb][ks] = src[ks];
+    if (DZ) core.dzblk[tb] = p.dz + (tok[tb] >> 5) * (p.ldz >> 5) * 1024 + lane * 16;
   }
 
   // ---- target logit (split 0 only). Lanes l and l + 32 hold the two halves of the hidden row of
@@ -552,15 +612,17 @@ hipError_t launch_compact_rows(const uint8_t* mask, int64_t T, char* ws, const F
   return hipGetLastError();
 }
 
-template <int D, bool FIXED, bool ASYM>
+template <int D, bool FIXED, bool ASYM, bool DZ = false>
 static void launch_mfma(const FwdParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, FIXED, kFwdTokBlocks, ASYM>), dim3(grid),
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, FIXED, kFwdTokBlocks, ASYM, DZ>), dim3(grid),
                      dim3(WaveShape<kFwdTokBlocks>::kThreads), 0, st, p);
 }
 
 template <int D>
 static void launch_mfma_d(const FwdParams& p, int grid, hipStream_t st) {
-  if (p.sc.asym) {
+  if (p.dz) {   // the caller checked fwd_writes_dz
+    launch_mfma<D, true, false, true>(p, grid, st);
+  } else if (p.sc.asym) {
     if (p.sc.fixed) launch_mfma<D, true, true>(p, grid, st);
     else launch_mfma<D, false, true>(p, grid, st);
   } else {
@@ -569,10 +631,16 @@ static void launch_mfma_d(const FwdParams& p, int grid, hipStream_t st) {
   }
 }
 
+bool fwd_writes_dz(int32_t dtype, int32_t D, float cap_pos, float cap_neg) {
+  const Softcap sc = Softcap::make(cap_pos, cap_neg);
+  return dtype == 0 && mfma_width(D) && sc.fixed && !sc.asym;
+}
+
 hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t* target,
                       const uint8_t* mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
-                      float* nats, float* lse, char* ws, const DeviceInfo& dev, hipStream_t st) {
+                      float* nats, float* lse, char* ws, const DeviceInfo& dev, hipStream_t st, uint16_t* dz) {
   if (T == 0) return hipSuccess;
+  if (dz && !fwd_writes_dz(dtype, D, cap_pos, cap_neg)) return hipErrorInvalidValue;
   const FwdWorkspace L = fwd_workspace(T, D, V);
   const Softcap sc = Softcap::make(cap_pos, cap_neg);
   const int32_t* rows = nullptr;
@@ -610,6 +678,8 @@ hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t
   p.part_l = reinterpret_cast<float*>(ws + L.part_l);
   p.part_m = reinterpret_cast<float*>(ws + L.part_m);
   p.s_target = reinterpret_cast<float*>(ws + L.s_target);
+  p.dz = dz;
+  p.ldz = (int64_t)p.n_vtiles * kVocabTile;
 
   const int64_t rt = (T + kRowsPerWG - 1) / kRowsPerWG;
   const int ncu = dev.cu_count > 0 ? (dev.cu_count < 1024 ? dev.cu_count : 1024) : 256;

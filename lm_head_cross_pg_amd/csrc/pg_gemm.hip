@@ -236,7 +236,8 @@ void gemm_bf16_kernel(GemmParams g) {
   __builtin_amdgcn_s_setprio(0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the clamped loads past the end landed
 
-  // ---- epilogue: alpha * acc to C (row-scattered) or to this split's partial tile
+  // ---- epilogue: alpha (times the row's scale when given) * acc to C (row-scattered) or to this
+  //      split's partial tile
   float* C = g.C + (int64_t)blockIdx.z * g.split_stride;
 #pragma unroll
   for (int bm = 0; bm < WM; ++bm)
@@ -248,7 +249,8 @@ void gemm_bf16_kernel(GemmParams g) {
         const int64_t m = m0 + (wm * WM + bm) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < M && n < g.N) {
           const int64_t crow = g.crows ? (int64_t)g.crows[m] : m;
-          C[crow * g.ldc + n] = g.alpha * acc[bm][bn][r];
+          const float f = g.row_scale ? g.alpha * g.row_scale[m] : g.alpha;
+          C[crow * g.ldc + n] = f * acc[bm][bn][r];
         }
       }
     }

@@ -43,9 +43,28 @@ struct DeviceInfo {
 // cap_neg (equal for the symmetric softcap); 0 = uncapped side.
 hipError_t launch_compact_rows(const uint8_t* mask, int64_t T, char* ws, const FwdWorkspace& L,
                                float* nats, float* lse, hipStream_t st);
+// dz (nullable): when given, the forward also writes the unnormalised dZ blocks (only where
+// fwd_writes_dz holds; rows padded to 256, vocabulary rows to the tile).
 hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t* target,
                       const uint8_t* mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
-                      float* nats, float* lse, char* ws, const DeviceInfo& dev, hipStream_t st);
+                      float* nats, float* lse, char* ws, const DeviceInfo& dev, hipStream_t st,
+                      uint16_t* dz = nullptr);
+// The forward can write the unnormalised dZ: bf16 MFMA widths, one cap in the fixed-shift range.
+bool fwd_writes_dz(int32_t dtype, int32_t D, float cap_pos, float cap_neg);
+
+// Forward + backward in one call (pg_bwd.hip). Where fwd_writes_dz holds, the forward writes the
+// unnormalised dZ and no logit is computed twice; otherwise it is launch_fwd then launch_bwd.
+struct TrainWorkspace {
+  size_t fwd;        // FwdWorkspace
+  size_t bwd;        // BwdWorkspace (dz, scaled compacted hidden rows, dE partials)
+  size_t row_scale;  // f32[T]: per compacted row, g 2^(M - lse log2 e) (-1 / M^2)
+  size_t total;
+};
+TrainWorkspace train_workspace(int64_t T, int32_t D, int32_t V);
+hipError_t launch_train(const void* H, const void* E, int32_t dtype, const int32_t* target,
+                        const uint8_t* mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
+                        float grad_scale, float* nats, float* lse, float* dH, float* dE, char* ws,
+                        const DeviceInfo& dev, hipStream_t st);
 
 // Backward launcher (pg_bwd.hip).
 hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t* target,
@@ -88,6 +107,7 @@ struct GemmParams {
   int64_t ldc;
   const int32_t* crows;   // output row of m when given
   int64_t split_stride;   // elements between the partial outputs of k splits
+  const float* row_scale; // when given: C row m = alpha * row_scale[m] * (A B)[m]
 };
 // a_trans: A's element (m, k) is dZ[k][m] (else dZ[m][k]). k is split over ksplit workgroups per
 // output tile; with several splits, C receives one partial output per split at split_stride.

@@ -77,6 +77,15 @@ def bwd(lib, **kw):
                                 a["D"], a["V"], a["c"], a["g"], a["dh"], a["de"], a["ws"], a["wsb"], a["stream"])
 
 
+def fwd_bwd(lib, **kw):
+    a = dict(hidden=P, embed=P, dtype=0, target=P, mask=None, T=256, D=64, V=512, c=30.0, g=1 / 256,
+             nats=P, lse=P, dh=P, de=P, ws=P, wsb=BIG, stream=None)
+    a.update(kw)
+    return lib.pg_lmhead_ce_fwd_bwd(a["hidden"], a["embed"], a["dtype"], a["target"], a["mask"], a["T"], a["D"],
+                                    a["V"], a["c"], a["g"], a["nats"], a["lse"], a["dh"], a["de"], a["ws"],
+                                    a["wsb"], a["stream"])
+
+
 def fwd_asym(lib, **kw):
     a = dict(hidden=P, embed=P, dtype=0, target=P, mask=None, T=256, D=64, V=512, cp=30.0, cn=10.0,
              nats=P, lse=P, ws=P, wsb=BIG, stream=None)
@@ -115,13 +124,28 @@ def bpb(lib, **kw):
                              a["ws"], a["wsb"], a["stream"])
 
 
-@pytest.mark.parametrize("call", [fwd, bwd, fwd_asym, bwd_asym, fwd_q8, bpb])
+@pytest.mark.parametrize("call", [fwd, bwd, fwd_bwd, fwd_asym, bwd_asym, fwd_q8, bpb])
 def test_validation_codes(lib, call):
     assert call(lib, T=-1) == -2
     assert call(lib, V=0) == -2
     assert call(lib, ws=None) == -1
     assert call(lib, ws=P + 8) == -6
     assert call(lib, wsb=16) == -5
+
+
+def test_fused_training_validation(lib):
+    assert fwd_bwd(lib, lse=None) == -1           # required here (the backward half needs it)
+    assert fwd_bwd(lib, nats=None) == -1
+    assert fwd_bwd(lib, dh=None) == -1
+    assert fwd_bwd(lib, de=None) == -1
+    assert fwd_bwd(lib, dtype=2) == -3
+    assert fwd_bwd(lib, c=-1.0) == -4
+    assert fwd_bwd(lib, g=float("nan")) == -4
+    assert fwd_bwd(lib, dh=P + 4) == -6
+    T, D, V = 65536, 512, 8192
+    need = abi.workspace_bytes(abi.PG_OP_FWD_BWD, T, D, V)
+    assert need >= abi.workspace_bytes(abi.PG_OP_FWD, T, D, V) + abi.workspace_bytes(abi.PG_OP_BWD, T, D, V)
+    assert fwd_bwd(lib, T=T, D=D, V=V, wsb=need - 1) == -5
 
 
 def test_forward_validation(lib):

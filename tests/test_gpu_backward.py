@@ -7,7 +7,7 @@ import torch
 
 from lm_head_cross_pg_amd import abi, synth
 from oracle import oracle as ora
-from tests.gpu_helpers import GRAD_RL2, ensure_lib, host_inputs, rel_l2
+from tests.gpu_helpers import GRAD_RL2, NATS_ATOL, ensure_lib, host_inputs, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -21,21 +21,30 @@ def workload(name, **over):
     return dataclasses.replace(synth.WORKLOADS[name], **over)
 
 
-def run_bwd(inp, softcap=None, mask=None, grad_scale=None):
+def run_bwd(inp, softcap=None, mask=None, grad_scale=None, fused=False):
+    """The backward on the GPU against the oracle; fused: through pg_lmhead_ce_fwd_bwd, whose nats
+    and lse are checked against the oracle's forward as well."""
     T, D, V = inp["T"], inp["D"], inp["V"]
     c = inp["softcap"] if softcap is None else softcap
     mask = inp["mask"] if mask is None else mask
     n_scored = T if mask is None else int(mask.sum())
     g = (1.0 / max(n_scored, 1)) if grad_scale is None else grad_scale
-    print(f"[case] bwd {inp['workload']} seed={inp['seed']} T={T} D={D} V={V} c={c} masked={mask is not None}",
-          flush=True)
+    print(f"[case] bwd{' fused' if fused else ''} {inp['workload']} seed={inp['seed']} T={T} D={D} V={V} c={c} "
+          f"masked={mask is not None}", flush=True)
     d = abi.to_device(inp)
     mask_t = None if mask is None else torch.from_numpy(mask).cuda()
     nats = torch.empty(T, device="cuda")
     lse = torch.empty(T, device="cuda")
     dH = torch.full((T, D), float("nan"), device="cuda")
     dE = torch.full((V, D), float("nan"), device="cuda")
-    if isinstance(c, tuple):
+    if fused:
+        abi.pg_lmhead_ce_fwd_bwd(d["hidden"], d["embed"], d["target"], mask_t, c, g, nats, lse, dH, dE)
+        torch.cuda.synchronize()
+        H, E = host_inputs(inp)
+        onats, olse = ora.forward(H, E, inp["target"], c, mask)
+        assert np.max(np.abs(nats.cpu().numpy() - onats)) <= NATS_ATOL
+        assert np.max(np.abs(lse.cpu().numpy() - olse)) <= NATS_ATOL
+    elif isinstance(c, tuple):
         abi.pg_lmhead_ce_fwd_asym(d["hidden"], d["embed"], d["target"], mask_t, c[0], c[1], nats, lse)
         abi.pg_lmhead_ce_bwd_asym(d["hidden"], d["embed"], d["target"], mask_t, lse, c[0], c[1], g, dH, dE)
     else:
@@ -90,66 +99,112 @@ def test_masked_full_size():
     run_bwd(synth.make_inputs("masked_stride64", 0))
 
 
-def test_training_full_size_sampled():
-    """T = 65536, D = 512, V = 8192, mean loss (g = 1/T), in the benchmark's launch configuration:
-    sampled dH rows and dE rows against the oracle, plus <dH, H> = <dE, E> over everything."""
+# ------------------------------------------------ forward and backward in one call (pg_lmhead_ce_fwd_bwd)
+
+def test_fused_fd_shapes():
+    run_bwd(synth.make_inputs("fd", 0), fused=True)                                  # f32: two calls
+    run_bwd(synth.make_inputs(workload("fd", dtype="bf16"), 0), fused=True)          # one pass
+
+
+@pytest.mark.parametrize("seed", [0, 42])
+def test_fused_training_shape_small(seed):
+    run_bwd(synth.make_inputs("train_v8192", seed, T=700), fused=True)
+
+
+@pytest.mark.parametrize("D,V", [(32, 4000), (64, 1000), (128, 777), (256, 300), (48, 200), (512, 130)])
+def test_fused_widths(D, V):
+    run_bwd(synth.make_inputs(workload("train_v8192", D=D, V=V, T=520, stream=170 + D), 0), fused=True)
+
+
+@pytest.mark.parametrize("c", [0.0, 5.0, 40.0, 50.0])
+def test_fused_caps(c):
+    """c = 0 and c = 50 (beyond the fixed shift) take the two calls; 5 and 40 the single pass."""
+    run_bwd(synth.make_inputs(workload("train_v8192", V=1500, T=400, stream=180, softcap=c), 1), softcap=c,
+            fused=True)
+
+
+def test_fused_stress_and_large_logits():
+    """|z| up to 5c (every block leaves the series) and hidden x 8 at D = 512 (mixed blocks)."""
+    run_bwd(synth.make_inputs("stress", 0), fused=True)
+    run_bwd(synth.make_inputs(workload("train_v8192", T=1500, stream=181, hidden_scale=8.0), 0), fused=True)
+
+
+@pytest.mark.parametrize("T", [1, 255, 257, 4097])
+def test_fused_ragged_rows(T):
+    run_bwd(synth.make_inputs(workload("train_v8192", V=2048, stream=182), 0, T=T), fused=True)
+
+
+def test_fused_masked():
+    run_bwd(synth.make_inputs("masked_stride64", 0, T=4096), fused=True)
+    run_bwd(synth.make_inputs("masked_stride64", 1), fused=True)
+
+
+def test_fused_grad_scale_zero_and_two():
+    inp = synth.make_inputs("train_v8192", 3, T=300)
+    T, D, V = inp["T"], inp["D"], inp["V"]
+    d = abi.to_device(inp)
+    nats, lse = torch.empty(T, device="cuda"), torch.empty(T, device="cuda")
+    dH = torch.full((T, D), float("nan"), device="cuda")
+    dE = torch.full((V, D), float("nan"), device="cuda")
+    abi.pg_lmhead_ce_fwd_bwd(d["hidden"], d["embed"], d["target"], None, inp["softcap"], 0.0, nats, lse, dH, dE)
+    torch.cuda.synchronize()
+    assert torch.all(dH == 0).item() and torch.all(dE == 0).item()
+    run_bwd(inp, grad_scale=2.0, fused=True)
+
+
+def _full_size_check(inp, rows_extra, seed, label):
+    """Both training entry points on one full-size input: sampled dH rows and dE rows against the
+    oracle (computed once), the <dH, H> = <dE, E> identity, and nats / lse on sampled rows."""
     from tests.gpu_helpers import oracle_forward_chunked
-    inp = synth.make_inputs("train_v8192", 0)
     T, D, V, c = inp["T"], inp["D"], inp["V"], inp["softcap"]
     g = 1.0 / T
     d = abi.to_device(inp)
-    nats = torch.empty(T, device="cuda")
-    lse = torch.empty(T, device="cuda")
-    abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, c, nats, lse)
-    dH = torch.empty((T, D), device="cuda")
-    dE = torch.empty((V, D), device="cuda")
-    abi.pg_lmhead_ce_bwd(d["hidden"], d["embed"], d["target"], None, lse, c, g, dH, dE)
-    torch.cuda.synchronize()
-    dH, dE = dH.cpu().numpy().astype(np.float64), dE.cpu().numpy().astype(np.float64)
     H, E = host_inputs(inp)
     y = inp["target"]
-    rng = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([rng.choice(T, 256, replace=False), [0, 255, 256, T - 1]]))
-    odH, _ = ora.backward(H[rows], E, y[rows], c, g)
-    assert rel_l2(dH[rows], odH) <= GRAD_RL2, rel_l2(dH[rows], odH)
-    _, olse = oracle_forward_chunked(H, E, y, c)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.choice(T, 256, replace=False), rows_extra]))
     vrows = np.unique(np.concatenate([[0, 1, 2, 100, V - 1], rng.choice(V, 59, replace=False)]))
+    onats, olse = oracle_forward_chunked(H, E, y, c)
+    odH, _ = ora.backward(H[rows], E, y[rows], c, g)
     odE = ora.embed_grad_rows(H, E, y, c, g, olse, vrows)
-    assert rel_l2(dE[vrows], odE) <= GRAD_RL2, rel_l2(dE[vrows], odE)
-    a, b = np.sum(dH * H), np.sum(dE * E)
-    assert abs(a - b) <= 1e-2 * abs(b), (a, b)
+    for fused in (False, True):
+        print(f"[case] {label} fused={fused}", flush=True)
+        nats = torch.empty(T, device="cuda")
+        lse = torch.empty(T, device="cuda")
+        dH = torch.empty((T, D), device="cuda")
+        dE = torch.empty((V, D), device="cuda")
+        if fused:
+            abi.pg_lmhead_ce_fwd_bwd(d["hidden"], d["embed"], d["target"], None, c, g, nats, lse, dH, dE)
+        else:
+            abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, c, nats, lse)
+            abi.pg_lmhead_ce_bwd(d["hidden"], d["embed"], d["target"], None, lse, c, g, dH, dE)
+        torch.cuda.synchronize()
+        n, l = nats.cpu().numpy(), lse.cpu().numpy()
+        assert np.max(np.abs(n[rows] - onats[rows])) <= NATS_ATOL
+        assert np.max(np.abs(l[rows] - olse[rows])) <= NATS_ATOL
+        dHn, dEn = dH.cpu().numpy().astype(np.float64), dE.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(dHn)) and np.all(np.isfinite(dEn))
+        assert rel_l2(dHn[rows], odH) <= GRAD_RL2, rel_l2(dHn[rows], odH)
+        assert rel_l2(dEn[vrows], odE) <= GRAD_RL2, rel_l2(dEn[vrows], odE)
+        a, b = np.sum(dHn * H), np.sum(dEn * E)
+        assert abs(a - b) <= 1e-2 * abs(b), (a, b)
+
+
+def test_training_full_size_sampled():
+    """T = 65536, D = 512, V = 8192, mean loss (g = 1/T), in the benchmark's launch configuration,
+    through both training entry points."""
+    inp = synth.make_inputs("train_v8192", 0)
+    T = inp["T"]
+    _full_size_check(inp, [0, 255, 256, T - 1], 11, "train full size")
 
 
 def test_dz_beyond_2_31_elements():
     """T = 300,007 rows at V = 8192: dZ holds 2.46e9 elements (4.9 GB), so its block offsets and
-    the GEMMs' reads of it pass 2^31. D = 32 keeps the oracle's full forward cheap. Sampled dH and
-    dE rows against the oracle, plus <dH, H> = <dE, E> over everything."""
-    from tests.gpu_helpers import oracle_forward_chunked
+    the GEMMs' reads of it pass 2^31. D = 32 keeps the oracle's full forward cheap. Both training
+    entry points."""
     inp = synth.make_inputs(workload("train_v8192", T=300007, D=32, stream=60, hidden_scale=8.0), 0)
-    T, D, V, c = inp["T"], inp["D"], inp["V"], inp["softcap"]
-    print(f"[case] bwd T={T} D={D} V={V}", flush=True)
-    g = 1.0 / T
-    d = abi.to_device(inp)
-    nats = torch.empty(T, device="cuda")
-    lse = torch.empty(T, device="cuda")
-    abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, c, nats, lse)
-    dH = torch.empty((T, D), device="cuda")
-    dE = torch.empty((V, D), device="cuda")
-    abi.pg_lmhead_ce_bwd(d["hidden"], d["embed"], d["target"], None, lse, c, g, dH, dE)
-    torch.cuda.synchronize()
-    dH, dE = dH.cpu().numpy().astype(np.float64), dE.cpu().numpy().astype(np.float64)
-    H, E = host_inputs(inp)
-    y = inp["target"]
-    rng = np.random.default_rng(12)
-    rows = np.unique(np.concatenate([rng.choice(T, 256, replace=False), [0, 262143, 262144, T - 1]]))
-    odH, _ = ora.backward(H[rows], E, y[rows], c, g)
-    assert rel_l2(dH[rows], odH) <= GRAD_RL2, rel_l2(dH[rows], odH)
-    _, olse = oracle_forward_chunked(H, E, y, c)
-    vrows = np.unique(np.concatenate([[0, 1, 2, 100, V - 1], rng.choice(V, 59, replace=False)]))
-    odE = ora.embed_grad_rows(H, E, y, c, g, olse, vrows)
-    assert rel_l2(dE[vrows], odE) <= GRAD_RL2, rel_l2(dE[vrows], odE)
-    a, b = np.sum(dH * H), np.sum(dE * E)
-    assert abs(a - b) <= 1e-2 * abs(b), (a, b)
+    T = inp["T"]
+    _full_size_check(inp, [0, 262143, 262144, T - 1], 12, "dZ beyond 2^31")
 
 
 @pytest.mark.parametrize("caps", [(30.0, 10.0), (10.0, 30.0), (30.0, 0.0), (0.0, 20.0)])
