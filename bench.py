@@ -383,12 +383,17 @@ def main():
             torch.cuda.synchronize()
             return (time.perf_counter() - t0) / ksteps, ksteps
 
-        tw, ksteps = time_train(train_step, td["hidden"])
-        tw2, _ = time_train(train_step_two_calls, td["hidden"])
+        # two interleaved rounds per path and input, the better of each (the clock settles over the
+        # first round of a heavy loop)
         hid8 = td["hidden"] * 8                     # logits of trained-model size, as for the forward
-        tw8, _ = time_train(train_step, hid8)
-        tw82, _ = time_train(train_step_two_calls, hid8)
+        best = {}
+        for _ in range(2):
+            for key, step, hid in (("one", train_step, td["hidden"]), ("two", train_step_two_calls, td["hidden"]),
+                                   ("one8", train_step, hid8), ("two8", train_step_two_calls, hid8)):
+                t, ksteps = time_train(step, hid)
+                best[key] = min(best.get(key, t), t)
         del hid8
+        tw, tw2, tw8, tw82 = best["one"], best["two"], best["one8"], best["two8"]
         result["train_step"] = {
             "workload": "train_v8192: T=65536, D=512, V=8192, bf16 in, fp32 dH/dE, mean CE (g=1/T)",
             "entry": "pg_lmhead_ce_fwd_bwd",

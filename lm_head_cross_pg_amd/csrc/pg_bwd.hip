@@ -378,9 +378,9 @@ void bwd_dz_kernel(DzParams p) {
 // The step from the forward's unnormalised dZ to what the two GEMMs read, one wave per compacted
 // row i. The forward stored d = 2^t t (t - K) for every logit (t = s log2 e - M), and g dZ of a
 // non-target element is f d with the row's factor f = g 2^(M - lse log2 e) (-1 / M^2). This kernel
-// writes f (the dH product scales its output rows by it), the hidden row times f in bf16 (the B
-// operand of dE, whose sum runs over rows), and the target element as (p_y - 1) slope_y / (f / g),
-// from the row's nats and lse (p_y = e^-nats; s_y log2 e = (lse - nats) log2 e). Rows from the last
+// writes the target element as (p_y - 1) slope_y / (f / g), from the row's nats and lse
+// (p_y = e^-nats; s_y log2 e = (lse - nats) log2 e), then f (the dH product scales its output rows
+// by it) and the hidden row times f in bf16 (the B operand of dE, whose sum runs over rows). Rows from the last
 // scored row to the end of its 256-row tile are cleared: the forward wrote them from duplicated
 // hidden rows, and the dE sum runs over them.
 __global__ __launch_bounds__(256) void train_prep_kernel(const uint16_t* H, const int32_t* target, const float* nats,
@@ -407,7 +407,23 @@ __global__ __launch_bounds__(256) void train_prep_kernel(const uint16_t* H, cons
   }
   const int64_t r = rows ? (int64_t)rows[i] : i;
   const float lse2 = lse[r] * kLog2e;
-  const float f = g * fexp2(sc.M - lse2) * (-sc.invM * sc.invM);
+  float f = g * fexp2(sc.M - lse2) * (-sc.invM * sc.invM);
+  // The target element: (p_y - 1) slope_y / (f / g), rounded to bf16. It outweighs the rest of the
+  // row about V / sqrt(V) times in dH, so the row factor is then taken from the rounded value
+  // (f = g val / stored): the target term becomes exact, and the other elements of the row move by
+  // the same relative amount, at most 2^-9.
+  const int y = target[r];
+  if (y >= 0 && y < V) {
+    const float nl2 = nats[r] * kLog2e;
+    const float w = (lse2 - nl2) * sc.invM;                      // s_y / c
+    const float val = (fexp2(-nl2) - 1.f) * (1.f - w * w);       // (p_y - 1) slope_y
+    const __bf16 stored = (__bf16)(val * (-sc.M * sc.M) * fexp2(lse2 - sc.M));
+    if ((float)stored != 0.f) f = g * val / (float)stored;
+    if (lane == 0) {
+      const int L = l0 + 32 * ((y >> 2) & 1);
+      zblk[(int64_t)(y >> 5) * 1024 + 16 * L + 4 * ((y & 31) >> 3) + (y & 3)] = __builtin_bit_cast(uint16_t, stored);
+    }
+  }
   if (lane == 0) row_scale[i] = f;
   for (int d0 = lane * 8; d0 < D; d0 += 512) {
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(H + r * D + d0);
@@ -415,18 +431,6 @@ __global__ __launch_bounds__(256) void train_prep_kernel(const uint16_t* H, cons
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (__bf16)(f * (float)x[e]);
     *reinterpret_cast<bf16x8*>(hs + i * D + d0) = o;
-  }
-  if (lane == 0) {
-    const int y = target[r];
-    if (y >= 0 && y < V) {
-      const float nl2 = nats[r] * kLog2e;
-      const float w = (lse2 - nl2) * sc.invM;                    // s_y / c
-      const float val = (fexp2(-nl2) - 1.f) * (1.f - w * w);     // (p_y - 1) slope_y
-      const float stored = val * (-sc.M * sc.M) * fexp2(lse2 - sc.M);
-      const int L = l0 + 32 * ((y >> 2) & 1);
-      zblk[(int64_t)(y >> 5) * 1024 + 16 * L + 4 * ((y & 31) >> 3) + (y & 3)] =
-          __builtin_bit_cast(uint16_t, (__bf16)stored);
-    }
   }
 }
 
