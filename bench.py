@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 F
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_mfma_T65536_D512_V8192_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "lm_head_cross_pg_amd", "csrc", f)
                   for f in ("pg_fwd.hip", "pg_common.h", "pg_tile.h")]
-FWD_KERNEL = "fwd_mfma_kernel<512, true, 1, false"
+FWD_KERNEL = "fwd_mfma_kernel<512, true, 1, false, false"   # the symmetric, fixed-shift forward (no dZ)
 COPY_BYTES = 1 << 29          # --calibrate-copy moves 512 MiB each way per launch
 
 
@@ -266,7 +266,7 @@ def main():
                    "T": T, "D": D, "V": V, "softcap": c, "seed": args.seed},
         "pct_bf16_mfma_peak_step": 100.0 * flop_fwd / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "bpb": bpb[3],
-        "roofline": {"bound": "mfma", "kernel": "fwd_mfma_kernel<512, true, 1, false>", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": FWD_KERNEL + ">", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(), "launch_ms": fwd_ms,
                      "launch_ms_p10_p50_p90": [float(np.percentile(launch, q)) for q in (10, 50, 90)],
