@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -39,10 +40,15 @@ COPY_BYTES = 1 << 29          # --calibrate-copy moves 512 MiB each way per laun
 
 
 def kernel_source_hash() -> str:
+    """Hash of the forward kernel's sources without comments and blank space, so that the counter
+    runs stay attached to the code they measured across comment edits."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

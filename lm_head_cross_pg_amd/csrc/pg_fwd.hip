@@ -6,19 +6,19 @@
 // reach memory.
 //
 // Kernel layout (bf16, D in {32..512}):
-//   * one workgroup = 4 waves (one per SIMD) = 256 token rows; each wave keeps the bf16 hidden
-//     rows of its 64 tokens in registers (VGPRs and AGPRs) as the B operands of
-//     v_mfma_f32_32x32x16_bf16 (lane l: token l % 32 of each 32-token block, half l / 32 of the
-//     hidden width), so every embedding fragment read from LDS feeds two MFMAs;
+//   * one workgroup = 8 waves (two per SIMD) = 256 token rows; each wave keeps the bf16 hidden
+//     rows of its 32 tokens in registers as the B operand of v_mfma_f32_32x32x16_bf16 (lane l:
+//     token l % 32, half l / 32 of the hidden width);
 //   * the embedding streams through LDS in tiles of 64 vocabulary rows, double-buffered, loaded
-//     with global_load_lds_dwordx4 (no VGPR round trip) into a XOR-swizzled layout;
+//     with global_load_lds_dwordx4 (no VGPR round trip) into a padded or XOR-swizzled layout;
 //   * each 32 x 32 accumulator holds 16 vocabulary rows of one token per lane, so the softcap and
 //     the log-sum-exp run per lane with no cross-lane traffic until the very end;
 //   * for 0 < c <= 40 the log-sum-exp uses the fixed shift c (|s| <= c): no running maximum, no
 //     rescaling. A block whose logits all satisfy |z| <= c/8 evaluates the cap by the tanh series
 //     (one exp2 per logit); otherwise by exp2, fma, rcp (three transcendentals per logit);
-//   * the epilogue of one vocabulary block is issued after the MFMA chain of the next block so the
-//     two overlap;
+//   * the epilogue of one vocabulary block is interleaved with the MFMA chain of the next block;
+//   * a variant also writes, for training, the gradient of every logit up to a per-row factor
+//     (see FwdCore, DZ);
 //   * a grid smaller than the chip (few scored rows) splits the vocabulary across workgroups and
 //     merges the partial sums in a second kernel, in a fixed order.
 #include "pg_common.h"
