@@ -55,6 +55,15 @@ def run_bwd(inp, softcap=None, mask=None, grad_scale=None, fused=False):
     H, E = host_inputs(inp)
     odH, odE = ora.backward(H, E, inp["target"], c, g, mask)
     assert np.all(np.isfinite(dH)) and np.all(np.isfinite(dE))
+    if not np.any(odH) and not np.any(odE):
+        # V = 1: the softmax of one entry is 1 and the gradient exactly 0. The one-call path forms the
+        # target's p from e^-nats, whose target logit comes from the forward's own dot product, so it
+        # leaves a residual of the order of the float32 rounding of lse. It is bounded against each
+        # gradient's natural scale: |dH| <= 1e-5 g max|E|, |dE| <= 1e-5 g sum_t max_d |H[t]|.
+        tH = 1e-5 * g * np.max(np.abs(E))
+        tE = 1e-5 * g * np.sum(np.max(np.abs(H), axis=1))
+        assert np.max(np.abs(dH)) <= tH and np.max(np.abs(dE)) <= tE, (np.max(np.abs(dH)), tH, np.max(np.abs(dE)), tE)
+        return dH, dE
     assert rel_l2(dH, odH) <= GRAD_RL2, rel_l2(dH, odH)
     assert rel_l2(dE, odE) <= GRAD_RL2, rel_l2(dE, odE)
     if mask is not None:
@@ -111,7 +120,8 @@ def test_fused_training_shape_small(seed):
     run_bwd(synth.make_inputs("train_v8192", seed, T=700), fused=True)
 
 
-@pytest.mark.parametrize("D,V", [(32, 4000), (64, 1000), (128, 777), (256, 300), (48, 200), (512, 130)])
+@pytest.mark.parametrize("D,V", [(32, 4000), (64, 1000), (128, 777), (256, 300), (48, 200), (512, 130),
+                                 (512, 1), (64, 65)])
 def test_fused_widths(D, V):
     run_bwd(synth.make_inputs(workload("train_v8192", D=D, V=V, T=520, stream=170 + D), 0), fused=True)
 
