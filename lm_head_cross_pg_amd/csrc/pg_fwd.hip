@@ -55,8 +55,11 @@ __device__ __forceinline__ int device_splits(int64_t n, int n_vtiles, int grid) 
   return s < 1 ? 1 : (s > n_vtiles ? n_vtiles : s);
 }
 
-// LDS fragment reads issued this many MFMA steps ahead of their use.
-constexpr int kPrefetch = 4;
+// LDS fragment reads issued this many MFMA steps ahead of their use. Two steps cover the LDS
+// latency under the epilogue work between MFMAs; four keep 16 more VGPRs live and make the D = 512
+// kernels spill. Two take 5460 instead of 6005 shader cycles per tile, but the launch time is the
+// same: the kernel is power-limited and its clock falls by as much.
+constexpr int kPrefetch = 2;
 
 #ifndef PG_FWD_TOK_BLOCKS
 #define PG_FWD_TOK_BLOCKS 1
