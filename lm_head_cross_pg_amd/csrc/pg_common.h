@@ -70,6 +70,7 @@ struct Softcap {
   bool fixed;     // fixed log-sum-exp shift M (every side capped, caps <= kFixedShiftMaxCap)
   bool asym;      // separate cap cn for z < 0
   float cn, alpha_n, M_n, invK_n;   // the z < 0 side (asym only)
+  float q1n, q2n;                    // series coefficients of the z < 0 side (asym only; q0 is shared)
   __host__ static Softcap make(float cap) { return make(cap, cap); }
   __host__ static Softcap make(float cap, float cap_neg) {
     Softcap s{};
@@ -86,14 +87,19 @@ struct Softcap {
       s.q0 = (float)l2e;
       s.q1 = (float)(-l2e / (3.0 * c * c));
       s.q2 = (float)(2.0 * l2e / (15.0 * c * c * c * c));
-      s.thr = (cap >= 0.01f && !s.asym) ? cap / 8.0f : 0.0f;
+      s.thr = cap >= 0.01f ? cap / 8.0f : 0.0f;
     }
     if (s.asym && cap_neg > 0.f) {
+      const double cn = cap_neg;
       s.cn = cap_neg;
-      s.alpha_n = (float)(2.0 * l2e / cap_neg);
-      s.M_n = (float)(cap_neg * l2e);
+      s.alpha_n = (float)(2.0 * l2e / cn);
+      s.M_n = (float)(cn * l2e);
       s.invK_n = 1.0f / (-2.0f * s.M_n);
+      s.q1n = (float)(-l2e / (3.0 * cn * cn));
+      s.q2n = (float)(2.0 * l2e / (15.0 * cn * cn * cn * cn));
     }
+    // asymmetric caps: the series on both sides needs both capped, below the smaller cap / 8
+    if (s.asym) s.thr = (cap >= 0.01f && cap_neg >= 0.01f) ? (cap < cap_neg ? cap : cap_neg) / 8.0f : 0.0f;
     s.fixed = cap > 0.f && cap <= kFixedShiftMaxCap &&
               (!s.asym || (cap_neg > 0.f && cap_neg <= kFixedShiftMaxCap));
     return s;

@@ -245,8 +245,9 @@ struct FwdCore {
   //   series (|z| <= c/8): u = z^2, q = Q(u), 2^(z q - M), sum: five VALU and one exp2 per logit. It
   //     is speculative: when some |z| of `prev` exceeds c/8 (a wave-uniform branch) the exact sum
   //     replaces it after the chain, and the next blocks take the exact form directly;
-  //   exact: 2^(z alpha), fma, rcp, 2^(K r), sum: three transcendentals per logit, any z; the only
-  //     form of the asymmetric caps (each side with its own constants).
+  //   exact: 2^(z alpha), fma, rcp, 2^(K r), sum: three transcendentals per logit, any z.
+  // With asymmetric caps both forms take each side's constants, and the series needs both sides
+  // capped (below the smaller cap / 8); otherwise they take the exact form.
   // After a series miss the exact form runs for kExactRun blocks, then the series is tried again, so
   // inputs whose logits are mostly large pay the speculation once per kExactRun blocks.
   static constexpr int kExactRun = 16;
@@ -269,7 +270,7 @@ struct FwdCore {
     float w[DZ ? NE : 1];   // DZ: t (t - K), then the stored value
     // DZ adds a stage: 4 also forms t (t - K), 5 multiplies it by 2^t, 6 stores eight at a time
     constexpr int NST = DZ ? 7 : 6;
-    if (ASYM || exact_left > 0) {
+    if (exact_left > 0 || (ASYM && !(sc.thr > 0.f))) {
       pipelined<LOAD, NST>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
         const bool neg = ASYM && z < 0.f;
         switch (st) {
@@ -292,7 +293,7 @@ struct FwdCore {
       });
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) lsum[tb] += part[tb];
-      if (!ASYM) --exact_left;
+      if (exact_left > 0) --exact_left;
       return;
     }
     float u[NE];
@@ -300,7 +301,11 @@ struct FwdCore {
     pipelined<LOAD, NST>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
       switch (st) {
         case 0: u[e] = z * z; amax = fmaxf(amax, fabsf(z)); break;
-        case 1: q[e] = __builtin_fmaf(sc.q2, u[e], sc.q1); break;
+        case 1: {   // asymmetric caps: each side's own coefficients (q0 = log2 e is shared)
+          const bool neg = ASYM && z < 0.f;
+          q[e] = __builtin_fmaf(neg ? sc.q2n : sc.q2, u[e], neg ? sc.q1n : sc.q1);
+          break;
+        }
         case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
         case 3: q[e] = __builtin_fmaf(z, q[e], -sc.M); break;
         case 4:

@@ -152,10 +152,13 @@ def test_large_logits_exact_path():
     run(inp)
 
 
-def test_series_and_exact_blocks_mixed():
+@pytest.mark.parametrize("caps", [30.0, (30.0, 20.0), (20.0, 30.0), (6.0, 40.0)])
+def test_series_and_exact_blocks_mixed(caps):
     """Most blocks take the tanh series; the embedding rows of a few vocabulary tiles are scaled by
     32 (exact in bf16) so that their blocks miss it. The forward then switches to the exact form
-    for a run of blocks and back to the series; every row is checked against the oracle."""
+    for a run of blocks and back to the series; every row is checked against the oracle. With
+    asymmetric caps the series threshold is the smaller cap / 8 and each side takes its own
+    series coefficients; at caps (6, 40) the threshold is 0.75 and most blocks miss it."""
     inp = synth.make_inputs(workload("fwd_v8192", T=2048, stream=98), 0)
     E = synth.as_f64(inp["embed"], inp["dtype"]).copy()
     for tile in (3, 40, 41, 100):
@@ -165,7 +168,7 @@ def test_series_and_exact_blocks_mixed():
     assert np.array_equal(E2, E)
     z = H[:32] @ E2[3 * 64:4 * 64].T
     assert np.max(np.abs(z)) > 30.0 / 8
-    run(inp)
+    run(inp, softcap=caps)
 
 
 def test_ragged_full_width_direct():
