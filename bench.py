@@ -378,6 +378,12 @@ def main():
             abi.pg_lmhead_ce_fwd(hid, td["embed"], td["target"], None, c, nats, tl, ws_fwd)
             abi.pg_lmhead_ce_bwd(hid, td["embed"], td["target"], None, tl, c, 1.0 / T, dH, dE, ws_bwd)
 
+        caps = (30.0, 20.0)
+
+        def train_step_asym(hid):     # asymmetric caps, one call
+            abi.pg_lmhead_ce_fwd_bwd_asym(hid, td["embed"], td["target"], None, caps[0], caps[1], 1.0 / T, nats, tl,
+                                          dH, dE, ws_fb)
+
         def time_train(step, hid):
             ksteps = max(3, args.steps // 5)
             for _ in range(max(5, args.warmup // 2)):
@@ -395,7 +401,8 @@ def main():
         best = {}
         for _ in range(2):
             for key, step, hid in (("one", train_step, td["hidden"]), ("two", train_step_two_calls, td["hidden"]),
-                                   ("one8", train_step, hid8), ("two8", train_step_two_calls, hid8)):
+                                   ("one8", train_step, hid8), ("two8", train_step_two_calls, hid8),
+                                   ("asym", train_step_asym, td["hidden"])):
                 t, ksteps = time_train(step, hid)
                 best[key] = min(best.get(key, t), t)
         del hid8
@@ -409,6 +416,7 @@ def main():
             "ms_per_step_large_logits": tw8 * 1e3,
             "ms_per_step_two_calls": tw2 * 1e3,
             "ms_per_step_two_calls_large_logits": tw82 * 1e3,
+            "ms_per_step_asym_caps_30_20": best["asym"] * 1e3,
         }
 
     if not args.no_cpu:

@@ -123,9 +123,11 @@ pg_status pg_lmhead_ce_fwd_bwd(const void* hidden, const void* embed, int32_t dt
  * that side uncapped). The pages name an "AsymLogit" change to the head (HYDRA Golf site,
  * leaderboard table, entries #1 and #4; README leaderboard, PR #2135 and PR #1945 rows) without
  * defining it; separate caps for positive and negative logits is the reading taken here. With
- * cap_pos == cap_neg these equal pg_lmhead_ce_fwd / pg_lmhead_ce_bwd. Arguments, workspace sizes
- * and errors are those of the symmetric entry points; either cap negative or not finite gives
- * PG_ERR_SOFTCAP.
+ * cap_pos == cap_neg these equal pg_lmhead_ce_fwd / pg_lmhead_ce_bwd / pg_lmhead_ce_fwd_bwd.
+ * Arguments, workspace sizes and errors are those of the symmetric entry points; either cap
+ * negative or not finite gives PG_ERR_SOFTCAP. pg_lmhead_ce_fwd_bwd_asym computes the logits once
+ * when both caps lie in (0, 40] (bf16, D as for pg_lmhead_ce_fwd_bwd); otherwise it runs the two
+ * asymmetric calls.
  */
 pg_status pg_lmhead_ce_fwd_asym(const void* hidden, const void* embed, int32_t dtype,
                                 const int32_t* target, const uint8_t* score_mask,
@@ -138,6 +140,12 @@ pg_status pg_lmhead_ce_bwd_asym(const void* hidden, const void* embed, int32_t d
                                 int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg, float grad_scale,
                                 float* dhidden, float* dembed,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+pg_status pg_lmhead_ce_fwd_bwd_asym(const void* hidden, const void* embed, int32_t dtype,
+                                    const int32_t* target, const uint8_t* score_mask,
+                                    int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
+                                    float grad_scale, float* nats, float* lse, float* dhidden, float* dembed,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Quantised tied head. The model is quantised to fit the artifact (trios issue #19, approach

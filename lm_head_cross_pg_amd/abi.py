@@ -26,6 +26,7 @@ STATUS_NAMES = {0: "PG_OK", -1: "PG_ERR_NULL", -2: "PG_ERR_SHAPE", -3: "PG_ERR_D
 
 # every symbol the header declares
 EXPORTS = ("pg_lmhead_ce_fwd", "pg_lmhead_ce_bwd", "pg_lmhead_ce_fwd_bwd", "pg_lmhead_ce_fwd_asym", "pg_lmhead_ce_bwd_asym",
+           "pg_lmhead_ce_fwd_bwd_asym",
            "pg_quantize_q8", "pg_lmhead_ce_fwd_q8", "pg_bpb_reduce", "pg_workspace_bytes", "pg_status_str",
            "pg_abi_version")
 
@@ -54,6 +55,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pg_lmhead_ce_bwd.restype = i32
     lib.pg_lmhead_ce_fwd_bwd.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, f32, f32, vp, vp, vp, vp, vp, sz, vp]
     lib.pg_lmhead_ce_fwd_bwd.restype = i32
+    lib.pg_lmhead_ce_fwd_bwd_asym.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, f32, f32, f32, vp, vp, vp, vp, vp,
+                                              sz, vp]
+    lib.pg_lmhead_ce_fwd_bwd_asym.restype = i32
     lib.pg_lmhead_ce_fwd_asym.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, f32, f32, vp, vp, vp, sz, vp]
     lib.pg_lmhead_ce_fwd_asym.restype = i32
     lib.pg_lmhead_ce_bwd_asym.argtypes = [vp, vp, i32, vp, vp, vp, i64, i32, i32, f32, f32, f32, vp, vp, vp, sz, vp]
@@ -185,6 +189,20 @@ def pg_lmhead_ce_bwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: tor
                                       float(grad_scale), _ptr(dhidden), _ptr(dembed), _ptr(ws), ws.numel(),
                                       _stream(stream))
     _check(st, "pg_lmhead_ce_bwd_asym")
+
+
+def pg_lmhead_ce_fwd_bwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Tensor,
+                              score_mask: Optional[torch.Tensor], cap_pos: float, cap_neg: float, grad_scale: float,
+                              nats: torch.Tensor, lse: torch.Tensor, dhidden: torch.Tensor, dembed: torch.Tensor,
+                              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    T, D = hidden.shape
+    V = embed.shape[0]
+    ws = _workspace(PG_OP_FWD_BWD, T, D, V, embed, workspace)
+    st = load().pg_lmhead_ce_fwd_bwd_asym(_ptr(hidden), _ptr(embed), _dtype_code(hidden), _ptr(target),
+                                          _ptr(score_mask), T, D, V, float(cap_pos), float(cap_neg), float(grad_scale),
+                                          _ptr(nats), _ptr(lse), _ptr(dhidden), _ptr(dembed), _ptr(ws), ws.numel(),
+                                          _stream(stream))
+    _check(st, "pg_lmhead_ce_fwd_bwd_asym")
 
 
 def pg_quantize_q8(embed: torch.Tensor, embed_q8: torch.Tensor, embed_scale: torch.Tensor, stream=None) -> None:

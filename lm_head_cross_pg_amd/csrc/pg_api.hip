@@ -149,17 +149,16 @@ pg_status pg_lmhead_ce_bwd(const void* hidden, const void* embed, int32_t dtype,
                   dembed, workspace, workspace_bytes, stream);
 }
 
-pg_status pg_lmhead_ce_fwd_bwd(const void* hidden, const void* embed, int32_t dtype,
-                               const int32_t* target, const uint8_t* score_mask,
-                               int64_t T, int32_t D, int32_t V, float softcap, float grad_scale,
-                               float* nats, float* lse, float* dhidden, float* dembed,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+static pg_status train_impl(const void* hidden, const void* embed, int32_t dtype, const int32_t* target,
+                            const uint8_t* score_mask, int64_t T, int32_t D, int32_t V, float cap_pos,
+                            float cap_neg, float grad_scale, float* nats, float* lse, float* dhidden,
+                            float* dembed, void* workspace, size_t workspace_bytes, void* stream) {
   pg_status s;
   if ((s = check_shape(T, D, V)) != PG_OK) return s;
   if (T > 0 && (!hidden || !target || !nats || !lse || !dhidden)) return PG_ERR_NULL;
   if (!embed || !dembed || !workspace) return PG_ERR_NULL;
   if (dtype != PG_DTYPE_BF16 && dtype != PG_DTYPE_F32) return PG_ERR_DTYPE;
-  if ((s = check_softcap(softcap)) != PG_OK) return s;
+  if ((s = check_softcap(cap_pos)) != PG_OK || (s = check_softcap(cap_neg)) != PG_OK) return s;
   if (!std::isfinite(grad_scale)) return PG_ERR_SOFTCAP;
   if (misaligned(hidden) || misaligned(embed) || misaligned(target) || misaligned(score_mask) ||
       misaligned(nats) || misaligned(lse) || misaligned(dhidden) || misaligned(dembed) || misaligned(workspace))
@@ -167,10 +166,28 @@ pg_status pg_lmhead_ce_fwd_bwd(const void* hidden, const void* embed, int32_t dt
   if (workspace_bytes < pg_workspace_bytes(PG_OP_FWD_BWD, T, D, V)) return PG_ERR_WORKSPACE;
   pg::DeviceInfo dev{};
   if ((s = device_check(dev)) != PG_OK) return s;
-  hipError_t e = pg::launch_train(hidden, embed, dtype, target, score_mask, T, D, V, softcap, softcap, grad_scale,
+  hipError_t e = pg::launch_train(hidden, embed, dtype, target, score_mask, T, D, V, cap_pos, cap_neg, grad_scale,
                                   nats, lse, dhidden, dembed, static_cast<char*>(workspace), dev,
                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PG_OK : PG_ERR_HIP;
+}
+
+pg_status pg_lmhead_ce_fwd_bwd(const void* hidden, const void* embed, int32_t dtype,
+                               const int32_t* target, const uint8_t* score_mask,
+                               int64_t T, int32_t D, int32_t V, float softcap, float grad_scale,
+                               float* nats, float* lse, float* dhidden, float* dembed,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return train_impl(hidden, embed, dtype, target, score_mask, T, D, V, softcap, softcap, grad_scale, nats, lse,
+                    dhidden, dembed, workspace, workspace_bytes, stream);
+}
+
+pg_status pg_lmhead_ce_fwd_bwd_asym(const void* hidden, const void* embed, int32_t dtype,
+                                    const int32_t* target, const uint8_t* score_mask,
+                                    int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
+                                    float grad_scale, float* nats, float* lse, float* dhidden, float* dembed,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return train_impl(hidden, embed, dtype, target, score_mask, T, D, V, cap_pos, cap_neg, grad_scale, nats, lse,
+                    dhidden, dembed, workspace, workspace_bytes, stream);
 }
 
 pg_status pg_lmhead_ce_fwd_asym(const void* hidden, const void* embed, int32_t dtype,

@@ -376,8 +376,9 @@ void bwd_dz_kernel(DzParams p) {
 }
 
 // The step from the forward's unnormalised dZ to what the two GEMMs read, one wave per compacted
-// row i. The forward stored d = 2^t t (t - K) for every logit (t = s log2 e - M), and g dZ of a
-// non-target element is f d with the row's factor f = g 2^(M - lse log2 e) (-1 / M^2). This kernel
+// row i. The forward stored d = 2^t t (t - K) for every logit (t = s log2 e - M; with asymmetric
+// caps, z < 0 logits carry that side's slope in the same scale), and g dZ of a non-target element
+// is f d with the row's factor f = g 2^(M - lse log2 e) (-1 / M^2). This kernel
 // writes the target element as (p_y - 1) slope_y / (f / g), from the row's nats and lse
 // (p_y = e^-nats; s_y log2 e = (lse - nats) log2 e), then f (the dH product scales its output rows
 // by it) and the hidden row times f in bf16 (the B operand of dE, whose sum runs over rows). Rows from the last
@@ -415,7 +416,8 @@ __global__ __launch_bounds__(256) void train_prep_kernel(const uint16_t* H, cons
   const int y = target[r];
   if (y >= 0 && y < V) {
     const float nl2 = nats[r] * kLog2e;
-    const float w = (lse2 - nl2) * sc.invM;                      // s_y / c
+    const float sy2 = lse2 - nl2;                                // s_y log2 e
+    const float w = sy2 * (sc.asym && sy2 < 0.f ? sc.invM_n : sc.invM);   // s_y / (its side's cap)
     const float val = (fexp2(-nl2) - 1.f) * (1.f - w * w);       // (p_y - 1) slope_y
     const __bf16 stored = (__bf16)(val * (-sc.M * sc.M) * fexp2(lse2 - sc.M));
     if ((float)stored != 0.f) f = g * val / (float)stored;

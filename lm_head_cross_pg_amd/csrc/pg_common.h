@@ -71,6 +71,10 @@ struct Softcap {
   bool asym;      // separate cap cn for z < 0
   float cn, alpha_n, M_n, invK_n;   // the z < 0 side (asym only)
   float q1n, q2n;                    // series coefficients of the z < 0 side (asym only; q0 is shared)
+  // z < 0 side of the stored training gradient (asym only): with t = s log2 e - M, the slope
+  // 1 - (s / cn)^2 is -(t + dza_n)(t + dzb_n) dzw_n / M^2 (dza_n = M - M_n, dzb_n = M + M_n,
+  // dzw_n = M^2 / M_n^2), the form of the z >= 0 side, -t (t - K) / M^2, with other constants
+  float dza_n, dzb_n, dzw_n, invM_n;
   __host__ static Softcap make(float cap) { return make(cap, cap); }
   __host__ static Softcap make(float cap, float cap_neg) {
     Softcap s{};
@@ -97,6 +101,11 @@ struct Softcap {
       s.invK_n = 1.0f / (-2.0f * s.M_n);
       s.q1n = (float)(-l2e / (3.0 * cn * cn));
       s.q2n = (float)(2.0 * l2e / (15.0 * cn * cn * cn * cn));
+      const double Mp = cap > 0.f ? (double)cap * l2e : 0.0, Mn = cn * l2e;
+      s.dza_n = (float)(Mp - Mn);
+      s.dzb_n = (float)(Mp + Mn);
+      s.dzw_n = (float)((Mp * Mp) / (Mn * Mn));
+      s.invM_n = (float)(1.0 / Mn);
     }
     // asymmetric caps: the series on both sides needs both capped, below the smaller cap / 8
     if (s.asym) s.thr = (cap >= 0.01f && cap_neg >= 0.01f) ? (cap < cap_neg ? cap : cap_neg) / 8.0f : 0.0f;

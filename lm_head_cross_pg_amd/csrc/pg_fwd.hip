@@ -77,7 +77,7 @@ constexpr int kFwdTokBlocks = PG_FWD_TOK_BLOCKS;
 // then as well).
 template <int D, bool FIXED, int NB, bool ASYM, bool DZ = false>
 struct FwdCore {
-  static_assert(!DZ || (FIXED && !ASYM), "unnormalised dZ needs the fixed shift and one cap");
+  static_assert(!DZ || FIXED, "unnormalised dZ needs the fixed shift");
   static constexpr int KS = D / 16;
   static constexpr int kWaves = WaveShape<NB>::kWaves;
   static constexpr int kLoads = embed_loads_per_wave<D, kWaves>();
@@ -102,15 +102,23 @@ struct FwdCore {
     *reinterpret_cast<bf16x8*>(dzblk[tb] + (int64_t)(vbase >> 5) * 1024 + 8 * j8) = o;
   }
 
-  // DZ, not pipelined: the exact exponent t of each logit, d = 2^t t (t - K); MASKED stores 0 for
-  // rows >= V.
+  // DZ: the slope factor of the stored gradient from the exponent t = s log2 e - M: t (t - K) for
+  // z >= 0; with asymmetric caps, (t + dza_n)(t + dzb_n) dzw_n for z < 0 (the same row factor
+  // -2^(M - lse log2 e) / M^2 then turns either into the gradient).
+  __device__ __forceinline__ float dz_slope(float t, bool neg) const {
+    if (!ASYM) return t * (t - sc.K);
+    return neg ? (t + sc.dza_n) * (t + sc.dzb_n) * sc.dzw_n : t * (t - sc.K);
+  }
+
+  // DZ, not pipelined: the exact exponent t of each logit, d = 2^t times its slope factor; MASKED
+  // stores 0 for rows >= V.
   template <bool MASKED>
   __device__ __forceinline__ void dz_exact(const f32x16& acc, int vbase, int tb) const {
     float d[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float t = capped_shifted_sc(acc[r], sc);
-      d[r] = fexp2(t) * (t * (t - sc.K));
+      d[r] = fexp2(t) * dz_slope(t, ASYM && acc[r] < 0.f);
       if (MASKED) d[r] = (vbase + 8 * (r >> 2) + 4 * h + (r & 3)) < V ? d[r] : 0.f;
     }
     store8(d, vbase, tb, 0);
@@ -119,19 +127,6 @@ struct FwdCore {
 
   __device__ __forceinline__ void chain(int buf, int vb, f32x16 (&acc)[NB]) const {
     logit_blocks<D, NB>(lds, buf, vb, h, col, hf, acc);
-  }
-
-  // Exp-sum with the fixed shift M by the tanh series (valid when |z| <= c/8).
-  __device__ __forceinline__ float part_series(const f32x16& acc) const {
-    float part = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float z = acc[r];
-      const float u = z * z;
-      const float q = __builtin_fmaf(__builtin_fmaf(sc.q2, u, sc.q1), u, sc.q0);
-      part += fexp2(__builtin_fmaf(z, q, -sc.M));
-    }
-    return part;
   }
 
   // Exp-sum with the fixed shift M, exact softcap. Register r holds vocabulary row
@@ -267,8 +262,8 @@ struct FwdCore {
     }
     float part[NB] = {};
     float q[NE];
-    float w[DZ ? NE : 1];   // DZ: t (t - K), then the stored value
-    // DZ adds a stage: 4 also forms t (t - K), 5 multiplies it by 2^t, 6 stores eight at a time
+    float w[DZ ? NE : 1];   // DZ: the slope factor of t, then the stored value
+    // DZ adds a stage: 4 also forms the slope factor, 5 multiplies it by 2^t, 6 stores eight at a time
     constexpr int NST = DZ ? 7 : 6;
     if (exact_left > 0 || (ASYM && !(sc.thr > 0.f))) {
       pipelined<LOAD, NST>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
@@ -279,8 +274,9 @@ struct FwdCore {
           case 2: { const float ik = neg ? sc.invK_n : sc.invK; q[e] = __builtin_fmaf(q[e], ik, ik); break; }
           case 3: q[e] = frcp(q[e]); break;                                  // K r = (s - c) log2 e
           case 4:
-            if (DZ) w[e] = q[e] * (q[e] - sc.K);
-            q[e] = fexp2(ASYM ? q[e] + (neg ? sc.M_n - sc.M : 0.f) : q[e]);
+            if (ASYM) q[e] += neg ? sc.M_n - sc.M : 0.f;
+            if (DZ) w[e] = dz_slope(q[e], neg);
+            q[e] = fexp2(q[e]);
             break;
           case 5:
             part[e / 16] += q[e];
@@ -309,7 +305,7 @@ struct FwdCore {
         case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
         case 3: q[e] = __builtin_fmaf(z, q[e], -sc.M); break;
         case 4:
-          if (DZ) w[e] = q[e] * (q[e] - sc.K);
+          if (DZ) w[e] = dz_slope(q[e], ASYM && z < 0.f);
           q[e] = fexp2(q[e]);
           break;
         case 5:
@@ -629,7 +625,8 @@ static void launch_mfma(const FwdParams& p, int grid, hipStream_t st) {
 template <int D>
 static void launch_mfma_d(const FwdParams& p, int grid, hipStream_t st) {
   if (p.dz) {   // the caller checked fwd_writes_dz
-    launch_mfma<D, true, false, true>(p, grid, st);
+    if (p.sc.asym) launch_mfma<D, true, true, true>(p, grid, st);
+    else launch_mfma<D, true, false, true>(p, grid, st);
   } else if (p.sc.asym) {
     if (p.sc.fixed) launch_mfma<D, true, true>(p, grid, st);
     else launch_mfma<D, false, true>(p, grid, st);
@@ -641,7 +638,7 @@ static void launch_mfma_d(const FwdParams& p, int grid, hipStream_t st) {
 
 bool fwd_writes_dz(int32_t dtype, int32_t D, float cap_pos, float cap_neg) {
   const Softcap sc = Softcap::make(cap_pos, cap_neg);
-  return dtype == 0 && mfma_width(D) && sc.fixed && !sc.asym;
+  return dtype == 0 && mfma_width(D) && sc.fixed;
 }
 
 hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t* target,

@@ -49,7 +49,8 @@ hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t
                       const uint8_t* mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
                       float* nats, float* lse, char* ws, const DeviceInfo& dev, hipStream_t st,
                       uint16_t* dz = nullptr);
-// The forward can write the unnormalised dZ: bf16 MFMA widths, one cap in the fixed-shift range.
+// The forward can write the unnormalised dZ: bf16 MFMA widths, every side capped within the
+// fixed-shift range (one cap, or two).
 bool fwd_writes_dz(int32_t dtype, int32_t D, float cap_pos, float cap_neg);
 
 // Forward + backward in one call (pg_bwd.hip). Where fwd_writes_dz holds, the forward writes the

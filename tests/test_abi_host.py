@@ -103,6 +103,15 @@ def bwd_asym(lib, **kw):
                                      a["wsb"], a["stream"])
 
 
+def fwd_bwd_asym(lib, **kw):
+    a = dict(hidden=P, embed=P, dtype=0, target=P, mask=None, T=256, D=64, V=512, cp=30.0, cn=10.0, g=1 / 256,
+             nats=P, lse=P, dh=P, de=P, ws=P, wsb=BIG, stream=None)
+    a.update(kw)
+    return lib.pg_lmhead_ce_fwd_bwd_asym(a["hidden"], a["embed"], a["dtype"], a["target"], a["mask"], a["T"],
+                                         a["D"], a["V"], a["cp"], a["cn"], a["g"], a["nats"], a["lse"], a["dh"],
+                                         a["de"], a["ws"], a["wsb"], a["stream"])
+
+
 def quant(lib, **kw):
     a = dict(embed=P, dtype=0, V=512, D=64, q=P, scale=P, stream=None)
     a.update(kw)
@@ -124,7 +133,7 @@ def bpb(lib, **kw):
                              a["ws"], a["wsb"], a["stream"])
 
 
-@pytest.mark.parametrize("call", [fwd, bwd, fwd_bwd, fwd_asym, bwd_asym, fwd_q8, bpb])
+@pytest.mark.parametrize("call", [fwd, bwd, fwd_bwd, fwd_asym, bwd_asym, fwd_bwd_asym, fwd_q8, bpb])
 def test_validation_codes(lib, call):
     assert call(lib, T=-1) == -2
     assert call(lib, V=0) == -2
@@ -173,7 +182,7 @@ def test_backward_validation(lib):
     assert bwd(lib, de=P + 12) == -6
 
 
-@pytest.mark.parametrize("call", [fwd_asym, bwd_asym])
+@pytest.mark.parametrize("call", [fwd_asym, bwd_asym, fwd_bwd_asym])
 def test_asymmetric_cap_validation(lib, call):
     assert call(lib, cp=-1.0) == -4
     assert call(lib, cn=-0.5) == -4
@@ -181,6 +190,15 @@ def test_asymmetric_cap_validation(lib, call):
     assert call(lib, cp=float("inf")) == -4
     assert call(lib, hidden=None) == -1
     assert call(lib, dtype=3) == -3
+
+
+def test_fused_training_asymmetric_validation(lib):
+    assert fwd_bwd_asym(lib, lse=None) == -1
+    assert fwd_bwd_asym(lib, de=None) == -1
+    assert fwd_bwd_asym(lib, g=float("inf")) == -4
+    assert fwd_bwd_asym(lib, dh=P + 4) == -6
+    need = abi.workspace_bytes(abi.PG_OP_FWD_BWD, 256, 64, 512)
+    assert fwd_bwd_asym(lib, wsb=need - 1) == -5
 
 
 def test_quantised_head_validation(lib):
@@ -217,6 +235,7 @@ def test_valid_arguments_reach_the_device_check(lib):
     assert bwd(lib) == -7
     assert fwd_asym(lib) == -7
     assert bwd_asym(lib) == -7
+    assert fwd_bwd_asym(lib) == -7
     assert quant(lib) == -7
     assert fwd_q8(lib) == -7
     assert bpb(lib) == -7

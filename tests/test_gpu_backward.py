@@ -38,7 +38,11 @@ def run_bwd(inp, softcap=None, mask=None, grad_scale=None, fused=False):
     dH = torch.full((T, D), float("nan"), device="cuda")
     dE = torch.full((V, D), float("nan"), device="cuda")
     if fused:
-        abi.pg_lmhead_ce_fwd_bwd(d["hidden"], d["embed"], d["target"], mask_t, c, g, nats, lse, dH, dE)
+        if isinstance(c, tuple):
+            abi.pg_lmhead_ce_fwd_bwd_asym(d["hidden"], d["embed"], d["target"], mask_t, c[0], c[1], g, nats, lse,
+                                          dH, dE)
+        else:
+            abi.pg_lmhead_ce_fwd_bwd(d["hidden"], d["embed"], d["target"], mask_t, c, g, nats, lse, dH, dE)
         torch.cuda.synchronize()
         H, E = host_inputs(inp)
         onats, olse = ora.forward(H, E, inp["target"], c, mask)
@@ -162,11 +166,13 @@ def test_fused_grad_scale_zero_and_two():
     run_bwd(inp, grad_scale=2.0, fused=True)
 
 
-def _full_size_check(inp, rows_extra, seed, label):
+def _full_size_check(inp, rows_extra, seed, label, caps=None):
     """Both training entry points on one full-size input: sampled dH rows and dE rows against the
-    oracle (computed once), the <dH, H> = <dE, E> identity, and nats / lse on sampled rows."""
+    oracle (computed once), the <dH, H> = <dE, E> identity, and nats / lse on sampled rows. caps:
+    (c_pos, c_neg) for the asymmetric entry points."""
     from tests.gpu_helpers import oracle_forward_chunked
-    T, D, V, c = inp["T"], inp["D"], inp["V"], inp["softcap"]
+    T, D, V = inp["T"], inp["D"], inp["V"]
+    c = inp["softcap"] if caps is None else caps
     g = 1.0 / T
     d = abi.to_device(inp)
     H, E = host_inputs(inp)
@@ -183,7 +189,13 @@ def _full_size_check(inp, rows_extra, seed, label):
         lse = torch.empty(T, device="cuda")
         dH = torch.empty((T, D), device="cuda")
         dE = torch.empty((V, D), device="cuda")
-        if fused:
+        if caps is not None and fused:
+            abi.pg_lmhead_ce_fwd_bwd_asym(d["hidden"], d["embed"], d["target"], None, c[0], c[1], g, nats, lse,
+                                          dH, dE)
+        elif caps is not None:
+            abi.pg_lmhead_ce_fwd_asym(d["hidden"], d["embed"], d["target"], None, c[0], c[1], nats, lse)
+            abi.pg_lmhead_ce_bwd_asym(d["hidden"], d["embed"], d["target"], None, lse, c[0], c[1], g, dH, dE)
+        elif fused:
             abi.pg_lmhead_ce_fwd_bwd(d["hidden"], d["embed"], d["target"], None, c, g, nats, lse, dH, dE)
         else:
             abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, c, nats, lse)
@@ -208,6 +220,13 @@ def test_training_full_size_sampled():
     _full_size_check(inp, [0, 255, 256, T - 1], 11, "train full size")
 
 
+def test_training_full_size_sampled_asymmetric():
+    """The same at caps (30, 20), through both asymmetric training entry points."""
+    inp = synth.make_inputs("train_v8192", 0)
+    T = inp["T"]
+    _full_size_check(inp, [0, 255, 256, T - 1], 13, "train full size caps (30, 20)", caps=(30.0, 20.0))
+
+
 def test_dz_beyond_2_31_elements():
     """T = 300,007 rows at V = 8192: dZ holds 2.46e9 elements (4.9 GB), so its block offsets and
     the GEMMs' reads of it pass 2^31. D = 32 keeps the oracle's full forward cheap. Both training
@@ -222,6 +241,28 @@ def test_asymmetric_caps(caps):
     """Gradients with separate caps for z >= 0 and z < 0; logits reach both caps' curvature."""
     w = workload("train_v8192", T=520, V=1500, stream=99, hidden_scale=40.0)
     run_bwd(synth.make_inputs(w, 1), softcap=caps)
+
+
+@pytest.mark.parametrize("caps", [(30.0, 10.0), (10.0, 30.0), (30.0, 20.0), (6.0, 40.0), (30.0, 0.0), (0.0, 20.0),
+                                  (50.0, 20.0)])
+@pytest.mark.parametrize("scale", [1.0, 40.0])
+def test_fused_asymmetric_caps(caps, scale):
+    """pg_lmhead_ce_fwd_bwd_asym: one pass when both caps lie in (0, 40], with each side's slope
+    stored in the common scale of the row factor; the two calls otherwise (an uncapped side, a cap
+    above 40). Initialisation-scale logits (the tanh series) and hidden x 40 (both caps' curvature,
+    the exact form)."""
+    w = workload("train_v8192", T=520, V=1500, stream=99, hidden_scale=scale)
+    run_bwd(synth.make_inputs(w, 1), softcap=caps, fused=True)
+
+
+def test_fused_asymmetric_widths_masked_ragged():
+    for D, V in ((32, 700), (64, 1000), (128, 777), (256, 300), (48, 200)):
+        run_bwd(synth.make_inputs(workload("train_v8192", D=D, V=V, T=520, stream=190 + D, hidden_scale=8.0), 0),
+                softcap=(30.0, 15.0), fused=True)
+    run_bwd(synth.make_inputs("masked_stride64", 0, T=4096), softcap=(30.0, 15.0), fused=True)
+    run_bwd(synth.make_inputs(workload("train_v8192", V=2048, stream=195), 0, T=257), softcap=(20.0, 30.0),
+            fused=True)
+    run_bwd(synth.make_inputs("stress", 0), softcap=(30.0, 10.0), fused=True)
 
 
 def test_asymmetric_caps_generic_and_masked():
