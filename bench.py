@@ -182,6 +182,47 @@ def cpu_baseline(inp, seconds: float = 12.0):
                       f"{chunk}-row chunks), float64 forward (numpy matmul + tanh/exp/log), {dt:.1f} s wall"}
 
 
+def library_gemm(steps):
+    """The vendor GEMM (torch.mm, hipBLASLt on this stack) on the products of the head at T = 65536,
+    D = 512, V = 8192, bf16 in: the logits H E^T (written out, T x V bf16), dZ E (T x D) and
+    dZ^T H (V x D), with float32 outputs where torch offers them. Context for the fused kernels,
+    which never write the logits; the medians of HIP-event-timed calls."""
+    import torch
+    T, D, V = 65536, 512, 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    H = torch.randn(T, D, device="cuda", generator=g).bfloat16()
+    E = (torch.randn(V, D, device="cuda", generator=g) * 0.02).bfloat16()
+    dZ = (torch.randn(T, V, device="cuda", generator=g) * 1e-3).bfloat16()
+    Et = E.t().contiguous()
+
+    def med_ms(f):
+        for _ in range(5):
+            f()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record()
+            f()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    flop = 2.0 * T * D * V
+    cases = {"logits H E^T (bf16 out)": lambda: torch.mm(H, Et),
+             "dH = dZ E (bf16 out)": lambda: torch.mm(dZ, E),
+             "dE = dZ^T H (bf16 out)": lambda: torch.mm(dZ.t(), H)}
+    try:
+        torch.mm(dZ, E, out_dtype=torch.float32)
+        cases["dH = dZ E (f32 out)"] = lambda: torch.mm(dZ, E, out_dtype=torch.float32)
+        cases["dE = dZ^T H (f32 out)"] = lambda: torch.mm(dZ.t(), H, out_dtype=torch.float32)
+    except (TypeError, RuntimeError):
+        pass
+    res = {}
+    for k, f in cases.items():
+        ms = med_ms(f)
+        res[k] = {"ms": ms, "tflops": flop / (ms * 1e-3) / 1e12, "frac": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    print(json.dumps({"library_gemm": res, "T": T, "D": D, "V": V, "calls": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +235,8 @@ def main():
                     help="only run a plain 512 MiB device-to-device copy (HBM counter calibration)")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB scratch tensor between timed forward launches (cold L2/MALL)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time the vendor GEMM (torch.mm on hipBLASLt) on the head's three product shapes")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="summarise rocprofv3 counter runs under DIR into profiles/ and exit")
     args = ap.parse_args()
@@ -214,6 +257,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "launches": 5}))
+        return
+    if args.library_gemm:
+        library_gemm(args.steps)
         return
     from lm_head_cross_pg_amd import abi, build, synth
     if not os.path.exists(abi.LIB_PATH):
