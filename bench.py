@@ -182,6 +182,50 @@ def cpu_baseline(inp, seconds: float = 12.0):
                       f"{chunk}-row chunks), float64 forward (numpy matmul + tanh/exp/log), {dt:.1f} s wall"}
 
 
+def other_configs(abi, synth, args):
+    """Forward + bits per byte on the smaller workloads, each as its own step: the tiny fp32 shape,
+    the baseline vocabulary (T = 8192, V = 1024) and the stride-64 masked evaluation (2048 scored
+    rows of 65536). Mean step time over --steps back-to-back steps after --warmup, and the mean of
+    HIP-event-timed single steps."""
+    import torch
+    res = {}
+    for name in ("tiny_f32", "fwd_v1024", "masked_stride64"):
+        inp = synth.make_inputs(name, args.seed)
+        T, D, V, c = inp["T"], inp["D"], inp["V"], inp["softcap"]
+        d = abi.to_device(inp)
+        nats = torch.empty(T, dtype=torch.float32, device="cuda")
+        out = torch.empty(4, dtype=torch.float64, device="cuda")
+        ws_f = torch.empty(abi.workspace_bytes(abi.PG_OP_FWD, T, D, V), dtype=torch.uint8, device="cuda")
+        ws_b = torch.empty(abi.workspace_bytes(abi.PG_OP_BPB, T, D, V), dtype=torch.uint8, device="cuda")
+
+        def step():
+            abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], d["mask"], c, nats, None, ws_f)
+            abi.pg_bpb_reduce(nats, d["target"], d["mask"], d["byte_len"], None, V, out, ws_b)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        ev_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        n_scored = int(out[2].item())
+        flop = 2.0 * n_scored * D * V
+        res[name] = {"T": T, "D": D, "V": V, "dtype": inp["dtype"], "scored_rows": n_scored,
+                     "ms_per_step": wall * 1e3, "event_ms_per_step": ev_ms,
+                     "scored_tokens_per_s": n_scored / wall,
+                     "frac_bf16_peak": flop / wall / 1e12 / PEAK_BF16_TFLOPS, "bpb": float(out[3].item())}
+    print(json.dumps({"other_configs": res, "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def library_gemm(steps):
     """The vendor GEMM (torch.mm, hipBLASLt on this stack) on the products of the head at T = 65536,
     D = 512, V = 8192, bf16 in: the logits H E^T (written out, T x V bf16), dZ E (T x D) and
@@ -235,6 +279,8 @@ def main():
                     help="only run a plain 512 MiB device-to-device copy (HBM counter calibration)")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB scratch tensor between timed forward launches (cold L2/MALL)")
+    ap.add_argument("--other-configs", action="store_true",
+                    help="only time forward + bits per byte on the smaller workloads (their own JSON line)")
     ap.add_argument("--library-gemm", action="store_true",
                     help="only time the vendor GEMM (torch.mm on hipBLASLt) on the head's three product shapes")
     ap.add_argument("--summarize-counters", metavar="DIR",
@@ -265,6 +311,9 @@ def main():
     if not os.path.exists(abi.LIB_PATH):
         build.build()
     abi.load()
+    if args.other_configs:
+        other_configs(abi, synth, args)
+        return
 
     inp = synth.make_inputs("fwd_v8192", args.seed)
     T, D, V, c = inp["T"], inp["D"], inp["V"], inp["softcap"]

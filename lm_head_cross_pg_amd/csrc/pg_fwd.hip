@@ -492,14 +492,35 @@ __global__ __launch_bounds__(256) void fwd_finalize_kernel(FwdParams p, int main
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int S = p.splits_host > 0 ? p.splits_host : device_splits(n, p.n_vtiles, main_grid);
+  // partials in split order; the loads go out eight at a time so that their latencies overlap
+  constexpr int kBatch = 8;
   float lse2;
   if (fixed) {
     float l = 0.f;
-    for (int s = 0; s < S; ++s) l += p.part_l[(int64_t)s * n + i];
+    int s = 0;
+    for (; s + kBatch <= S; s += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) v[j] = p.part_l[(int64_t)(s + j) * n + i];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) l += v[j];
+    }
+    for (; s < S; ++s) l += p.part_l[(int64_t)s * n + i];
     lse2 = p.sc.M + flog2(l);
   } else {
     float m = -INFINITY, l = 0.f;
-    for (int s = 0; s < S; ++s) lse_merge(m, l, p.part_m[(int64_t)s * n + i], p.part_l[(int64_t)s * n + i]);
+    int s = 0;
+    for (; s + kBatch <= S; s += kBatch) {
+      float vm[kBatch], vl[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        vm[j] = p.part_m[(int64_t)(s + j) * n + i];
+        vl[j] = p.part_l[(int64_t)(s + j) * n + i];
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) lse_merge(m, l, vm[j], vl[j]);
+    }
+    for (; s < S; ++s) lse_merge(m, l, p.part_m[(int64_t)s * n + i], p.part_l[(int64_t)s * n + i]);
     lse2 = m + flog2(l);
   }
   const int64_t r = p.rows ? (int64_t)p.rows[i] : i;
@@ -553,35 +574,78 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(const TIn* H, const TI
   }
 }
 
-// Scored-row selection: one workgroup scans the mask, writes the ascending list of scored rows and
-// their count, and zeroes the outputs of unscored rows.
-__global__ __launch_bounds__(1024) void compact_rows_kernel(const uint8_t* mask, int64_t T, int32_t* rows,
-                                                            int32_t* n_out, float* nats, float* lse) {
-  __shared__ int64_t scan[1024];
-  const int tid = threadIdx.x;
-  const int64_t chunk = (T + 1023) / 1024;
-  const int64_t b = (int64_t)tid * chunk;
-  const int64_t e = (b + chunk < T) ? b + chunk : T;
-  int64_t cnt = 0;
-  for (int64_t t = b; t < e; ++t) cnt += mask[t] != 0;
-  scan[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int64_t v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  int64_t pos = scan[tid] - cnt;
-  for (int64_t t = b; t < e; ++t) {
-    if (mask[t]) {
-      rows[pos++] = (int32_t)t;
-    } else {
-      if (nats) nats[t] = 0.f;
-      if (lse) lse[t] = 0.f;
+// Scored-row selection: one workgroup walks the mask in chunks of 16 KiB, each thread taking 16
+// consecutive rows with one aligned 16-byte load (the next chunk's load is issued before the
+// current chunk is processed). Each thread counts its scored rows; a scan within each wave and the
+// wave totals in wave order give its offset in the ascending list of scored rows, which it then
+// writes. It also writes 0 to nats and lse of all its 16 rows with 16-byte stores: the forward
+// overwrites the scored ones afterwards, in stream order. The count goes to n_out at the end.
+constexpr int kCompactThreads = 1024;
+__global__ __launch_bounds__(kCompactThreads) void compact_rows_kernel(const uint8_t* mask, int64_t T, int32_t* rows,
+                                                                       int32_t* n_out, float* nats, float* lse) {
+  constexpr int kWaves = kCompactThreads / 64;
+  constexpr int64_t kChunk = (int64_t)kCompactThreads * 16;
+  __shared__ int wsum[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // this thread's 16 mask bytes of the chunk at c0 (zero past T)
+  auto load16 = [&](int64_t c0) -> uint4 {
+    const int64_t t0 = c0 + (int64_t)tid * 16;
+    if (t0 + 16 <= T) return *reinterpret_cast<const uint4*>(mask + t0);   // mask and t0 16-byte aligned
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < 16; ++j)
+      if (t0 + j < T) w[j >> 2] |= (uint32_t)mask[t0 + j] << (8 * (j & 3));
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  };
+  int64_t base = 0;   // scored rows before the current chunk (the same in every thread)
+  uint4 cur = T > 0 ? load16(0) : make_uint4(0u, 0u, 0u, 0u);
+  for (int64_t c0 = 0; c0 < T; c0 += kChunk) {
+    const uint4 nxt = c0 + kChunk < T ? load16(c0 + kChunk) : make_uint4(0u, 0u, 0u, 0u);
+    const int64_t t0 = c0 + (int64_t)tid * 16;
+    if (t0 < T && (nats || lse)) {
+      if (t0 + 16 <= T) {
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (nats) reinterpret_cast<float4*>(nats + t0)[q] = z;
+          if (lse) reinterpret_cast<float4*>(lse + t0)[q] = z;
+        }
+      } else {
+        for (int64_t t = t0; t < T; ++t) {
+          if (nats) nats[t] = 0.f;
+          if (lse) lse[t] = 0.f;
+        }
+      }
     }
+    const uint32_t w[4] = {cur.x, cur.y, cur.z, cur.w};
+    uint8_t m[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cnt += m[j] != 0;
+    int x = cnt;   // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      before += w2 < wave ? wsum[w2] : 0;
+      total += wsum[w2];
+    }
+    int64_t pos = base + before + (x - cnt);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (m[j]) rows[pos++] = (int32_t)(t0 + j);   // m[j] is 0 past T
+    base += total;
+    cur = nxt;
+    __syncthreads();   // wsum is rewritten by the next chunk
   }
-  if (tid == 1023) *n_out = (int32_t)scan[1023];
+  if (tid == 0) *n_out = (int32_t)base;
 }
 
 // ------------------------------------------------------------------------------------ host side
@@ -610,7 +674,7 @@ FwdWorkspace fwd_workspace(int64_t T, int32_t D, int32_t V) {
 
 hipError_t launch_compact_rows(const uint8_t* mask, int64_t T, char* ws, const FwdWorkspace& L,
                                float* nats, float* lse, hipStream_t st) {
-  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(1024), 0, st, mask, T,
+  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(kCompactThreads), 0, st, mask, T,
                      reinterpret_cast<int32_t*>(ws + L.rows), reinterpret_cast<int32_t*>(ws + L.n_rows),
                      nats, lse);
   return hipGetLastError();
