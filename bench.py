@@ -291,7 +291,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the data-parallel head needs no exchange until the "
-              "final three-scalar sum, and this build runs on a single MI355X (use --gpus 1).",
+              "final three-scalar sum, and this benchmark measures a single MI355X (use --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
 
