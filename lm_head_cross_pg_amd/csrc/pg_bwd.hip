@@ -407,6 +407,12 @@ __global__ __launch_bounds__(256) void train_prep_kernel(const uint16_t* H, cons
     return;
   }
   const int64_t r = rows ? (int64_t)rows[i] : i;
+  // the row's hidden values go out first, so that their latency overlaps the row factor's loads
+  constexpr int kMaxChunks = 1;   // D <= 512 (the MFMA widths): one 8-element chunk per lane
+  bf16x8 xh[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+    if (lane * 8 + c * 512 < D) xh[c] = *reinterpret_cast<const bf16x8*>(H + r * D + lane * 8 + c * 512);
   const float lse2 = lse[r] * kLog2e;
   float f = g * fexp2(sc.M - lse2) * (-sc.invM * sc.invM);
   // The target element: (p_y - 1) slope_y / (f / g), rounded to bf16. It outweighs the rest of the
@@ -427,11 +433,13 @@ __global__ __launch_bounds__(256) void train_prep_kernel(const uint16_t* H, cons
     }
   }
   if (lane == 0) row_scale[i] = f;
-  for (int d0 = lane * 8; d0 < D; d0 += 512) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(H + r * D + d0);
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int d0 = lane * 8 + c * 512;
+    if (d0 >= D) break;
     bf16x8 o;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (__bf16)(f * (float)x[e]);
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)(f * (float)xh[c][e]);
     *reinterpret_cast<bf16x8*>(hs + i * D + d0) = o;
   }
 }
