@@ -33,19 +33,6 @@ struct TileLayout {
   __device__ static int swz(int row) { return PAD ? 0 : (row / RPB) % SWZ; }
 };
 
-// Hint to interleave one 32-row block's MFMA chain (KS steps: one LDS read + one MFMA each) with
-// the epilogue of the previous block (about 6 VALU / transcendental instructions per logit).
-template <int KS, int VALU_PER_STEP>
-__device__ __forceinline__ void interleave_hint() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // two LDS reads ahead
-#pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read
-    __builtin_amdgcn_sched_group_barrier(0x402, VALU_PER_STEP, 0);  // VALU + transcendental
-  }
-}
-
 // One 16-byte-per-lane LDS DMA (global_load_lds_dwordx4: lane i's 16 bytes land at lds_base + 16 i)
 // issued as assembly. Issued through the builtin, a DMA still in flight makes the compiler wait for
 // every outstanding LDS read (lgkmcnt(0)) before each MFMA operand is used, which cancels the read
@@ -214,30 +201,6 @@ __device__ __forceinline__ void logit_blocks(const lds_char* lds, int buf, int v
     mfma_step<NB, KS>(acc, a, hf, ks);
   }
   mfma_finish<NB>(acc);
-}
-
-// Interleave hint for a chain of KS steps (one LDS read + kTokBlocks MFMAs each) overlapped with
-// VALU_TOTAL VALU / transcendental instructions of an epilogue.
-template <int KS, int VALU_TOTAL>
-__device__ __forceinline__ void interleave_hint2() {
-  constexpr int per = (VALU_TOTAL + KS - 1) / KS;
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x402, per / 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x402, per - per / 2, 0);
-  }
-}
-
-// Largest |z| of a block, over the whole wave.
-__device__ __forceinline__ float wave_absmax16(const f32x16& acc) {
-  float m = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[r]));
-  return m;
 }
 
 }  // namespace pg
