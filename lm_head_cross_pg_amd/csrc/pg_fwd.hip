@@ -303,9 +303,17 @@ struct FwdCore {
           break;
         }
         case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
-        case 3: q[e] = __builtin_fmaf(z, q[e], -sc.M); break;
+        case 3: q[e] = (ASYM && DZ) ? z * q[e] : __builtin_fmaf(z, q[e], -sc.M); break;
         case 4:
-          if (DZ) w[e] = dz_slope(q[e], ASYM && z < 0.f);
+          if (ASYM && DZ) {
+            // q = s log2 e here; |s| <= min(caps) / 8, so the slope factor can be formed as
+            // (s log2 e)^2 M^2 / M_side^2 - M^2 without cancellation: one select instead of three
+            const float tp = q[e];
+            q[e] = tp - sc.M;
+            w[e] = __builtin_fmaf(tp * (z < 0.f ? sc.dzw_n : 1.f), tp, -sc.M * sc.M);
+          } else if (DZ) {
+            w[e] = dz_slope(q[e], false);
+          }
           q[e] = fexp2(q[e]);
           break;
         case 5:
@@ -394,11 +402,14 @@ void fwd_mfma_kernel(FwdParams p) {
     if (DZ) core.dzblk[tb] = p.dz + (tok[tb] >> 5) * (p.ldz >> 5) * 1024 + lane * 16;
   }
 
-  // ---- target logit (split 0 only). Lanes l and l + 32 hold the two halves of the hidden row of
+  // ---- target logit (one split per wave, below). Lanes l and l + 32 hold the two halves of the hidden row of
   //      token l % 32; each dots its half with the same half of E[y] (bf16 pairs, float32
   //      accumulation, loads in batches of up to 16 x 16 bytes) and the two halves are added.
   float sy[NB] = {};
-  if (split == 0) {
+  // split w % S computes the target logits of wave w (every split when the vocabulary is not
+  // split), so that with several splits this work is shared instead of falling on split 0
+  const bool tgt = (wave % S) == split;
+  if (tgt) {
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) {
       const int y = p.target[grow[tb]];
@@ -480,7 +491,7 @@ void fwd_mfma_kernel(FwdParams p) {
       } else {
         p.part_l[(int64_t)split * n + tok[tb]] = l;
         if (!FIXED) p.part_m[(int64_t)split * n + tok[tb]] = m;
-        if (split == 0) p.s_target[tok[tb]] = sy[tb];
+        if (tgt) p.s_target[tok[tb]] = sy[tb];
       }
     }
   }
