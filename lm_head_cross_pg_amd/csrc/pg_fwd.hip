@@ -659,6 +659,90 @@ __global__ __launch_bounds__(kCompactThreads) void compact_rows_kernel(const uin
   if (tid == 0) *n_out = (int32_t)base;
 }
 
+// Scored-row selection for up to kCompactMultiMaxRows rows, in one launch of one workgroup per
+// 4096-row chunk. Workgroup b writes 0 to nats and lse of its rows (the forward overwrites the
+// scored ones afterwards), counts the scored rows of all chunks before it (rereading the mask
+// there: at most 1 MiB per workgroup, with every load issued at once), then places its own rows
+// with a scan over its threads; the last workgroup writes the count. Each workgroup's sum is
+// exact in integers, so the list is the same as the single-workgroup kernel's.
+constexpr int kCompactMultiThreads = 256;
+constexpr int64_t kCompactMultiChunk = (int64_t)kCompactMultiThreads * 16;
+constexpr int64_t kCompactMultiMaxRows = (int64_t)1 << 20;
+
+// Scored (nonzero) bytes among the four of w.
+__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
+  uint32_t t = w | (w >> 4);
+  t |= t >> 2;
+  t |= t >> 1;
+  return __builtin_popcount(t & 0x01010101u);
+}
+
+__global__ __launch_bounds__(kCompactMultiThreads) void compact_rows_multi_kernel(const uint8_t* mask, int64_t T,
+                                                                                  int32_t* rows, int32_t* n_out,
+                                                                                  float* nats, float* lse) {
+  constexpr int kWaves = kCompactMultiThreads / 64;
+  __shared__ int wsum[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kCompactMultiChunk;
+  const int64_t t0 = c0 + (int64_t)tid * 16;
+  // this thread's 16 rows: mask bytes (0 past T), and zeros for nats and lse
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (t0 + 16 <= T) {   // the mask is 16-byte aligned and t0 a multiple of 16
+    const uint4 v = *reinterpret_cast<const uint4*>(mask + t0);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else {
+    for (int j = 0; j < 16; ++j)
+      if (t0 + j < T) w[j >> 2] |= (uint32_t)mask[t0 + j] << (8 * (j & 3));
+  }
+  if (t0 < T && (nats || lse)) {
+    if (t0 + 16 <= T) {
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (nats) reinterpret_cast<float4*>(nats + t0)[q] = z;
+        if (lse) reinterpret_cast<float4*>(lse + t0)[q] = z;
+      }
+    } else {
+      for (int64_t t = t0; t < T; ++t) {
+        if (nats) nats[t] = 0.f;
+        if (lse) lse[t] = 0.f;
+      }
+    }
+  }
+  // scored rows before this chunk: the mask bytes of [0, c0), whole 16-byte pieces
+  int before_chunk = 0;
+  for (int64_t o = (int64_t)tid * 16; o < c0; o += kCompactMultiChunk) {
+    const uint4 v = *reinterpret_cast<const uint4*>(mask + o);
+    before_chunk += nonzero_bytes(v.x) + nonzero_bytes(v.y) + nonzero_bytes(v.z) + nonzero_bytes(v.w);
+  }
+  const int cnt = nonzero_bytes(w[0]) + nonzero_bytes(w[1]) + nonzero_bytes(w[2]) + nonzero_bytes(w[3]);
+  // inclusive scan of cnt over the wave; the wave sum of before_chunk rides along
+  int x = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) before_chunk += __shfl_xor(before_chunk, off);
+  __shared__ int bsum[kWaves];
+  if (lane == 63) wsum[wave] = x;
+  if (lane == 0) bsum[wave] = before_chunk;
+  __syncthreads();
+  int base = 0, before = 0, total = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    base += bsum[v];
+    before += v < wave ? wsum[v] : 0;
+    total += wsum[v];
+  }
+  int64_t pos = (int64_t)base + before + (x - cnt);
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if ((w[j >> 2] >> (8 * (j & 3))) & 0xffu) rows[pos++] = (int32_t)(t0 + j);
+  if (blockIdx.x == gridDim.x - 1 && tid == 0) *n_out = base + total;
+}
+
 // ------------------------------------------------------------------------------------ host side
 
 int64_t fwd_partial_entries(int64_t T) {
@@ -685,9 +769,15 @@ FwdWorkspace fwd_workspace(int64_t T, int32_t D, int32_t V) {
 
 hipError_t launch_compact_rows(const uint8_t* mask, int64_t T, char* ws, const FwdWorkspace& L,
                                float* nats, float* lse, hipStream_t st) {
-  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(kCompactThreads), 0, st, mask, T,
-                     reinterpret_cast<int32_t*>(ws + L.rows), reinterpret_cast<int32_t*>(ws + L.n_rows),
-                     nats, lse);
+  int32_t* rows = reinterpret_cast<int32_t*>(ws + L.rows);
+  int32_t* n_out = reinterpret_cast<int32_t*>(ws + L.n_rows);
+  if (T > 0 && T <= kCompactMultiMaxRows) {
+    const unsigned blocks = (unsigned)((T + kCompactMultiChunk - 1) / kCompactMultiChunk);
+    hipLaunchKernelGGL(compact_rows_multi_kernel, dim3(blocks), dim3(kCompactMultiThreads), 0, st, mask, T, rows,
+                       n_out, nats, lse);
+  } else {
+    hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(kCompactThreads), 0, st, mask, T, rows, n_out, nats, lse);
+  }
   return hipGetLastError();
 }
 

@@ -134,6 +134,14 @@ def test_random_masks_ragged(T):
     run(inp, mask=np.ones(T, np.uint8))
 
 
+def test_random_mask_beyond_multi_workgroup_selection():
+    """T = 1,100,000 rows (past the 2^20 rows that the multi-workgroup scored-row selection takes;
+    the single-workgroup kernel runs) with a random mask of density 0.3, at D = 32, V = 128."""
+    T = 1_100_000
+    inp = synth.make_inputs(workload("fwd_v1024", T=T, D=32, V=128, stream=121), 0)
+    run(inp, mask=(np.random.default_rng(5).random(T) < 0.3).astype(np.uint8))
+
+
 def test_masked_stride64_full_size():
     run(synth.make_inputs("masked_stride64", 0))
 
