@@ -123,15 +123,19 @@ def test_masked_stride64_small(seed):
     run(synth.make_inputs("masked_stride64", seed, T=8192))
 
 
-@pytest.mark.parametrize("T", [1, 15, 16, 17, 16383, 16384, 16385, 50001])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 4095, 4097, 16383, 16384, 16385, 50001])
 def test_random_masks_ragged(T):
-    """Scored-row selection over ragged lengths around its 16-row and 16 Ki-row steps: random masks
-    of density 0.3, and all-ones; unscored rows must come out 0, scored rows as the oracle's."""
+    """Scored-row selection over ragged lengths around its 16-row, 4096-row and 16 Ki-row steps:
+    random masks of density 0.3, all-ones, and masks of arbitrary nonzero bytes; unscored rows
+    must come out 0, scored rows as the oracle's."""
     w = workload("fwd_v1024", T=T, D=64, V=512, stream=120)
     inp = synth.make_inputs(w, 0)
     rng = np.random.default_rng(T)
     run(inp, mask=(rng.random(T) < 0.3).astype(np.uint8))
     run(inp, mask=np.ones(T, np.uint8))
+    # any nonzero byte marks a scored row
+    vals = np.array([0, 0, 0, 1, 2, 127, 128, 255], np.uint8)
+    run(inp, mask=vals[rng.integers(0, len(vals), T)])
 
 
 def test_random_mask_beyond_multi_workgroup_selection():
