@@ -226,6 +226,98 @@ def other_configs(abi, synth, args):
     print(json.dumps({"other_configs": res, "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
+def summarize_trace(d):
+    """profiles/kernels_fwd_bwd_T65536_D512_V8192.md from a profiling directory: per-kernel trace
+    statistics (d/trace, from `rocprofv3 --kernel-trace --stats ... -- python3 bench.py --no-cpu`),
+    the run of event-timed main-forward launches, and per-kernel counters of the training step
+    (d/cnt/train_mfma)."""
+    import collections
+    import csv
+    stats = list(csv.DictReader(open(os.path.join(d, "trace", "run_kernel_stats.csv"))))
+    main_kernel = "void pg::" + FWD_KERNEL + ">"
+    lines = ["# Kernel time, bench step + training step (T=65536, D=512, V=8192, bf16, softcap 30)", "",
+             "rocprofv3 `--kernel-trace --stats` of the benchmark: per kernel, the number of launches and the",
+             f"average / min / max duration. The main forward (`{FWD_KERNEL}>`) runs in the",
+             "bench steps, the event-timed launches, the quantised-head launches and the training steps; the",
+             "asymmetric-cap forward (`<512, true, 1, true, false>`) is a kernel of its own; the dZ-writing",
+             "forwards (`..., false, true>`, and `..., true, true>` for asymmetric caps) and the backward kernels",
+             "run once per training step. The kernels run back to back, so the clock falls under the sustained",
+             "load: compare the min column with isolated launches.", "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:72]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    # bench.py's order: the sustained forward + BPB loop, then the roofline loop of --steps forward
+    # launches with events between them, then the asymmetric-cap and large-logit runs. The event-timed
+    # launches are the first run of consecutive main-forward launches.
+    tr = sorted(csv.DictReader(open(os.path.join(d, "trace", "run_kernel_trace.csv"))),
+                key=lambda r: int(r["Start_Timestamp"]))
+    runs, cur = [], []
+    for r in tr:
+        if r["Kernel_Name"].startswith(main_kernel):
+            cur.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        else:
+            if len(cur) >= 5:
+                runs.append(cur)
+            cur = []
+    if len(cur) >= 5:
+        runs.append(cur)
+    if runs:
+        first = runs[0]
+        lines += ["", f"The roofline figure of `bench.py` times the main forward alone, {len(first)} launches back "
+                      "to back", "with HIP events between them (the first run of consecutive main-forward launches "
+                      "in this trace, taken", "on the same command as the benchmark line minus its CPU baseline):",
+                  f"mean {sum(first) / len(first):.1f} us, min {min(first):.1f}, max {max(first):.1f}."]
+        if len(runs) > 1:
+            big = runs[1]
+            lines += [f"The next run ({len(big)} launches, warmup included) is the large-logit forward (hidden x 8):",
+                      f"mean {sum(big) / len(big):.1f} us, min {min(big):.1f}, max {max(big):.1f}."]
+    lines += ["", "Commands (cd /tmp first; R = repository root; summarised by "
+                  "`python3 bench.py --summarize-trace <dir>`):", "", "```",
+              "rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- python3 $R/bench.py --no-cpu",
+              "```", ""]
+    rows = []
+    for root, _, files in os.walk(os.path.join(d, "cnt", "train_mfma")):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                rows += list(csv.DictReader(open(os.path.join(root, f))))
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(list)
+    for r in rows:
+        k, c = r["Kernel_Name"], r["Counter_Name"]
+        per[k][c].append(float(r["Counter_Value"]))
+        if c == "GRBM_GUI_ACTIVE":
+            dur[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines += ["## Counters per kernel (training step)", "",
+              "From `rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU "
+              "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT --output-format csv -d <dir>/train_mfma -- python3 $R/bench.py "
+              "--steps 3 --warmup 1 --no-cpu`.",
+              "Per kernel, the mean over its launches. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 "
+              "XCDs x 1024 SIMDs);",
+              "clock = GRBM_GUI_ACTIVE / 8 / duration. The MFMA kernels each execute 2·T·D·V = 5.5e11 bf16 MFMA FLOP",
+              "(SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512).", "",
+              "| kernel | launches | duration us | MFMA busy | clock GHz | MFMA FLOP | VALU instr | LDS instr | "
+              "LDS bank conflicts |",
+              "|---|---|---|---|---|---|---|---|---|"]
+
+    def mean(v):
+        return sum(v) / len(v) if v else float("nan")
+    for k in sorted(per, key=lambda k: -mean(dur[k])):
+        mops = mean(per[k]["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
+        if not mops > 0:
+            continue
+        dk, cyc = mean(dur[k]), mean(per[k]["GRBM_GUI_ACTIVE"]) / 8.0
+        busy = mean(per[k]["SQ_VALU_MFMA_BUSY_CYCLES"])
+        nm = k.split("(")[0].replace("void ", "").replace("pg::", "")
+        lines.append(f"| `{nm}` | {len(dur[k])} | {dk / 1e3:.0f} | {100 * busy / (cyc * 1024):.1f} % | {cyc / dk:.2f} | "
+                     f"{mops * 512:.3g} | {mean(per[k]['SQ_INSTS_VALU']):.3g} | {mean(per[k]['SQ_INSTS_LDS']):.3g} | "
+                     f"{mean(per[k]['SQ_LDS_BANK_CONFLICT']):.0f} |")
+    out = os.path.join(ROOT, "profiles", "kernels_fwd_bwd_T65536_D512_V8192.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 def library_gemm(steps):
     """The vendor GEMM (torch.mm, hipBLASLt on this stack) on the products of the head at T = 65536,
     D = 512, V = 8192, bf16 in: the logits H E^T (written out, T x V bf16), dZ E (T x D) and
@@ -283,11 +375,17 @@ def main():
                     help="only time forward + bits per byte on the smaller workloads (their own JSON line)")
     ap.add_argument("--library-gemm", action="store_true",
                     help="only time the vendor GEMM (torch.mm on hipBLASLt) on the head's three product shapes")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="summarise a rocprofv3 kernel trace (DIR/trace) and the training counter run "
+                         "(DIR/cnt/train_mfma) into profiles/ and exit")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="summarise rocprofv3 counter runs under DIR into profiles/ and exit")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the data-parallel head needs no exchange until the "
