@@ -28,7 +28,11 @@
  *   - Arguments are validated on the host before anything is launched; a non-zero status means
  *     nothing was enqueued. Data errors found on the device (a target outside [0, V) on a scored
  *     row, NaN/Inf inputs) are not reported as codes: they turn the affected nats into NaN, which
- *     propagates into the bits-per-byte.
+ *     propagates into the bits-per-byte, and in the backward into that row of dhidden and, since
+ *     every entry of dembed sums over the rows, into all of dembed (the loss itself is NaN then).
+ *   - nats >= 0 on every scored row: the target's logit is taken from the same accumulation that
+ *     forms the log-sum-exp, so p(target) <= 1 holds in floating point too (a one-entry vocabulary
+ *     gives exactly 0).
  *   - Unscored rows (score_mask[t] == 0) get nats = lse = 0, zero dH rows, and add nothing to any
  *     sum. A NULL score_mask scores every row.
  */
@@ -59,9 +63,13 @@ enum {
 enum { PG_DTYPE_BF16 = 0, PG_DTYPE_F32 = 1 }; /* dtype of H and E (they share one) */
 enum { PG_OP_FWD = 0, PG_OP_BWD = 1, PG_OP_BPB = 2, PG_OP_FWD_Q8 = 3, PG_OP_FWD_BWD = 4 };
 
-/* Largest supported sizes: T rows up to 2^31 - 1 (each row index fits an int32), V and D up to
- * 2^20. bf16 with D in {32, 64, 128, 256, 512} runs the MFMA kernels; any other D, and f32 inputs,
- * run a plain vector kernel with the same results up to rounding. */
+/* Largest supported sizes: T rows up to 2^31 - 256 (each row index fits an int32, and one launch
+ * of 512-thread workgroups over 256-row tiles stays within 2^32 - 1 work items), V and D up to
+ * 2^20. The backward entry points on the MFMA path also need their dhidden product's grid of
+ * 256 x 256 output tiles to fit one launch: T < 2^30 at D = 512, T < 2^31 - 256 at D <= 256.
+ * Beyond these, PG_ERR_SHAPE (and pg_workspace_bytes returns 0). bf16 with D in
+ * {32, 64, 128, 256, 512} runs the MFMA kernels; any other D, and f32 inputs, run a plain vector
+ * kernel with the same results up to rounding. */
 
 /*
  * Forward: per-row softcapped cross-entropy, without ever writing the T x V logits to memory.

@@ -91,19 +91,79 @@ def workspace_bytes(op: int, T: int, D: int, V: int) -> int:
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
-    if t is None:
-        return None
-    if not t.is_contiguous():
-        raise ValueError("tensor must be contiguous")
-    return t.data_ptr()
+    return None if t is None else t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.uint16, torch.int16)
+_MASK = (torch.uint8, torch.bool)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype in (torch.bfloat16, torch.uint16, torch.int16):
+    if t.dtype in _BF16:
         return PG_DTYPE_BF16
     if t.dtype == torch.float32:
         return PG_DTYPE_F32
     raise ValueError(f"unsupported dtype {t.dtype} (bf16 or float32)")
+
+
+class _Args:
+    """Checks of the tensors of one call, made before the library is touched: dtype, element count
+    and layout of each tensor first, then that every one of them lives on one CUDA (HIP) device. The
+    C ABI takes bare pointers and sizes, so a wrong shape or dtype would otherwise reach the kernels
+    as out-of-bounds accesses or silently misread data."""
+
+    def __init__(self, where: str):
+        self.where = where
+        self.seen = []
+
+    def __call__(self, t, name, dtypes, numel=None, shape=None, min_numel=None, optional=False):
+        if t is None:
+            if optional:
+                return None
+            raise ValueError(f"{self.where}: {name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.where}: {name} must be a torch.Tensor, got {type(t).__name__}")
+        if t.dtype not in dtypes:
+            raise ValueError(f"{self.where}: {name} has dtype {t.dtype}; expected one of "
+                             f"{', '.join(str(d) for d in dtypes)}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{self.where}: {name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+        if numel is not None and t.numel() != numel:
+            raise ValueError(f"{self.where}: {name} has {t.numel()} elements; expected {numel}")
+        if min_numel is not None and t.numel() < min_numel:
+            raise ValueError(f"{self.where}: {name} has {t.numel()} elements; at least {min_numel} needed")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.where}: {name} must be contiguous")
+        self.seen.append((name, t))
+        return t
+
+    def same_device(self):
+        dev = None
+        for name, t in self.seen:
+            if t.device.type != "cuda":
+                raise ValueError(f"{self.where}: {name} is on {t.device}; every tensor must be on a CUDA (HIP) device")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{self.where}: {name} is on {t.device}, other tensors on {dev}")
+
+
+def _matrix(a: _Args, t, name, dtypes):
+    a(t, name, dtypes)
+    if t.dim() != 2:
+        raise ValueError(f"{a.where}: {name} must be 2-D, got shape {tuple(t.shape)}")
+    return t.shape
+
+
+def _head(a: _Args, hidden, embed, target, score_mask, hidden_dtypes=_BF16 + (torch.float32,)):
+    """hidden [T, D] and embed [V, D] of one dtype, target int32 [T], score_mask uint8/bool [T]."""
+    T, D = _matrix(a, hidden, "hidden", hidden_dtypes)
+    V, De = _matrix(a, embed, "embed", _BF16 if hidden.dtype in _BF16 else (torch.float32,))
+    if De != D:
+        raise ValueError(f"{a.where}: embed has {De} columns, hidden {D}")
+    a(target, "target", (torch.int32,), numel=T)
+    a(score_mask, "score_mask", _MASK, numel=T, optional=True)
+    return T, D, V
 
 
 def _stream(stream) -> Optional[int]:
@@ -114,9 +174,12 @@ def _stream(stream) -> Optional[int]:
     return None
 
 
-def _workspace(op: int, T: int, D: int, V: int, ref: torch.Tensor, workspace):
+def _workspace(a: _Args, op: int, T: int, D: int, V: int, ref: torch.Tensor, workspace):
     if workspace is not None:
+        a(workspace, "workspace", (torch.uint8, torch.int8))
+        a.same_device()
         return workspace
+    a.same_device()
     return torch.empty(max(workspace_bytes(op, T, D, V), 256), dtype=torch.uint8, device=ref.device)
 
 
@@ -129,22 +192,31 @@ def pg_lmhead_ce_fwd(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Te
                      score_mask: Optional[torch.Tensor], softcap: float,
                      nats: torch.Tensor, lse: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    T, D = hidden.shape
-    V = embed.shape[0]
-    ws = _workspace(PG_OP_FWD, T, D, V, embed, workspace)
+    a = _Args("pg_lmhead_ce_fwd")
+    T, D, V = _head(a, hidden, embed, target, score_mask)
+    a(nats, "nats", (torch.float32,), numel=T)
+    a(lse, "lse", (torch.float32,), numel=T, optional=True)
+    ws = _workspace(a, PG_OP_FWD, T, D, V, embed, workspace)
     st = load().pg_lmhead_ce_fwd(_ptr(hidden), _ptr(embed), _dtype_code(hidden), _ptr(target), _ptr(score_mask),
                                  T, D, V, float(softcap), _ptr(nats), _ptr(lse), _ptr(ws), ws.numel(),
                                  _stream(stream))
     _check(st, "pg_lmhead_ce_fwd")
 
 
+def _bwd_outputs(a: _Args, T, D, V, dhidden, dembed):
+    a(dhidden, "dhidden", (torch.float32,), numel=T * D)
+    a(dembed, "dembed", (torch.float32,), numel=V * D)
+
+
 def pg_lmhead_ce_bwd(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Tensor,
                      score_mask: Optional[torch.Tensor], lse: torch.Tensor, softcap: float,
                      grad_scale: float, dhidden: torch.Tensor, dembed: torch.Tensor,
                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    T, D = hidden.shape
-    V = embed.shape[0]
-    ws = _workspace(PG_OP_BWD, T, D, V, embed, workspace)
+    a = _Args("pg_lmhead_ce_bwd")
+    T, D, V = _head(a, hidden, embed, target, score_mask)
+    a(lse, "lse", (torch.float32,), numel=T)
+    _bwd_outputs(a, T, D, V, dhidden, dembed)
+    ws = _workspace(a, PG_OP_BWD, T, D, V, embed, workspace)
     st = load().pg_lmhead_ce_bwd(_ptr(hidden), _ptr(embed), _dtype_code(hidden), _ptr(target), _ptr(score_mask),
                                  _ptr(lse), T, D, V, float(softcap), float(grad_scale), _ptr(dhidden),
                                  _ptr(dembed), _ptr(ws), ws.numel(), _stream(stream))
@@ -155,9 +227,12 @@ def pg_lmhead_ce_fwd_bwd(hidden: torch.Tensor, embed: torch.Tensor, target: torc
                          score_mask: Optional[torch.Tensor], softcap: float, grad_scale: float,
                          nats: torch.Tensor, lse: torch.Tensor, dhidden: torch.Tensor, dembed: torch.Tensor,
                          workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    T, D = hidden.shape
-    V = embed.shape[0]
-    ws = _workspace(PG_OP_FWD_BWD, T, D, V, embed, workspace)
+    a = _Args("pg_lmhead_ce_fwd_bwd")
+    T, D, V = _head(a, hidden, embed, target, score_mask)
+    a(nats, "nats", (torch.float32,), numel=T)
+    a(lse, "lse", (torch.float32,), numel=T)
+    _bwd_outputs(a, T, D, V, dhidden, dembed)
+    ws = _workspace(a, PG_OP_FWD_BWD, T, D, V, embed, workspace)
     st = load().pg_lmhead_ce_fwd_bwd(_ptr(hidden), _ptr(embed), _dtype_code(hidden), _ptr(target), _ptr(score_mask),
                                      T, D, V, float(softcap), float(grad_scale), _ptr(nats), _ptr(lse),
                                      _ptr(dhidden), _ptr(dembed), _ptr(ws), ws.numel(), _stream(stream))
@@ -168,9 +243,11 @@ def pg_lmhead_ce_fwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: tor
                           score_mask: Optional[torch.Tensor], cap_pos: float, cap_neg: float,
                           nats: torch.Tensor, lse: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    T, D = hidden.shape
-    V = embed.shape[0]
-    ws = _workspace(PG_OP_FWD, T, D, V, embed, workspace)
+    a = _Args("pg_lmhead_ce_fwd_asym")
+    T, D, V = _head(a, hidden, embed, target, score_mask)
+    a(nats, "nats", (torch.float32,), numel=T)
+    a(lse, "lse", (torch.float32,), numel=T, optional=True)
+    ws = _workspace(a, PG_OP_FWD, T, D, V, embed, workspace)
     st = load().pg_lmhead_ce_fwd_asym(_ptr(hidden), _ptr(embed), _dtype_code(hidden), _ptr(target),
                                       _ptr(score_mask), T, D, V, float(cap_pos), float(cap_neg), _ptr(nats),
                                       _ptr(lse), _ptr(ws), ws.numel(), _stream(stream))
@@ -181,9 +258,11 @@ def pg_lmhead_ce_bwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: tor
                           score_mask: Optional[torch.Tensor], lse: torch.Tensor, cap_pos: float, cap_neg: float,
                           grad_scale: float, dhidden: torch.Tensor, dembed: torch.Tensor,
                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    T, D = hidden.shape
-    V = embed.shape[0]
-    ws = _workspace(PG_OP_BWD, T, D, V, embed, workspace)
+    a = _Args("pg_lmhead_ce_bwd_asym")
+    T, D, V = _head(a, hidden, embed, target, score_mask)
+    a(lse, "lse", (torch.float32,), numel=T)
+    _bwd_outputs(a, T, D, V, dhidden, dembed)
+    ws = _workspace(a, PG_OP_BWD, T, D, V, embed, workspace)
     st = load().pg_lmhead_ce_bwd_asym(_ptr(hidden), _ptr(embed), _dtype_code(hidden), _ptr(target),
                                       _ptr(score_mask), _ptr(lse), T, D, V, float(cap_pos), float(cap_neg),
                                       float(grad_scale), _ptr(dhidden), _ptr(dembed), _ptr(ws), ws.numel(),
@@ -195,9 +274,12 @@ def pg_lmhead_ce_fwd_bwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target:
                               score_mask: Optional[torch.Tensor], cap_pos: float, cap_neg: float, grad_scale: float,
                               nats: torch.Tensor, lse: torch.Tensor, dhidden: torch.Tensor, dembed: torch.Tensor,
                               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    T, D = hidden.shape
-    V = embed.shape[0]
-    ws = _workspace(PG_OP_FWD_BWD, T, D, V, embed, workspace)
+    a = _Args("pg_lmhead_ce_fwd_bwd_asym")
+    T, D, V = _head(a, hidden, embed, target, score_mask)
+    a(nats, "nats", (torch.float32,), numel=T)
+    a(lse, "lse", (torch.float32,), numel=T)
+    _bwd_outputs(a, T, D, V, dhidden, dembed)
+    ws = _workspace(a, PG_OP_FWD_BWD, T, D, V, embed, workspace)
     st = load().pg_lmhead_ce_fwd_bwd_asym(_ptr(hidden), _ptr(embed), _dtype_code(hidden), _ptr(target),
                                           _ptr(score_mask), T, D, V, float(cap_pos), float(cap_neg), float(grad_scale),
                                           _ptr(nats), _ptr(lse), _ptr(dhidden), _ptr(dembed), _ptr(ws), ws.numel(),
@@ -206,7 +288,11 @@ def pg_lmhead_ce_fwd_bwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target:
 
 
 def pg_quantize_q8(embed: torch.Tensor, embed_q8: torch.Tensor, embed_scale: torch.Tensor, stream=None) -> None:
-    V, D = embed.shape
+    a = _Args("pg_quantize_q8")
+    V, D = _matrix(a, embed, "embed", _BF16 + (torch.float32,))
+    a(embed_q8, "embed_q8", (torch.int8,), numel=V * D)
+    a(embed_scale, "embed_scale", (torch.float32,), numel=V)
+    a.same_device()
     st = load().pg_quantize_q8(_ptr(embed), _dtype_code(embed), V, D, _ptr(embed_q8), _ptr(embed_scale),
                                _stream(stream))
     _check(st, "pg_quantize_q8")
@@ -216,20 +302,35 @@ def pg_lmhead_ce_fwd_q8(hidden: torch.Tensor, embed_q8: torch.Tensor, embed_scal
                         target: torch.Tensor, score_mask: Optional[torch.Tensor], softcap: float,
                         nats: torch.Tensor, lse: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    T, D = hidden.shape
-    V = embed_q8.shape[0]
-    ws = _workspace(PG_OP_FWD_Q8, T, D, V, embed_q8, workspace)
+    a = _Args("pg_lmhead_ce_fwd_q8")
+    T, D = _matrix(a, hidden, "hidden", _BF16)
+    V, Dq = _matrix(a, embed_q8, "embed_q8", (torch.int8,))
+    if Dq != D:
+        raise ValueError(f"pg_lmhead_ce_fwd_q8: embed_q8 has {Dq} columns, hidden {D}")
+    a(embed_scale, "embed_scale", (torch.float32,), numel=V)
+    a(target, "target", (torch.int32,), numel=T)
+    a(score_mask, "score_mask", _MASK, numel=T, optional=True)
+    a(nats, "nats", (torch.float32,), numel=T)
+    a(lse, "lse", (torch.float32,), numel=T, optional=True)
+    ws = _workspace(a, PG_OP_FWD_Q8, T, D, V, embed_q8, workspace)
     st = load().pg_lmhead_ce_fwd_q8(_ptr(hidden), _ptr(embed_q8), _ptr(embed_scale), _ptr(target),
                                     _ptr(score_mask), T, D, V, float(softcap), _ptr(nats), _ptr(lse), _ptr(ws),
                                     ws.numel(), _stream(stream))
     _check(st, "pg_lmhead_ce_fwd_q8")
 
 
-def pg_bpb_reduce(nats: torch.Tensor, target: torch.Tensor, score_mask: Optional[torch.Tensor],
-                  byte_len: torch.Tensor, byte_per_pos: Optional[torch.Tensor], V: int,
+def pg_bpb_reduce(nats: torch.Tensor, target: Optional[torch.Tensor], score_mask: Optional[torch.Tensor],
+                  byte_len: Optional[torch.Tensor], byte_per_pos: Optional[torch.Tensor], V: int,
                   out: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    T = nats.shape[0]
-    ws = _workspace(PG_OP_BPB, T, 1, V, out, workspace)
+    a = _Args("pg_bpb_reduce")
+    a(nats, "nats", (torch.float32,))
+    T = nats.numel()
+    a(byte_per_pos, "byte_per_pos", (torch.int32,), numel=T, optional=True)
+    a(target, "target", (torch.int32,), numel=T, optional=byte_per_pos is not None)
+    a(byte_len, "byte_len", (torch.int32,), min_numel=int(V), optional=byte_per_pos is not None)
+    a(score_mask, "score_mask", _MASK, numel=T, optional=True)
+    a(out, "out", (torch.float64,), min_numel=4)
+    ws = _workspace(a, PG_OP_BPB, T, 1, V, out, workspace)
     st = load().pg_bpb_reduce(_ptr(nats), _ptr(target), _ptr(score_mask), _ptr(byte_len), _ptr(byte_per_pos),
                               T, int(V), _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "pg_bpb_reduce")

@@ -40,11 +40,21 @@ pg_status device_check(pg::DeviceInfo& info) {
 
 inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
-constexpr int64_t kMaxRows = 2147483647LL;
+// Rows up to 2^31 - 256: every row index fits an int32, and the MFMA kernels' grids of one
+// 512-thread workgroup per 256 rows stay within the 2^32 - 1 work items of a launch.
+constexpr int64_t kMaxRows = 2147483648LL - 256;
 constexpr int32_t kMaxWidth = 1 << 20;
 
 pg_status check_shape(int64_t T, int32_t D, int32_t V) {
   if (T < 0 || T > kMaxRows || D < 1 || D > kMaxWidth || V < 1 || V > kMaxWidth) return PG_ERR_SHAPE;
+  return PG_OK;
+}
+
+// The backward's products on the MFMA path: the dH grid grows with T D (256 x 256 output tiles).
+pg_status check_bwd_shape(int64_t T, int32_t D, int32_t V) {
+  if (!pg::mfma_width(D)) return PG_OK;   // vector kernels: grid-stride loops
+  if (pg::gemm_grid_x(T, D, false) > pg::kMaxGrid512 || pg::gemm_grid_x(V, D, true) > pg::kMaxGrid512)
+    return PG_ERR_SHAPE;
   return PG_OK;
 }
 
@@ -78,9 +88,13 @@ size_t pg_workspace_bytes(int32_t op, int64_t T, int32_t D, int32_t V) {
   if (check_shape(T, D, V) != PG_OK) return 0;
   switch (op) {
     case PG_OP_FWD: return pg::fwd_workspace(T, D, V).total;
-    case PG_OP_BWD: return pg::bwd_workspace(T, D, V).total;
+    case PG_OP_BWD:
+      if (check_bwd_shape(T, D, V) != PG_OK) return 0;
+      return pg::bwd_workspace(T, D, V).total;
     case PG_OP_BPB: return pg::bpb_workspace(T).total;
-    case PG_OP_FWD_BWD: return pg::train_workspace(T, D, V).total;
+    case PG_OP_FWD_BWD:
+      if (check_bwd_shape(T, D, V) != PG_OK) return 0;
+      return pg::train_workspace(T, D, V).total;
     case PG_OP_FWD_Q8:
       if (D % 8 != 0) return 0;
       return pg::align256((size_t)V * (size_t)D * 2) + pg::fwd_workspace(T, D, V).total;
@@ -113,7 +127,7 @@ static pg_status bwd_impl(const void* hidden, const void* embed, int32_t dtype, 
                           float cap_pos, float cap_neg, float grad_scale, float* dhidden, float* dembed,
                           void* workspace, size_t workspace_bytes, void* stream) {
   pg_status s;
-  if ((s = check_shape(T, D, V)) != PG_OK) return s;
+  if ((s = check_shape(T, D, V)) != PG_OK || (s = check_bwd_shape(T, D, V)) != PG_OK) return s;
   if (T > 0 && (!hidden || !target || !lse || !dhidden)) return PG_ERR_NULL;
   if (!embed || !dembed || !workspace) return PG_ERR_NULL;
   if (dtype != PG_DTYPE_BF16 && dtype != PG_DTYPE_F32) return PG_ERR_DTYPE;
@@ -154,7 +168,7 @@ static pg_status train_impl(const void* hidden, const void* embed, int32_t dtype
                             float cap_neg, float grad_scale, float* nats, float* lse, float* dhidden,
                             float* dembed, void* workspace, size_t workspace_bytes, void* stream) {
   pg_status s;
-  if ((s = check_shape(T, D, V)) != PG_OK) return s;
+  if ((s = check_shape(T, D, V)) != PG_OK || (s = check_bwd_shape(T, D, V)) != PG_OK) return s;
   if (T > 0 && (!hidden || !target || !nats || !lse || !dhidden)) return PG_ERR_NULL;
   if (!embed || !dembed || !workspace) return PG_ERR_NULL;
   if (dtype != PG_DTYPE_BF16 && dtype != PG_DTYPE_F32) return PG_ERR_DTYPE;

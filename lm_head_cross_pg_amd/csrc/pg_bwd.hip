@@ -26,22 +26,24 @@ __global__ __launch_bounds__(256) void dz_generic_kernel(const TIn* H, const TIn
                                                          const int32_t* n_dev, int64_t n_host, int D, int V,
                                                          Softcap sc, uint16_t* dz) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t n = n_dev ? (int64_t)(*n_dev) : n_host;
-  if (i >= n) return;
-  const int64_t r = rows ? (int64_t)rows[i] : i;
-  const TIn* hrow = H + r * D;
-  const int y = target[r];
-  const float lse2 = lse[r] * kLog2e;
-  for (int v = lane; v < V; v += 64) {
-    const TIn* erow = E + (int64_t)v * D;
-    float z = 0.f;
-    for (int d = 0; d < D; ++d) z = __builtin_fmaf(bload(hrow, d), bload(erow, d), z);
-    float s2, slope;
-    capped_log2_slope(z, sc, s2, slope);                        // s log2 e, 1 - (s / c)^2
-    const float p = fexp2(s2 - lse2);
-    const float g = (v == y) ? p - 1.0f : p;
-    dz[i * V + v] = f32_to_bf16(g * slope);
+  // one row per wave, grid-stride over the rows
+  for (int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < n; i += (int64_t)gridDim.x * 4) {
+    const int64_t r = rows ? (int64_t)rows[i] : i;
+    const TIn* hrow = H + r * D;
+    const int y = target[r];
+    // a target outside [0, V) poisons the row (NaN nats in the forward): NaN dZ, so NaN dH and dE
+    const float lse2 = (y >= 0 && y < V) ? lse[r] * kLog2e : __builtin_nanf("");
+    for (int v = lane; v < V; v += 64) {
+      const TIn* erow = E + (int64_t)v * D;
+      float z = 0.f;
+      for (int d = 0; d < D; ++d) z = __builtin_fmaf(bload(hrow, d), bload(erow, d), z);
+      float s2, slope;
+      capped_log2_slope(z, sc, s2, slope);                        // s log2 e, 1 - (s / c)^2
+      const float p = fexp2(s2 - lse2);
+      const float g = (v == y) ? p - 1.0f : p;
+      dz[i * V + v] = f32_to_bf16(g * slope);
+    }
   }
 }
 
@@ -51,14 +53,15 @@ __global__ __launch_bounds__(256) void dh_generic_kernel(const uint16_t* dz, con
                                                          const int32_t* n_dev, int64_t n_host, int D, int V,
                                                          float g, float* dH) {
   const int64_t n = n_dev ? (int64_t)(*n_dev) : n_host;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t i = idx / D;
-  const int d = (int)(idx % D);
-  if (i >= n) return;
-  float acc = 0.f;
-  for (int v = 0; v < V; ++v) acc = __builtin_fmaf(bf16_to_f32(dz[i * V + v]), bload(E, (int64_t)v * D + d), acc);
-  const int64_t r = rows ? (int64_t)rows[i] : i;
-  dH[r * D + d] = g * acc;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n * D;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = idx / D;
+    const int d = (int)(idx % D);
+    float acc = 0.f;
+    for (int v = 0; v < V; ++v) acc = __builtin_fmaf(bf16_to_f32(dz[i * V + v]), bload(E, (int64_t)v * D + d), acc);
+    const int64_t r = rows ? (int64_t)rows[i] : i;
+    dH[r * D + d] = g * acc;
+  }
 }
 
 // dE[v, d] = g * sum_i dZ[i, v] H[rows[i], d]: one thread per output (plain vector code).
@@ -67,33 +70,36 @@ __global__ __launch_bounds__(256) void de_generic_kernel(const uint16_t* dz, con
                                                          const int32_t* n_dev, int64_t n_host, int D, int V,
                                                          float g, float* dE) {
   const int64_t n = n_dev ? (int64_t)(*n_dev) : n_host;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t v = idx / D;
-  const int d = (int)(idx % D);
-  if (v >= V) return;
-  float acc = 0.f;
-  for (int64_t i = 0; i < n; ++i) {
-    const int64_t r = rows ? (int64_t)rows[i] : i;
-    acc = __builtin_fmaf(bf16_to_f32(dz[i * V + v]), bload(H, r * D + d), acc);
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < (int64_t)V * D;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t v = idx / D;
+    const int d = (int)(idx % D);
+    float acc = 0.f;
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t r = rows ? (int64_t)rows[i] : i;
+      acc = __builtin_fmaf(bf16_to_f32(dz[i * V + v]), bload(H, r * D + d), acc);
+    }
+    dE[v * D + d] = g * acc;
   }
-  dE[v * D + d] = g * acc;
 }
 
 // Hc[i] = H[rows[i]] for the compacted scored rows (16 bytes per thread).
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* H, const int32_t* rows, const int32_t* n_dev,
                                                           int64_t T, int D, uint16_t* Hc) {
   const int64_t cpr = D / 8;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t i = idx / cpr, c = idx % cpr;
-  if (i >= T || i >= (int64_t)(*n_dev)) return;
-  reinterpret_cast<uint4*>(Hc + i * D)[c] = reinterpret_cast<const uint4*>(H + (int64_t)rows[i] * D)[c];
+  const int64_t n = (int64_t)(*n_dev) < T ? (int64_t)(*n_dev) : T;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n * cpr;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = idx / cpr, c = idx % cpr;
+    reinterpret_cast<uint4*>(Hc + i * D)[c] = reinterpret_cast<const uint4*>(H + (int64_t)rows[i] * D)[c];
+  }
 }
 
 // Zero the dH rows of unscored positions.
 __global__ __launch_bounds__(256) void zero_unscored_kernel(const uint8_t* mask, int64_t T, int D, float* dH) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= T * D) return;
-  if (!mask[idx / D]) dH[idx] = 0.f;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < T * D;
+       idx += (int64_t)gridDim.x * blockDim.x)
+    if (!mask[idx / D]) dH[idx] = 0.f;
 }
 
 // =============================================================================== MFMA path
@@ -142,7 +148,8 @@ struct DzCore {
   int h, col, V;
   Softcap sc;
   bf16x8 hf[NB][KS];
-  float bias[NB];      // -lse * log2 e of this lane's rows (-inf for padding rows)
+  float bias[NB];      // -lse * log2 e of this lane's rows (-inf for padding rows, NaN for a
+                       // target outside [0, V): the row's dZ, and with it dH and dE, become NaN)
   int ytok[NB];        // targets of this lane's rows (never matching for padding rows)
   uint16_t* dzblk[NB]; // this lane's 16 elements of block (token block, vocabulary block 0)
 
@@ -307,7 +314,8 @@ void bwd_dz_kernel(DzParams p) {
   constexpr int kTokPerWave = WaveShape<NB>::kTok;
   constexpr int kFwdWaves = WaveShape<NB>::kWaves;
   __shared__ __attribute__((aligned(1024))) char smem[2 * TL::TILEB];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
   const int h = lane >> 5, col = lane & 31;
   const int64_t n = p.n_dev ? (int64_t)(*p.n_dev) : p.n_host;
   const int rt = blockIdx.x;
@@ -333,8 +341,9 @@ void bwd_dz_kernel(DzParams p) {
     const bf16x8* src = reinterpret_cast<const bf16x8*>(p.H + grow * D + h * (D / 2));
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) core.hf[tb][ks] = src[ks];
-    core.bias[tb] = valid ? -p.lse[grow] * kLog2e : -INFINITY;
-    core.ytok[tb] = valid ? p.target[grow] : -(1 << 30);
+    const int y = p.target[grow];
+    core.bias[tb] = !valid ? -INFINITY : (y >= 0 && y < V) ? -p.lse[grow] * kLog2e : __builtin_nanf("");
+    core.ytok[tb] = valid ? y : -(1 << 30);
     core.dzblk[tb] = p.dz + ((tok >> 5) * (p.ldz >> 5)) * 1024 + lane * 16;
   }
 
@@ -384,15 +393,10 @@ void bwd_dz_kernel(DzParams p) {
 // by it) and the hidden row times f in bf16 (the B operand of dE, whose sum runs over rows). Rows from the last
 // scored row to the end of its 256-row tile are cleared: the forward wrote them from duplicated
 // hidden rows, and the dE sum runs over them.
-__global__ __launch_bounds__(256) void train_prep_kernel(const uint16_t* H, const int32_t* target, const float* nats,
-                                                         const float* lse, const int32_t* rows, const int32_t* n_dev,
-                                                         int64_t n_host, int D, int V, int64_t nvb, Softcap sc,
-                                                         float g, uint16_t* dz, uint16_t* hs, float* row_scale) {
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int64_t n = n_dev ? (int64_t)(*n_dev) : n_host;
-  const int64_t npad = (n + kRowsPerWG - 1) / kRowsPerWG * kRowsPerWG;
-  if (i >= npad) return;
+__device__ __forceinline__ void train_prep_row(int64_t i, int lane, const uint16_t* H, const int32_t* target,
+                                               const float* nats, const float* lse, const int32_t* rows, int64_t n,
+                                               int D, int V, int64_t nvb, const Softcap& sc, float g, uint16_t* dz,
+                                               uint16_t* hs, float* row_scale) {
   uint16_t* zblk = dz + (i >> 5) * nvb * 1024;   // vocabulary block 0 of the row's token block
   const int l0 = (int)(i & 31);                  // the row's two 16-element runs: lanes l0, l0 + 32
   if (i >= n) {
@@ -431,6 +435,8 @@ __global__ __launch_bounds__(256) void train_prep_kernel(const uint16_t* H, cons
       const int L = l0 + 32 * ((y >> 2) & 1);
       zblk[(int64_t)(y >> 5) * 1024 + 16 * L + 4 * ((y & 31) >> 3) + (y & 3)] = __builtin_bit_cast(uint16_t, stored);
     }
+  } else {
+    f = __builtin_nanf("");   // a target outside [0, V) poisons the row: NaN dH row, NaN dE
   }
   if (lane == 0) row_scale[i] = f;
 #pragma unroll
@@ -442,6 +448,18 @@ __global__ __launch_bounds__(256) void train_prep_kernel(const uint16_t* H, cons
     for (int e = 0; e < 8; ++e) o[e] = (__bf16)(f * (float)xh[c][e]);
     *reinterpret_cast<bf16x8*>(hs + i * D + d0) = o;
   }
+}
+
+__global__ __launch_bounds__(256) void train_prep_kernel(const uint16_t* H, const int32_t* target, const float* nats,
+                                                         const float* lse, const int32_t* rows, const int32_t* n_dev,
+                                                         int64_t n_host, int D, int V, int64_t nvb, Softcap sc,
+                                                         float g, uint16_t* dz, uint16_t* hs, float* row_scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n = n_dev ? (int64_t)(*n_dev) : n_host;
+  const int64_t npad = (n + kRowsPerWG - 1) / kRowsPerWG * kRowsPerWG;
+  // one row per wave, grid-stride over the rows up to the end of the last 256-row tile
+  for (int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < npad; i += (int64_t)gridDim.x * 4)
+    train_prep_row(i, lane, H, target, nats, lse, rows, n, D, V, nvb, sc, g, dz, hs, row_scale);
 }
 
 // ------------------------------------------------------------------------------------ host side
@@ -494,8 +512,7 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     if (e != hipSuccess) return e;
     rows = reinterpret_cast<const int32_t*>(ws + L.rows);
     n_dev = reinterpret_cast<const int32_t*>(ws + L.n_rows);
-    const int64_t tot = T * D;
-    hipLaunchKernelGGL(zero_unscored_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, mask, T, D, dH);
+    hipLaunchKernelGGL(zero_unscored_kernel, dim3(stride_blocks(T * D, 256)), dim3(256), 0, st, mask, T, D, dH);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   uint16_t* dz = reinterpret_cast<uint16_t*>(ws + L.dz);
@@ -552,8 +569,7 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     b.B = (const uint16_t*)H; b.ldb = D;
     if (rows) {   // masked: the scored hidden rows, compacted, so that k runs over them directly
       uint16_t* hc = reinterpret_cast<uint16_t*>(ws + L.hc);
-      const int64_t cnt = T * (D / 8);
-      hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, st, (const uint16_t*)H,
+      hipLaunchKernelGGL(gather_rows_kernel, dim3(stride_blocks(T * (D / 8), 256)), dim3(256), 0, st, (const uint16_t*)H,
                          rows, n_dev, T, D, hc);
       if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
       b.B = hc;
@@ -566,9 +582,9 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     if (e != hipSuccess || ks == 1) return e;
     return launch_sum_splits(part, (int)ks, (int64_t)V * D, (int64_t)V * D, dE, st);
   }
-  const unsigned rblocks = (unsigned)((T + 3) / 4);
-  const unsigned hblocks = (unsigned)((T * D + 255) / 256);
-  const unsigned eblocks = (unsigned)(((int64_t)V * D + 255) / 256);
+  const unsigned rblocks = stride_blocks(T, 4);
+  const unsigned hblocks = stride_blocks(T * D, 256);
+  const unsigned eblocks = stride_blocks((int64_t)V * D, 256);
   if (T > 0) {
     if (dtype == 0) {
       hipLaunchKernelGGL(dz_generic_kernel<uint16_t>, dim3(rblocks), dim3(256), 0, st, (const uint16_t*)H,
@@ -621,15 +637,14 @@ hipError_t launch_train(const void* H, const void* E, int32_t dtype, const int32
   const int32_t* rows = mask ? reinterpret_cast<const int32_t*>(ws + W.fwd + F.rows) : nullptr;
   const int32_t* n_dev = mask ? reinterpret_cast<const int32_t*>(ws + W.fwd + F.n_rows) : nullptr;
   if (mask) {
-    const int64_t tot = T * D;
-    hipLaunchKernelGGL(zero_unscored_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, mask, T, D, dH);
+    hipLaunchKernelGGL(zero_unscored_kernel, dim3(stride_blocks(T * D, 256)), dim3(256), 0, st, mask, T, D, dH);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t ldz = (int64_t)((V + kVocabTile - 1) / kVocabTile) * kVocabTile;
   const int64_t rblk = (T + kRowsPerWG - 1) / kRowsPerWG;
   uint16_t* hs = reinterpret_cast<uint16_t*>(ws + W.bwd + L.hc);
   float* row_scale = reinterpret_cast<float*>(ws + W.row_scale);
-  hipLaunchKernelGGL(train_prep_kernel, dim3((unsigned)(rblk * kRowsPerWG / 4)), dim3(256), 0, st,
+  hipLaunchKernelGGL(train_prep_kernel, dim3(stride_blocks(rblk * kRowsPerWG, 4)), dim3(256), 0, st,
                      (const uint16_t*)H, target, nats, lse, rows, n_dev, T, D, V, ldz / 32, sc, grad_scale, dz, hs,
                      row_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -67,8 +67,8 @@ constexpr int kPrefetch = 2;
 // 32-token MFMA column blocks per wave in the forward (see WaveShape).
 constexpr int kFwdTokBlocks = PG_FWD_TOK_BLOCKS;
 
-// ASYM: separate caps for z >= 0 and z < 0 (the epilogue takes the exact form only); a template
-// parameter so that it compiles to a kernel of its own.
+// ASYM: separate caps for z >= 0 and z < 0, each side with its own constants in both epilogue
+// forms; a template parameter so that it compiles to a kernel of its own.
 // DZ (fixed shift, one cap): the epilogue also stores, for every logit, the unnormalised gradient
 //   d = 2^t t (t - K),  t = s log2 e - M  (the exponent it sums),  K = -2 M,
 // in the dZ block layout. Since s / c = 1 + t / M, the softcap's slope is 1 - (s / c)^2 =
@@ -91,7 +91,47 @@ struct FwdCore {
   float lsum[NB];
   float mrun[NB];
   int exact_left;   // blocks still to take the exact form before the series is tried again (uniform)
-  uint16_t* dzblk[NB];   // DZ: this lane's 16 elements of block (its token block, vocabulary block 0)
+  uint16_t* dzblk[NB];   // DZ: block (its token block, vocabulary block 0); wave-uniform
+  int dzlane;            // DZ: this lane's 16 elements in a block (element offset lane * 16)
+  // The target logit is taken from the accumulators the log-sum-exp sums, so that the two share
+  // every rounding: ykey is the target id when this lane holds its logit (lane half h holds rows
+  // with ((v >> 2) & 1) == h of every 32-row block), else -1. ty is, with the fixed shift, the very
+  // term 2^t that the exp-sum added for the target (-1 until found); with a running maximum, the
+  // target's s log2 e (-inf until found).
+  int ykey[NB];
+  float ty[NB];
+
+  // The term 2^t the exp-sum adds for logit z in each form: the operations of the pipelined stages
+  // below (and of part_exact), in the same order, so the value is the one that was summed.
+  __device__ __forceinline__ float term_exact(float z) const { return fexp2(capped_shifted_sc(z, sc)); }
+  __device__ __forceinline__ float term_series(float z) const {
+    const bool neg = ASYM && z < 0.f;
+    const float u = z * z;
+    float q = __builtin_fmaf(neg ? sc.q2n : sc.q2, u, neg ? sc.q1n : sc.q1);
+    q = __builtin_fmaf(q, u, sc.q0);
+    return fexp2(__builtin_fmaf(z, q, -sc.M));
+  }
+
+  // After the epilogue of the block at vbase: a lane holding its target's logit there keeps the
+  // target's term (FIXED; `series` says which form the sum took) or s log2 e (running maximum).
+  // Wave-uniform branch: only blocks that hold some lane's target pay for the select.
+  __device__ __forceinline__ void take_target(const f32x16 (&acc)[NB], int vbase, bool series) {
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) {
+      const bool hit = (ykey[tb] >> 5) == (vbase >> 5);
+      if (__any(hit)) {
+        const int y = ykey[tb] & 31;
+        const int ri = 4 * (y >> 3) + (y & 3);     // accumulator register of row y of the block
+        float z = acc[tb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) z = ri == r ? acc[tb][r] : z;
+        if (hit) {
+          if (!FIXED) ty[tb] = capped_log2(z, sc);
+          else ty[tb] = series ? term_series(z) : term_exact(z);
+        }
+      }
+    }
+  }
 
   // DZ: eight values of this lane (accumulator registers 8 j8 .. 8 j8 + 7 of the block whose
   // vocabulary rows start at vbase) as one 16-byte store into the block layout.
@@ -99,7 +139,7 @@ struct FwdCore {
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (__bf16)vals[e];
-    *reinterpret_cast<bf16x8*>(dzblk[tb] + (int64_t)(vbase >> 5) * 1024 + 8 * j8) = o;
+    *reinterpret_cast<bf16x8*>(dzblk[tb] + (int64_t)(vbase >> 5) * 1024 + dzlane + 8 * j8) = o;
   }
 
   // DZ: the slope factor of the stored gradient from the exponent t = s log2 e - M: t (t - K) for
@@ -246,8 +286,9 @@ struct FwdCore {
   // After a series miss the exact form runs for kExactRun blocks, then the series is tried again, so
   // inputs whose logits are mostly large pay the speculation once per kExactRun blocks.
   static constexpr int kExactRun = 16;
+  // Returns true when the sums of `prev` came from the series (take_target needs the form).
   template <bool LOAD>
-  __device__ __forceinline__ void chain_with_epilogue(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
+  __device__ __forceinline__ bool chain_with_epilogue(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
                                                       int vprev, int load_tile = 0, int load_buf = 0) {
     constexpr int NE = NB * 16;
     if (!FIXED) {   // running maximum (c = 0 or caps above the fixed-shift range)
@@ -258,7 +299,7 @@ struct FwdCore {
       tile_stage_priority(vb, true);
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) online<false>(prev[tb], vprev, tb);
-      return;
+      return false;
     }
     float part[NB] = {};
     float q[NE];
@@ -290,7 +331,7 @@ struct FwdCore {
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) lsum[tb] += part[tb];
       if (exact_left > 0) --exact_left;
-      return;
+      return false;
     }
     float u[NE];
     float amax = 0.f;
@@ -303,13 +344,15 @@ struct FwdCore {
           break;
         }
         case 2: q[e] = __builtin_fmaf(q[e], u[e], sc.q0); break;
-        case 3: q[e] = (ASYM && DZ) ? z * q[e] : __builtin_fmaf(z, q[e], -sc.M); break;
+        case 3:
+          if (ASYM && DZ) w[e] = z * q[e];                       // s log2 e
+          q[e] = __builtin_fmaf(z, q[e], -sc.M);                 // t (the form term_series repeats)
+          break;
         case 4:
           if (ASYM && DZ) {
-            // q = s log2 e here; |s| <= min(caps) / 8, so the slope factor can be formed as
+            // w = s log2 e here; |s| <= min(caps) / 8, so the slope factor can be formed as
             // (s log2 e)^2 M^2 / M_side^2 - M^2 without cancellation: one select instead of three
-            const float tp = q[e];
-            q[e] = tp - sc.M;
+            const float tp = w[e];
             w[e] = __builtin_fmaf(tp * (z < 0.f ? sc.dzw_n : 1.f), tp, -sc.M * sc.M);
           } else if (DZ) {
             w[e] = dz_slope(q[e], false);
@@ -327,7 +370,8 @@ struct FwdCore {
     });
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) asm volatile("" ::"v"(part[tb]));   // keep the speculation in the pipeline
-    if (!__all(amax <= sc.thr)) {   // the exact sums replace the series; DZ stores again
+    const bool series = __all(amax <= sc.thr);
+    if (!series) {   // the exact sums replace the series; DZ stores again
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) {
         part[tb] = part_exact<false>(prev[tb], vprev);
@@ -337,15 +381,9 @@ struct FwdCore {
     }
 #pragma unroll
     for (int tb = 0; tb < NB; ++tb) lsum[tb] += part[tb];
+    return series;
   }
 };
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-// Elements 2 j and 2 j + 1 of v.
-__device__ __forceinline__ bf16x2 bf16_pair(const bf16x8& v, int j) {
-  bf16x2 r = {v[2 * j], v[2 * j + 1]};
-  return r;
-}
 
 template <int D, bool FIXED, int NB, bool ASYM, bool DZ = false>
 __global__ __launch_bounds__(WaveShape<NB>::kThreads) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
@@ -356,7 +394,8 @@ void fwd_mfma_kernel(FwdParams p) {
   constexpr int kFwdWaves = WaveShape<NB>::kWaves;
   __shared__ __attribute__((aligned(1024))) char smem[2 * TL::TILEB];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar addressing
   const int h = lane >> 5, col = lane & 31;
 
   const int64_t n = p.n_dev ? (int64_t)(*p.n_dev) : p.n_host;
@@ -388,50 +427,30 @@ void fwd_mfma_kernel(FwdParams p) {
   if (ntiles > 0) load_embed_tile<D, kFwdWaves>(smem, p.E, V, t_begin, 0, wave, lane);
 
   // ---- this lane's tokens: hidden row halves into registers (B operands of the MFMA)
-  int64_t tok[NB], grow[NB];
+  // (token and row indices are recomputed after the main loop, so that they hold no registers)
+  auto token = [&](int tb) -> int64_t { return tok0 + tb * 32 + col; };
+  auto row_of = [&](int64_t t) -> int64_t {
+    const int64_t ic = t < n ? t : n - 1;
+    return p.rows ? (int64_t)p.rows[ic] : ic;
+  };
+  core.dzlane = lane * 16;
 #pragma unroll
   for (int tb = 0; tb < NB; ++tb) {
     core.lsum[tb] = 0.f;
     core.mrun[tb] = -INFINITY;
-    tok[tb] = tok0 + tb * 32 + col;
-    const int64_t ic = tok[tb] < n ? tok[tb] : n - 1;
-    grow[tb] = p.rows ? (int64_t)p.rows[ic] : ic;
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(p.H + grow[tb] * D + h * (D / 2));
+    const int64_t grow = row_of(token(tb));
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(p.H + grow * D + h * (D / 2));
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) core.hf[tb][ks] = src[ks];
-    if (DZ) core.dzblk[tb] = p.dz + (tok[tb] >> 5) * (p.ldz >> 5) * 1024 + lane * 16;
-  }
+    // the wave's 32 tokens form one token block of dZ
+    if (DZ) core.dzblk[tb] = p.dz + ((tok0 >> 5) + tb) * (p.ldz >> 5) * 1024;
+    const int y = p.target[grow];
 
-  // ---- target logit (one split per wave, below). Lanes l and l + 32 hold the two halves of the hidden row of
-  //      token l % 32; each dots its half with the same half of E[y] (bf16 pairs, float32
-  //      accumulation, loads in batches of up to 16 x 16 bytes) and the two halves are added.
-  float sy[NB] = {};
-  // split w % S computes the target logits of wave w (every split when the vocabulary is not
-  // split), so that with several splits this work is shared instead of falling on split 0
-  const bool tgt = (wave % S) == split;
-  if (tgt) {
-#pragma unroll
-    for (int tb = 0; tb < NB; ++tb) {
-      const int y = p.target[grow[tb]];
-      const bool ok = (y >= 0) && (y < V);
-      const bf16x8* er = reinterpret_cast<const bf16x8*>(p.E + (int64_t)(ok ? y : 0) * D + h * (D / 2));
-      constexpr int BATCH = KS < 16 ? KS : 16;
-      float acc4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k0 = 0; k0 < KS; k0 += BATCH) {
-        bf16x8 ev[BATCH];
-#pragma unroll
-        for (int k = 0; k < BATCH; ++k) ev[k] = er[k0 + k];
-#pragma unroll
-        for (int k = 0; k < BATCH; ++k)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc4[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16_pair(core.hf[tb][k0 + k], j), bf16_pair(ev[k], j), acc4[j], false);
-      }
-      float zy = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
-      zy += __shfl_xor(zy, 32);
-      sy[tb] = ok ? capped_log2(zy, p.sc) : __builtin_nanf("");
-    }
+    // the target: its logit is picked from the accumulators in the main loop (take_target), by the
+    // one lane and split that compute it
+    const bool ok = (y >= 0) && (y < V);
+    core.ykey[tb] = (ok && ((y >> 2) & 1) == h) ? y : -1;
+    core.ty[tb] = FIXED ? -1.0f : -INFINITY;
   }
 
   // ---- main loop. Only the last tile of the vocabulary can be partial; it runs the masked
@@ -453,26 +472,42 @@ void fwd_mfma_kernel(FwdParams p) {
     if (next && !steady) load_embed_tile<D, kFwdWaves>(smem, p.E, V, tile + 1, buf ^ 1, wave, lane);
     if (last_partial && i + 1 == ntiles) {
       core.chain(buf, 0, a0);
-      if (vprev >= 0) core.template epilogue<false>(accp, vprev);
+      if (vprev >= 0) {
+        core.template epilogue<false>(accp, vprev);
+        core.take_target(accp, vprev, false);
+      }
       f32x16 a1[NB];
       core.chain(buf, 1, a1);
       core.template epilogue<true>(a0, vb0);
+      core.take_target(a0, vb0, false);
       core.template epilogue<true>(a1, vb0 + 32);
+      core.take_target(a1, vb0 + 32, false);
       vprev = -1;
     } else if (vprev < 0) {
       core.chain(buf, 0, a0);
-      core.template chain_with_epilogue<false>(buf, 1, accp, a0, vb0);
+      const bool ser = core.template chain_with_epilogue<false>(buf, 1, accp, a0, vb0);
+      core.take_target(a0, vb0, ser);
       vprev = vb0 + 32;
     } else {
-      if (next) core.template chain_with_epilogue<true>(buf, 0, a0, accp, vprev, tile + 1, buf ^ 1);
-      else core.template chain_with_epilogue<false>(buf, 0, a0, accp, vprev);
-      core.template chain_with_epilogue<false>(buf, 1, accp, a0, vb0);
+      bool ser;
+      if (next) ser = core.template chain_with_epilogue<true>(buf, 0, a0, accp, vprev, tile + 1, buf ^ 1);
+      else ser = core.template chain_with_epilogue<false>(buf, 0, a0, accp, vprev);
+      core.take_target(accp, vprev, ser);
+      ser = core.template chain_with_epilogue<false>(buf, 1, accp, a0, vb0);
+      core.take_target(a0, vb0, ser);
       vprev = vb0 + 32;
     }
   }
-  if (vprev >= 0) core.template epilogue<false>(accp, vprev);
+  if (vprev >= 0) {
+    core.template epilogue<false>(accp, vprev);
+    core.take_target(accp, vprev, false);
+  }
 
-  // ---- combine the two lane halves (each holds 16 of every 32 vocabulary rows) and write out
+  // ---- combine the two lane halves (each holds 16 of every 32 vocabulary rows) and write out.
+  //      With the fixed shift nats = ln 2 (log2 l - log2 e_y), where e_y is the target's own term of
+  //      the sum l: since l >= e_y, nats >= 0, and nats = 0 exactly when e_y is all of l (V = 1).
+  //      With a running maximum m, nats = ln 2 (m + log2 l - s_y log2 e), where l >= 1 (the maximum's
+  //      own term) and m >= s_y log2 e.
 #pragma unroll
   for (int tb = 0; tb < NB; ++tb) {
     float l = core.lsum[tb], m = core.mrun[tb];
@@ -483,15 +518,23 @@ void fwd_mfma_kernel(FwdParams p) {
       const float m2 = __shfl_xor(m, 32);
       lse_merge(m, l, m2, l2);
     }
-    if (h == 0 && tok[tb] < n) {
+    const float ty = fmaxf(core.ty[tb], __shfl_xor(core.ty[tb], 32));   // the half that found it
+    const bool found = FIXED ? ty >= 0.f : ty > -INFINITY;
+    // log2 of the target's term (fixed shift) or its s log2 e; NaN when the target is not in [0, V)
+    const float sy = found ? (FIXED ? flog2(ty) : ty) : __builtin_nanf("");
+    const int64_t tok = token(tb);
+    if (h == 0 && tok < n) {
+      const int64_t grow = row_of(tok);
       if (p.direct) {
         const float lse2 = (FIXED ? p.sc.M : m) + flog2(l);
-        p.nats[grow[tb]] = kLn2 * (lse2 - sy[tb]);
-        if (p.lse) p.lse[grow[tb]] = kLn2 * lse2;
+        p.nats[grow] = kLn2 * (FIXED ? flog2(l) - sy : lse2 - sy);
+        if (p.lse) p.lse[grow] = kLn2 * lse2;
       } else {
-        p.part_l[(int64_t)split * n + tok[tb]] = l;
-        if (!FIXED) p.part_m[(int64_t)split * n + tok[tb]] = m;
-        if (tgt) p.s_target[tok[tb]] = sy[tb];
+        p.part_l[(int64_t)split * n + tok] = l;
+        if (!FIXED) p.part_m[(int64_t)split * n + tok] = m;
+        // the split whose tiles hold the target writes it; split 0 marks a target outside [0, V)
+        const int y = p.target[grow];
+        if (found || (split == 0 && !(y >= 0 && y < V))) p.s_target[tok] = sy;
       }
     }
   }
@@ -517,7 +560,11 @@ __global__ __launch_bounds__(256) void fwd_finalize_kernel(FwdParams p, int main
       for (int j = 0; j < kBatch; ++j) l += v[j];
     }
     for (; s < S; ++s) l += p.part_l[(int64_t)s * n + i];
-    lse2 = p.sc.M + flog2(l);
+    // s_target holds log2 of the target's own term of l (see fwd_mfma_kernel)
+    const int64_t r = p.rows ? (int64_t)p.rows[i] : i;
+    p.nats[r] = kLn2 * (flog2(l) - p.s_target[i]);
+    if (p.lse) p.lse[r] = kLn2 * (p.sc.M + flog2(l));
+    return;
   } else {
     float m = -INFINITY, l = 0.f;
     int s = 0;
@@ -554,34 +601,37 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(const TIn* H, const TI
                                                           int64_t n_host, int D, int V, Softcap sc,
                                                           float* nats, float* lse) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t n = n_dev ? (int64_t)(*n_dev) : n_host;
-  if (i >= n) return;
-  const int64_t r = rows ? (int64_t)rows[i] : i;
-  const TIn* hrow = H + r * D;
-  float m = -INFINITY, l = 0.f;
-  for (int v = lane; v < V; v += 64) {
-    const TIn* erow = E + (int64_t)v * D;
-    float z = 0.f;
-    for (int d = 0; d < D; ++d) z = __builtin_fmaf(load_in(hrow, d), load_in(erow, d), z);
-    lse_merge(m, l, capped_log2(z, sc), 1.0f);
-  }
-  for (int off = 32; off >= 1; off >>= 1) {
-    float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
-    lse_merge(m, l, m2, l2);
-  }
-  if (lane == 0) {
-    const int y = target[r];
-    float sy = __builtin_nanf("");
-    if (y >= 0 && y < V) {
-      const TIn* erow = E + (int64_t)y * D;
+  // one row per wave, grid-stride over the rows
+  for (int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < n; i += (int64_t)gridDim.x * 4) {
+    const int64_t r = rows ? (int64_t)rows[i] : i;
+    const TIn* hrow = H + r * D;
+    float m = -INFINITY, l = 0.f;
+    for (int v = lane; v < V; v += 64) {
+      const TIn* erow = E + (int64_t)v * D;
       float z = 0.f;
       for (int d = 0; d < D; ++d) z = __builtin_fmaf(load_in(hrow, d), load_in(erow, d), z);
-      sy = capped_log2(z, sc);
+      lse_merge(m, l, capped_log2(z, sc), 1.0f);
     }
-    const float lse2 = m + flog2(l);
-    nats[r] = kLn2 * (lse2 - sy);
-    if (lse) lse[r] = kLn2 * lse2;
+    for (int off = 32; off >= 1; off >>= 1) {
+      float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+      lse_merge(m, l, m2, l2);
+    }
+    if (lane == 0) {
+      // the target's logit by the same loop as the lane that summed it: the same value, so
+      // m >= s_y and l >= 1 (the maximum's own term) give nats >= 0
+      const int y = target[r];
+      float sy = __builtin_nanf("");
+      if (y >= 0 && y < V) {
+        const TIn* erow = E + (int64_t)y * D;
+        float z = 0.f;
+        for (int d = 0; d < D; ++d) z = __builtin_fmaf(load_in(hrow, d), load_in(erow, d), z);
+        sy = capped_log2(z, sc);
+      }
+      const float lse2 = m + flog2(l);
+      nats[r] = kLn2 * (lse2 - sy);
+      if (lse) lse[r] = kLn2 * lse2;
+    }
   }
 }
 
@@ -823,12 +873,12 @@ hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t
   }
 
   if (dtype != 0 || !mfma_width(D)) {
-    const int64_t blocks = (T + 3) / 4;
+    const unsigned blocks = stride_blocks(T, 4);
     if (dtype == 0)
-      hipLaunchKernelGGL(fwd_generic_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
+      hipLaunchKernelGGL(fwd_generic_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st,
                          (const uint16_t*)H, (const uint16_t*)E, target, rows, n_dev, T, D, V, sc, nats, lse);
     else
-      hipLaunchKernelGGL(fwd_generic_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
+      hipLaunchKernelGGL(fwd_generic_kernel<float>, dim3(blocks), dim3(256), 0, st,
                          (const float*)H, (const float*)E, target, rows, n_dev, T, D, V, sc, nats, lse);
     return hipGetLastError();
   }

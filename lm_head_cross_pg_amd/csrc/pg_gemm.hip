@@ -259,11 +259,11 @@ void gemm_bf16_kernel(GemmParams g) {
 // out[i] = sum over s of part[s * stride + i], in split order.
 __global__ __launch_bounds__(256) void sum_splits_kernel(const float* part, int nsplit, int64_t stride, int64_t count,
                                                          float* out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= count) return;
-  float s = 0.f;
-  for (int k = 0; k < nsplit; ++k) s += part[(int64_t)k * stride + i];
-  out[i] = s;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x) {
+    float s = 0.f;
+    for (int k = 0; k < nsplit; ++k) s += part[(int64_t)k * stride + i];
+    out[i] = s;
+  }
 }
 
 
@@ -273,11 +273,16 @@ using DeShape = GemmShape<4, 2, 2>;
 int gemm_tile_m(bool a_trans) { return a_trans ? DeShape::BM : DhShape::BM; }
 int gemm_tile_n(bool a_trans) { return a_trans ? DeShape::BN : DhShape::BN; }
 
-hipError_t launch_gemm(const GemmParams& g, bool a_trans, int ksplit, hipStream_t st) {
+int64_t gemm_grid_x(int64_t M, int64_t N, bool a_trans) {
   const int64_t bm = gemm_tile_m(a_trans), bn = gemm_tile_n(a_trans);
-  const int64_t mt = (g.M + bm - 1) / bm, nt = (g.N + bn - 1) / bn;
-  const int64_t gx = nt > 1 ? 8 * nt * ((mt + 7) / 8) : mt;   // the id mapping of the kernel
+  const int64_t mt = (M + bm - 1) / bm, nt = (N + bn - 1) / bn;
+  return nt > 1 ? 8 * nt * ((mt + 7) / 8) : mt;   // the id mapping of the kernel
+}
+
+hipError_t launch_gemm(const GemmParams& g, bool a_trans, int ksplit, hipStream_t st) {
+  const int64_t gx = gemm_grid_x(g.M, g.N, a_trans);
   if (gx == 0 || ksplit < 1) return hipSuccess;
+  if (gx > kMaxGrid512) return hipErrorInvalidConfiguration;   // the API layer rejects such shapes first
   const dim3 grid((unsigned)gx, 1, (unsigned)ksplit);
   if (a_trans) hipLaunchKernelGGL((gemm_bf16_kernel<true, 4, 2, 2, 3>), grid, dim3(512), 0, st, g);
   else hipLaunchKernelGGL((gemm_bf16_kernel<false, 4, 2, 2, 4>), grid, dim3(512), 0, st, g);
@@ -286,7 +291,7 @@ hipError_t launch_gemm(const GemmParams& g, bool a_trans, int ksplit, hipStream_
 
 hipError_t launch_sum_splits(const float* part, int nsplit, int64_t stride, int64_t count, float* out,
                              hipStream_t st) {
-  hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, part, nsplit,
+  hipLaunchKernelGGL(sum_splits_kernel, dim3(stride_blocks(count, 256)), dim3(256), 0, st, part, nsplit,
                      stride, count, out);
   return hipGetLastError();
 }

@@ -117,6 +117,10 @@ hipError_t launch_gemm(const GemmParams& g, bool a_trans, int ksplit, hipStream_
 // Output tile of each product (rows x columns).
 int gemm_tile_m(bool a_trans);
 int gemm_tile_n(bool a_trans);
+// Workgroups along x of the launch of an M x N product (512 threads each).
+int64_t gemm_grid_x(int64_t M, int64_t N, bool a_trans);
+// Most workgroups of 512 threads one launch can hold (2^32 - 1 work items).
+constexpr int64_t kMaxGrid512 = ((int64_t)1 << 23) - 1;
 // out[i] = sum over s < nsplit of part[s * stride + i], in split order (nsplit = 0 writes zeros).
 hipError_t launch_sum_splits(const float* part, int nsplit, int64_t stride, int64_t count, float* out,
                              hipStream_t st);
@@ -127,5 +131,14 @@ inline bool mfma_width(int32_t D) {
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workgroups of a grid-stride launch over `count` items at `per_block` items per workgroup and
+// pass. A launch may hold at most 2^32 - 1 work items, so element-wise and row-wise kernels loop
+// over their range with a grid capped at kMaxStrideBlocks workgroups (16 Mi threads at 256).
+constexpr int64_t kMaxStrideBlocks = (int64_t)1 << 16;
+inline unsigned stride_blocks(int64_t count, int64_t per_block) {
+  const int64_t b = (count + per_block - 1) / per_block;
+  return (unsigned)(b < 1 ? 1 : (b > kMaxStrideBlocks ? kMaxStrideBlocks : b));
+}
 
 }  // namespace pg

@@ -36,24 +36,24 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const TIn* E, int V,
 // E'[v, d] = bf16(float(q[v, d]) * scale[v]), 8 elements per thread.
 __global__ __launch_bounds__(256) void dequantize_rows_kernel(const int8_t* q, const float* scale, int64_t n8, int D,
                                                               uint16_t* E) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const int64_t e0 = i * 8;
-  const float s = scale[e0 / D];
-  const uint2 raw = reinterpret_cast<const uint2*>(q)[i];
-  const uint32_t w[2] = {raw.x, raw.y};
-  uint16_t out[8];
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = i * 8;
+    const float s = scale[e0 / D];
+    const uint2 raw = reinterpret_cast<const uint2*>(q)[i];
+    const uint32_t w[2] = {raw.x, raw.y};
+    uint16_t out[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int8_t qi = (int8_t)((w[k >> 2] >> (8 * (k & 3))) & 0xff);
-    out[k] = f32_to_bf16((float)qi * s);
+    for (int k = 0; k < 8; ++k) {
+      const int8_t qi = (int8_t)((w[k >> 2] >> (8 * (k & 3))) & 0xff);
+      out[k] = f32_to_bf16((float)qi * s);
+    }
+    uint4 o;
+    o.x = out[0] | ((uint32_t)out[1] << 16);
+    o.y = out[2] | ((uint32_t)out[3] << 16);
+    o.z = out[4] | ((uint32_t)out[5] << 16);
+    o.w = out[6] | ((uint32_t)out[7] << 16);
+    reinterpret_cast<uint4*>(E)[i] = o;
   }
-  uint4 o;
-  o.x = out[0] | ((uint32_t)out[1] << 16);
-  o.y = out[2] | ((uint32_t)out[3] << 16);
-  o.z = out[4] | ((uint32_t)out[5] << 16);
-  o.w = out[6] | ((uint32_t)out[7] << 16);
-  reinterpret_cast<uint4*>(E)[i] = o;
 }
 
 hipError_t launch_quantize(const void* E, int32_t dtype, int32_t V, int32_t D, int8_t* q, float* scale,
@@ -69,7 +69,7 @@ hipError_t launch_quantize(const void* E, int32_t dtype, int32_t V, int32_t D, i
 
 hipError_t launch_dequantize(const int8_t* q, const float* scale, int32_t V, int32_t D, uint16_t* E, hipStream_t st) {
   const int64_t n8 = (int64_t)V * D / 8;
-  hipLaunchKernelGGL(dequantize_rows_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, q, scale, n8, D, E);
+  hipLaunchKernelGGL(dequantize_rows_kernel, dim3(stride_blocks(n8, 256)), dim3(256), 0, st, q, scale, n8, D, E);
   return hipGetLastError();
 }
 

@@ -34,6 +34,8 @@ What it computes, and where the pages state it:
 * Backward of L = g * sum_scored nats (repo-explainer, ``loss.backward()``):
   dS = g (softmax(s) - onehot(target)), dZ = dS * ds/dz with ds/dz = 1 - tanh(z/c)^2,
   dH = dZ . E, dE = dZ^T . H (the LM-head part of the tied embedding's gradient).
+  A scored row whose target lies outside [0, V) has NaN nats, so its loss term, and with it its
+  row of dZ, is NaN: that dH row and all of dE are NaN (the reading of such a target as poison).
 
 Every function works on float64 arrays (bf16 inputs are widened exactly before they get here).
 Nothing is blocked, fused or reordered beyond the formulas above; numpy's matmul is the only
@@ -212,11 +214,14 @@ def backward(H, E, target, c: float, g: float, mask=None):
     z = logits(H, E)
     s = softcap(z, c)
     p = np.exp(s - log_sum_exp(s)[:, None])
+    valid = (target >= 0) & (target < V)
     onehot = np.zeros((T, V))
-    onehot[np.arange(T), target] = 1.0
+    rows = np.nonzero(valid)[0]
+    onehot[rows, target[rows]] = 1.0
     dS = g * (p - onehot)
     dZ = dS * softcap_derivative(z, c)
-    dZ[~_scored(T, mask)] = 0.0
+    dZ[~valid] = np.nan                  # the row's nats are NaN: so is its gradient
+    dZ[~_scored(T, mask)] = 0.0          # unscored rows enter nothing, whatever their target
     dH = dZ @ E
     dE = dZ.T @ H
     return dH, dE
@@ -238,5 +243,6 @@ def embed_grad_rows(H, E, target, c: float, g: float, lse, vocab_rows, mask=None
     p = np.exp(s - np.asarray(lse, dtype=np.float64)[:, None])
     onehot = (target[:, None] == vocab_rows[None, :]).astype(np.float64)
     dZ = g * (p - onehot) * softcap_derivative(z, c)
+    dZ[~((target >= 0) & (target < E.shape[0]))] = np.nan   # poisoned rows, as in :func:`backward`
     dZ[~_scored(T, mask)] = 0.0
     return dZ.T @ H

@@ -7,6 +7,8 @@ GPU library. Run from the repository root: python tests/golden/make_closed_forms
 import json
 import math
 import os
+import struct
+from fractions import Fraction
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LN2 = math.log(2.0)
@@ -96,11 +98,74 @@ def uniform():
     }
 
 
+def _half_even(x):
+    """Nearest integer to the Fraction x, a tie going to the even neighbour (the definition, spelled out)."""
+    f = x.numerator // x.denominator          # floor
+    d = x - f
+    if d > Fraction(1, 2):
+        return f + 1
+    if d < Fraction(1, 2):
+        return f
+    return f if f % 2 == 0 else f + 1
+
+
+def _bf16_nearest(x):
+    """The bfloat16 value nearest to the Fraction x > 0 (8 significant bits), ties to the even
+    significand: x = m 2^e with 2^7 <= m < 2^8 rounded to an integer by _half_even."""
+    e = x.numerator.bit_length() - x.denominator.bit_length() - 7
+    while x / Fraction(2) ** e >= 256:
+        e += 1
+    while x / Fraction(2) ** e < 128:
+        e -= 1
+    return _half_even(x / Fraction(2) ** e) * Fraction(2) ** e
+
+
+def _f32_bits(v):
+    return struct.unpack("<I", struct.pack("<f", float(v)))[0]
+
+
+def rounding_ties():
+    # 1. int8 codes of rows whose quotients E / scale are exact halves
+    units = [127.0, 0.5, 1.5, 2.5, 3.5, 126.5, -0.5, -1.5, -2.5, -3.5, -125.5, 64.5, 63.5, 0.0, 10.0, -127.0]
+    exps = [-6, 3]
+    q8_rows = [[u * 2.0 ** e for u in units] for e in exps]
+    codes = [_half_even(Fraction(u)) for u in units]
+    # 2. bfloat16 rounding of q * scale where the product lies halfway between two bfloat16 values:
+    #    scale = 1 + 2^-8 (float32-exact); for q = 2^k, q * scale = 2^k + 2^(k-8) is a tie
+    scale = 1.0 + 2.0 ** -8
+    qs = [1, 2, 4, 8, 16, 32, 64, 127, 3, 5, 96, -1, -2, -64, -3, 0] * 2
+    dq_rows = [[q * scale for q in qs[:16]] + [q * scale for q in qs[16:]]]
+    deq = [float(_bf16_nearest(Fraction(abs(q) * scale)) * (1 if q >= 0 else -1)) if q else 0.0 for q in qs]
+    # 3. float32 -> bfloat16 for values exactly halfway (and one bit either side)
+    f32 = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), -(1.0 + 3 * 2.0 ** -8),
+           1.0 + 2.0 ** -8 + 2.0 ** -23, 1.0 + 2.0 ** -8 - 2.0 ** -23, 3.0 * 2.0 ** -100 * (1 + 2.0 ** -8),
+           255.0 + 0.5, 254.0 + 0.5]
+    bf = [float(_bf16_nearest(Fraction(abs(v))) * (1 if v >= 0 else -1)) for v in f32]
+    return {
+        "what": "round-half-to-even ties of the int8 quantiser, of its bfloat16 dequantisation and of float32 -> bfloat16",
+        "source": ("definition only: the quantised tied head's format is a reading (the pages name int8 quantisation, "
+                   "trios issue #19, approach table; README leaderboard, GPTQ and LQER rows, without a format); the "
+                   "reading fixes round-half-to-even at both steps, as bfloat16 conversion does"),
+        "derivation": ("q8: rows units[i] * 2^e with max |unit| = 127, so scale = 2^e exactly and E / scale = units[i]; "
+                       "an exact half k + 1/2 goes to the even one of k, k + 1. dequantised: scale = 1 + 2^-8, "
+                       "q * scale = 2^k + 2^(k-8) for q = 2^k lies halfway between 2^k and 2^k + 2^(k-7) and goes "
+                       "to 2^k (even significand); other q by the nearest 8-bit significand. f32_to_bf16: the same "
+                       "rule for values given by their float32 bit patterns. Expected values by exact rational "
+                       "arithmetic (fractions.Fraction), not by a rounding routine."),
+        "q8": {"exponents": exps, "units": units, "rows": q8_rows, "codes": codes,
+               "scales": [2.0 ** e for e in exps]},
+        "dequant": {"scale": scale, "codes": qs, "rows_f32": dq_rows, "bf16": deq},
+        "f32_to_bf16": {"f32_bits": [_f32_bits(v) for v in f32], "bf16_bits": [_f32_bits(v) >> 16 for v in bf],
+                        "bf16": bf},
+    }
+
+
 if __name__ == "__main__":
     for name, obj in [("worked_softcap30.json", worked_softcap30()),
                       ("worked_nocap_one_bit_per_byte.json", worked_nocap()),
                       ("worked_asym_softcap_30_10.json", worked_asym()),
-                      ("stride64_windows.json", stride64()), ("uniform_logits.json", uniform())]:
+                      ("stride64_windows.json", stride64()), ("uniform_logits.json", uniform()),
+                      ("rounding_ties.json", rounding_ties())]:
         with open(os.path.join(HERE, name), "w") as f:
             json.dump(obj, f, indent=1)
             f.write("\n")

@@ -247,3 +247,83 @@ def _has_gpu():
         return torch.cuda.is_available()
     except Exception:
         return False
+
+
+def test_row_and_grid_limits(lib):
+    """Rows up to 2^31 - 256 (the MFMA grids of one 512-thread workgroup per 256 rows stay within a
+    launch's 2^32 - 1 work items); the backward also needs its dH product's grid to fit, which
+    bounds T D. Both are rejected on the host, before anything is enqueued."""
+    top = (1 << 31) - 256
+    assert fwd(lib, T=top + 1) == -2
+    assert bpb(lib, T=top + 1) == -2
+    if not _has_gpu():
+        assert fwd(lib, T=top) == -7               # valid: only the device check is left
+        assert bwd(lib, T=1 << 30, D=32, wsb=1 << 50) == -7
+    assert bwd(lib, T=1 << 30, D=512) == -2
+    assert fwd_bwd(lib, T=1 << 30, D=512) == -2
+    assert abi.workspace_bytes(abi.PG_OP_BWD, 1 << 30, 512, 8192) == 0
+    assert abi.workspace_bytes(abi.PG_OP_FWD, top, 512, 8192) > 0
+
+
+# ------------------------------------------------ the Python binding checks its tensors first
+def _cpu(T=8, D=32, V=16):
+    import torch
+    return dict(H=torch.zeros((T, D), dtype=torch.bfloat16), E=torch.zeros((V, D), dtype=torch.bfloat16),
+                y=torch.zeros(T, dtype=torch.int32), nats=torch.zeros(T), lse=torch.zeros(T),
+                dH=torch.zeros((T, D)), dE=torch.zeros((V, D)), m=torch.ones(T, dtype=torch.uint8))
+
+
+@pytest.fixture
+def no_library(monkeypatch):
+    """Any call into the library (or its loader) fails the test: the checks must come first."""
+    def fail(*a, **k):
+        pytest.fail("the library was called")
+    monkeypatch.setattr(abi, "load", fail)
+
+
+def test_binding_rejects_mismatched_tensors(no_library):
+    import torch
+    t = _cpu()
+    H, E, y, nats, lse, dH, dE, m = t["H"], t["E"], t["y"], t["nats"], t["lse"], t["dH"], t["dE"], t["m"]
+    fwd_ = abi.pg_lmhead_ce_fwd
+    cases = [
+        (lambda: fwd_(H, E.float(), y, None, 30.0, nats), "embed has dtype"),
+        (lambda: fwd_(H, E[:, :16].contiguous(), y, None, 30.0, nats), "embed has 16 columns"),
+        (lambda: fwd_(H, E, y.long(), None, 30.0, nats), "target has dtype torch.int64"),
+        (lambda: fwd_(H, E, y[:7], None, 30.0, nats), "target has 7 elements"),
+        (lambda: fwd_(H, E, y, m.float(), 30.0, nats), "score_mask has dtype"),
+        (lambda: fwd_(H, E, y, m[:3], 30.0, nats), "score_mask has 3 elements"),
+        (lambda: fwd_(H, E, y, None, 30.0, nats.double()), "nats has dtype"),
+        (lambda: fwd_(H, E, y, None, 30.0, nats, lse[:5]), "lse has 5 elements"),
+        (lambda: fwd_(H.t(), E, y, None, 30.0, nats), "hidden must be contiguous"),
+        (lambda: fwd_(H[0], E, y, None, 30.0, nats), "hidden must be 2-D"),
+        (lambda: fwd_(H.double(), E, y, None, 30.0, nats), "hidden has dtype"),
+        (lambda: fwd_(H, E, y, None, 30.0, nats), "is on cpu"),
+        (lambda: abi.pg_lmhead_ce_bwd(H, E, y, None, lse, 30.0, 0.1, dH[:4], dE), "dhidden has 128 elements"),
+        (lambda: abi.pg_lmhead_ce_bwd(H, E, y, None, lse, 30.0, 0.1, dH, dE[:, :8].contiguous()), "dembed has"),
+        (lambda: abi.pg_lmhead_ce_bwd(H, E, y, None, None, 30.0, 0.1, dH, dE), "lse is required"),
+        (lambda: abi.pg_lmhead_ce_fwd_bwd(H, E, y, None, 30.0, 0.1, nats, None, dH, dE), "lse is required"),
+        (lambda: abi.pg_lmhead_ce_fwd_bwd_asym(H, E, y, None, 30.0, 20.0, 0.1, nats, lse, dH.double(), dE),
+         "dhidden has dtype"),
+        (lambda: abi.pg_lmhead_ce_bwd_asym(H, E, y, None, lse, 30.0, 20.0, 0.1, dH, dE), "is on cpu"),
+        (lambda: abi.pg_lmhead_ce_fwd_asym(H, E, y.long(), None, 30.0, 20.0, nats), "target has dtype"),
+        (lambda: abi.pg_quantize_q8(E, torch.zeros((16, 32), dtype=torch.int16), torch.zeros(16)),
+         "embed_q8 has dtype"),
+        (lambda: abi.pg_quantize_q8(E, torch.zeros((16, 32), dtype=torch.int8), torch.zeros(15)),
+         "embed_scale has 15 elements"),
+        (lambda: abi.pg_lmhead_ce_fwd_q8(H.float(), torch.zeros((16, 32), dtype=torch.int8), torch.zeros(16), y,
+                                         None, 30.0, nats), "hidden has dtype"),
+        (lambda: abi.pg_lmhead_ce_fwd_q8(H, torch.zeros((16, 24), dtype=torch.int8), torch.zeros(16), y,
+                                         None, 30.0, nats), "embed_q8 has 24 columns"),
+        (lambda: abi.pg_bpb_reduce(nats, y, None, torch.zeros(15, dtype=torch.int32), None, 16,
+                                   torch.zeros(4, dtype=torch.float64)), "at least 16"),
+        (lambda: abi.pg_bpb_reduce(nats, None, None, torch.zeros(16, dtype=torch.int32), None, 16,
+                                   torch.zeros(4, dtype=torch.float64)), "target is required"),
+        (lambda: abi.pg_bpb_reduce(nats, y, None, torch.zeros(16, dtype=torch.int32), None, 16,
+                                   torch.zeros(4)), "out has dtype"),
+        (lambda: abi.pg_bpb_reduce(nats, y, None, torch.zeros(16, dtype=torch.int32), y.long(), 16,
+                                   torch.zeros(4, dtype=torch.float64)), "byte_per_pos has dtype"),
+    ]
+    for call, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            call()

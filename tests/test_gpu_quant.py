@@ -96,3 +96,44 @@ def test_quantised_forward_full_size():
     b_gpu = ora.bpb(g, inp["target"], inp["byte_len"])[3]
     b_ora = ora.bpb(onats, inp["target"], inp["byte_len"])[3]
     assert abs(b_gpu - b_ora) <= BPB_RTOL * b_ora
+
+
+def test_rounding_ties_bit_exact():
+    """The ties of tests/golden/rounding_ties.json on the GPU: quotients that are exact halves give
+    the even codes (bf16 and f32 input), and a head whose q * scale products lie halfway between
+    two bfloat16 values scores exactly as the bf16 entry point does on the fixture's even-rounded
+    embedding (torch.equal on nats), so the dequantisation rounds those ties to even too."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "rounding_ties.json")) as f:
+        g = json.load(f)
+    rows = np.array(g["q8"]["rows"], dtype=np.float32)
+    print("[case] q8 ties", flush=True)
+    for Et in (torch.from_numpy(rows).cuda(),
+               torch.from_numpy(synth.bf16_bits(rows).view(np.int16)).cuda().view(torch.bfloat16)):
+        q, s = quantize_gpu(Et)
+        for row in q.cpu().numpy():
+            np.testing.assert_array_equal(row, g["q8"]["codes"])
+        np.testing.assert_array_equal(s.cpu().numpy(), np.array(g["q8"]["scales"], dtype=np.float32))
+    # dequantised ties: V = 6 rows, row j = codes * scale * 2^-j (powers of two keep every tie)
+    dq = g["dequant"]
+    V, D, T = 6, len(dq["codes"]), 256
+    base = np.array(dq["rows_f32"][0], dtype=np.float64)
+    E32 = np.stack([base * 2.0 ** -j for j in range(V)]).astype(np.float32)
+    Eexp = np.stack([np.array(dq["bf16"]) * 2.0 ** -j for j in range(V)])
+    q, s = quantize_gpu(torch.from_numpy(E32).cuda())
+    for j in range(V):
+        np.testing.assert_array_equal(q.cpu().numpy()[j], dq["codes"])
+    np.testing.assert_array_equal(ora.dequantize_rows_q8(q.cpu().numpy(), s.cpu().numpy()), Eexp)
+    rng = np.random.default_rng(17)
+    Hb = synth.bf16_bits(rng.standard_normal((T, D)).astype(np.float32))
+    Ht = torch.from_numpy(Hb.view(np.int16)).cuda().view(torch.bfloat16)
+    y = torch.from_numpy(rng.integers(0, V, T).astype(np.int32)).cuda()
+    nats, ref = torch.empty(T, device="cuda"), torch.empty(T, device="cuda")
+    abi.pg_lmhead_ce_fwd_q8(Ht, q, s, y, None, 30.0, nats, None)
+    Eb = torch.from_numpy(synth.bf16_bits(Eexp.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+    abi.pg_lmhead_ce_fwd(Ht, Eb, y, None, 30.0, ref, None)
+    torch.cuda.synchronize()
+    assert torch.equal(nats, ref)
+    onats, _ = ora.forward(synth.bf16_to_f64(Hb), Eexp, y.cpu().numpy(), 30.0)
+    assert np.max(np.abs(nats.cpu().numpy() - onats)) <= NATS_ATOL

@@ -155,3 +155,31 @@ def test_asymmetric_caps_match_torch_autograd():
     dH, dE = ora.backward(H, E, y, (cp, cn), 1.0)
     np.testing.assert_allclose(dH, Ht.grad.numpy(), rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(dE, Et.grad.numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_out_of_range_target_poisons_gradients():
+    """A scored row whose target lies outside [0, V) (above V or negative, which must not wrap
+    around to the last entry) has NaN nats, so its dH row and all of dE are NaN; its other dH rows
+    are those of the same call with that row unscored, and unscored it changes nothing."""
+    inp = synth.make_inputs("fd", 3)
+    H, E = synth.as_f64(inp["hidden"], "f32"), synth.as_f64(inp["embed"], "f32")
+    y = inp["target"].astype(np.int64).copy()
+    T, V = H.shape[0], E.shape[0]
+    y[4], y[9] = V, -1
+    dH, dE = ora.backward(H, E, y, 30.0, 1.0 / T)
+    assert np.isnan(dH[[4, 9]]).all() and np.isnan(dE).all()
+    keep = np.ones(T, np.uint8)
+    keep[[4, 9]] = 0
+    mH, mE = ora.backward(H, E, y, 30.0, 1.0 / T, keep)
+    assert np.all(mH[[4, 9]] == 0.0) and np.all(np.isfinite(mE))
+    rest = np.delete(np.arange(T), [4, 9])
+    np.testing.assert_allclose(dH[rest], mH[rest], rtol=1e-12, atol=0)
+    # unscored rows enter nothing: the same as dropping them
+    sH, sE = ora.backward(H[rest], E, y[rest], 30.0, 1.0 / T)
+    np.testing.assert_allclose(mH[rest], sH, rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(mE, sE, rtol=1e-10, atol=1e-300)
+    # the columns of dE are the forward's sensitivity: y = -1 must not act as y = V - 1
+    y2 = y.copy()
+    y2[9] = V - 1
+    aH, _ = ora.backward(H, E, y2, 30.0, 1.0 / T, keep | (np.arange(T) == 9))
+    assert np.all(np.isfinite(aH[9]))

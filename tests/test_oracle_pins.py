@@ -348,3 +348,35 @@ def test_q8_round_trip_error_bound():
     bound = s[:, None].astype(np.float64) * (0.5 + 1e-6) + np.abs(Ed) * 2.0 ** -8
     assert np.all(np.abs(Ed - E) <= bound)
     assert np.max(np.abs(Ed - E) / s[:, None]) > 0.45        # the bound is nearly reached
+
+
+# ---------------------------------------------------------------- rounding ties (tests/golden/rounding_ties.json)
+def test_q8_ties_round_half_to_even():
+    """Rows whose quotients E / scale are exact halves k + 1/2: the codes are the even neighbours
+    (a half-away or floor(x + 1/2) rounding gives other codes at 0.5, 2.5, -0.5, 126.5, ...)."""
+    g = _load("rounding_ties.json")["q8"]
+    q, s = ora.quantize_rows_q8(np.array(g["rows"], dtype=np.float32))
+    np.testing.assert_array_equal(s, np.array(g["scales"], dtype=np.float32))
+    for row in q:
+        np.testing.assert_array_equal(row, g["codes"])
+
+
+def test_q8_dequantised_ties_round_half_to_even():
+    """q * (1 + 2^-8) for q = 2^k lies halfway between two bfloat16 values; the dequantised head
+    takes the even one. The same row, quantised, gives its codes and scale back exactly."""
+    g = _load("rounding_ties.json")["dequant"]
+    q = np.array([g["codes"]], dtype=np.int8)
+    s = np.array([g["scale"]], dtype=np.float32)
+    np.testing.assert_array_equal(ora.dequantize_rows_q8(q, s)[0], g["bf16"])
+    q2, s2 = ora.quantize_rows_q8(np.array(g["rows_f32"], dtype=np.float32))
+    np.testing.assert_array_equal(q2[0], g["codes"])
+    assert s2[0] == np.float32(g["scale"])
+
+
+def test_bf16_rounding_ties_to_even():
+    """float32 values halfway between two bfloat16 values (and one float32 ulp either side): the
+    oracle's rounding and the input generator's both take the even significand."""
+    g = _load("rounding_ties.json")["f32_to_bf16"]
+    x = np.array(g["f32_bits"], dtype=np.uint32).view(np.float32)
+    np.testing.assert_array_equal(ora._bf16_round(x), np.array(g["bf16"]))
+    np.testing.assert_array_equal(synth.bf16_bits(x), np.array(g["bf16_bits"], dtype=np.uint16))
