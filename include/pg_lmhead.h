@@ -57,7 +57,8 @@ enum {
   PG_ERR_WORKSPACE = -5, /* workspace smaller than pg_workspace_bytes() asks for */
   PG_ERR_ALIGN = -6,     /* a pointer is not 16-byte aligned */
   PG_ERR_DEVICE = -7,    /* no HIP device, or the current device is not gfx950 */
-  PG_ERR_HIP = -8        /* a HIP runtime call or kernel launch failed */
+  PG_ERR_HIP = -8,       /* a HIP runtime call or kernel launch failed */
+  PG_ERR_SCRATCH = -9    /* pg_lmhead_ce_fwd_noalloc: the shape needs more than its static scratch */
 };
 
 enum { PG_DTYPE_BF16 = 0, PG_DTYPE_F32 = 1 }; /* dtype of H and E (they share one) */
@@ -90,6 +91,22 @@ pg_status pg_lmhead_ce_fwd(const void* hidden, const void* embed, int32_t dtype,
                            int64_t T, int32_t D, int32_t V, float softcap,
                            float* nats, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pg_lmhead_ce_fwd without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation. It computes
+ * exactly what pg_lmhead_ce_fwd computes (the same kernels) and allocates nothing: its scratch is a
+ * static device array of 16 MiB + 256 B that each GPU the library runs on holds until the process
+ * ends, which covers T <= 2^20 rows for any D and V (pg_workspace_bytes(PG_OP_FWD, T, D, V) must
+ * fit; otherwise PG_ERR_SCRATCH, nothing enqueued). Every call on one GPU shares that GPU's array,
+ * so calls that may overlap on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller; calls in one stream are safe. Arguments and other errors as for
+ * pg_lmhead_ce_fwd.
+ */
+pg_status pg_lmhead_ce_fwd_noalloc(const void* hidden, const void* embed, int32_t dtype,
+                                   const int32_t* target, const uint8_t* score_mask,
+                                   int64_t T, int32_t D, int32_t V, float softcap,
+                                   float* nats, float* lse, void* stream);
 
 /*
  * Backward of L = grad_scale * sum over scored rows of nats (mean cross-entropy: grad_scale =

@@ -22,10 +22,11 @@ PG_DTYPE_BF16 = 0
 PG_DTYPE_F32 = 1
 PG_OP_FWD, PG_OP_BWD, PG_OP_BPB, PG_OP_FWD_Q8, PG_OP_FWD_BWD = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "PG_OK", -1: "PG_ERR_NULL", -2: "PG_ERR_SHAPE", -3: "PG_ERR_DTYPE", -4: "PG_ERR_SOFTCAP",
-                -5: "PG_ERR_WORKSPACE", -6: "PG_ERR_ALIGN", -7: "PG_ERR_DEVICE", -8: "PG_ERR_HIP"}
+                -5: "PG_ERR_WORKSPACE", -6: "PG_ERR_ALIGN", -7: "PG_ERR_DEVICE", -8: "PG_ERR_HIP",
+                -9: "PG_ERR_SCRATCH"}
 
 # every symbol the header declares
-EXPORTS = ("pg_lmhead_ce_fwd", "pg_lmhead_ce_bwd", "pg_lmhead_ce_fwd_bwd", "pg_lmhead_ce_fwd_asym", "pg_lmhead_ce_bwd_asym",
+EXPORTS = ("pg_lmhead_ce_fwd", "pg_lmhead_ce_fwd_noalloc", "pg_lmhead_ce_bwd", "pg_lmhead_ce_fwd_bwd", "pg_lmhead_ce_fwd_asym", "pg_lmhead_ce_bwd_asym",
            "pg_lmhead_ce_fwd_bwd_asym",
            "pg_quantize_q8", "pg_lmhead_ce_fwd_q8", "pg_bpb_reduce", "pg_workspace_bytes", "pg_status_str",
            "pg_abi_version")
@@ -51,6 +52,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.pg_lmhead_ce_fwd.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, f32, vp, vp, vp, sz, vp]
     lib.pg_lmhead_ce_fwd.restype = i32
+    lib.pg_lmhead_ce_fwd_noalloc.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, f32, vp, vp, vp]
+    lib.pg_lmhead_ce_fwd_noalloc.restype = i32
     lib.pg_lmhead_ce_bwd.argtypes = [vp, vp, i32, vp, vp, vp, i64, i32, i32, f32, f32, vp, vp, vp, sz, vp]
     lib.pg_lmhead_ce_bwd.restype = i32
     lib.pg_lmhead_ce_fwd_bwd.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, f32, f32, vp, vp, vp, vp, vp, sz, vp]
@@ -201,6 +204,20 @@ def pg_lmhead_ce_fwd(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Te
                                  T, D, V, float(softcap), _ptr(nats), _ptr(lse), _ptr(ws), ws.numel(),
                                  _stream(stream))
     _check(st, "pg_lmhead_ce_fwd")
+
+
+def pg_lmhead_ce_fwd_noalloc(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Tensor,
+                             score_mask: Optional[torch.Tensor], softcap: float,
+                             nats: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    a = _Args("pg_lmhead_ce_fwd_noalloc")
+    T, D, V = _head(a, hidden, embed, target, score_mask)
+    a(nats, "nats", (torch.float32,), numel=T)
+    a(lse, "lse", (torch.float32,), numel=T, optional=True)
+    a.same_device()
+    st = load().pg_lmhead_ce_fwd_noalloc(_ptr(hidden), _ptr(embed), _dtype_code(hidden), _ptr(target),
+                                         _ptr(score_mask), T, D, V, float(softcap), _ptr(nats), _ptr(lse),
+                                         _stream(stream))
+    _check(st, "pg_lmhead_ce_fwd_noalloc")
 
 
 def _bwd_outputs(a: _Args, T, D, V, dhidden, dembed):

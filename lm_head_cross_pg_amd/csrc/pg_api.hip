@@ -3,6 +3,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/pg_lmhead.h"
 #include "pg_internal.h"
@@ -39,6 +40,37 @@ pg_status device_check(pg::DeviceInfo& info) {
 }
 
 inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Scratch of pg_lmhead_ce_fwd_noalloc: a file-scope device array that every GPU the library runs
+// on holds until the process ends. Its size covers the forward's workspace for T <= 2^20 rows
+// (scored-row list, target terms and per-split partial sums: 16 MiB + 256 B there), whatever D and
+// V are. In host code `scratch` is only a stand-in for the symbol: its device address is looked up
+// once per device with hipGetSymbolAddress, with that device current, and only that address is
+// handed to kernels.
+constexpr size_t kScratchBytes = ((size_t)16 << 20) + 256;
+__device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of this device's scratch array (the caller has run device_check).
+pg_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return PG_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return PG_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PG_OK;
+}
 
 // Rows up to 2^31 - 256: every row index fits an int32, and the MFMA kernels' grids of one
 // 512-thread workgroup per 256 rows stay within the 2^32 - 1 work items of a launch.
@@ -80,6 +112,7 @@ const char* pg_status_str(pg_status s) {
     case PG_ERR_ALIGN: return "pointer not 16-byte aligned";
     case PG_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
     case PG_ERR_HIP: return "HIP runtime or kernel launch failure";
+    case PG_ERR_SCRATCH: return "the shape needs more scratch than the static buffer of the allocation-free entry holds";
     default: return "unknown status";
   }
 }
@@ -102,18 +135,30 @@ size_t pg_workspace_bytes(int32_t op, int64_t T, int32_t D, int32_t V) {
   }
 }
 
+// The forward's arguments other than the workspace (host only, in the order of the status codes).
+static pg_status fwd_args(const void* hidden, const void* embed, int32_t dtype, const int32_t* target,
+                          const uint8_t* score_mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
+                          const float* nats, const float* lse) {
+  pg_status s;
+  if ((s = check_shape(T, D, V)) != PG_OK) return s;
+  if (T > 0 && (!hidden || !target || !nats)) return PG_ERR_NULL;
+  if (!embed) return PG_ERR_NULL;
+  if (dtype != PG_DTYPE_BF16 && dtype != PG_DTYPE_F32) return PG_ERR_DTYPE;
+  if ((s = check_softcap(cap_pos)) != PG_OK || (s = check_softcap(cap_neg)) != PG_OK) return s;
+  if (misaligned(hidden) || misaligned(embed) || misaligned(target) || misaligned(score_mask) ||
+      misaligned(nats) || misaligned(lse))
+    return PG_ERR_ALIGN;
+  return PG_OK;
+}
+
 static pg_status fwd_impl(const void* hidden, const void* embed, int32_t dtype, const int32_t* target,
                           const uint8_t* score_mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
                           float* nats, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   pg_status s;
-  if ((s = check_shape(T, D, V)) != PG_OK) return s;
-  if (T > 0 && (!hidden || !target || !nats)) return PG_ERR_NULL;
-  if (!embed || !workspace) return PG_ERR_NULL;
-  if (dtype != PG_DTYPE_BF16 && dtype != PG_DTYPE_F32) return PG_ERR_DTYPE;
-  if ((s = check_softcap(cap_pos)) != PG_OK || (s = check_softcap(cap_neg)) != PG_OK) return s;
-  if (misaligned(hidden) || misaligned(embed) || misaligned(target) || misaligned(score_mask) ||
-      misaligned(nats) || misaligned(lse) || misaligned(workspace))
-    return PG_ERR_ALIGN;
+  if ((s = fwd_args(hidden, embed, dtype, target, score_mask, T, D, V, cap_pos, cap_neg, nats, lse)) != PG_OK)
+    return s;
+  if (!workspace) return PG_ERR_NULL;
+  if (misaligned(workspace)) return PG_ERR_ALIGN;
   if (workspace_bytes < pg_workspace_bytes(PG_OP_FWD, T, D, V)) return PG_ERR_WORKSPACE;
   pg::DeviceInfo dev{};
   if ((s = device_check(dev)) != PG_OK) return s;
@@ -152,6 +197,25 @@ pg_status pg_lmhead_ce_fwd(const void* hidden, const void* embed, int32_t dtype,
                            void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_impl(hidden, embed, dtype, target, score_mask, T, D, V, softcap, softcap, nats, lse, workspace,
                   workspace_bytes, stream);
+}
+
+pg_status pg_lmhead_ce_fwd_noalloc(const void* hidden, const void* embed, int32_t dtype,
+                                   const int32_t* target, const uint8_t* score_mask,
+                                   int64_t T, int32_t D, int32_t V, float softcap,
+                                   float* nats, float* lse, void* stream) {
+  pg_status s;
+  if ((s = fwd_args(hidden, embed, dtype, target, score_mask, T, D, V, softcap, softcap, nats, lse)) != PG_OK)
+    return s;
+  if (pg::fwd_workspace(T, D, V).total > kScratchBytes) return PG_ERR_SCRATCH;
+  pg::DeviceInfo dev{};
+  if ((s = device_check(dev)) != PG_OK) return s;
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != PG_OK) return s;
+  // the forward writes every scratch entry it reads (row count, scored rows, partial sums) in the
+  // same stream first, so nothing has to be cleared between calls
+  hipError_t e = pg::launch_fwd(hidden, embed, dtype, target, score_mask, T, D, V, softcap, softcap, nats, lse,
+                                static_cast<char*>(ws), dev, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PG_OK : PG_ERR_HIP;
 }
 
 pg_status pg_lmhead_ce_bwd(const void* hidden, const void* embed, int32_t dtype,

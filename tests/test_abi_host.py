@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert abi.abi_version() == 1
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         assert abi.status_str(code) and abi.status_str(code) != "unknown status"
     assert abi.status_str(-99) == "unknown status"
 
@@ -327,3 +327,26 @@ def test_binding_rejects_mismatched_tensors(no_library):
     for call, msg in cases:
         with pytest.raises(ValueError, match=msg):
             call()
+
+
+def fwd_noalloc(lib, **kw):
+    a = dict(hidden=P, embed=P, dtype=0, target=P, mask=None, T=256, D=64, V=512, c=30.0, nats=P, lse=P,
+             stream=None)
+    a.update(kw)
+    return lib.pg_lmhead_ce_fwd_noalloc(a["hidden"], a["embed"], a["dtype"], a["target"], a["mask"], a["T"],
+                                        a["D"], a["V"], a["c"], a["nats"], a["lse"], a["stream"])
+
+
+def test_noalloc_forward_validation(lib):
+    """The allocation-free forward validates like pg_lmhead_ce_fwd, and rejects a shape whose scratch
+    would not fit its static buffer (T > 2^20 rows) with PG_ERR_SCRATCH before anything else runs."""
+    assert fwd_noalloc(lib, T=-1) == -2
+    assert fwd_noalloc(lib, nats=None) == -1
+    assert fwd_noalloc(lib, dtype=2) == -3
+    assert fwd_noalloc(lib, c=-1.0) == -4
+    assert fwd_noalloc(lib, lse=P + 4) == -6
+    assert fwd_noalloc(lib, T=(1 << 20) + 1) == -9
+    assert abi.status_str(-9) != "unknown status"
+    if not _has_gpu():
+        assert fwd_noalloc(lib, T=1 << 20) == -7        # fits: only the device check is left
+        assert fwd_noalloc(lib) == -7
