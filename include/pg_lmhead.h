@@ -215,6 +215,62 @@ pg_status pg_bpb_reduce(const float* nats, const int32_t* target, const uint8_t*
                         int64_t T, int32_t V, double* out,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pg_bpb_reduce that adds to running sums instead of overwriting them: out[0..2] (sum_nats,
+ * sum_bytes, n_scored) must hold the sums of the earlier calls (zeros before the first), this call's
+ * sums are added in a fixed order and out[3] becomes the bits per byte of the running sums. Calls
+ * in one stream therefore accumulate an evaluation that spans many batches, such as the sliding
+ * windows below. Arguments, workspace and errors as for pg_bpb_reduce.
+ */
+pg_status pg_bpb_accumulate(const float* nats, const int32_t* target, const uint8_t* score_mask,
+                            const int32_t* byte_len, const int32_t* byte_per_pos,
+                            int64_t T, int32_t V, double* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sliding-window evaluation of a token stream (parameter-golf README leaderboard, "Sliding Window
+ * Eval" row: windows advancing by a stride of 64 tokens, "increasing context for eval"), with
+ * score-first test-time training (README leaderboard, "Legal Score-First TTT" rows and "phased TTT
+ * over already-scored validation chunks"; HYDRA Golf site, leaderboard entry #2).
+ *
+ * Schedule. tokens[0 .. n_tokens) is the stream; prediction p (p = 0 .. n_tokens - 2) is token
+ * p + 1 given tokens 0 .. p. Window w covers input positions [w stride, w stride + window).
+ * Window 0 scores predictions [0, window); window w >= 1 scores [w stride + window - stride,
+ * w stride + window): the predictions it adds, each with at least window - stride tokens of
+ * context. Every prediction is scored exactly once; stride <= window.
+ *
+ * pg_window_count: the number of windows that cover the stream (0 when n_tokens < 2).
+ * pg_window_scored: the number of predictions that windows first_window .. first_window +
+ *   n_windows - 1 score. Both are host arithmetic (no device, no stream) and return
+ *   PG_ERR_SHAPE (negative) for n_tokens < 0, window < 1, stride < 1, stride > window,
+ *   first_window < 0 or n_windows < 0.
+ * pg_window_rows: the rows of a batch of windows, laid out as n_windows x window rows, row
+ *   (b, r) being input position (first_window + b) stride + r: target [n_windows * window] int32
+ *   gets token p + 1 of each row's position p (0 past the stream), score_mask the same count of
+ *   uint8 (1 where that window scores the row). The caller supplies the hidden states of the same
+ *   rows (the model run on each window) and passes target and score_mask on to pg_lmhead_ce_fwd
+ *   (or pg_lmhead_ce_fwd_bwd) and pg_bpb_accumulate. tokens is a device array; a token outside
+ *   [0, V) poisons its row as in the forward. Errors: PG_ERR_SHAPE (as above, n_windows < 1, or more
+ *   rows than the forward takes), PG_ERR_NULL, PG_ERR_ALIGN, PG_ERR_DEVICE, PG_ERR_HIP.
+ * pg_sgd_step_bf16: one SGD step of score-first test-time training on the tied embedding, kept as
+ *   float32 master weights with a bf16 copy that the head reads: for i < n,
+ *   master[i] = fl(master[i] - fl(lr * grad[i])) (two float32 roundings, no fused multiply-add)
+ *   and embed_bf16[i] = bf16_round_half_even(master[i]). grad is dembed from the training entry
+ *   points on an already-scored batch, so a later batch is scored with the updated embedding and
+ *   no batch with one trained on itself. PG_ERR_SOFTCAP for a non-finite lr.
+ */
+int64_t pg_window_count(int64_t n_tokens, int32_t window, int32_t stride);
+
+int64_t pg_window_scored(int64_t n_tokens, int32_t window, int32_t stride, int64_t first_window,
+                         int32_t n_windows);
+
+pg_status pg_window_rows(const int32_t* tokens, int64_t n_tokens, int32_t window, int32_t stride,
+                         int64_t first_window, int32_t n_windows, int32_t* target, uint8_t* score_mask,
+                         void* stream);
+
+pg_status pg_sgd_step_bf16(float* master, const float* grad, float lr, int64_t n, void* embed_bf16,
+                           void* stream);
+
 /* Workspace bytes an entry point needs for these sizes (0 for invalid sizes). */
 size_t pg_workspace_bytes(int32_t op, int64_t T, int32_t D, int32_t V);
 

@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "PG_OK", -1: "PG_ERR_NULL", -2: "PG_ERR_SHAPE", -3: "PG_ERR_D
 # every symbol the header declares
 EXPORTS = ("pg_lmhead_ce_fwd", "pg_lmhead_ce_fwd_noalloc", "pg_lmhead_ce_bwd", "pg_lmhead_ce_fwd_bwd", "pg_lmhead_ce_fwd_asym", "pg_lmhead_ce_bwd_asym",
            "pg_lmhead_ce_fwd_bwd_asym",
-           "pg_quantize_q8", "pg_lmhead_ce_fwd_q8", "pg_bpb_reduce", "pg_workspace_bytes", "pg_status_str",
+           "pg_quantize_q8", "pg_lmhead_ce_fwd_q8", "pg_bpb_reduce", "pg_bpb_accumulate", "pg_window_count",
+           "pg_window_scored", "pg_window_rows", "pg_sgd_step_bf16", "pg_workspace_bytes", "pg_status_str",
            "pg_abi_version")
 
 
@@ -71,6 +72,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pg_lmhead_ce_fwd_q8.restype = i32
     lib.pg_bpb_reduce.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, sz, vp]
     lib.pg_bpb_reduce.restype = i32
+    lib.pg_bpb_accumulate.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, sz, vp]
+    lib.pg_bpb_accumulate.restype = i32
+    lib.pg_window_count.argtypes = [i64, i32, i32]
+    lib.pg_window_count.restype = i64
+    lib.pg_window_scored.argtypes = [i64, i32, i32, i64, i32]
+    lib.pg_window_scored.restype = i64
+    lib.pg_window_rows.argtypes = [vp, i64, i32, i32, i64, i32, vp, vp, vp]
+    lib.pg_window_rows.restype = i32
+    lib.pg_sgd_step_bf16.argtypes = [vp, vp, f32, i64, vp, vp]
+    lib.pg_sgd_step_bf16.restype = i32
     lib.pg_workspace_bytes.argtypes = [i32, i64, i32, i32]
     lib.pg_workspace_bytes.restype = sz
     lib.pg_status_str.argtypes = [i32]
@@ -338,8 +349,9 @@ def pg_lmhead_ce_fwd_q8(hidden: torch.Tensor, embed_q8: torch.Tensor, embed_scal
 
 def pg_bpb_reduce(nats: torch.Tensor, target: Optional[torch.Tensor], score_mask: Optional[torch.Tensor],
                   byte_len: Optional[torch.Tensor], byte_per_pos: Optional[torch.Tensor], V: int,
-                  out: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    a = _Args("pg_bpb_reduce")
+                  out: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None,
+                  _entry: str = "pg_bpb_reduce") -> None:
+    a = _Args(_entry)
     a(nats, "nats", (torch.float32,))
     T = nats.numel()
     a(byte_per_pos, "byte_per_pos", (torch.int32,), numel=T, optional=True)
@@ -348,9 +360,55 @@ def pg_bpb_reduce(nats: torch.Tensor, target: Optional[torch.Tensor], score_mask
     a(score_mask, "score_mask", _MASK, numel=T, optional=True)
     a(out, "out", (torch.float64,), min_numel=4)
     ws = _workspace(a, PG_OP_BPB, T, 1, V, out, workspace)
-    st = load().pg_bpb_reduce(_ptr(nats), _ptr(target), _ptr(score_mask), _ptr(byte_len), _ptr(byte_per_pos),
-                              T, int(V), _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
-    _check(st, "pg_bpb_reduce")
+    st = getattr(load(), _entry)(_ptr(nats), _ptr(target), _ptr(score_mask), _ptr(byte_len), _ptr(byte_per_pos),
+                                 T, int(V), _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, _entry)
+
+
+def pg_bpb_accumulate(nats: torch.Tensor, target: Optional[torch.Tensor], score_mask: Optional[torch.Tensor],
+                      byte_len: Optional[torch.Tensor], byte_per_pos: Optional[torch.Tensor], V: int,
+                      out: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """pg_bpb_reduce adding into the running sums held in out[0..2]."""
+    pg_bpb_reduce(nats, target, score_mask, byte_len, byte_per_pos, V, out, workspace, stream,
+                  _entry="pg_bpb_accumulate")
+
+
+def pg_window_count(n_tokens: int, window: int, stride: int) -> int:
+    n = int(load().pg_window_count(int(n_tokens), int(window), int(stride)))
+    if n < 0:
+        raise PgError(n, "pg_window_count")
+    return n
+
+
+def pg_window_scored(n_tokens: int, window: int, stride: int, first_window: int, n_windows: int) -> int:
+    n = int(load().pg_window_scored(int(n_tokens), int(window), int(stride), int(first_window), int(n_windows)))
+    if n < 0:
+        raise PgError(n, "pg_window_scored")
+    return n
+
+
+def pg_window_rows(tokens: torch.Tensor, window: int, stride: int, first_window: int, n_windows: int,
+                   target: torch.Tensor, score_mask: torch.Tensor, stream=None) -> None:
+    a = _Args("pg_window_rows")
+    a(tokens, "tokens", (torch.int32,))
+    rows = int(n_windows) * int(window)
+    a(target, "target", (torch.int32,), min_numel=rows)
+    a(score_mask, "score_mask", _MASK, min_numel=rows)
+    a.same_device()
+    st = load().pg_window_rows(_ptr(tokens), tokens.numel(), int(window), int(stride), int(first_window),
+                               int(n_windows), _ptr(target), _ptr(score_mask), _stream(stream))
+    _check(st, "pg_window_rows")
+
+
+def pg_sgd_step_bf16(master: torch.Tensor, grad: torch.Tensor, lr: float, embed: torch.Tensor, stream=None) -> None:
+    a = _Args("pg_sgd_step_bf16")
+    a(master, "master", (torch.float32,))
+    n = master.numel()
+    a(grad, "grad", (torch.float32,), numel=n)
+    a(embed, "embed", _BF16, numel=n)
+    a.same_device()
+    st = load().pg_sgd_step_bf16(_ptr(master), _ptr(grad), float(lr), n, _ptr(embed), _stream(stream))
+    _check(st, "pg_sgd_step_bf16")
 
 
 def to_device(inp: dict, device="cuda") -> dict:

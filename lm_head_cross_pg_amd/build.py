@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpg_lmhead.so")
-SOURCES = ["pg_api.hip", "pg_fwd.hip", "pg_bwd.hip", "pg_gemm.hip", "pg_bpb.hip", "pg_quant.hip"]
+SOURCES = ["pg_api.hip", "pg_fwd.hip", "pg_bwd.hip", "pg_gemm.hip", "pg_bpb.hip", "pg_quant.hip", "pg_window.hip"]
 # Kernels that keep MFMA accumulators in VGPRs so that the hidden-row operands can live in AGPRs.
 VGPR_ACC_SOURCES = {"pg_fwd.hip", "pg_bwd.hip"}
 ARCH = "gfx950"

@@ -107,7 +107,7 @@ const char* pg_status_str(pg_status s) {
     case PG_ERR_NULL: return "a required pointer is NULL";
     case PG_ERR_SHAPE: return "invalid shape (T < 0, D < 1, V < 1 or beyond the supported range)";
     case PG_ERR_DTYPE: return "unknown dtype";
-    case PG_ERR_SOFTCAP: return "softcap or grad_scale is negative or not finite";
+    case PG_ERR_SOFTCAP: return "softcap negative or not finite, or grad_scale or learning rate not finite";
     case PG_ERR_WORKSPACE: return "workspace smaller than pg_workspace_bytes()";
     case PG_ERR_ALIGN: return "pointer not 16-byte aligned";
     case PG_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
@@ -327,10 +327,9 @@ pg_status pg_lmhead_ce_fwd_q8(const void* hidden, const int8_t* embed_q8, const 
   return e == hipSuccess ? PG_OK : PG_ERR_HIP;
 }
 
-pg_status pg_bpb_reduce(const float* nats, const int32_t* target, const uint8_t* score_mask,
-                        const int32_t* byte_len, const int32_t* byte_per_pos,
-                        int64_t T, int32_t V, double* out,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+static pg_status bpb_impl(const float* nats, const int32_t* target, const uint8_t* score_mask,
+                          const int32_t* byte_len, const int32_t* byte_per_pos, int64_t T, int32_t V, double* out,
+                          void* workspace, size_t workspace_bytes, void* stream, bool accumulate) {
   pg_status s;
   if ((s = check_shape(T, 1, V)) != PG_OK) return s;
   if (T > 0 && (!nats || (!byte_per_pos && !target))) return PG_ERR_NULL;
@@ -343,7 +342,69 @@ pg_status pg_bpb_reduce(const float* nats, const int32_t* target, const uint8_t*
   pg::DeviceInfo dev{};
   if ((s = device_check(dev)) != PG_OK) return s;
   hipError_t e = pg::launch_bpb(nats, target, score_mask, byte_len, byte_per_pos, T, V, out,
-                                static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+                                static_cast<char*>(workspace), static_cast<hipStream_t>(stream), accumulate);
+  return e == hipSuccess ? PG_OK : PG_ERR_HIP;
+}
+
+pg_status pg_bpb_reduce(const float* nats, const int32_t* target, const uint8_t* score_mask,
+                        const int32_t* byte_len, const int32_t* byte_per_pos,
+                        int64_t T, int32_t V, double* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return bpb_impl(nats, target, score_mask, byte_len, byte_per_pos, T, V, out, workspace, workspace_bytes, stream,
+                  false);
+}
+
+pg_status pg_bpb_accumulate(const float* nats, const int32_t* target, const uint8_t* score_mask,
+                            const int32_t* byte_len, const int32_t* byte_per_pos,
+                            int64_t T, int32_t V, double* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return bpb_impl(nats, target, score_mask, byte_len, byte_per_pos, T, V, out, workspace, workspace_bytes, stream,
+                  true);
+}
+
+// ------------------------------------------------------------------ sliding-window evaluation
+
+static bool window_args_ok(int64_t n_tokens, int32_t window, int32_t stride) {
+  return n_tokens >= 0 && window >= 1 && stride >= 1 && stride <= window;
+}
+
+int64_t pg_window_count(int64_t n_tokens, int32_t window, int32_t stride) {
+  if (!window_args_ok(n_tokens, window, stride)) return PG_ERR_SHAPE;
+  return pg::window_count(n_tokens, window, stride);
+}
+
+int64_t pg_window_scored(int64_t n_tokens, int32_t window, int32_t stride, int64_t first_window, int32_t n_windows) {
+  if (!window_args_ok(n_tokens, window, stride) || first_window < 0 || n_windows < 0) return PG_ERR_SHAPE;
+  return pg::window_scored(n_tokens, window, stride, first_window, n_windows);
+}
+
+pg_status pg_window_rows(const int32_t* tokens, int64_t n_tokens, int32_t window, int32_t stride,
+                         int64_t first_window, int32_t n_windows, int32_t* target, uint8_t* score_mask,
+                         void* stream) {
+  if (!window_args_ok(n_tokens, window, stride) || first_window < 0 || n_windows < 1 ||
+      (int64_t)n_windows * window > kMaxRows)
+    return PG_ERR_SHAPE;
+  if ((n_tokens > 0 && !tokens) || !target || !score_mask) return PG_ERR_NULL;
+  if (misaligned(tokens) || misaligned(target) || misaligned(score_mask)) return PG_ERR_ALIGN;
+  pg::DeviceInfo dev{};
+  pg_status s;
+  if ((s = device_check(dev)) != PG_OK) return s;
+  hipError_t e = pg::launch_window_rows(tokens, n_tokens, window, stride, first_window, n_windows, target,
+                                        score_mask, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PG_OK : PG_ERR_HIP;
+}
+
+pg_status pg_sgd_step_bf16(float* master, const float* grad, float lr, int64_t n, void* embed_bf16, void* stream) {
+  if (n < 0) return PG_ERR_SHAPE;
+  if (!std::isfinite(lr)) return PG_ERR_SOFTCAP;
+  if (n == 0) return PG_OK;
+  if (!master || !grad || !embed_bf16) return PG_ERR_NULL;
+  if (misaligned(master) || misaligned(grad) || misaligned(embed_bf16)) return PG_ERR_ALIGN;
+  pg::DeviceInfo dev{};
+  pg_status s;
+  if ((s = device_check(dev)) != PG_OK) return s;
+  hipError_t e = pg::launch_sgd_step(master, grad, lr, n, static_cast<uint16_t*>(embed_bf16),
+                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PG_OK : PG_ERR_HIP;
 }
 

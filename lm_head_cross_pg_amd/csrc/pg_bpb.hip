@@ -69,7 +69,10 @@ __global__ __launch_bounds__(kBpbThreads) void bpb_partial_kernel(const float* n
   if (threadIdx.x == 0) part[blockIdx.x] = acc;
 }
 
-__global__ __launch_bounds__(kBpbThreads) void bpb_final_kernel(const BpbPartial* part, int nblocks, double* out) {
+// accumulate: out[0..2] already hold running sums (of earlier calls in stream order); this call's
+// sums are added to them and out[3] is the bits per byte of the running sums.
+__global__ __launch_bounds__(kBpbThreads) void bpb_final_kernel(const BpbPartial* part, int nblocks, double* out,
+                                                                int accumulate) {
   BpbPartial acc{0.0, 0, 0};
   for (int i = threadIdx.x; i < nblocks; i += kBpbThreads) {
     acc.nats += part[i].nats;
@@ -79,10 +82,16 @@ __global__ __launch_bounds__(kBpbThreads) void bpb_final_kernel(const BpbPartial
   acc = block_reduce(acc);
   if (threadIdx.x == 0) {
     double sum_nats = acc.nats;
-    double sum_bytes = (double)acc.bytes;
+    double sum_bytes = (double)acc.bytes;   // exact below 2^53 bytes
+    double count = (double)acc.count;
+    if (accumulate) {
+      sum_nats += out[0];
+      sum_bytes += out[1];
+      count += out[2];
+    }
     out[0] = sum_nats;
     out[1] = sum_bytes;
-    out[2] = (double)acc.count;
+    out[2] = count;
     out[3] = sum_nats / (0.6931471805599453 * sum_bytes);
   }
 }
@@ -106,7 +115,7 @@ BpbWorkspace bpb_workspace(int64_t T) {
 
 hipError_t launch_bpb(const float* nats, const int32_t* target, const uint8_t* mask,
                       const int32_t* byte_len, const int32_t* byte_per_pos, int64_t T, int32_t V,
-                      double* out, char* ws, hipStream_t st) {
+                      double* out, char* ws, hipStream_t st, bool accumulate) {
   int blocks;
   int64_t rpb;
   bpb_grid(T, blocks, rpb);
@@ -115,7 +124,7 @@ hipError_t launch_bpb(const float* nats, const int32_t* target, const uint8_t* m
                      byte_per_pos, T, V, rpb, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bpb_final_kernel, dim3(1), dim3(kBpbThreads), 0, st, part, blocks, out);
+  hipLaunchKernelGGL(bpb_final_kernel, dim3(1), dim3(kBpbThreads), 0, st, part, blocks, out, (int)accumulate);
   return hipGetLastError();
 }
 

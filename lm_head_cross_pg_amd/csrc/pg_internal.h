@@ -78,10 +78,19 @@ hipError_t launch_quantize(const void* E, int32_t dtype, int32_t V, int32_t D, i
                            hipStream_t st);
 hipError_t launch_dequantize(const int8_t* q, const float* scale, int32_t V, int32_t D, uint16_t* E, hipStream_t st);
 
-// Bits-per-byte launcher (pg_bpb.hip).
+// Bits-per-byte launcher (pg_bpb.hip); accumulate adds to the running sums already in out.
 hipError_t launch_bpb(const float* nats, const int32_t* target, const uint8_t* mask,
                       const int32_t* byte_len, const int32_t* byte_per_pos, int64_t T, int32_t V,
-                      double* out, char* ws, hipStream_t st);
+                      double* out, char* ws, hipStream_t st, bool accumulate = false);
+
+// Sliding-window evaluation (pg_window.hip): the schedule's arithmetic on the host, the targets and
+// score mask of a batch of windows, and the SGD step of score-first test-time training.
+int64_t window_count(int64_t n_tokens, int32_t window, int32_t stride);
+int64_t window_scored(int64_t n_tokens, int32_t window, int32_t stride, int64_t first_window, int64_t n_windows);
+hipError_t launch_window_rows(const int32_t* tokens, int64_t n_tokens, int32_t window, int32_t stride,
+                              int64_t first_window, int64_t n_windows, int32_t* target, uint8_t* mask,
+                              hipStream_t st);
+hipError_t launch_sgd_step(float* master, const float* grad, float lr, int64_t n, uint16_t* out, hipStream_t st);
 
 // dZ block layout (the backward's workspace). dZ[t][v] is stored in 32 x 32 blocks laid out like
 // the accumulator of v_mfma_f32_32x32x16_bf16: block (bt, bv) holds tokens 32 bt .. 32 bt + 31 and

@@ -30,7 +30,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "make_inputs", "bf16_bits", "bf16_to_f64", "as_f64",
-    "stride_mask", "zipf_pmf",
+    "stride_mask", "zipf_pmf", "make_stream", "window_hidden",
 ]
 
 
@@ -187,3 +187,30 @@ def make_inputs(w: Workload | str, seed: int = 0, T: Optional[int] = None) -> di
         hidden=np.ascontiguousarray(hidden), embed=np.ascontiguousarray(embed),
         target=y.astype(np.int32), byte_len=blen.astype(np.int32), mask=mask,
     )
+
+
+def make_stream(seed: int, n_tokens: int, V: int, bos_rate: float = 1.0 / 700.0, D: int = 512,
+                embed_std: float = 0.02) -> dict:
+    """A token stream for the sliding-window evaluation, drawn from
+    ``numpy.random.default_rng([seed, 8])`` in the order embedding, tokens, byte lengths, BOS: a bf16
+    N(0, embed_std^2) tied embedding [V, D], Zipf(1.1) token ids over 1..V-1 with BOS (id 0, zero
+    bytes) at geometric gaps of mean 1 / bos_rate, and byte lengths 1 + min(Poisson(2.7), 15)."""
+    rng = np.random.default_rng([int(seed), 8])
+    e = (rng.standard_normal((V, D), dtype=np.float32) * np.float32(embed_std)).astype(np.float32)
+    toks = 1 + _zipf_draw(rng, n_tokens, V - 1, 1.1)
+    blen = 1 + np.minimum(rng.poisson(2.7, size=V), 15)
+    gaps = rng.geometric(bos_rate, size=max(16, int(3 * n_tokens * bos_rate) + 16))
+    pos = np.cumsum(gaps) - 1
+    toks[pos[pos < n_tokens]] = 0
+    blen[0] = 0
+    return dict(tokens=toks.astype(np.int32), byte_len=blen.astype(np.int32), embed=bf16_bits(e), V=V, D=D)
+
+
+def window_hidden(seed: int, w: int, n: int, D: int) -> np.ndarray:
+    """Stand-in for the model's hidden states of the n predictions that window w scores (bf16 bits
+    [n, D]): unit-RMS rows drawn from ``numpy.random.default_rng([seed, 9, w])``. A position's row
+    depends on the window, as a model's does on the window's context."""
+    rng = np.random.default_rng([int(seed), 9, int(w)])
+    h = rng.standard_normal((n, D), dtype=np.float32)
+    rms = np.sqrt(np.mean(h.astype(np.float64) ** 2, axis=1, keepdims=True))
+    return bf16_bits((h / rms).astype(np.float32))

@@ -1,0 +1,82 @@
+"""Sliding-window evaluation of a token stream, with optional score-first test-time training of the
+tied embedding, driven through the library's C ABI (include/pg_lmhead.h).
+
+Windows of ``window`` tokens advance by ``stride`` over the stream; each scores only the predictions
+no earlier window scored (parameter-golf README leaderboard, "Sliding Window Eval" row, stride 64).
+Batches of ``windows_per_batch`` windows are scored one after another, and the bits per byte
+accumulate over all of them on the device. With ``ttt_lr > 0`` each batch, once scored, also yields
+the gradients of its mean loss, and the tied embedding takes one SGD step on them before the next
+batch is scored: score-first test-time training, every chunk adapted on only after it has been
+scored (README leaderboard, "Legal Score-First TTT" rows, "phased TTT over already-scored validation
+chunks").
+
+This module only sequences calls: the schedule's arithmetic, the rows of each batch, the forward,
+the backward, the sums and the update all run in the library. The hidden states of each batch
+come from the caller (the model run on each window).
+"""
+from __future__ import annotations
+
+from typing import Iterator, Optional, Tuple
+
+import torch
+
+from . import abi
+
+
+class SlidingWindowEval:
+    def __init__(self, tokens: torch.Tensor, byte_len: torch.Tensor, V: int, D: int, window: int = 2048,
+                 stride: int = 64, windows_per_batch: int = 32, softcap: float = 30.0, ttt_lr: float = 0.0,
+                 embed_master: Optional[torch.Tensor] = None):
+        if ttt_lr and embed_master is None:
+            raise ValueError("score-first TTT needs float32 master weights of the embedding (embed_master)")
+        self.tokens, self.byte_len, self.V, self.D = tokens, byte_len, int(V), int(D)
+        self.window, self.stride, self.per_batch = int(window), int(stride), int(windows_per_batch)
+        self.softcap, self.ttt_lr, self.embed_master = float(softcap), float(ttt_lr), embed_master
+        self.n_windows = abi.pg_window_count(tokens.numel(), self.window, self.stride)
+        dev = tokens.device
+        rows = self.per_batch * self.window
+        self.target = torch.empty(rows, dtype=torch.int32, device=dev)
+        self.mask = torch.empty(rows, dtype=torch.uint8, device=dev)
+        self.nats = torch.empty(rows, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(rows, dtype=torch.float32, device=dev)
+        self.out = torch.zeros(4, dtype=torch.float64, device=dev)
+        op = abi.PG_OP_FWD_BWD if self.ttt_lr else abi.PG_OP_FWD
+        self.ws = torch.empty(max(abi.workspace_bytes(op, rows, self.D, self.V), 256), dtype=torch.uint8, device=dev)
+        self.ws_bpb = torch.empty(max(abi.workspace_bytes(abi.PG_OP_BPB, rows, 1, self.V), 256), dtype=torch.uint8,
+                                  device=dev)
+        if self.ttt_lr:
+            self.dH = torch.empty((rows, self.D), dtype=torch.float32, device=dev)
+            self.dE = torch.empty((self.V, self.D), dtype=torch.float32, device=dev)
+
+    def batches(self) -> Iterator[Tuple[int, int]]:
+        """(first window, number of windows) of each batch, in order."""
+        for w0 in range(0, self.n_windows, self.per_batch):
+            yield w0, min(self.per_batch, self.n_windows - w0)
+
+    def scored(self, first_window: int, n_windows: int) -> int:
+        return abi.pg_window_scored(self.tokens.numel(), self.window, self.stride, first_window, n_windows)
+
+    def step(self, hidden: torch.Tensor, embed: torch.Tensor, first_window: int, n_windows: int) -> int:
+        """Score one batch. hidden: [n_windows * window, D] bf16, row (b, r) the hidden state of
+        input position (first_window + b) stride + r in its window (only scored rows are read).
+        embed: the bf16 tied embedding [V, D], updated in place by the SGD step when ttt_lr > 0.
+        Returns the number of predictions the batch scored."""
+        rows = n_windows * self.window
+        tgt, msk, nats, lse = self.target[:rows], self.mask[:rows], self.nats[:rows], self.lse[:rows]
+        abi.pg_window_rows(self.tokens, self.window, self.stride, first_window, n_windows, tgt, msk)
+        n = self.scored(first_window, n_windows)
+        if self.ttt_lr and n > 0:
+            # the batch's scores and the gradients of its mean loss come from the same embedding;
+            # the update reaches only later batches
+            abi.pg_lmhead_ce_fwd_bwd(hidden, embed, tgt, msk, self.softcap, 1.0 / n, nats, lse, self.dH[:rows],
+                                     self.dE, self.ws)
+            abi.pg_bpb_accumulate(nats, tgt, msk, self.byte_len, None, self.V, self.out, self.ws_bpb)
+            abi.pg_sgd_step_bf16(self.embed_master, self.dE, self.ttt_lr, embed)
+        else:
+            abi.pg_lmhead_ce_fwd(hidden, embed, tgt, msk, self.softcap, nats, lse, self.ws)
+            abi.pg_bpb_accumulate(nats, tgt, msk, self.byte_len, None, self.V, self.out, self.ws_bpb)
+        return n
+
+    def result(self):
+        """(sum of nats, sum of bytes, predictions scored, bits per byte) over the batches so far."""
+        return self.out.cpu().tolist()

@@ -31,6 +31,13 @@ What it computes, and where the pages state it:
   "byte-sidecar BPB accounting").
 * Scored rows: a mask selects the rows that count (README leaderboard, "Sliding Window Eval" row,
   stride 64). Unscored rows get nats = 0 and lse = 0 and enter no sum.
+* Sliding-window evaluation of a token stream (same row: windows advance by the stride, "increasing
+  context for eval"): each window scores the predictions no earlier window scored
+  (window_schedule); with score-first test-time training (README leaderboard, "Legal Score-First
+  TTT" rows, "phased TTT over already-scored validation chunks") each batch of windows, once scored,
+  gives one SGD step on the tied embedding for the batches after it (sliding_window_eval). The
+  reading taken for the step: float32 master weights, w <- w - lr g with each operation rounded to
+  float32, and the head reads their bfloat16 rounding.
 * Backward of L = g * sum_scored nats (repo-explainer, ``loss.backward()``):
   dS = g (softmax(s) - onehot(target)), dZ = dS * ds/dz with ds/dz = 1 - tanh(z/c)^2,
   dH = dZ . E, dE = dZ^T . H (the LM-head part of the tied embedding's gradient).
@@ -48,7 +55,8 @@ import numpy as np
 LN2 = float(np.log(2.0))
 
 __all__ = ["LN2", "logits", "softcap", "softcap_derivative", "log_sum_exp", "forward", "bpb",
-           "backward", "embed_grad_rows", "loss", "quantize_rows_q8", "dequantize_rows_q8", "forward_q8"]
+           "backward", "embed_grad_rows", "loss", "quantize_rows_q8", "dequantize_rows_q8", "forward_q8",
+           "window_schedule", "sliding_window_eval"]
 
 
 def logits(H: np.ndarray, E: np.ndarray) -> np.ndarray:
@@ -246,3 +254,63 @@ def embed_grad_rows(H, E, target, c: float, g: float, lse, vocab_rows, mask=None
     dZ[~((target >= 0) & (target < E.shape[0]))] = np.nan   # poisoned rows, as in :func:`backward`
     dZ[~_scored(T, mask)] = 0.0
     return dZ.T @ H
+
+
+def window_schedule(n_tokens: int, window: int, stride: int):
+    """The scored predictions of each window of a sliding-window evaluation, as lists of input
+    positions (position p predicts token p + 1; the predictions are p = 0 .. n_tokens - 2).
+
+    Window w covers input positions w * stride .. w * stride + window - 1 and scores every prediction
+    there that no earlier window has scored; windows are added until every prediction is scored.
+    """
+    n_pred = n_tokens - 1
+    windows = []
+    frontier = 0                       # predictions 0 .. frontier - 1 are scored
+    w = 0
+    while frontier < n_pred:
+        start = w * stride
+        stop = min(start + window, n_pred)
+        windows.append(list(range(max(frontier, start), stop)))
+        frontier = max(frontier, stop)
+        w += 1
+    return windows
+
+
+def sliding_window_eval(tokens, byte_len, hidden_of_window, E, c, window: int, stride: int,
+                        windows_per_batch: int, lr: float = 0.0):
+    """Bits per byte of a token stream under the sliding-window schedule, batch by batch.
+
+    hidden_of_window(w, n) returns the hidden states [n, D] of the n predictions window w scores, in
+    position order (the model run on window w). Batches hold windows_per_batch consecutive windows.
+    With lr > 0, after a batch is scored the gradient of its mean loss (backward with g = 1 / its
+    scored count) gives one SGD step on the embedding: float32 master weights w <- w - lr g, each
+    operation rounded to float32, and the next batch is scored with their bfloat16 rounding.
+    Returns a dict with the sums, the bits per byte, and per batch the positions, the nats and, with
+    lr > 0, the gradients (dH of the scored rows, dE) and the embedding the batch was scored with.
+    """
+    tokens = np.asarray(tokens, dtype=np.int64)
+    byte_len = np.asarray(byte_len, dtype=np.int64)
+    E_used = np.asarray(E, dtype=np.float64)
+    master = E_used.astype(np.float32)
+    sched = window_schedule(len(tokens), window, stride)
+    res = {"sum_nats": 0.0, "sum_bytes": 0, "n_scored": 0, "batches": []}
+    for b0 in range(0, len(sched), windows_per_batch):
+        ws = range(b0, min(b0 + windows_per_batch, len(sched)))
+        pos = np.array([p for w in ws for p in sched[w]], dtype=np.int64)
+        H = np.vstack([np.asarray(hidden_of_window(w, len(sched[w])), dtype=np.float64) for w in ws])
+        y = tokens[pos + 1]
+        nats, _ = forward(H, E_used, y, c)
+        sn, sb, n, _ = bpb(nats, y, byte_len)
+        res["sum_nats"] += sn
+        res["sum_bytes"] += sb
+        res["n_scored"] += n
+        batch = {"first_window": b0, "positions": pos, "nats": nats, "embed": E_used}
+        if lr:
+            dH, dE = backward(H, E_used, y, c, 1.0 / len(pos))
+            batch["dH"], batch["dE"] = dH, dE
+            master = master - np.float32(lr) * dE.astype(np.float32)
+            E_used = _bf16_round(master)
+        res["batches"].append(batch)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        res["bpb"] = float(np.float64(res["sum_nats"]) / (np.float64(LN2) * np.float64(res["sum_bytes"])))
+    return res

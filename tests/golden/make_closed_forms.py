@@ -160,12 +160,35 @@ def rounding_ties():
     }
 
 
+def window_schedules():
+    # written out by hand from the rule; nothing here is computed
+    return {
+        "what": "scored predictions of each window of a sliding-window evaluation of a token stream",
+        "source": ("parameter-golf README leaderboard, 'Sliding Window Eval' row (stride 64, 'increasing context for "
+                   "eval'); the rule for the first window and the stream's end is the reading taken"),
+        "derivation": ("prediction p (p = 0 .. n_tokens - 2) is token p + 1 after tokens 0..p; window w covers input "
+                       "positions w*stride .. w*stride + window - 1 and scores the predictions there that no earlier "
+                       "window scored, until all are scored. E.g. n_tokens = 14, window 8, stride 2: 13 predictions; "
+                       "window 0 (positions 0-7) scores 0-7, window 1 (2-9) adds 8, 9, window 2 (4-11) adds 10, 11, "
+                       "window 3 (6-13) adds 12 (13 predicts past the end)."),
+        "cases": [
+            {"n_tokens": 14, "window": 8, "stride": 2,
+             "windows": [[0, 1, 2, 3, 4, 5, 6, 7], [8, 9], [10, 11], [12]]},
+            {"n_tokens": 5, "window": 8, "stride": 2, "windows": [[0, 1, 2, 3]]},
+            {"n_tokens": 1, "window": 8, "stride": 2, "windows": []},
+            {"n_tokens": 10, "window": 8, "stride": 8, "windows": [[0, 1, 2, 3, 4, 5, 6, 7], [8]]},
+            {"n_tokens": 8, "window": 4, "stride": 1, "windows": [[0, 1, 2, 3], [4], [5], [6]]},
+            {"n_tokens": 12, "window": 6, "stride": 4, "windows": [[0, 1, 2, 3, 4, 5], [6, 7, 8, 9], [10]]},
+        ],
+    }
+
+
 if __name__ == "__main__":
     for name, obj in [("worked_softcap30.json", worked_softcap30()),
                       ("worked_nocap_one_bit_per_byte.json", worked_nocap()),
                       ("worked_asym_softcap_30_10.json", worked_asym()),
                       ("stride64_windows.json", stride64()), ("uniform_logits.json", uniform()),
-                      ("rounding_ties.json", rounding_ties())]:
+                      ("rounding_ties.json", rounding_ties()), ("window_schedules.json", window_schedules())]:
         with open(os.path.join(HERE, name), "w") as f:
             json.dump(obj, f, indent=1)
             f.write("\n")
