@@ -56,8 +56,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // q1 = -log2 e / (3 c^2), q2 = 2 log2 e / (15 c^4): two fma and two multiplies, no transcendental.
 //
 // Asymmetric caps: c (the fields above) applies to z >= 0 and cn to z < 0, each side with its own
-// constants; 0 leaves that side uncapped. The series fast path is not used then (thr = 0), and the
-// fixed log-sum-exp shift is M = c log2 e, the largest possible s * log2 e.
+// constants (series coefficients included); 0 leaves that side uncapped. The series then needs
+// both sides capped and is taken below the smaller cap / 8 (thr); the fixed log-sum-exp shift is
+// M = c log2 e.
 struct Softcap {
   float c;        // cap (0 = none); the cap of z >= 0 when asym
   float alpha;    // 2 log2 e / c
