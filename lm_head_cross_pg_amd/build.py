@@ -33,6 +33,8 @@ def flags() -> list[str]:
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 instructions stay off: the compiler still vectorises with plain ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # check the generated machine code: a backend slip fails the build instead of running
+        "-mllvm", "-verify-machineinstrs",
         "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument",
     ]
 

@@ -142,7 +142,6 @@ struct DzCore {
   static constexpr int kWaves = WaveShape<NB>::kWaves;
   static constexpr int kLoads = embed_loads_per_wave<D, kWaves>();
   const lds_char* lds;
-  char* smem;
   const uint16_t* E;
   int wave, lane;
   int h, col, V;
@@ -241,7 +240,7 @@ struct DzCore {
       if (k < KS) tile_step_priority<KS>(vb, k);
       if (k + PF < KS) fr[k + PF] = frag(k + PF);
       if (LOAD && k % LOAD_EVERY == 0 && k / LOAD_EVERY < kLoads)
-        load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);
+        load_embed_piece<D, kWaves>(lds, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);
       if (k < KS) mfma_step<NB, KS>(a, fr[k], hf, k);
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
@@ -268,7 +267,7 @@ struct DzCore {
                                                    int vprev, int load_tile = 0, int load_buf = 0) {
     if (!CAPPED || KS < 2 * kNST || (ASYM && !(sc.c > 0.f && sc.cn > 0.f))) {   // not pipelined
       if (LOAD)
-        for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, i);
+        for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(lds, E, V, load_tile, load_buf, wave, lane, i);
       tile_stage_priority(vb, false);
       chain(buf, vb, a);
       tile_stage_priority(vb, true);
@@ -323,8 +322,8 @@ void bwd_dz_kernel(DzParams p) {
   const int V = p.V;
 
   DzCore<D, CAPPED, NB, ASYM> core;
-  core.lds = (const lds_char*)smem;
-  core.smem = smem;
+  const lds_char* lds = (const lds_char*)smem;
+  core.lds = lds;
   core.E = p.E;
   core.wave = wave;
   core.lane = lane;
@@ -351,7 +350,7 @@ void bwd_dz_kernel(DzParams p) {
   const bool last_partial = (V % kVocabTile) != 0;
   f32x16 accp[NB];
   int vprev = -1;
-  load_embed_tile<D, kFwdWaves>(smem, p.E, V, 0, 0, wave, lane);
+  load_embed_tile<D, kFwdWaves>(lds, p.E, V, 0, 0, wave, lane);
   for (int i = 0; i < ntiles; ++i) {
     const int buf = i & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -359,7 +358,7 @@ void bwd_dz_kernel(DzParams p) {
     const bool next = i + 1 < ntiles;
     // the steady state spreads the next tile's load over its first chain; elsewhere it goes first
     const bool steady = !(last_partial && i + 1 == ntiles) && vprev >= 0;
-    if (next && !steady) load_embed_tile<D, kFwdWaves>(smem, p.E, V, i + 1, buf ^ 1, wave, lane);
+    if (next && !steady) load_embed_tile<D, kFwdWaves>(lds, p.E, V, i + 1, buf ^ 1, wave, lane);
     const int vb0 = i * kVocabTile;
     f32x16 a0[NB];
     if (last_partial && i + 1 == ntiles) {

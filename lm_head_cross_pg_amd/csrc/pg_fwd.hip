@@ -82,7 +82,6 @@ struct FwdCore {
   static constexpr int kWaves = WaveShape<NB>::kWaves;
   static constexpr int kLoads = embed_loads_per_wave<D, kWaves>();
   const lds_char* lds;
-  char* smem;
   const uint16_t* E;
   int wave, lane;
   int h, col, V;
@@ -101,9 +100,19 @@ struct FwdCore {
   int ykey[NB];
   float ty[NB];
 
+  // (s log2 e) - M (fixed shift) and s log2 e (running maximum) of logit z. The cap form is chosen
+  // by the template parameter, so a symmetric kernel carries no code or constants of the other side.
+  __device__ __forceinline__ float shifted(float z) const {
+    return ASYM ? capped_shifted_sc(z, sc) : capped_shifted(z, sc.alpha, sc.invK);
+  }
+  __device__ __forceinline__ float log2cap(float z) const {
+    if (ASYM) return capped_log2(z, sc);
+    return sc.c > 0.f ? sc.M + capped_shifted(z, sc.alpha, sc.invK) : z * kLog2e;
+  }
+
   // The term 2^t the exp-sum adds for logit z in each form: the operations of the pipelined stages
   // below (and of part_exact), in the same order, so the value is the one that was summed.
-  __device__ __forceinline__ float term_exact(float z) const { return fexp2(capped_shifted_sc(z, sc)); }
+  __device__ __forceinline__ float term_exact(float z) const { return fexp2(shifted(z)); }
   __device__ __forceinline__ float term_series(float z) const {
     const bool neg = ASYM && z < 0.f;
     const float u = z * z;
@@ -126,7 +135,7 @@ struct FwdCore {
 #pragma unroll
         for (int r = 1; r < 16; ++r) z = ri == r ? acc[tb][r] : z;
         if (hit) {
-          if (!FIXED) ty[tb] = capped_log2(z, sc);
+          if (!FIXED) ty[tb] = log2cap(z);
           else ty[tb] = series ? term_series(z) : term_exact(z);
         }
       }
@@ -157,7 +166,7 @@ struct FwdCore {
     float d[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float t = capped_shifted_sc(acc[r], sc);
+      const float t = shifted(acc[r]);
       d[r] = fexp2(t) * dz_slope(t, ASYM && acc[r] < 0.f);
       if (MASKED) d[r] = (vbase + 8 * (r >> 2) + 4 * h + (r & 3)) < V ? d[r] : 0.f;
     }
@@ -176,7 +185,7 @@ struct FwdCore {
     float part = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float w = fexp2(capped_shifted_sc(acc[r], sc));
+      const float w = fexp2(shifted(acc[r]));
       if (MASKED) {
         const int v = vbase + 8 * (r >> 2) + 4 * h + (r & 3);
         part += v < V ? w : 0.f;
@@ -195,7 +204,7 @@ struct FwdCore {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int v = vbase + 8 * (r >> 2) + 4 * h + (r & 3);
-      s2[r] = (!MASKED || v < V) ? capped_log2(acc[r], sc) : -INFINITY;
+      s2[r] = (!MASKED || v < V) ? log2cap(acc[r]) : -INFINITY;
       bm = fmaxf(bm, s2[r]);
     }
     const float mn = fmaxf(mrun[tb], bm);
@@ -254,7 +263,7 @@ struct FwdCore {
       if (k < KS) tile_step_priority<KS>(vb, k);
       if (k + PF < KS) fr[k + PF] = frag(k + PF);
       if (LOAD && k % LOAD_EVERY == 0 && k / LOAD_EVERY < kLoads)
-        load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);
+        load_embed_piece<D, kWaves>(lds, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);
       if (k < KS) {
         if (NB == 2) lds_wait_upto((k + PF < KS ? k + PF : KS - 1) - k);
         mfma_step<NB, KS>(a, fr[k], hf, k);
@@ -293,7 +302,7 @@ struct FwdCore {
     constexpr int NE = NB * 16;
     if (!FIXED) {   // running maximum (c = 0 or caps above the fixed-shift range)
       if (LOAD)
-        for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(smem, E, V, load_tile, load_buf, wave, lane, i);
+        for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(lds, E, V, load_tile, load_buf, wave, lane, i);
       tile_stage_priority(vb, false);
       chain(buf, vb, a);
       tile_stage_priority(vb, true);
@@ -328,6 +337,11 @@ struct FwdCore {
             break;
         }
       });
+      // as for the series below: a use of the sums right here keeps the compiler from sinking the
+      // whole epilogue past the chain to where lsum is next read (it would then run after the
+      // MFMAs instead of between them)
+#pragma unroll
+      for (int tb = 0; tb < NB; ++tb) asm volatile("" ::"v"(part[tb]));
 #pragma unroll
       for (int tb = 0; tb < NB; ++tb) lsum[tb] += part[tb];
       if (exact_left > 0) --exact_left;
@@ -411,8 +425,8 @@ void fwd_mfma_kernel(FwdParams p) {
   const int64_t tok0 = (int64_t)rt * kRowsPerWG + wave * kTokPerWave;   // first token of this wave
 
   FwdCore<D, FIXED, NB, ASYM, DZ> core;
-  core.lds = (const lds_char*)smem;
-  core.smem = smem;
+  const lds_char* lds = (const lds_char*)smem;
+  core.lds = lds;
   core.E = p.E;
   core.wave = wave;
   core.lane = lane;
@@ -424,7 +438,7 @@ void fwd_mfma_kernel(FwdParams p) {
 
   // ---- the first embedding tile goes out first, so that its latency overlaps the prologue
   const int ntiles = t_end - t_begin;
-  if (ntiles > 0) load_embed_tile<D, kFwdWaves>(smem, p.E, V, t_begin, 0, wave, lane);
+  if (ntiles > 0) load_embed_tile<D, kFwdWaves>(lds, p.E, V, t_begin, 0, wave, lane);
 
   // ---- this lane's tokens: hidden row halves into registers (B operands of the MFMA)
   // (token and row indices are recomputed after the main loop, so that they hold no registers)
@@ -469,7 +483,7 @@ void fwd_mfma_kernel(FwdParams p) {
     f32x16 a0[NB];
     // the steady state spreads the next tile's load over the first chain; elsewhere it goes first
     const bool steady = !(last_partial && i + 1 == ntiles) && vprev >= 0;
-    if (next && !steady) load_embed_tile<D, kFwdWaves>(smem, p.E, V, tile + 1, buf ^ 1, wave, lane);
+    if (next && !steady) load_embed_tile<D, kFwdWaves>(lds, p.E, V, tile + 1, buf ^ 1, wave, lane);
     if (last_partial && i + 1 == ntiles) {
       core.chain(buf, 0, a0);
       if (vprev >= 0) {

@@ -52,11 +52,12 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, const lds_char* lds_
       : "memory");
 }
 
-// One embedding tile from global memory into LDS buffer `buf` with global_load_lds_dwordx4
+// One embedding tile from global memory into LDS buffer `buf` (LDS pointers throughout: a generic
+// pointer cast back to LDS in the loop costs a null check per cast) with global_load_lds_dwordx4
 // (1 KiB per instruction, no VGPR round trip), spread over `nwaves` waves. Rows past the end of
 // the vocabulary repeat the last row (valid memory; their logits are masked by the caller).
 template <int D, int NWAVES>
-__device__ __forceinline__ void load_embed_tile(char* smem, const uint16_t* E, int V, int tile, int buf,
+__device__ __forceinline__ void load_embed_tile(const lds_char* lds, const uint16_t* E, int V, int tile, int buf,
                                                 int wave, int lane) {
   using TL = TileLayout<D>;
   constexpr int NI = kVocabTile * TL::ROWB / 1024;
@@ -69,8 +70,7 @@ __device__ __forceinline__ void load_embed_tile(char* smem, const uint16_t* E, i
     const int lchunk = pchunk ^ TL::swz(row);
     const int v = min(v0 + row, V - 1);
     const char* g = reinterpret_cast<const char*>(E + (int64_t)v * D) + lchunk * 16;
-    char* dst = smem + buf * TL::TILEB + (TL::PAD ? j * TL::PITCH : j * 1024);
-    lds_dma16(g, (const lds_char*)dst);
+    lds_dma16(g, lds + buf * TL::TILEB + (TL::PAD ? j * TL::PITCH : j * 1024));
   }
 }
 
@@ -83,7 +83,7 @@ __host__ __device__ constexpr int embed_loads_per_wave() {
   return (kVocabTile * TileLayout<D>::ROWB / 1024 + NWAVES - 1) / NWAVES;
 }
 template <int D, int NWAVES>
-__device__ __forceinline__ void load_embed_piece(char* smem, const uint16_t* E, int V, int tile, int buf, int wave,
+__device__ __forceinline__ void load_embed_piece(const lds_char* lds, const uint16_t* E, int V, int tile, int buf, int wave,
                                                  int lane, int i) {
   using TL = TileLayout<D>;
   constexpr int NI = kVocabTile * TL::ROWB / 1024;
@@ -96,8 +96,7 @@ __device__ __forceinline__ void load_embed_piece(char* smem, const uint16_t* E, 
   const int lchunk = pchunk ^ TL::swz(row);
   const int v = min(v0 + row, V - 1);
   const char* g = reinterpret_cast<const char*>(E + (int64_t)v * D) + lchunk * 16;
-  char* dst = smem + buf * TL::TILEB + (TL::PAD ? j * TL::PITCH : j * 1024);
-  lds_dma16(g, (const lds_char*)dst);
+  lds_dma16(g, lds + buf * TL::TILEB + (TL::PAD ? j * TL::PITCH : j * 1024));
 }
 
 // v_mfma_f32_32x32x16_bf16 with the B operand (hidden rows) read straight from AGPRs and the
