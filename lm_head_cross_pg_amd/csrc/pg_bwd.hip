@@ -235,12 +235,16 @@ struct DzCore {
 #pragma unroll
     for (int k = 0; k < PF; ++k) fr[k] = frag(k);
     constexpr int LOAD_EVERY = (KS / kLoads) < 4 ? ((KS / kLoads) < 1 ? 1 : KS / kLoads) : 4;
+    PieceBase pb{};
+    if (LOAD && TL::PAD) pb = piece_base<D>(lds, load_tile, load_buf, wave);
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
       if (k < KS) tile_step_priority<KS>(vb, k);
       if (k + PF < KS) fr[k + PF] = frag(k + PF);
-      if (LOAD && k % LOAD_EVERY == 0 && k / LOAD_EVERY < kLoads)
-        load_embed_piece<D, kWaves>(lds, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);
+      if (LOAD && k % LOAD_EVERY == 0 && k / LOAD_EVERY < kLoads) {
+        if constexpr (TL::PAD) load_embed_piece_padded<D, kWaves>(pb, E, V, lane, k / LOAD_EVERY);
+        else load_embed_piece<D, kWaves>(lds, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);
+      }
       if (k < KS) mfma_step<NB, KS>(a, fr[k], hf, k);
 #pragma unroll
       for (int st = 0; st < NST; ++st) {

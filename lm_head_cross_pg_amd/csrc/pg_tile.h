@@ -52,6 +52,20 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, const lds_char* lds_
       : "memory");
 }
 
+// The same DMA with the LDS address given as a 32-bit value (an SGPR).
+__device__ __forceinline__ void lds_dma16_m0(const void* gptr, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(lds_addr)
+      : "memory");
+}
+
 // One embedding tile from global memory into LDS buffer `buf` (LDS pointers throughout: a generic
 // pointer cast back to LDS in the loop costs a null check per cast) with global_load_lds_dwordx4
 // (1 KiB per instruction, no VGPR round trip), spread over `nwaves` waves. Rows past the end of
@@ -82,6 +96,32 @@ template <int D, int NWAVES>
 __host__ __device__ constexpr int embed_loads_per_wave() {
   return (kVocabTile * TileLayout<D>::ROWB / 1024 + NWAVES - 1) / NWAVES;
 }
+// Per-tile bases of the pieces of padded (D = 512) tiles, where piece i of wave w is the whole row
+// w + NWAVES i: the LDS address of the wave's first row in the buffer and its vocabulary row. Both
+// are made opaque to the compiler, so that each piece's address is one scalar add from them: left
+// to itself, the compiler hoists every piece's offsets out of the loop as invariants, which do not
+// fit the SGPRs and come back as VALU lane reads in every chain.
+struct PieceBase {
+  uint32_t lds;   // LDS address of row `wave` of the buffer
+  int row;        // vocabulary row of that row
+};
+template <int D>
+__device__ __forceinline__ PieceBase piece_base(const lds_char* lds, int tile, int buf, int wave) {
+  using TL = TileLayout<D>;
+  PieceBase b;
+  b.lds = (uint32_t)(uintptr_t)(lds + buf * TL::TILEB + wave * TL::PITCH);
+  b.row = tile * kVocabTile + wave;
+  asm volatile("" : "+s"(b.lds), "+s"(b.row));
+  return b;
+}
+template <int D, int NWAVES>
+__device__ __forceinline__ void load_embed_piece_padded(const PieceBase& b, const uint16_t* E, int V, int lane, int i) {
+  using TL = TileLayout<D>;
+  static_assert(TL::PAD, "rows of 1 KiB");
+  const int v = min(b.row + i * NWAVES, V - 1);
+  lds_dma16_m0(reinterpret_cast<const char*>(E + (int64_t)v * D) + lane * 16, b.lds + i * NWAVES * TL::PITCH);
+}
+
 template <int D, int NWAVES>
 __device__ __forceinline__ void load_embed_piece(const lds_char* lds, const uint16_t* E, int V, int tile, int buf, int wave,
                                                  int lane, int i) {
