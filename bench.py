@@ -325,9 +325,9 @@ def summarize_trace(d, steps, warmup):
     for r in stats:
         lines.append(f"| `{r['Name'][:72]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
-    # bench.py's order: warmup + timed steps of the sustained loop (each forward followed by the two
-    # bits-per-byte kernels), then --steps isolated forwards back to back. A main-forward launch is
-    # classed by the kernel after it.
+    # bench.py's order: --steps isolated forwards back to back, then the warmup and timed steps of the
+    # sustained loop (each forward followed by the two bits-per-byte kernels). A main-forward launch
+    # is classed by the kernel after it.
     tr = sorted(csv.DictReader(open(os.path.join(d, "trace", "run_kernel_trace.csv"))),
                 key=lambda r: int(r["Start_Timestamp"]))
     sustained, isolated = [], []
@@ -336,24 +336,25 @@ def summarize_trace(d, steps, warmup):
             continue
         dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         nxt = tr[i + 1]["Kernel_Name"] if i + 1 < len(tr) else ""
-        if "bpb_partial_kernel" in nxt and not isolated:
+        if "bpb_partial_kernel" in nxt:
             sustained.append(dt)
-        elif len(isolated) < steps and (nxt.startswith(main_kernel) or isolated):
+        elif not sustained and len(isolated) < steps:
             isolated.append(dt)
-    timed = sustained[-steps:]
+    timed = sustained[warmup:warmup + steps]
     flop = 2.0 * 65536 * 512 * 8192
+    if isolated:
+        m = sum(isolated) / len(isolated)
+        lines += ["", f"The {len(isolated)} isolated forwards that open the run (back to back, events between them, "
+                      "while the clock settles): mean",
+                  f"{m:.1f} us (min {min(isolated):.1f}, max {max(isolated):.1f}), frac "
+                  f"{flop / (m * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.3f}."]
     if timed:
         m = sum(timed) / len(timed)
         lines += ["", f"The `roofline` figure of `bench.py` is the forward's own time inside its sustained loop: the "
-                      f"{len(timed)} timed forwards", f"(after {len(sustained) - len(timed)} warmup steps), each "
+                      f"{len(timed)} timed forwards", f"(after {warmup} warmup steps), each "
                       "followed by the bits-per-byte reduction, in this trace taken on the benchmark's command:",
                   f"mean {m:.1f} us (min {min(timed):.1f}, max {max(timed):.1f}): "
                   f"{flop / (m * 1e-6) / 1e12:.0f} TFLOP/s, frac {flop / (m * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.3f}."]
-    if isolated:
-        m = sum(isolated) / len(isolated)
-        lines += [f"The {len(isolated)} isolated forwards that follow (back to back, events between them): mean "
-                  f"{m:.1f} us (min {min(isolated):.1f}, max {max(isolated):.1f}), frac "
-                  f"{flop / (m * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.3f}."]
     lines += ["", "Commands (cd /tmp first; R = repository root; summarised by "
                   "`python3 bench.py --summarize-trace <dir>`):", "", "```",
               f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace -o run -- python3 $R/bench.py "
