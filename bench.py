@@ -541,8 +541,8 @@ def main():
         abi.pg_bpb_reduce(nats, d["target"], None, d["byte_len"], None, V, out, ws_bpb)
 
     # the forward alone, launches back to back with events between them (the isolated figure). It
-    # runs first: the GPU's power management takes about 10 ms of load to settle (launch times dip by
-    # up to 20 % on the way), so the main loop's warmup and timed steps then see the settled clock.
+    # runs first: the GPU's power management takes 10-20 ms of load to settle (launches run up to 20 %
+    # slower on the way), so the main loop's warmup and timed steps then see the settled clock.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if args.cold else None
     for a, b in ev:
