@@ -241,9 +241,10 @@ pg_status pg_bpb_accumulate(const float* nats, const int32_t* target, const uint
  *
  * pg_window_count: the number of windows that cover the stream (0 when n_tokens < 2).
  * pg_window_scored: the number of predictions that windows first_window .. first_window +
- *   n_windows - 1 score. Both are host arithmetic (no device, no stream) and return
- *   PG_ERR_SHAPE (negative) for n_tokens < 0, window < 1, stride < 1, stride > window,
- *   first_window < 0 or n_windows < 0.
+ *   n_windows - 1 score (windows past the last one score none). Both are host arithmetic (no
+ *   device, no stream) and return PG_ERR_SHAPE (negative) for n_tokens < 0 or > 2^40,
+ *   window < 1, stride < 1, stride > window, first_window < 0 or > pg_window_count, or
+ *   n_windows < 0.
  * pg_window_rows: the rows of a batch of windows, laid out as n_windows x window rows, row
  *   (b, r) being input position (first_window + b) stride + r: target [n_windows * window] int32
  *   gets token p + 1 of each row's position p (0 past the stream), score_mask the same count of

@@ -364,8 +364,17 @@ pg_status pg_bpb_accumulate(const float* nats, const int32_t* target, const uint
 
 // ------------------------------------------------------------------ sliding-window evaluation
 
+// A stream longer than 2^40 tokens (4 TiB of ids) cannot be in device memory; the bound keeps
+// every position w stride + r of a window that starts in the stream far inside int64.
+constexpr int64_t kMaxStreamTokens = (int64_t)1 << 40;
+
 static bool window_args_ok(int64_t n_tokens, int32_t window, int32_t stride) {
-  return n_tokens >= 0 && window >= 1 && stride >= 1 && stride <= window;
+  return n_tokens >= 0 && n_tokens <= kMaxStreamTokens && window >= 1 && stride >= 1 && stride <= window;
+}
+
+// first_window may name the window just past the last one (an empty run) but nothing beyond it.
+static bool first_window_ok(int64_t n_tokens, int32_t window, int32_t stride, int64_t first_window) {
+  return first_window >= 0 && first_window <= pg::window_count(n_tokens, window, stride);
 }
 
 int64_t pg_window_count(int64_t n_tokens, int32_t window, int32_t stride) {
@@ -374,15 +383,17 @@ int64_t pg_window_count(int64_t n_tokens, int32_t window, int32_t stride) {
 }
 
 int64_t pg_window_scored(int64_t n_tokens, int32_t window, int32_t stride, int64_t first_window, int32_t n_windows) {
-  if (!window_args_ok(n_tokens, window, stride) || first_window < 0 || n_windows < 0) return PG_ERR_SHAPE;
+  if (!window_args_ok(n_tokens, window, stride) || !first_window_ok(n_tokens, window, stride, first_window) ||
+      n_windows < 0)
+    return PG_ERR_SHAPE;
   return pg::window_scored(n_tokens, window, stride, first_window, n_windows);
 }
 
 pg_status pg_window_rows(const int32_t* tokens, int64_t n_tokens, int32_t window, int32_t stride,
                          int64_t first_window, int32_t n_windows, int32_t* target, uint8_t* score_mask,
                          void* stream) {
-  if (!window_args_ok(n_tokens, window, stride) || first_window < 0 || n_windows < 1 ||
-      (int64_t)n_windows * window > kMaxRows)
+  if (!window_args_ok(n_tokens, window, stride) || !first_window_ok(n_tokens, window, stride, first_window) ||
+      n_windows < 1 || (int64_t)n_windows * window > kMaxRows)
     return PG_ERR_SHAPE;
   if ((n_tokens > 0 && !tokens) || !target || !score_mask) return PG_ERR_NULL;
   if (misaligned(tokens) || misaligned(target) || misaligned(score_mask)) return PG_ERR_ALIGN;

@@ -58,16 +58,20 @@ int64_t window_count(int64_t n_tokens, int32_t window, int32_t stride) {
   return 1 + (n_pred - window + stride - 1) / stride;
 }
 
+// Predictions scored by windows 0 .. k - 1: the frontier after window k - 1, min(n_pred,
+// (k - 1) stride + window) (each window scores the run from the previous frontier to its end).
+static int64_t window_frontier(int64_t n_pred, int32_t window, int32_t stride, int64_t k) {
+  if (k <= 0 || n_pred <= 0) return 0;
+  const int64_t end = (k - 1) * stride + window;
+  return end < n_pred ? end : n_pred;
+}
+
 int64_t window_scored(int64_t n_tokens, int32_t window, int32_t stride, int64_t first_window, int64_t n_windows) {
   const int64_t n_pred = n_tokens - 1;
-  int64_t total = 0;
-  for (int64_t w = first_window; w < first_window + n_windows; ++w) {
-    const int64_t lo = w == 0 ? 0 : w * stride + window - stride;
-    const int64_t hi = w * stride + window;
-    const int64_t top = hi < n_pred ? hi : n_pred;
-    total += top > lo ? top - lo : 0;
-  }
-  return total;
+  const int64_t count = window_count(n_tokens, window, stride);
+  const int64_t a = first_window < count ? first_window : count;
+  const int64_t b = n_windows < count - a ? a + n_windows : count;
+  return window_frontier(n_pred, window, stride, b) - window_frontier(n_pred, window, stride, a);
 }
 
 hipError_t launch_window_rows(const int32_t* tokens, int64_t n_tokens, int32_t window, int32_t stride,

@@ -67,6 +67,24 @@ def test_abi_schedule_arithmetic_matches_oracle(lib):
     assert lib.pg_window_scored(10, 4, 2, -1, 1) == -2 and lib.pg_window_count(10, 0, 1) == -2
 
 
+def test_abi_schedule_bounds(lib):
+    """Runs that reach past the last window score only up to the end of the stream; a first window
+    past the one after the last, or a stream beyond 2^40 tokens, is a shape error; huge counts
+    are arithmetic, not loops."""
+    n, L, s = 4625, 2048, 64
+    count = abi.pg_window_count(n, L, s)
+    assert count == 42
+    assert lib.pg_window_scored(n, L, s, count, 5) == 0                 # the empty run just past the end
+    assert lib.pg_window_scored(n, L, s, count + 1, 1) == -2
+    assert lib.pg_window_scored(n, L, s, 0, 2**31 - 1) == n - 1         # every prediction once
+    assert lib.pg_window_scored(n, L, s, 40, 2**31 - 1) == sum(len(w) for w in ora.window_schedule(n, L, s)[40:])
+    big = 2**40
+    assert lib.pg_window_count(big, L, s) == 1 + (big - 1 - L + s - 1) // s
+    assert lib.pg_window_scored(big, L, s, 0, 2**31 - 1) == L + (2**31 - 2) * s
+    assert lib.pg_window_count(big + 1, L, s) == -2
+    assert lib.pg_window_scored(big + 1, L, s, 0, 1) == -2
+
+
 def _stream(seed=0, n=700, V=300, D=16):
     st = synth.make_stream(seed, n, V, bos_rate=1 / 50, D=D)
     return st["tokens"], st["byte_len"], synth.bf16_to_f64(st["embed"])
