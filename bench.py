@@ -139,6 +139,42 @@ def summarize_counters(d):
             if v is not None:
                 out[nm] = v
                 lines.append(f"| {nm} per launch | {v:.4g} |")
+    trows = _counter_rows(os.path.join(d, "tcc"))
+    if trows:
+        hit, _ = _per_dispatch(trows, FWD_KERNEL, "TCC_HIT_sum")
+        miss, _ = _per_dispatch(trows, FWD_KERNEL, "TCC_MISS_sum")
+        if hit is not None and miss is not None and hit + miss > 0:
+            out["l2_hit_pct"] = 100.0 * hit / (hit + miss)
+            lines.append(f"| L2 hits / (hits + misses), TCC_HIT_sum and TCC_MISS_sum | {out['l2_hit_pct']:.1f} % "
+                         f"({hit:.4g} hits, {miss:.4g} misses) |")
+    # HBM traffic of every kernel of the training step (and the rest of the benchmark), same scales
+    tf, tw = _counter_rows(os.path.join(d, "train_fetch")), _counter_rows(os.path.join(d, "train_write"))
+    train_lines = []
+    if tf and tw:
+        names = sorted({r["Kernel_Name"] for r in tf if r["Kernel_Name"].startswith("void pg::") or
+                        r["Kernel_Name"].startswith("pg::")})
+        train_lines = ["", "HBM traffic per launch of each library kernel in the benchmark run with the training "
+                           "step (without the sliding-window leg), at each kernel's largest grid (the T = 65536 "
+                           "workloads): FETCH_SIZE x fetch scale, WRITE_SIZE x write scale, MiB.", "",
+                       "| kernel | grid (work-items) | launches | fetched | written |", "|---|---|---|---|---|"]
+
+        def at_grid(rows, nm, counter, grid):
+            per = {}
+            for r in rows:
+                if r["Kernel_Name"] == nm and r["Counter_Name"] == counter and int(r["Grid_Size"]) == grid:
+                    per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+            return (sum(per.values()) / len(per), len(per)) if per else (None, 0)
+
+        for nm in names:
+            short = nm.split("(")[0].replace("void ", "")
+            grid = max(int(r["Grid_Size"]) for r in tf if r["Kernel_Name"] == nm)
+            fv, n = at_grid(tf, nm, "FETCH_SIZE", grid)
+            wv, _ = at_grid(tw, nm, "WRITE_SIZE", grid)
+            if fv is None or wv is None:
+                continue
+            train_lines.append(f"| `{short}` | {grid} | {n} | {fv * 1024.0 * kf / 2**20:.1f} | "
+                               f"{wv * 1024.0 * kw / 2**20:.1f} |")
+    lines += train_lines
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
@@ -151,6 +187,9 @@ def summarize_counters(d):
               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/calib_write -- python3 bench.py --calibrate-copy",
               "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU "
               "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT --output-format csv -d <dir>/mfma -- python3 bench.py --steps 3 --warmup 1 --no-train --no-cpu",
+              "rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d <dir>/tcc -- python3 bench.py --steps 3 --warmup 1 --no-train --no-cpu",
+              "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/train_fetch -- python3 bench.py --steps 3 --warmup 1 --no-cpu --no-window",
+              "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/train_write -- python3 bench.py --steps 3 --warmup 1 --no-cpu --no-window",
               "python3 bench.py --summarize-counters <dir>",
               "```", ""]
     with open(md, "w") as f:
@@ -158,10 +197,12 @@ def summarize_counters(d):
     print(json.dumps(out))
 
 
-def cpu_baseline(inp, chunk: int = 1024):
-    """The float64 oracle over every row of the workload once (the full forward), in row chunks run
-    concurrently on all of the host's cores: each worker thread calls the unchanged oracle on its
-    chunks with one BLAS thread (numpy releases the GIL in the matmul and the elementwise steps)."""
+def _oracle_pass(inp, rows, train: bool, chunk: int = 1024):
+    """The float64 oracle over the given rows of a workload once, in row chunks run concurrently
+    on all of the host's cores: each worker thread calls the unchanged oracle on its chunks with one
+    BLAS thread (numpy releases the GIL in the matmul and the elementwise steps). train adds the
+    oracle's backward (g = 1 / rows) after the forward of each chunk. Returns (rows, seconds,
+    worker threads)."""
     from concurrent.futures import ThreadPoolExecutor
     from oracle import oracle as ora
     from lm_head_cross_pg_amd import synth
@@ -170,13 +211,18 @@ def cpu_baseline(inp, chunk: int = 1024):
     except AttributeError:
         cores = os.cpu_count() or 1
     E = synth.as_f64(inp["embed"], inp["dtype"])
-    y = inp["target"]
-    T = inp["T"]
+    c = inp["softcap"]
+    rows = np.asarray(rows)
+    g = 1.0 / max(len(rows), 1)
 
     def work(r0):
-        H = synth.as_f64(inp["hidden"][r0:r0 + chunk], inp["dtype"])
-        ora.forward(H, E, y[r0:r0 + chunk], inp["softcap"])
-        return H.shape[0]
+        r = rows[r0:r0 + chunk]
+        H = synth.as_f64(inp["hidden"][r], inp["dtype"])
+        y = inp["target"][r]
+        ora.forward(H, E, y, c)
+        if train:
+            ora.backward(H, E, y, c, g)
+        return len(r)
 
     import contextlib
     try:
@@ -187,10 +233,17 @@ def cpu_baseline(inp, chunk: int = 1024):
     with one_blas_thread:
         t0 = time.perf_counter()
         with ThreadPoolExecutor(max_workers=cores) as ex:
-            rows = sum(ex.map(work, range(0, T, chunk)))
+            done = sum(ex.map(work, range(0, len(rows), chunk)))
         dt = time.perf_counter() - t0
+    return done, dt, cores
+
+
+def cpu_baseline(inp, train: bool = False):
+    """The oracle's forward (or forward + backward) over every row of the workload once."""
+    rows, dt, cores = _oracle_pass(inp, np.arange(inp["T"]), train)
+    what = "forward + backward" if train else "forward"
     return {"value": rows / dt, "unit": "scored tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"the full forward: all {rows} rows of the same workload once, {chunk}-row chunks on {cores} "
+            "sample": f"the full {what}: all {rows} rows of the same workload once, 1024-row chunks on {cores} "
                       f"worker threads (one per host core, one BLAS thread each), float64 numpy "
                       f"(matmul, tanh, exp, log), {dt:.1f} s wall"}
 
@@ -236,6 +289,16 @@ def other_configs(abi, synth, args):
                      "ms_per_step": wall * 1e3, "event_ms_per_step": ev_ms,
                      "scored_tokens_per_s": n_scored / wall,
                      "frac_bf16_peak": flop / wall / 1e12 / PEAK_BF16_TFLOPS, "bpb": float(out[3].item())}
+        if not args.no_cpu:
+            # the oracle beside it: its forward over the scored rows (the definition's loop), the
+            # median of 5 passes
+            rows = np.arange(T) if inp["mask"] is None else np.nonzero(inp["mask"])[0]
+            passes = [_oracle_pass(inp, rows, False) for _ in range(5)]
+            dt = float(np.median([p[1] for p in passes]))
+            res[name]["cpu_baseline"] = {
+                "value": len(rows) / dt, "unit": "scored tokens/s", "cores": passes[0][2], "kind": "oracle",
+                "sample": f"the forward over the {len(rows)} scored rows, median of 5 passes on "
+                          f"{passes[0][2]} worker threads, float64 numpy, {dt * 1e3:.1f} ms per pass"}
     print(json.dumps({"other_configs": res, "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
@@ -476,6 +539,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-window", action="store_true",
+                    help="leave out the sliding-window driver leg (for counter runs of the training step)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (HBM counter calibration)")
     ap.add_argument("--cold", action="store_true",
@@ -748,7 +813,10 @@ def main():
             "note": "medians of HIP-event-timed steps run back to back (20 for the variants)",
         }
 
-    if not args.no_train:
+        if not args.no_cpu:
+            result["train_step"]["cpu_baseline"] = cpu_baseline(tin, train=True)
+
+    if not args.no_train and not args.no_window:
         result["window_eval"] = window_eval(abi, synth, args)
 
     if not args.no_cpu:

@@ -32,7 +32,7 @@
  *     every entry of dembed sums over the rows, into all of dembed (the loss itself is NaN then).
  *   - nats >= 0 on every scored row: the target's logit is taken from the same accumulation that
  *     forms the log-sum-exp, so p(target) <= 1 holds in floating point too (a one-entry vocabulary
- *     gives exactly 0).
+ *     gives exactly 0; the last step, a difference of two hardware log2 values, is floored at 0).
  *   - Unscored rows (score_mask[t] == 0) get nats = lse = 0, zero dH rows, and add nothing to any
  *     sum. A NULL score_mask scores every row.
  */

@@ -27,6 +27,13 @@ constexpr int kVocabTile = 64;
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+// log2(l) - ly for a sum l of non-negative terms one of which is 2^ly: l >= 2^ly exactly, so the
+// difference is >= 0 wherever the hardware log2 is monotone; a negative rounding artefact is
+// returned as 0 (NaN, the poison of an unmatched target, passes through).
+__device__ __forceinline__ float log2_ratio(float l, float ly) {
+  const float d = flog2(l) - ly;
+  return d < 0.f ? 0.f : d;
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);

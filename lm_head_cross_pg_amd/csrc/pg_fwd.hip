@@ -523,7 +523,8 @@ void fwd_mfma_kernel(FwdParams p) {
 
   // ---- combine the two lane halves (each holds 16 of every 32 vocabulary rows) and write out.
   //      With the fixed shift nats = ln 2 (log2 l - log2 e_y), where e_y is the target's own term of
-  //      the sum l: since l >= e_y, nats >= 0, and nats = 0 exactly when e_y is all of l (V = 1).
+  //      the sum l: since l >= e_y, nats >= 0 (log2_ratio floors a rounding of the hardware log2
+  //      below 0 at 0), and nats = 0 exactly when e_y is all of l (V = 1).
   //      With a running maximum m, nats = ln 2 (m + log2 l - s_y log2 e), where l >= 1 (the maximum's
   //      own term) and m >= s_y log2 e.
 #pragma unroll
@@ -545,7 +546,7 @@ void fwd_mfma_kernel(FwdParams p) {
       const int64_t grow = row_of(tok);
       if (p.direct) {
         const float lse2 = (FIXED ? p.sc.M : m) + flog2(l);
-        p.nats[grow] = kLn2 * (FIXED ? flog2(l) - sy : lse2 - sy);
+        p.nats[grow] = kLn2 * (FIXED ? log2_ratio(l, sy) : lse2 - sy);
         if (p.lse) p.lse[grow] = kLn2 * lse2;
       } else {
         p.part_l[(int64_t)split * n + tok] = l;
@@ -580,7 +581,7 @@ __global__ __launch_bounds__(256) void fwd_finalize_kernel(FwdParams p, int main
     for (; s < S; ++s) l += p.part_l[(int64_t)s * n + i];
     // s_target holds log2 of the target's own term of l (see fwd_mfma_kernel)
     const int64_t r = p.rows ? (int64_t)p.rows[i] : i;
-    p.nats[r] = kLn2 * (flog2(l) - p.s_target[i]);
+    p.nats[r] = kLn2 * log2_ratio(l, p.s_target[i]);
     if (p.lse) p.lse[r] = kLn2 * (p.sc.M + flog2(l));
     return;
   } else {

@@ -298,6 +298,39 @@ def test_bpb_reduction_row_counts(T):
         assert out[3] == pytest.approx(b, rel=1e-12)
 
 
+def test_bpb_accumulated_over_calls():
+    """pg_bpb_accumulate over consecutive chunks of 1,000,003 rows (chunk sizes around the
+    reduction's workgroup sizes, one without scored rows), with a mask, targets outside the
+    vocabulary and a byte sidecar: the running sums after the last call are the oracle's sums over
+    all rows (integers exactly), and out[3] is their ratio after every call."""
+    V, T = 8192, 1000003
+    rng = np.random.default_rng(17)
+    nats = rng.uniform(0.0, 12.0, size=T).astype(np.float32)
+    y = rng.integers(-2, V + 2, size=T).astype(np.int32)
+    blen = rng.integers(0, 17, size=V).astype(np.int32)
+    mask = (rng.random(T) < 0.7).astype(np.uint8)
+    bpp = rng.integers(0, 9, size=T).astype(np.int32)
+    # chunk starts 16-byte aligned for every array (the entry points require it); a 262,144-row
+    # chunk is 1024 workgroups of 256 rows, the last one takes several rows per thread
+    cuts = [0, 16, 256, 272, 608, 608 + 262144, 608 + 262144 + 16, T]
+    mask[608:608 + 262144] = 0                             # a chunk with no scored row
+    print("[case] bpb accumulated over calls", flush=True)
+    t_y, t_n = torch.from_numpy(y).cuda(), torch.from_numpy(nats).cuda()
+    t_m, t_s, t_b = torch.from_numpy(mask).cuda(), torch.from_numpy(bpp).cuda(), torch.from_numpy(blen).cuda()
+    for side in (None, t_s):
+        out = torch.zeros(4, dtype=torch.float64, device="cuda")
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            abi.pg_bpb_accumulate(t_n[a:b], t_y[a:b], t_m[a:b], t_b, None if side is None else side[a:b], V, out)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            sn, sb, n, bb = ora.bpb(nats[:b].astype(np.float64), y[:b], blen, mask[:b],
+                                    None if side is None else bpp[:b], V=V)
+            assert got[1] == sb and got[2] == n
+            assert got[0] == pytest.approx(sn, rel=1e-12)
+            if sb:
+                assert got[3] == pytest.approx(bb, rel=1e-12)
+
+
 def test_bitwise_reproducible():
     inp = synth.make_inputs("fwd_v1024", 0)
     d = abi.to_device(inp)
