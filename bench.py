@@ -21,7 +21,6 @@ import argparse
 import hashlib
 import re
 import json
-import math
 import os
 import sys
 import time

@@ -1,7 +1,6 @@
 """GPU parity at the size limits of the C ABI: the widest vocabulary (V = 2^20) and the widest hidden
 state (D = 2^20) the entry points accept, and a vocabulary beyond 2^16 through one-call training,
 against the float64 oracle."""
-import dataclasses
 
 import numpy as np
 import pytest
