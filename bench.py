@@ -196,12 +196,12 @@ def summarize_counters(d):
     print(json.dumps(out))
 
 
-def _oracle_pass(inp, rows, train: bool, chunk: int = 1024):
+def _oracle_pass(inp, rows, train: bool, chunk: int = 1024, fn=None):
     """The float64 oracle over the given rows of a workload once, in row chunks run concurrently
     on all of the host's cores: each worker thread calls the unchanged oracle on its chunks with one
     BLAS thread (numpy releases the GIL in the matmul and the elementwise steps). train adds the
-    oracle's backward (g = 1 / rows) after the forward of each chunk. Returns (rows, seconds,
-    worker threads)."""
+    oracle's backward (g = 1 / rows) after the forward of each chunk; fn(H, y), when given, replaces
+    both (another oracle entry on the chunk). Returns (rows, seconds, worker threads)."""
     from concurrent.futures import ThreadPoolExecutor
     from oracle import oracle as ora
     from lm_head_cross_pg_amd import synth
@@ -218,6 +218,9 @@ def _oracle_pass(inp, rows, train: bool, chunk: int = 1024):
         r = rows[r0:r0 + chunk]
         H = synth.as_f64(inp["hidden"][r], inp["dtype"])
         y = inp["target"][r]
+        if fn is not None:
+            fn(H, y)
+            return len(r)
         ora.forward(H, E, y, c)
         if train:
             ora.backward(H, E, y, c, g)
@@ -237,10 +240,10 @@ def _oracle_pass(inp, rows, train: bool, chunk: int = 1024):
     return done, dt, cores
 
 
-def cpu_baseline(inp, train: bool = False):
-    """The oracle's forward (or forward + backward) over every row of the workload once."""
-    rows, dt, cores = _oracle_pass(inp, np.arange(inp["T"]), train)
-    what = "forward + backward" if train else "forward"
+def cpu_baseline(inp, train: bool = False, fn=None, what=None):
+    """The oracle's forward (or forward + backward, or fn) over every row of the workload once."""
+    rows, dt, cores = _oracle_pass(inp, np.arange(inp["T"]), train, fn=fn)
+    what = what or ("forward + backward" if train else "forward")
     return {"value": rows / dt, "unit": "scored tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"the full {what}: all {rows} rows of the same workload once, 1024-row chunks on {cores} "
                       f"worker threads (one per host core, one BLAS thread each), float64 numpy "
@@ -523,8 +526,32 @@ def window_eval(abi, synth, args):
             if it:                                   # the first pass is a warmup
                 times.append(a.elapsed_time(b))
         ms = float(np.median(times))
-        res["ttt_lr_%g" % lr] = {"ms_per_pass": ms, "predictions": n, "scored_tokens_per_s": n / (ms * 1e-3),
-                                 "bpb": drv.result()[3]}
+        # per scored row: the forward, and with training the embedding's gradient dE (the driver takes
+        # no gradient of the hidden states, so that product does not run and is not counted)
+        flop = (4.0 if lr else 2.0) * n * D * V
+        entry = {"ms_per_pass": ms, "predictions": n, "scored_tokens_per_s": n / (ms * 1e-3),
+                 "frac_bf16_peak": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                 "frac_counted_as": "4 T_s D V (forward + dE)" if lr else "2 T_s D V (forward)",
+                 "bpb": drv.result()[3]}
+        if not args.no_cpu:
+            # the oracle's own sliding-window loop on the same stream, hidden states and steps
+            from oracle import oracle as ora
+            try:
+                cores = len(os.sched_getaffinity(0))
+            except AttributeError:
+                cores = os.cpu_count() or 1
+            t0 = time.perf_counter()
+            ref = ora.sliding_window_eval(st["tokens"], st["byte_len"],
+                                          lambda w, k: synth.bf16_to_f64(synth.window_hidden(args.seed, w, k, D)),
+                                          synth.bf16_to_f64(st["embed"]), 30.0, L, s, B, lr=lr)
+            dt = time.perf_counter() - t0
+            entry["bpb_oracle"] = ref["bpb"]
+            entry["cpu_baseline"] = {
+                "value": ref["n_scored"] / dt, "unit": "scored tokens/s", "cores": cores, "kind": "oracle",
+                "sample": f"the oracle's sliding-window loop over the same {ref['n_scored']} predictions "
+                          f"(3 batches{', each with its backward and SGD step' if lr else ''}), float64 numpy "
+                          f"(BLAS on every core, the elementwise steps on one thread), {dt:.1f} s wall"}
+        res["ttt_lr_%g" % lr] = entry
     res["workload"] = "stream of %d tokens, windows of %d at stride %d, %d windows per batch, D=%d, V=%d" % (
         n_tokens, L, s, B, D, V)
     return res
@@ -698,6 +725,11 @@ def main():
         "achieved_tflops": flop_fwd / (asym_ms * 1e-3) / 1e12,
         "frac": flop_fwd / (asym_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bpb": float(out[3].item()),
         "note": "fused forward with separate caps for z >= 0 and z < 0 (each side's tanh series below min(caps)/8, exact softcap above)"}
+    if not args.no_cpu:
+        from oracle import oracle as ora
+        E64 = synth.as_f64(inp["embed"], inp["dtype"])
+        result["asym_softcap"]["cpu_baseline"] = cpu_baseline(
+            inp, fn=lambda H, y: ora.forward(H, E64, y, caps), what="forward with caps (30, 20)")
 
     # the same head on logits of a trained model's magnitude: hidden x 8 (exact in bf16) gives z with
     # standard deviation ~3.6, so almost every 32 x 32 block has some |z| > c/8 and the epilogue
@@ -747,6 +779,11 @@ def main():
         "launch_ms": q8_ms, "tokens_per_s": T / (q8_ms * 1e-3),
         "frac": flop_fwd / (q8_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bpb": float(out[3].item()),
         "note": "launch = dequantise (8 MiB bf16 written) + fused forward"}
+    if not args.no_cpu:
+        from oracle import oracle as ora
+        q_o, s_o = ora.quantize_rows_q8(synth.as_f64(inp["embed"], inp["dtype"]))
+        result["q8_head"]["cpu_baseline"] = cpu_baseline(
+            inp, fn=lambda H, y: ora.forward_q8(H, q_o, s_o, y, c), what="forward on the int8 head")
 
     if not args.no_train:
         tin = synth.make_inputs("train_v8192", args.seed)

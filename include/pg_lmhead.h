@@ -112,7 +112,9 @@ pg_status pg_lmhead_ce_fwd_noalloc(const void* hidden, const void* embed, int32_
  * Backward of L = grad_scale * sum over scored rows of nats (mean cross-entropy: grad_scale =
  * 1 / number of scored rows). The logits are recomputed from hidden and embed; lse must be the
  * output of pg_lmhead_ce_fwd on the same inputs.
- *   dhidden     [T, D] f32 out, overwritten; rows of unscored positions are zero
+ *   dhidden     [T, D] f32 out, overwritten; rows of unscored positions are zero. NULL leaves
+ *               dH out (its product is not run): for callers that train the embedding alone, such
+ *               as score-first test-time training of the tied embedding
  *   dembed      [V, D] f32 out, overwritten; the LM-head part of the tied embedding's gradient
  *               only (the caller adds the gradient of the input lookup)
  *   workspace   at least pg_workspace_bytes(PG_OP_BWD, T, D, V) bytes (holds bf16 dZ [T, V])

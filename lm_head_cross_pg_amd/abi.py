@@ -232,13 +232,13 @@ def pg_lmhead_ce_fwd_noalloc(hidden: torch.Tensor, embed: torch.Tensor, target: 
 
 
 def _bwd_outputs(a: _Args, T, D, V, dhidden, dembed):
-    a(dhidden, "dhidden", (torch.float32,), numel=T * D)
+    a(dhidden, "dhidden", (torch.float32,), numel=T * D, optional=True)   # None: no dH
     a(dembed, "dembed", (torch.float32,), numel=V * D)
 
 
 def pg_lmhead_ce_bwd(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Tensor,
                      score_mask: Optional[torch.Tensor], lse: torch.Tensor, softcap: float,
-                     grad_scale: float, dhidden: torch.Tensor, dembed: torch.Tensor,
+                     grad_scale: float, dhidden: Optional[torch.Tensor], dembed: torch.Tensor,
                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     a = _Args("pg_lmhead_ce_bwd")
     T, D, V = _head(a, hidden, embed, target, score_mask)
@@ -253,7 +253,7 @@ def pg_lmhead_ce_bwd(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Te
 
 def pg_lmhead_ce_fwd_bwd(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Tensor,
                          score_mask: Optional[torch.Tensor], softcap: float, grad_scale: float,
-                         nats: torch.Tensor, lse: torch.Tensor, dhidden: torch.Tensor, dembed: torch.Tensor,
+                         nats: torch.Tensor, lse: torch.Tensor, dhidden: Optional[torch.Tensor], dembed: torch.Tensor,
                          workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     a = _Args("pg_lmhead_ce_fwd_bwd")
     T, D, V = _head(a, hidden, embed, target, score_mask)
@@ -284,7 +284,7 @@ def pg_lmhead_ce_fwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: tor
 
 def pg_lmhead_ce_bwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Tensor,
                           score_mask: Optional[torch.Tensor], lse: torch.Tensor, cap_pos: float, cap_neg: float,
-                          grad_scale: float, dhidden: torch.Tensor, dembed: torch.Tensor,
+                          grad_scale: float, dhidden: Optional[torch.Tensor], dembed: torch.Tensor,
                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     a = _Args("pg_lmhead_ce_bwd_asym")
     T, D, V = _head(a, hidden, embed, target, score_mask)
@@ -300,7 +300,7 @@ def pg_lmhead_ce_bwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: tor
 
 def pg_lmhead_ce_fwd_bwd_asym(hidden: torch.Tensor, embed: torch.Tensor, target: torch.Tensor,
                               score_mask: Optional[torch.Tensor], cap_pos: float, cap_neg: float, grad_scale: float,
-                              nats: torch.Tensor, lse: torch.Tensor, dhidden: torch.Tensor, dembed: torch.Tensor,
+                              nats: torch.Tensor, lse: torch.Tensor, dhidden: Optional[torch.Tensor], dembed: torch.Tensor,
                               workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     a = _Args("pg_lmhead_ce_fwd_bwd_asym")
     T, D, V = _head(a, hidden, embed, target, score_mask)

@@ -173,7 +173,7 @@ static pg_status bwd_impl(const void* hidden, const void* embed, int32_t dtype, 
                           void* workspace, size_t workspace_bytes, void* stream) {
   pg_status s;
   if ((s = check_shape(T, D, V)) != PG_OK || (s = check_bwd_shape(T, D, V)) != PG_OK) return s;
-  if (T > 0 && (!hidden || !target || !lse || !dhidden)) return PG_ERR_NULL;
+  if (T > 0 && (!hidden || !target || !lse)) return PG_ERR_NULL;   // dhidden may be NULL: no dH
   if (!embed || !dembed || !workspace) return PG_ERR_NULL;
   if (dtype != PG_DTYPE_BF16 && dtype != PG_DTYPE_F32) return PG_ERR_DTYPE;
   if ((s = check_softcap(cap_pos)) != PG_OK || (s = check_softcap(cap_neg)) != PG_OK) return s;
@@ -233,7 +233,7 @@ static pg_status train_impl(const void* hidden, const void* embed, int32_t dtype
                             float* dembed, void* workspace, size_t workspace_bytes, void* stream) {
   pg_status s;
   if ((s = check_shape(T, D, V)) != PG_OK || (s = check_bwd_shape(T, D, V)) != PG_OK) return s;
-  if (T > 0 && (!hidden || !target || !nats || !lse || !dhidden)) return PG_ERR_NULL;
+  if (T > 0 && (!hidden || !target || !nats || !lse)) return PG_ERR_NULL;   // dhidden may be NULL: no dH
   if (!embed || !dembed || !workspace) return PG_ERR_NULL;
   if (dtype != PG_DTYPE_BF16 && dtype != PG_DTYPE_F32) return PG_ERR_DTYPE;
   if ((s = check_softcap(cap_pos)) != PG_OK || (s = check_softcap(cap_neg)) != PG_OK) return s;

@@ -515,8 +515,10 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     if (e != hipSuccess) return e;
     rows = reinterpret_cast<const int32_t*>(ws + L.rows);
     n_dev = reinterpret_cast<const int32_t*>(ws + L.n_rows);
-    hipLaunchKernelGGL(zero_unscored_kernel, dim3(stride_blocks(T * D, 256)), dim3(256), 0, st, mask, T, D, dH);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (dH) {
+      hipLaunchKernelGGL(zero_unscored_kernel, dim3(stride_blocks(T * D, 256)), dim3(256), 0, st, mask, T, D, dH);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   uint16_t* dz = reinterpret_cast<uint16_t*>(ws + L.dz);
   if (dtype == 0 && mfma_width(D)) {
@@ -545,17 +547,19 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
 
-      // dH = g dZ E
-      GemmParams a{};
-      a.A = dz; a.lda = q.ldz / 32;
-      a.a_mblocks = (int64_t)rblk * (kRowsPerWG / 32);   // token blocks of the padded dZ rows
-      a.B = (const uint16_t*)E; a.ldb = D;
-      a.n_dev = n_dev; a.m_dev = n_dev != nullptr; a.k_dev = 0;
-      a.M = T; a.N = D; a.K = V; a.kvalid = V;
-      a.alpha = grad_scale;
-      a.C = dH; a.ldc = D; a.crows = rows; a.split_stride = 0;
-      e = launch_gemm(a, false, 1, st);
-      if (e != hipSuccess) return e;
+      // dH = g dZ E (left out when the caller takes no dH)
+      if (dH) {
+        GemmParams a{};
+        a.A = dz; a.lda = q.ldz / 32;
+        a.a_mblocks = (int64_t)rblk * (kRowsPerWG / 32);   // token blocks of the padded dZ rows
+        a.B = (const uint16_t*)E; a.ldb = D;
+        a.n_dev = n_dev; a.m_dev = n_dev != nullptr; a.k_dev = 0;
+        a.M = T; a.N = D; a.K = V; a.kvalid = V;
+        a.alpha = grad_scale;
+        a.C = dH; a.ldc = D; a.crows = rows; a.split_stride = 0;
+        e = launch_gemm(a, false, 1, st);
+        if (e != hipSuccess) return e;
+      }
     }
     // dE = g dZ^T H, k split over workgroups when the output has few tiles
     const int64_t tiles = ((int64_t)(V + gemm_tile_m(true) - 1) / gemm_tile_m(true)) *
@@ -592,13 +596,15 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     if (dtype == 0) {
       hipLaunchKernelGGL(dz_generic_kernel<uint16_t>, dim3(rblocks), dim3(256), 0, st, (const uint16_t*)H,
                          (const uint16_t*)E, target, lse, rows, n_dev, T, D, V, sc, dz);
-      hipLaunchKernelGGL(dh_generic_kernel<uint16_t>, dim3(hblocks), dim3(256), 0, st, dz, (const uint16_t*)E,
-                         rows, n_dev, T, D, V, grad_scale, dH);
+      if (dH)
+        hipLaunchKernelGGL(dh_generic_kernel<uint16_t>, dim3(hblocks), dim3(256), 0, st, dz, (const uint16_t*)E,
+                           rows, n_dev, T, D, V, grad_scale, dH);
     } else {
       hipLaunchKernelGGL(dz_generic_kernel<float>, dim3(rblocks), dim3(256), 0, st, (const float*)H,
                          (const float*)E, target, lse, rows, n_dev, T, D, V, sc, dz);
-      hipLaunchKernelGGL(dh_generic_kernel<float>, dim3(hblocks), dim3(256), 0, st, dz, (const float*)E,
-                         rows, n_dev, T, D, V, grad_scale, dH);
+      if (dH)
+        hipLaunchKernelGGL(dh_generic_kernel<float>, dim3(hblocks), dim3(256), 0, st, dz, (const float*)E,
+                           rows, n_dev, T, D, V, grad_scale, dH);
     }
   }
   if (dtype == 0)
@@ -639,7 +645,7 @@ hipError_t launch_train(const void* H, const void* E, int32_t dtype, const int32
   const FwdWorkspace F = fwd_workspace(T, D, V);
   const int32_t* rows = mask ? reinterpret_cast<const int32_t*>(ws + W.fwd + F.rows) : nullptr;
   const int32_t* n_dev = mask ? reinterpret_cast<const int32_t*>(ws + W.fwd + F.n_rows) : nullptr;
-  if (mask) {
+  if (mask && dH) {
     hipLaunchKernelGGL(zero_unscored_kernel, dim3(stride_blocks(T * D, 256)), dim3(256), 0, st, mask, T, D, dH);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -652,16 +658,18 @@ hipError_t launch_train(const void* H, const void* E, int32_t dtype, const int32
                      row_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  // dH = f dZ' E, row by row
-  GemmParams a{};
-  a.A = dz; a.lda = ldz / 32;
-  a.a_mblocks = rblk * (kRowsPerWG / 32);
-  a.B = (const uint16_t*)E; a.ldb = D;
-  a.n_dev = n_dev; a.m_dev = n_dev != nullptr; a.k_dev = 0;
-  a.M = T; a.N = D; a.K = V; a.kvalid = V;
-  a.alpha = 1.f;
-  a.C = dH; a.ldc = D; a.crows = rows; a.split_stride = 0; a.row_scale = row_scale;
-  if ((e = launch_gemm(a, false, 1, st)) != hipSuccess) return e;
+  // dH = f dZ' E, row by row (left out when the caller takes no dH)
+  if (dH) {
+    GemmParams a{};
+    a.A = dz; a.lda = ldz / 32;
+    a.a_mblocks = rblk * (kRowsPerWG / 32);
+    a.B = (const uint16_t*)E; a.ldb = D;
+    a.n_dev = n_dev; a.m_dev = n_dev != nullptr; a.k_dev = 0;
+    a.M = T; a.N = D; a.K = V; a.kvalid = V;
+    a.alpha = 1.f;
+    a.C = dH; a.ldc = D; a.crows = rows; a.split_stride = 0; a.row_scale = row_scale;
+    if ((e = launch_gemm(a, false, 1, st)) != hipSuccess) return e;
+  }
 
   // dE = dZ'^T (f H): the row factors sit in the scaled hidden rows
   const int64_t tiles = ((int64_t)(V + gemm_tile_m(true) - 1) / gemm_tile_m(true)) *

@@ -26,12 +26,16 @@ from . import abi
 class SlidingWindowEval:
     def __init__(self, tokens: torch.Tensor, byte_len: torch.Tensor, V: int, D: int, window: int = 2048,
                  stride: int = 64, windows_per_batch: int = 32, softcap: float = 30.0, ttt_lr: float = 0.0,
-                 embed_master: Optional[torch.Tensor] = None):
+                 embed_master: Optional[torch.Tensor] = None, keep_dhidden: bool = False):
+        """keep_dhidden: with ttt_lr > 0, also compute the gradient of the hidden states of each
+        batch (into self.dH). The embedding step needs only dE, so by default dH is left out and
+        its product is not run."""
         if ttt_lr and embed_master is None:
             raise ValueError("score-first TTT needs float32 master weights of the embedding (embed_master)")
         self.tokens, self.byte_len, self.V, self.D = tokens, byte_len, int(V), int(D)
         self.window, self.stride, self.per_batch = int(window), int(stride), int(windows_per_batch)
         self.softcap, self.ttt_lr, self.embed_master = float(softcap), float(ttt_lr), embed_master
+        self.keep_dhidden = bool(keep_dhidden)
         self.n_windows = abi.pg_window_count(tokens.numel(), self.window, self.stride)
         dev = tokens.device
         rows = self.per_batch * self.window
@@ -44,8 +48,10 @@ class SlidingWindowEval:
         self.ws = torch.empty(max(abi.workspace_bytes(op, rows, self.D, self.V), 256), dtype=torch.uint8, device=dev)
         self.ws_bpb = torch.empty(max(abi.workspace_bytes(abi.PG_OP_BPB, rows, 1, self.V), 256), dtype=torch.uint8,
                                   device=dev)
+        self.dH = None
         if self.ttt_lr:
-            self.dH = torch.empty((rows, self.D), dtype=torch.float32, device=dev)
+            if self.keep_dhidden:
+                self.dH = torch.empty((rows, self.D), dtype=torch.float32, device=dev)
             self.dE = torch.empty((self.V, self.D), dtype=torch.float32, device=dev)
 
     def batches(self) -> Iterator[Tuple[int, int]]:
@@ -68,8 +74,8 @@ class SlidingWindowEval:
         if self.ttt_lr and n > 0:
             # the batch's scores and the gradients of its mean loss come from the same embedding;
             # the update reaches only later batches
-            abi.pg_lmhead_ce_fwd_bwd(hidden, embed, tgt, msk, self.softcap, 1.0 / n, nats, lse, self.dH[:rows],
-                                     self.dE, self.ws)
+            dH = self.dH[:rows] if self.dH is not None else None
+            abi.pg_lmhead_ce_fwd_bwd(hidden, embed, tgt, msk, self.softcap, 1.0 / n, nats, lse, dH, self.dE, self.ws)
             abi.pg_bpb_accumulate(nats, tgt, msk, self.byte_len, None, self.V, self.out, self.ws_bpb)
             abi.pg_sgd_step_bf16(self.embed_master, self.dE, self.ttt_lr, embed)
         else:

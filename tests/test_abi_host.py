@@ -145,7 +145,8 @@ def test_validation_codes(lib, call):
 def test_fused_training_validation(lib):
     assert fwd_bwd(lib, lse=None) == -1           # required here (the backward half needs it)
     assert fwd_bwd(lib, nats=None) == -1
-    assert fwd_bwd(lib, dh=None) == -1
+    # dhidden is optional (no dH): the call gets past the pointer checks to the workspace check
+    assert fwd_bwd(lib, dh=None, wsb=1) == -5
     assert fwd_bwd(lib, de=None) == -1
     assert fwd_bwd(lib, dtype=2) == -3
     assert fwd_bwd(lib, c=-1.0) == -4
@@ -175,7 +176,7 @@ def test_forward_validation(lib):
 
 def test_backward_validation(lib):
     assert bwd(lib, lse=None) == -1
-    assert bwd(lib, dh=None) == -1
+    assert bwd(lib, dh=None, wsb=1) == -5      # dhidden is optional (no dH)
     assert bwd(lib, de=None) == -1
     assert bwd(lib, g=float("nan")) == -4
     assert bwd(lib, dtype=5) == -3

@@ -321,3 +321,42 @@ def test_out_of_range_target_poisons_gradients(fused, name, over):
         else:
             assert np.all(n[bad] == 0.0) and np.all(dHn[bad] == 0.0)
             assert np.all(np.isfinite(dEn)) and rel_l2(dEn, mdE) <= GRAD_RL2
+
+
+@pytest.mark.parametrize("path,over,masked", [
+    ("fused", {}, False), ("fused", {}, True), ("two_calls", {}, False), ("two_calls", {}, True),
+    ("fused", {"D": 48}, True), ("two_calls", {"dtype": "f32", "D": 64}, False),
+    ("fused_asym", {}, True), ("fused", {"softcap": 50.0}, True)])
+def test_without_dhidden(path, over, masked):
+    """dhidden = NULL leaves dH out (its product is not run): dE, nats and lse are those of the call
+    that also computes dH, bit for bit, on the one-call path (where the forward writes dZ, and its
+    fallbacks: a generic width, a cap above the fixed-shift range), the two calls, and both
+    precisions, masked and not."""
+    w = workload("train_v8192", T=700, V=1500, stream=140 + len(over), **over)
+    inp = synth.make_inputs(w, 0)
+    T, D, V = inp["T"], inp["D"], inp["V"]
+    c = inp["softcap"]
+    mask = (np.random.default_rng(9).random(T) < 0.4).astype(np.uint8) if masked else None
+    print(f"[case] no dH {path} {over} masked={masked}", flush=True)
+    d = abi.to_device(inp)
+    mask_t = None if mask is None else torch.from_numpy(mask).cuda()
+    g = 1.0 / T
+    res = []
+    for with_dh in (True, False):
+        nats = torch.empty(T, device="cuda")
+        lse = torch.empty(T, device="cuda")
+        dH = torch.full((T, D), float("nan"), device="cuda") if with_dh else None
+        dE = torch.full((V, D), float("nan"), device="cuda")
+        if path == "fused":
+            abi.pg_lmhead_ce_fwd_bwd(d["hidden"], d["embed"], d["target"], mask_t, c, g, nats, lse, dH, dE)
+        elif path == "fused_asym":
+            abi.pg_lmhead_ce_fwd_bwd_asym(d["hidden"], d["embed"], d["target"], mask_t, 30.0, 20.0, g, nats, lse,
+                                          dH, dE)
+        else:
+            abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], mask_t, c, nats, lse)
+            abi.pg_lmhead_ce_bwd(d["hidden"], d["embed"], d["target"], mask_t, lse, c, g, dH, dE)
+        torch.cuda.synchronize()
+        res.append((nats.cpu().numpy(), lse.cpu().numpy(), dE.cpu().numpy()))
+    for a, b in zip(res[0], res[1]):
+        np.testing.assert_array_equal(a, b)
+    assert np.all(np.isfinite(res[1][2]))

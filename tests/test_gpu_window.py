@@ -71,7 +71,7 @@ def test_sgd_step_bit_exact():
     np.testing.assert_array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), synth.bf16_bits(exp))
 
 
-def _run(seed, n_tokens, windows_per_batch, lr, D=512, V=8192, window=2048, stride=64):
+def _run(seed, n_tokens, windows_per_batch, lr, D=512, V=8192, window=2048, stride=64, keep_dhidden=True):
     st = synth.make_stream(seed, n_tokens, V, D=D)
     tokens, blen = st["tokens"], st["byte_len"]
     sched = ora.window_schedule(n_tokens, window, stride)
@@ -82,7 +82,7 @@ def _run(seed, n_tokens, windows_per_batch, lr, D=512, V=8192, window=2048, stri
     E16 = torch.from_numpy(st["embed"].view(np.int16)).cuda().view(torch.bfloat16)
     master = torch.from_numpy(synth.bf16_to_f64(st["embed"]).astype(np.float32)).cuda() if lr else None
     drv = SlidingWindowEval(torch.from_numpy(tokens).cuda(), torch.from_numpy(blen).cuda(), V, D, window, stride,
-                            windows_per_batch, 30.0, ttt_lr=lr, embed_master=master)
+                            windows_per_batch, 30.0, ttt_lr=lr, embed_master=master, keep_dhidden=keep_dhidden)
     assert drv.n_windows == len(sched)
     got = []
     for w0, nw in drv.batches():
@@ -99,7 +99,8 @@ def _run(seed, n_tokens, windows_per_batch, lr, D=512, V=8192, window=2048, stri
         rec = {"n": n, "nats": drv.nats[:rows][mask].cpu().numpy().astype(np.float64)}
         if lr:
             rec["dE"] = drv.dE.cpu().numpy().astype(np.float64)
-            rec["dH"] = drv.dH[:rows][mask].cpu().numpy().astype(np.float64)
+            if keep_dhidden:
+                rec["dH"] = drv.dH[:rows][mask].cpu().numpy().astype(np.float64)
         got.append(rec)
     torch.cuda.synchronize()
     ref = ora.sliding_window_eval(tokens, blen, lambda w, n: synth.bf16_to_f64(hid(w, n)),
@@ -115,7 +116,8 @@ def _check(drv, got, ref):
         assert np.max(np.abs(g["nats"] - r["nats"])) <= NATS_ATOL
         if "dE" in r:
             assert rel_l2(g["dE"], r["dE"]) <= GRAD_RL2, rel_l2(g["dE"], r["dE"])
-            assert rel_l2(g["dH"], r["dH"]) <= GRAD_RL2, rel_l2(g["dH"], r["dH"])
+            if "dH" in g:
+                assert rel_l2(g["dH"], r["dH"]) <= GRAD_RL2, rel_l2(g["dH"], r["dH"])
     sn, sb, n, b = drv.result()
     assert n == ref["n_scored"] and sb == ref["sum_bytes"]
     assert abs(sn - ref["sum_nats"]) <= BPB_RTOL * ref["sum_nats"]
@@ -148,3 +150,17 @@ def test_driver_masked_workload_scale():
     drv, got, ref = _run(2, 2048 + 64 * 95 + 1, 32, 2.0)
     assert len(got) == 3
     _check(drv, got, ref)
+
+
+def test_driver_ttt_without_dhidden():
+    """Score-first training as the driver runs it by default, without the hidden states' gradient
+    (its product is left out): the nats, dE and bits per byte of every batch are those of the run
+    that also computes dH, bit for bit (dE does not depend on dH), and match the oracle."""
+    drv_h, got_h, _ = _run(3, 4625, 8, 2.0, keep_dhidden=True)
+    drv, got, ref = _run(3, 4625, 8, 2.0, keep_dhidden=False)
+    assert drv.dH is None
+    _check(drv, got, ref)
+    for a, b in zip(got, got_h):
+        np.testing.assert_array_equal(a["nats"], b["nats"])
+        np.testing.assert_array_equal(a["dE"], b["dE"])
+    assert drv.result() == drv_h.result()
