@@ -7,22 +7,24 @@
  *                                                    projection (trios issue #19, approach table,
  *                                                    "Tied embeddings"; parameter-golf README
  *                                                    leaderboard, "Naive Baseline": TiedEmbeddings)
- *   softcap     s = c * tanh(z / c), c = 0: s = z    ("fused softcapped CE kernel", HYDRA Golf site
+ *   softcap     s = c * tanh(z / c), c = 0: s = z    (a fused softcapped cross-entropy kernel: HYDRA Golf site
  *                                                    stack list; README leaderboard, PR #1787 row)
  *   loss        nats[t] = logsumexp_v s[t,v] - s[t,y[t]]   (trios issue, "Контекст": cross-entropy)
  *   metric      bpb = sum nats / (ln 2 * sum bytes(y[t])) over scored rows   (README introduction:
- *                                                    "evaluated by compression ... bits per byte")
+ *                                                    the challenge scores compression, in bits per byte)
  *   backward    dZ = g (softmax(s) - onehot(y)) * (1 - (s/c)^2), dH = dZ E, dE = dZ^T H
  *                                                    (repo-explainer, "The Baseline Is a Map":
- *                                                    loss.backward())
+ *                                                    the backward pass of the baseline's loss)
  *
  * Conventions for every entry point:
  *   - Array pointers are DEVICE pointers (hipMalloc'ed or equivalent), row-major and contiguous,
  *     16-byte aligned. H is [T, D], E is [V, D]; D is the fastest axis of both.
  *   - bf16 arrays hold raw bfloat16 bit patterns (uint16). f32 arrays are IEEE binary32.
  *   - The caller owns every buffer, including the workspace. The library allocates no device
- *     memory, keeps no pointer after a call returns and has no mutable global state beyond a
- *     per-device cache of the device check.
+ *     memory and keeps no caller pointer after a call returns. Its only global state is a
+ *     per-device cache of the device check and, for pg_lmhead_ce_fwd_noalloc, a static device
+ *     array per GPU (part of the loaded code object) with its cached address; that array keeps
+ *     the last such call's contents.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default stream) and never
  *     synchronises the host. Buffers must stay alive until the stream's work is done.
  *   - Arguments are validated on the host before anything is launched; a non-zero status means
@@ -128,7 +130,7 @@ pg_status pg_lmhead_ce_bwd(const void* hidden, const void* embed, int32_t dtype,
 /*
  * Forward and backward in one call: the outputs of pg_lmhead_ce_fwd (nats, lse) and of
  * pg_lmhead_ce_bwd (dhidden, dembed) for the same arguments, the training step of the head
- * (repo-explainer, baseline listing: loss = criterion(logits, y), then loss.backward()). For bf16
+ * (repo-explainer, baseline listing: the loss, then its backward pass). For bf16
  * with D in {32, 64, 128, 256, 512} and 0 < softcap <= 40 the logits are computed once: the forward
  * also stores the gradient of every logit with the fixed shift of its log-sum-exp in place of the
  * not yet known lse, and the row factor that corrects it is applied when lse is known (in the dH
@@ -207,7 +209,7 @@ pg_status pg_lmhead_ce_fwd_q8(const void* hidden, const int8_t* embed_q8, const 
  *                 [0, V) adds no bytes (pg_lmhead_ce_fwd gives such a row NaN nats)
  *   byte_len      [V] int32 - UTF-8 bytes of each vocabulary entry (BOS / specials = 0)
  *   byte_per_pos  [T] int32 or NULL - per-position byte counts that replace byte_len (README
- *                 leaderboard, PR #1736 row: "byte-sidecar BPB accounting")
+ *                 leaderboard, PR #1736 row: byte counts carried per position beside the tokens)
  *   out           [4] double, device: sum_nats, sum_bytes, n_scored, bits_per_byte
  *                 (0/0 = NaN for an empty mask, x/0 = +inf for zero bytes)
  * The sums use a fixed reduction order, so the result is bitwise reproducible.
@@ -231,9 +233,9 @@ pg_status pg_bpb_accumulate(const float* nats, const int32_t* target, const uint
 
 /*
  * Sliding-window evaluation of a token stream (parameter-golf README leaderboard, "Sliding Window
- * Eval" row: windows advancing by a stride of 64 tokens, "increasing context for eval"), with
- * score-first test-time training (README leaderboard, "Legal Score-First TTT" rows and "phased TTT
- * over already-scored validation chunks"; HYDRA Golf site, leaderboard entry #2).
+ * Eval" row: windows advancing by a stride of 64 tokens, so that each scored token sees a long context), with
+ * score-first test-time training (README leaderboard, "Legal Score-First TTT" rows, and the row that
+ * trains in phases on validation chunks already scored; HYDRA Golf site, leaderboard entry #2).
  *
  * Schedule. tokens[0 .. n_tokens) is the stream; prediction p (p = 0 .. n_tokens - 2) is token
  * p + 1 given tokens 0 .. p. Window w covers input positions [w stride, w stride + window).

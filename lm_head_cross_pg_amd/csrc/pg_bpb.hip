@@ -1,8 +1,8 @@
 // Bits per byte over the scored rows: sum of nats (float64), sum of UTF-8 bytes of the targets
 // (int64) and the number of scored rows, then bpb = sum_nats / (ln 2 * sum_bytes).
-// (README introduction: "evaluated by compression ... tokenizer-agnostic, bits per byte"; tproger
+// (README introduction: the score is compression in bits per byte, independent of the tokenizer; tproger
 // article, "Правила и метрика"; byte counts per position as in the README leaderboard's PR #1736
-// row, "byte-sidecar BPB accounting".)
+// row: byte counts carried per position beside the tokens.)
 //
 // Two launches, no atomics: every workgroup reduces a fixed contiguous range of rows in a fixed
 // order into one partial, then a single workgroup adds the partials in index order. The result is

@@ -1,6 +1,6 @@
 // Backward of the fused tied LM head + logit softcap + cross-entropy for gfx950.
 //
-// L = g * sum over scored rows of nats (repo-explainer, "The Baseline Is a Map": loss.backward()).
+// L = g * sum over scored rows of nats (repo-explainer, "The Baseline Is a Map": the backward pass of the baseline's loss).
 // With p = softmax(s) per row and s = c tanh(z / c):
 //   dZ[t, v] = (p[t, v] - [v == y[t]]) * (1 - (s / c)^2)   (g is applied later, in float32)
 //   dH = g * dZ . E          dE = g * dZ^T . H   (LM-head part of the tied embedding's gradient)

@@ -1,7 +1,7 @@
 // Forward of the fused tied LM head + logit softcap + cross-entropy for gfx950.
 //
 // What is computed (per scored row t): z = H[t] . E^T (tied head: trios issue #19, approach
-// table, "Tied embeddings"), s = c tanh(z / c) ("fused softcapped CE", HYDRA Golf stack list),
+// table, "Tied embeddings"), s = c tanh(z / c) (the fused softcapped cross-entropy of the HYDRA Golf stack list),
 // nats = logsumexp(s) - s[y[t]] (trios issue, "Контекст": cross-entropy). The T x V logits never
 // reach memory.
 //

@@ -3,9 +3,9 @@
 // Sliding-window evaluation scores each next-token prediction with a long context: windows of
 // `window` tokens advance by `stride` tokens, and each window scores only the predictions no earlier
 // window has scored (parameter-golf README leaderboard, "Sliding Window Eval" row: stride 64,
-// "increasing context for eval"). Score-first test-time training adapts the model only on
+// each scored token with a long context). Score-first test-time training adapts the model only on
 // validation chunks that have already been scored (README leaderboard, "Legal Score-First TTT"
-// rows and "phased TTT over already-scored validation chunks"; HYDRA Golf site, leaderboard entry
+// rows, and the row whose test-time training runs in phases over validation chunks already scored; HYDRA Golf site, leaderboard entry
 // #2, "Score-First TTT").
 //
 // Schedule (predictions p = 0 .. n_tokens - 2, prediction p being token p + 1 after tokens 0..p):

@@ -7,8 +7,8 @@ Batches of ``windows_per_batch`` windows are scored one after another, and the b
 accumulate over all of them on the device. With ``ttt_lr > 0`` each batch, once scored, also yields
 the gradients of its mean loss, and the tied embedding takes one SGD step on them before the next
 batch is scored: score-first test-time training, every chunk adapted on only after it has been
-scored (README leaderboard, "Legal Score-First TTT" rows, "phased TTT over already-scored validation
-chunks").
+scored (README leaderboard, "Legal Score-First TTT" rows, and the row that trains in phases on
+validation chunks already scored).
 
 This module only sequences calls: the schedule's arithmetic, the rows of each batch, the forward,
 the backward, the sums and the update all run in the library. The hidden states of each batch

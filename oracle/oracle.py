@@ -7,10 +7,10 @@ What it computes, and where the pages state it:
 
 * Tied LM head: the input embedding E[V, D] is reused as the output projection, so the logits are
   z = H . E^T (trios issue #19, table of approaches, "Tied embeddings"; parameter-golf README
-  leaderboard, "Naive Baseline" row: "TiedEmbeddings"; repo-explainer page, "The Baseline Is a Map",
-  ``logits = model(batch["x"])``).
+  leaderboard, "Naive Baseline" row: "TiedEmbeddings"; repo-explainer page, "The Baseline Is a Map":
+  the model maps the input tokens to logits).
 * Logit softcap: the pages only say the logits are "softcapped" (HYDRA Golf site, stack list,
-  "fused softcapped CE kernel"; README leaderboard, PR #1787 row). Reading taken: s = c * tanh(z / c)
+  a fused softcapped cross-entropy kernel; README leaderboard, PR #1787 row). Reading taken: s = c * tanh(z / c)
   with c = 30; c = 0 means no cap (s = z).
 * Asymmetric softcap: the pages name an "AsymLogit" head change (HYDRA Golf site, leaderboard
   table, entries #1 and #4; README leaderboard, PR #2135 and PR #1945 rows) without defining it.
@@ -23,22 +23,24 @@ What it computes, and where the pages state it:
   scales is the reading taken, and the head computes on the bfloat16 rounding of q * scale
   (quantize_rows_q8, dequantize_rows_q8, forward_q8).
 * Cross-entropy against the next token, in nats: lse(s) - s[target] (trios issue, "Контекст":
-  "cross-entropy loss / bits-per-byte"; repo-explainer, ``loss = criterion(logits, batch["y"])``).
+  cross-entropy loss and bits per byte; repo-explainer, baseline listing: the loss of the logits against
+  the next tokens).
 * Bits per byte: total -log2 p(target) over scored rows divided by the total UTF-8 bytes of those
-  targets, a ratio of sums (README introduction: "evaluated by compression ... tokenizer-agnostic,
-  bits per byte"; tproger article, "Правила и метрика": compression counted in bytes). A per-position
-  byte count may replace the per-vocabulary table (README leaderboard, PR #1736 row,
-  "byte-sidecar BPB accounting").
+  targets, a ratio of sums (README introduction: the score is compression in bits per byte,
+  independent of the tokenizer; tproger article, "Правила и метрика": compression counted in bytes).
+  A per-position byte count may replace the per-vocabulary table (README leaderboard, PR #1736 row:
+  byte counts carried per position beside the tokens).
 * Scored rows: a mask selects the rows that count (README leaderboard, "Sliding Window Eval" row,
   stride 64). Unscored rows get nats = 0 and lse = 0 and enter no sum.
-* Sliding-window evaluation of a token stream (same row: windows advance by the stride, "increasing
-  context for eval"): each window scores the predictions no earlier window scored
+* Sliding-window evaluation of a token stream (same row: windows advance by the stride, so that each
+  scored token sees a long context): each window scores the predictions no earlier window scored
   (window_schedule); with score-first test-time training (README leaderboard, "Legal Score-First
-  TTT" rows, "phased TTT over already-scored validation chunks") each batch of windows, once scored,
+  TTT" rows, and the row that trains in phases on validation chunks already scored) each batch of
+  windows, once scored,
   gives one SGD step on the tied embedding for the batches after it (sliding_window_eval). The
   reading taken for the step: float32 master weights, w <- w - lr g with each operation rounded to
   float32, and the head reads their bfloat16 rounding.
-* Backward of L = g * sum_scored nats (repo-explainer, ``loss.backward()``):
+* Backward of L = g * sum_scored nats (repo-explainer, baseline listing: the backward pass of the loss):
   dS = g (softmax(s) - onehot(target)), dZ = dS * ds/dz with ds/dz = 1 - tanh(z/c)^2,
   dH = dZ . E, dE = dZ^T . H (the LM-head part of the tied embedding's gradient).
   A scored row whose target lies outside [0, V) has NaN nats, so its loss term, and with it its

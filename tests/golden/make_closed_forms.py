@@ -20,8 +20,8 @@ def worked_softcap30():
     return {
         "what": "worked example of the softcapped cross-entropy and bits per byte, values in closed form",
         "source": ("definition only: the pages print no worked example. Softcap s = c*tanh(z/c) is the reading of "
-                   "'fused softcapped CE' (HYDRA Golf site stack list; parameter-golf README leaderboard, PR #1787 row); "
-                   "bits per byte as in the README introduction ('evaluated by compression ... bits per byte')."),
+                   "the fused softcapped cross-entropy the pages name (HYDRA Golf site stack list; parameter-golf "
+                   "README leaderboard, PR #1787 row); bits per byte as the README introduction scores compression."),
         "derivation": ("H = [[1]] for all three rows, E = [[30 ln 2], [30 ln 3], [0]], c = 30. Then z = E[:,0], "
                        "z/c = ln 2, ln 3, 0 and tanh(ln 2) = 3/5, tanh(ln 3) = 4/5, so s = [18, 24, 0]. "
                        "lse = 24 + log1p(e^-6 + e^-24); nats[t] = lse - s[target[t]] with targets [0, 1, 2]; "
@@ -164,8 +164,8 @@ def window_schedules():
     # written out by hand from the rule; nothing here is computed
     return {
         "what": "scored predictions of each window of a sliding-window evaluation of a token stream",
-        "source": ("parameter-golf README leaderboard, 'Sliding Window Eval' row (stride 64, 'increasing context for "
-                   "eval'); the rule for the first window and the stream's end is the reading taken"),
+        "source": ("parameter-golf README leaderboard, 'Sliding Window Eval' row (stride 64, each scored token with a "
+                   "long context); the rule for the first window and the stream's end is the reading taken"),
         "derivation": ("prediction p (p = 0 .. n_tokens - 2) is token p + 1 after tokens 0..p; window w covers input "
                        "positions w*stride .. w*stride + window - 1 and scores the predictions there that no earlier "
                        "window scored, until all are scored. E.g. n_tokens = 14, window 8, stride 2: 13 predictions; "
