@@ -43,7 +43,9 @@ class SlidingWindowEval:
         self.mask = torch.empty(rows, dtype=torch.uint8, device=dev)
         self.nats = torch.empty(rows, dtype=torch.float32, device=dev)
         self.lse = torch.empty(rows, dtype=torch.float32, device=dev)
-        self.out = torch.zeros(4, dtype=torch.float64, device=dev)
+        # running sums (nats, bytes, predictions) and their bits per byte: NaN (0 / 0) until a batch
+        # with predictions has been scored, as for a stream too short to predict anything
+        self.out = torch.tensor([0.0, 0.0, 0.0, float("nan")], dtype=torch.float64, device=dev)
         op = abi.PG_OP_FWD_BWD if self.ttt_lr else abi.PG_OP_FWD
         self.ws = torch.empty(max(abi.workspace_bytes(op, rows, self.D, self.V), 256), dtype=torch.uint8, device=dev)
         self.ws_bpb = torch.empty(max(abi.workspace_bytes(abi.PG_OP_BPB, rows, 1, self.V), 256), dtype=torch.uint8,

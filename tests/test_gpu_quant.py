@@ -57,27 +57,30 @@ def test_quantiser_zero_rows_and_exact_grid():
     assert s[7].item() == 0.0 and torch.all(q[7] == 0)
 
 
-def run_q8(inp, sample_rows=None):
+def run_q8(inp, sample_rows=None, mask=None):
     T, D, V, c = inp["T"], inp["D"], inp["V"], inp["softcap"]
-    print(f"[case] q8 forward {inp['workload']} T={T} D={D} V={V}", flush=True)
+    print(f"[case] q8 forward {inp['workload']} T={T} D={D} V={V} masked={mask is not None}", flush=True)
     d = abi.to_device(inp)
+    mask_t = None if mask is None else torch.from_numpy(mask).cuda()
     q, s = quantize_gpu(d["embed"])
     nats = torch.full((T,), float("nan"), device="cuda")
     lse = torch.full((T,), float("nan"), device="cuda")
-    abi.pg_lmhead_ce_fwd_q8(d["hidden"], q, s, d["target"], None, c, nats, lse)
+    abi.pg_lmhead_ce_fwd_q8(d["hidden"], q, s, d["target"], mask_t, c, nats, lse)
     torch.cuda.synchronize()
     H, E = host_inputs(inp)
     oq, os_ = ora.quantize_rows_q8(E)
     Ed = ora.dequantize_rows_q8(oq, os_)
     rows = np.arange(T) if sample_rows is None else np.asarray(sample_rows)
-    onats, olse = oracle_forward_chunked(H[rows], Ed, inp["target"][rows], c)
+    onats, olse = ora.forward_q8(H[rows], oq, os_, inp["target"][rows], c, None if mask is None else mask[rows])
     g = nats.cpu().numpy().astype(np.float64)
     assert np.max(np.abs(g[rows] - onats)) <= NATS_ATOL
     assert np.max(np.abs(lse.cpu().numpy()[rows] - olse)) <= NATS_ATOL
+    if mask is not None:
+        assert np.all(g[mask == 0] == 0.0)
     # the same head through the bf16 entry point, with the oracle's dequantised embedding: same bits
     Eb = torch.from_numpy(synth.bf16_bits(Ed.astype(np.float32)).view(np.int16)).cuda()
     ref = torch.empty(T, device="cuda")
-    abi.pg_lmhead_ce_fwd(d["hidden"], Eb, d["target"], None, c, ref, None)
+    abi.pg_lmhead_ce_fwd(d["hidden"], Eb, d["target"], mask_t, c, ref, None)
     torch.cuda.synchronize()
     assert torch.equal(ref, nats)
     return g, H, Ed
@@ -85,6 +88,15 @@ def run_q8(inp, sample_rows=None):
 
 def test_quantised_forward_small():
     run_q8(synth.make_inputs(workload("fwd_v8192", T=700, V=1500, stream=111), 0))
+
+
+@pytest.mark.parametrize("T,D,masked", [(700, 512, True), (4097, 512, False), (300, 48, True), (255, 64, False)])
+def test_quantised_forward_masked_ragged_and_generic(T, D, masked):
+    """The int8 head with a scored-row mask, ragged row counts, and a width without an MFMA
+    instantiation (D = 48, the vector kernel) against the oracle's forward on the dequantised head."""
+    inp = synth.make_inputs(workload("fwd_v8192", T=T, D=D, V=1000, stream=112 + D), 0)
+    mask = (np.random.default_rng(T).random(T) < 0.4).astype(np.uint8) if masked else None
+    run_q8(inp, mask=mask)
 
 
 def test_quantised_forward_full_size():

@@ -164,3 +164,16 @@ def test_driver_ttt_without_dhidden():
         np.testing.assert_array_equal(a["nats"], b["nats"])
         np.testing.assert_array_equal(a["dE"], b["dE"])
     assert drv.result() == drv_h.result()
+
+
+@pytest.mark.parametrize("n_tokens", [1, 2, 3, 1000, 2049])
+def test_driver_short_streams(n_tokens):
+    """Streams shorter than two windows: none to predict (one token: no window, BPB NaN as 0 / 0),
+    one prediction, part of one window, exactly one window, one window and one more token."""
+    drv, got, ref = _run(4, n_tokens, 8, 0.0, keep_dhidden=False)
+    sn, sb, n, b = drv.result()
+    assert drv.n_windows == len(ora.window_schedule(n_tokens, 2048, 64))
+    if n_tokens < 2:
+        assert len(got) == 0 and n == 0 and np.isnan(b) and np.isnan(ref["bpb"])
+    else:
+        _check(drv, got, ref)
