@@ -360,3 +360,27 @@ def test_without_dhidden(path, over, masked):
     for a, b in zip(res[0], res[1]):
         np.testing.assert_array_equal(a, b)
     assert np.all(np.isfinite(res[1][2]))
+
+
+@pytest.mark.parametrize("path", ["fused", "two_calls"])
+def test_no_rows_and_empty_mask(path):
+    """Nothing to learn from: T = 0 rows, and 300 rows none of which is scored. dembed comes back
+    exactly zero (the caller's buffer is overwritten, not left as it was), dhidden's rows too."""
+    inp = synth.make_inputs(workload("train_v8192", T=300, V=1500, stream=150), 0)
+    d = abi.to_device(inp)
+    V, D = inp["V"], inp["D"]
+    for T, mask in ((0, None), (300, torch.zeros(300, dtype=torch.uint8, device="cuda"))):
+        print(f"[case] no rows {path} T={T} masked={mask is not None}", flush=True)
+        H, y = d["hidden"][:T], d["target"][:T]
+        nats = torch.full((T,), 5.0, device="cuda")
+        lse = torch.full((T,), 5.0, device="cuda")
+        dH = torch.full((T, D), 3.0, device="cuda")
+        dE = torch.full((V, D), 3.0, device="cuda")
+        if path == "fused":
+            abi.pg_lmhead_ce_fwd_bwd(H, d["embed"], y, mask, 30.0, 1.0, nats, lse, dH, dE)
+        else:
+            abi.pg_lmhead_ce_fwd(H, d["embed"], y, mask, 30.0, nats, lse)
+            abi.pg_lmhead_ce_bwd(H, d["embed"], y, mask, lse, 30.0, 1.0, dH, dE)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(dE).item() == 0
+        assert torch.count_nonzero(dH).item() == 0 and torch.count_nonzero(nats).item() == 0
