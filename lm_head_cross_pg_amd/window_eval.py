@@ -5,8 +5,9 @@ Windows of ``window`` tokens advance by ``stride`` over the stream; each scores 
 no earlier window scored (parameter-golf README leaderboard, "Sliding Window Eval" row, stride 64).
 Batches of ``windows_per_batch`` windows are scored one after another, and the bits per byte
 accumulate over all of them on the device. With ``ttt_lr > 0`` each batch, once scored, also yields
-the gradients of its mean loss, and the tied embedding takes one SGD step on them before the next
-batch is scored: score-first test-time training, every chunk adapted on only after it has been
+the gradient of its mean loss with respect to the tied embedding (the hidden states' gradient only
+with ``keep_dhidden``), and the embedding takes one SGD step on it before the next batch is
+scored: score-first test-time training, every chunk adapted on only after it has been
 scored (README leaderboard, "Legal Score-First TTT" rows, and the row that trains in phases on
 validation chunks already scored).
 
