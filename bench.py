@@ -390,27 +390,27 @@ def summarize_trace(d, steps, warmup):
     for r in stats:
         lines.append(f"| `{r['Name'][:72]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
-    # bench.py's order: --steps isolated forwards back to back, then the warmup and timed steps of the
-    # sustained loop (each forward followed by the two bits-per-byte kernels). A main-forward launch
-    # is classed by the kernel after it.
+    # bench.py's order: untimed forwards while the clock settles, --steps isolated forwards back to
+    # back, then the warmup and timed steps of the sustained loop (each forward followed by the two
+    # bits-per-byte kernels). A main-forward launch followed by the reduction belongs to the loop;
+    # the isolated leg is the --steps forwards just before the loop's first one.
     tr = sorted(csv.DictReader(open(os.path.join(d, "trace", "run_kernel_trace.csv"))),
                 key=lambda r: int(r["Start_Timestamp"]))
-    sustained, isolated = [], []
+    fwds = []                 # (duration us, followed by the reduction)
     for i, r in enumerate(tr):
         if not r["Kernel_Name"].startswith(main_kernel):
             continue
-        dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         nxt = tr[i + 1]["Kernel_Name"] if i + 1 < len(tr) else ""
-        if "bpb_partial_kernel" in nxt:
-            sustained.append(dt)
-        elif not sustained and len(isolated) < steps:
-            isolated.append(dt)
+        fwds.append(((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3, "bpb_partial_kernel" in nxt))
+    first = next((k for k, (_, in_loop) in enumerate(fwds) if in_loop), len(fwds))
+    sustained = [dt for dt, in_loop in fwds if in_loop]
+    isolated = [dt for dt, _ in fwds[max(0, first - steps):first]]
     timed = sustained[warmup:warmup + steps]
     flop = 2.0 * 65536 * 512 * 8192
     if isolated:
         m = sum(isolated) / len(isolated)
-        lines += ["", f"The {len(isolated)} isolated forwards that open the run (back to back, events between them, "
-                      "while the clock settles): mean",
+        lines += ["", f"The {len(isolated)} isolated forwards (back to back, events between them, after untimed ones "
+                      "that let the clock settle): mean",
                   f"{m:.1f} us (min {min(isolated):.1f}, max {max(isolated):.1f}), frac "
                   f"{flop / (m * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.3f}."]
     if timed:
@@ -631,9 +631,12 @@ def main():
         abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, c, nats, lse, ws_fwd)
         abi.pg_bpb_reduce(nats, d["target"], None, d["byte_len"], None, V, out, ws_bpb)
 
-    # the forward alone, launches back to back with events between them (the isolated figure). It
-    # runs first: the GPU's power management takes 10-20 ms of load to settle (launches run up to 20 %
-    # slower on the way), so the main loop's warmup and timed steps then see the settled clock.
+    # the GPU's power management takes 10-20 ms of load to settle (launches run up to 20 % slower on
+    # the way): untimed forwards first, so that both timed legs below see the settled clock
+    for _ in range(max(30, args.warmup)):
+        abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], None, c, nats, lse, ws_fwd)
+    torch.cuda.synchronize()
+    # the forward alone, launches back to back with events between them (the isolated figure)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if args.cold else None
     for a, b in ev:
