@@ -10,6 +10,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -55,12 +56,17 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link libpg_lmhead.so next to this file; returns its path."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    jobs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         extra = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] if src in VGPR_ACC_SOURCES else []
-        _run([hipcc(), *flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append(([hipcc(), *flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    # one hipcc per source, in parallel: the translation units are independent
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for fut in [pool.submit(_run, cmd, verbose) for cmd, _ in jobs]:
+            fut.result()
+    objs = [obj for _, obj in jobs]
     tmp = LIB + ".tmp"
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
