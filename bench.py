@@ -487,8 +487,9 @@ def library_gemm(steps):
 def window_eval(abi, synth, args):
     """The sliding-window evaluation driver on a stream of 2048 + 95 x 64 + 1 tokens: 96 windows of
     2048 at stride 64 in 3 batches of 32 windows (65,536 rows each; 8128 predictions scored), D = 512,
-    V = 8192, with and without one score-first SGD step per batch. The hidden states of the scored
-    rows are drawn once and kept on the device; a pass is the driver's steps over the 3 batches."""
+    V = 8192, with and without one score-first SGD step per batch, and on the int8 head (evaluation
+    only). The hidden states of the scored rows are drawn once and kept on the device; a pass is the
+    driver's steps over the 3 batches."""
     import torch
     from lm_head_cross_pg_amd.window_eval import SlidingWindowEval
     n_tokens, L, s, B, D, V = 2048 + 95 * 64 + 1, 2048, 64, 32, 512, 8192
@@ -497,10 +498,13 @@ def window_eval(abi, synth, args):
     blen = torch.from_numpy(st["byte_len"]).cuda()
     res = {}
     E0 = torch.from_numpy(st["embed"].view(np.int16)).cuda().view(torch.bfloat16)
-    for lr in (0.0, 2.0):
+    q8 = torch.empty((V, D), dtype=torch.int8, device="cuda")
+    sc8 = torch.empty(V, dtype=torch.float32, device="cuda")
+    abi.pg_quantize_q8(E0, q8, sc8)
+    for lr, int8 in ((0.0, False), (2.0, False), (0.0, True)):
         E16 = E0.clone()
         master = E0.float() if lr else None
-        drv = SlidingWindowEval(tokens, blen, V, D, L, s, B, 30.0, ttt_lr=lr, embed_master=master)
+        drv = SlidingWindowEval(tokens, blen, V, D, L, s, B, 30.0, ttt_lr=lr, embed_master=master, int8_head=int8)
         hid = []
         for w0, nw in drv.batches():
             H = torch.zeros((nw * L, D), dtype=torch.bfloat16, device="cuda")
@@ -520,7 +524,10 @@ def window_eval(abi, synth, args):
                 master.copy_(E0.float())
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            n = sum(drv.step(H, E16, w0, nw) for H, (w0, nw) in zip(hid, drv.batches()))
+            if int8:
+                n = sum(drv.step_int8(H, q8, sc8, w0, nw) for H, (w0, nw) in zip(hid, drv.batches()))
+            else:
+                n = sum(drv.step(H, E16, w0, nw) for H, (w0, nw) in zip(hid, drv.batches()))
             b.record()
             torch.cuda.synchronize()
             if it:                                   # the first pass is a warmup
@@ -540,10 +547,13 @@ def window_eval(abi, synth, args):
                 cores = len(os.sched_getaffinity(0))
             except AttributeError:
                 cores = os.cpu_count() or 1
+            E_ref = synth.bf16_to_f64(st["embed"])
+            if int8:   # the head the int8 form scores: the dequantised embedding
+                E_ref = ora.dequantize_rows_q8(*ora.quantize_rows_q8(E_ref))
             t0 = time.perf_counter()
             ref = ora.sliding_window_eval(st["tokens"], st["byte_len"],
                                           lambda w, k: synth.bf16_to_f64(synth.window_hidden(args.seed, w, k, D)),
-                                          synth.bf16_to_f64(st["embed"]), 30.0, L, s, B, lr=lr)
+                                          E_ref, 30.0, L, s, B, lr=lr)
             dt = time.perf_counter() - t0
             entry["bpb_oracle"] = ref["bpb"]
             entry["cpu_baseline"] = {
@@ -551,7 +561,7 @@ def window_eval(abi, synth, args):
                 "sample": f"the oracle's sliding-window loop over the same {ref['n_scored']} predictions "
                           f"(3 batches{', each with its backward and SGD step' if lr else ''}), float64 numpy "
                           f"(BLAS on every core, the elementwise steps on one thread), {dt:.1f} s wall"}
-        res["ttt_lr_%g" % lr] = entry
+        res["int8_head" if int8 else "ttt_lr_%g" % lr] = entry
     res["workload"] = "stream of %d tokens, windows of %d at stride %d, %d windows per batch, D=%d, V=%d" % (
         n_tokens, L, s, B, D, V)
     return res
@@ -766,22 +776,41 @@ def main():
         a.record()
         abi.pg_quantize_q8(d["embed"], q8, sc8)
         b.record()
-    ev_f = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in ev_f:
-        a.record()
-        abi.pg_lmhead_ce_fwd_q8(d["hidden"], q8, sc8, d["target"], None, c, nats, lse, ws_q8)
-        b.record()
+    # int8 and bf16 launches alternate, so that both see the same clock
+    def q8_ab(mask_t, n):
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+              for _ in range(2)]
+        for i in range(n):
+            ev[0][i][0].record()
+            abi.pg_lmhead_ce_fwd_q8(d["hidden"], q8, sc8, d["target"], mask_t, c, nats, lse, ws_q8)
+            ev[0][i][1].record()
+            ev[1][i][0].record()
+            abi.pg_lmhead_ce_fwd(d["hidden"], d["embed"], d["target"], mask_t, c, nats, lse, ws_fwd)
+            ev[1][i][1].record()
+        torch.cuda.synchronize()
+        return [float(np.mean([a.elapsed_time(b) for a, b in e])) for e in ev]
+    q8_ms, bf16_ms = q8_ab(None, args.steps)
     torch.cuda.synchronize()
     quant_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_q]))
-    q8_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_f]))
+    abi.pg_lmhead_ce_fwd_q8(d["hidden"], q8, sc8, d["target"], None, c, nats, lse, ws_q8)
     abi.pg_bpb_reduce(nats, d["target"], None, d["byte_len"], None, V, out, ws_bpb)
+    bpb_q8 = float(out[3].item())
+    # the stride-64 evaluation's mask (the last 64 rows of each 2048 scored): few row tiles, so the
+    # head's bytes weigh more
+    m64 = torch.zeros(T, dtype=torch.uint8, device="cuda")
+    m64.view(-1, 2048)[:, -64:] = 1
+    q8_m_ms, bf16_m_ms = q8_ab(m64, max(args.steps, 20))
     quant_bytes = V * D * 2 + V * D + V * 4          # read bf16 E, write int8 q and float32 scales
     result["q8_head"] = {
         "format": "per-row symmetric int8, float32 scales; head computes on bf16(q * scale)",
         "quantize_us": quant_ms * 1e3, "quantize_gbps": quant_bytes / (quant_ms * 1e-3) / 1e9,
         "launch_ms": q8_ms, "tokens_per_s": T / (q8_ms * 1e-3),
-        "frac": flop_fwd / (q8_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bpb": float(out[3].item()),
-        "note": "launch = dequantise (8 MiB bf16 written) + fused forward"}
+        "frac": flop_fwd / (q8_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bpb": bpb_q8,
+        "bf16_launch_ms": bf16_ms,
+        "stride64_mask": {"scored": int(m64.sum().item()), "launch_ms": q8_m_ms, "bf16_launch_ms": bf16_m_ms},
+        "note": "all rows (launch_ms): the bf16 head is written first (one pass), then the bf16 forward; "
+                "with the stride-64 mask the forward reads the int8 rows and converts each tile on chip; "
+                "bf16_launch_ms: the bf16 head's forward, launches alternating with the int8 ones"}
     if not args.no_cpu:
         from oracle import oracle as ora
         q_o, s_o = ora.quantize_rows_q8(synth.as_f64(inp["embed"], inp["dtype"]))

@@ -188,9 +188,12 @@ pg_status pg_lmhead_ce_fwd_bwd_asym(const void* hidden, const void* embed, int32
  *
  * pg_quantize_q8: embed [V, D] (bf16 or f32, dtype as above) -> embed_q8 [V, D] int8 and
  *   embed_scale [V] f32, all device arrays. Needs no workspace.
- * pg_lmhead_ce_fwd_q8: the forward of pg_lmhead_ce_fwd (bf16 hidden) with the head E' rebuilt
- *   from (embed_q8, embed_scale) into the workspace, which must hold
- *   pg_workspace_bytes(PG_OP_FWD_Q8, T, D, V) bytes. nats and lse as for pg_lmhead_ce_fwd.
+ * pg_lmhead_ce_fwd_q8: the forward of pg_lmhead_ce_fwd (bf16 hidden) on the head E' of
+ *   (embed_q8, embed_scale). At D = 512 with one cap in (0, 40], calls with a score mask or at
+ *   most 8192 rows read the int8 rows in the forward itself, which forms E' tile by tile on chip;
+ *   other calls first write E' into the workspace. Either way the workspace must hold
+ *   pg_workspace_bytes(PG_OP_FWD_Q8, T, D, V) bytes, and the results are the same bits. nats and
+ *   lse as for pg_lmhead_ce_fwd.
  */
 pg_status pg_quantize_q8(const void* embed, int32_t dtype, int32_t V, int32_t D, int8_t* embed_q8,
                          float* embed_scale, void* stream);

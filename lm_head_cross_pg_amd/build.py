@@ -1,6 +1,7 @@
 """Build libpg_lmhead.so (the gfx950 HIP library) in place with hipcc.
 
     python -m lm_head_cross_pg_amd.build          # or: python lm_head_cross_pg_amd/build.py
+    python -m lm_head_cross_pg_amd.build --incremental   # only sources changed since their objects
 
 The library needs only the HIP runtime; no PyTorch headers are involved.
 """
@@ -52,21 +53,33 @@ def _run(cmd: list[str], verbose: bool) -> None:
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libpg_lmhead.so next to this file; returns its path."""
+def _headers() -> list[str]:
+    inc = os.path.join(ROOT, "include")
+    return [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
+           [os.path.join(inc, f) for f in os.listdir(inc) if f.endswith(".h")]
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source and link libpg_lmhead.so next to this file; returns its path.
+    incremental: skip a source whose object is newer than it and than every header."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    jobs = []
+    newest_header = max(os.path.getmtime(h) for h in _headers())
+    jobs, objs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        objs.append(obj)
+        path = os.path.join(CSRC, src)
+        if incremental and os.path.exists(obj) and \
+                os.path.getmtime(obj) > max(os.path.getmtime(path), newest_header):
+            continue
         extra = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] if src in VGPR_ACC_SOURCES else []
-        jobs.append(([hipcc(), *flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+        jobs.append(([hipcc(), *flags(), *extra, "-c", path, "-o", obj], obj))
     # one hipcc per source, in parallel: the translation units are independent
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(max_workers=workers) as pool:
         for fut in [pool.submit(_run, cmd, verbose) for cmd, _ in jobs]:
             fut.result()
-    objs = [obj for _, obj in jobs]
     tmp = LIB + ".tmp"
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
@@ -74,4 +87,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv[1:]))

@@ -319,11 +319,27 @@ pg_status pg_lmhead_ce_fwd_q8(const void* hidden, const int8_t* embed_q8, const 
   if ((s = device_check(dev)) != PG_OK) return s;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  uint16_t* deq = reinterpret_cast<uint16_t*>(ws);
-  hipError_t e = pg::launch_dequantize(embed_q8, embed_scale, V, D, deq, st);
-  if (e == hipSuccess)
-    e = pg::launch_fwd(hidden, deq, PG_DTYPE_BF16, target, score_mask, T, D, V, softcap, softcap, nats, lse,
-                       ws + pg::align256((size_t)V * (size_t)D * 2), dev, st);
+  char* fws = ws + pg::align256((size_t)V * (size_t)D * 2);
+  hipError_t e;
+  // Converting on chip costs every workgroup the conversion of every tile it visits (about 13 % of
+  // a full-size forward, which runs at the power limit); the bf16 head written first costs one fixed
+  // pass (about 7 us at V = 8192). So the forward converts on chip when few row tiles are scored:
+  // calls with a mask (sliding-window evaluation scores one row in 32) and calls of up to
+  // kQ8OnChipMaxRows rows.
+  constexpr int64_t kQ8OnChipMaxRows = 8192;
+  if (pg::fwd_reads_q8(D, softcap) && (score_mask || T <= kQ8OnChipMaxRows)) {
+    // the forward reads the int8 rows and converts each tile in LDS (the workspace's first
+    // V * D * 2 bytes stay unused)
+    e = pg::launch_fwd(hidden, nullptr, PG_DTYPE_BF16, target, score_mask, T, D, V, softcap, softcap, nats, lse, fws,
+                       dev, st, nullptr, embed_q8, embed_scale);
+  } else {
+    // other widths and caps: the bf16 rows into the workspace, then the bf16 forward on them
+    uint16_t* deq = reinterpret_cast<uint16_t*>(ws);
+    e = pg::launch_dequantize(embed_q8, embed_scale, V, D, deq, st);
+    if (e == hipSuccess)
+      e = pg::launch_fwd(hidden, deq, PG_DTYPE_BF16, target, score_mask, T, D, V, softcap, softcap, nats, lse, fws,
+                         dev, st);
+  }
   return e == hipSuccess ? PG_OK : PG_ERR_HIP;
 }
 

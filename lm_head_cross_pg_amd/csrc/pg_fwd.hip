@@ -46,6 +46,8 @@ struct FwdParams {
   float* s_target;
   uint16_t* dz;           // unnormalised dZ blocks (the kernels that write them), else unused
   int64_t ldz;            // vocabulary rows of dz (V rounded up to the tile)
+  const int8_t* Eq;       // int8 head (the kernel that reads it; E is then unused): q[V, D]
+  const float* qscale;    // and its per-row scales [V]
 };
 
 __device__ __forceinline__ int device_splits(int64_t n, int n_vtiles, int grid) {
@@ -75,14 +77,36 @@ constexpr int kFwdTokBlocks = PG_FWD_TOK_BLOCKS;
 // -t (t - K) / M^2, so the normalised dZ of a row is d 2^(M - lse log2 e) (-1 / M^2) - [v = y] slope,
 // a per-row factor applied after this kernel, where lse is known (the target element is rewritten
 // then as well).
-template <int D, bool FIXED, int NB, bool ASYM, bool DZ = false>
+// Q8 (D = 512, fixed shift, one cap): the head is the per-row int8 embedding q with scales s. Wave
+// w owns rows 8 w .. 8 w + 7 of each tile. During the first MFMA chain of a tile it copies the
+// int8 bytes of its rows of the next tile (4 KiB) by DMA into the tail of its own rows' region of
+// the next tile buffer (from byte kQ8StageOff of the 8 padded rows, 8320 bytes), and during the
+// second chain it turns them, row by row from the front, into the bf16 rows bf16(float(q) s) of
+// that region; the tile's barrier then publishes them. bf16 row p ends before int8 row p + 1
+// begins, so no byte is overwritten before it is read, and no wave touches another's region: the
+// staging needs no LDS of its own and no barrier. The bytes are biased (q ^ 0x80 = q + 128 as an
+// unsigned byte, which converts in one instruction), and fma(q + 128, s, -128 s) is float(q) s
+// rounded once, as the product is; the bf16 rounding is the hardware's round-to-nearest-even.
+template <int D, bool FIXED, int NB, bool ASYM, bool DZ = false, bool Q8 = false>
 struct FwdCore {
   static_assert(!DZ || FIXED, "unnormalised dZ needs the fixed shift");
+  static_assert(!Q8 || (D == 512 && NB == 1 && FIXED && !ASYM && !DZ), "int8 tiles: the D = 512 fixed-shift forward");
+  using TL = TileLayout<D>;
+  static constexpr int kQ8RowsPerWave = kVocabTile / 8;       // rows of a tile each wave stages
+  static constexpr int kQ8WaveBytes = kQ8RowsPerWave * D;    // int8 bytes each wave stages (4 KiB)
+  // where those bytes land in the wave's region of kQ8RowsPerWave padded rows: its last 4 KiB
+  static constexpr int kQ8StageOff = kQ8RowsPerWave * TL::PITCH - kQ8WaveBytes;
+  static_assert(!Q8 || (TL::PAD && kQ8StageOff % 16 == 0 &&
+                        (kQ8RowsPerWave - 2) * TL::PITCH + 2 * D <= kQ8StageOff + (kQ8RowsPerWave - 1) * D),
+                "bf16 row p must end before int8 row p + 1 begins");
   static constexpr int KS = D / 16;
   static constexpr int kWaves = WaveShape<NB>::kWaves;
   static constexpr int kLoads = embed_loads_per_wave<D, kWaves>();
   const lds_char* lds;
   const uint16_t* E;
+  const int8_t* Eq;      // Q8
+  const float* qscale;   // Q8
+  float qs;              // Q8: scale of tile row kQ8RowsPerWave * wave + (lane % 8) of the staged tile
   int wave, lane;
   int h, col, V;
   Softcap sc;
@@ -178,6 +202,56 @@ struct FwdCore {
     logit_blocks<D, NB>(lds, buf, vb, h, col, hf, acc);
   }
 
+  // Q8: this wave's staged bytes in buffer buf.
+  __device__ __forceinline__ const lds_char* q8_stage(int buf) const {
+    return lds + buf * TL::TILEB + kQ8RowsPerWave * wave * TL::PITCH + kQ8StageOff;
+  }
+  // Q8: the scale load of this wave's staged rows (lane l: row l % 8), issued with the DMA.
+  __device__ __forceinline__ void q8_scale(int tile) {
+    const int v = min(tile * kVocabTile + kQ8RowsPerWave * wave + (lane & 7), V - 1);
+    qs = qscale[v];
+  }
+  // Q8: DMA piece j of this wave's staged rows (1 KiB: two rows of D int8), rows past the end of
+  // the vocabulary repeating the last row (their logits are masked).
+  __device__ __forceinline__ void q8_dma(int tile, int buf, int j) const {
+    const int r = kQ8RowsPerWave * wave + 2 * j + (lane >> 5);
+    const int v = min(tile * kVocabTile + r, V - 1);
+    lds_dma16(Eq + (int64_t)v * D + 16 * (lane & 31), q8_stage(buf) + j * 1024);
+  }
+  // Q8: staged row p of this wave in buffer buf, lane l's 8 bytes (elements 8 l .. 8 l + 7).
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __device__ __forceinline__ u32x2 q8_read(int buf, int p) const {
+    return *(const __attribute__((address_space(3))) u32x2*)(q8_stage(buf) + p * D + 8 * lane);
+  }
+  // Q8: those 8 elements as bf16(float(q) s) into the row's logical chunk `lane` of buffer buf.
+  __device__ __forceinline__ void q8_write(int buf, int p, u32x2 raw) const {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const int r = kQ8RowsPerWave * wave + p;
+    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qs), p));
+    const float nb = -128.0f * sc;
+    const uint32_t w[2] = {raw[0] ^ 0x80808080u, raw[1] ^ 0x80808080u};
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f32x2 f;
+      f[0] = __builtin_fmaf((float)((w[e >> 1] >> (16 * (e & 1))) & 0xffu), sc, nb);
+      f[1] = __builtin_fmaf((float)((w[e >> 1] >> (16 * (e & 1) + 8)) & 0xffu), sc, nb);
+      o[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+    }
+    *(__attribute__((address_space(3))) u32x4*)(lds + buf * TL::TILEB + r * TL::PITCH + lane * 16) = o;
+  }
+  // Q8: a whole tile into buffer buf, not overlapped (first tile, and tiles after a partial one).
+  __device__ __forceinline__ void q8_load_tile(int tile, int buf) {
+    q8_scale(tile);
+#pragma unroll
+    for (int j = 0; j < kQ8WaveBytes / 1024; ++j) q8_dma(tile, buf, j);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int p = 0; p < kQ8RowsPerWave; ++p) q8_write(buf, p, q8_read(buf, p));
+  }
+
   // Exp-sum with the fixed shift M, exact softcap. Register r holds vocabulary row
   // vbase + 8 (r/4) + 4 h + r%4; MASKED drops rows >= V.
   template <bool MASKED>
@@ -238,10 +312,12 @@ struct FwdCore {
   // keep each step's instructions together. With LOAD the chain also issues this wave's pieces of
   // the load of embedding tile load_tile into LDS buffer load_buf, spread over its steps. Wave
   // priority is staged over the tile by tile_step_priority.
-  template <bool LOAD, int NST, typename Stage>
+  // Q8: LOAD issues the int8 DMA of load_tile into buffer load_buf instead (pieces on steps 0, 4, 8,
+  // 12, the scale load with the first), and CONVERT turns the staged bytes there into bf16 rows
+  // (row p read on step 4 p, converted and stored on step 4 p + 2, after a wait for the DMA).
+  template <bool LOAD, int NST, bool CONVERT = false, typename Stage>
   __device__ __forceinline__ void pipelined(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB], int load_tile,
                                             int load_buf, Stage&& stage) {
-    using TL = TileLayout<D>;
     constexpr int NE = NB * 16;                     // logits of `prev` per lane
     constexpr int EPC = (NE + KS - 1) / KS;         // elements per group
     constexpr int NG = (NE + EPC - 1) / EPC;        // element groups
@@ -259,12 +335,20 @@ struct FwdCore {
     for (int k = 0; k < PF; ++k) fr[k] = frag(k);
     constexpr int LOAD_EVERY = (KS / kLoads) < 4 ? ((KS / kLoads) < 1 ? 1 : KS / kLoads) : 4;
     PieceBase pb{};
-    if (LOAD && TL::PAD) pb = piece_base<D>(lds, load_tile, load_buf, wave);
+    if (LOAD && !Q8 && TL::PAD) pb = piece_base<D>(lds, load_tile, load_buf, wave);
+    u32x2 qraw{};
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
       if (k < KS) tile_step_priority<KS>(vb, k);
       if (k + PF < KS) fr[k + PF] = frag(k + PF);
-      if (LOAD && k % LOAD_EVERY == 0 && k / LOAD_EVERY < kLoads) {
+      if constexpr (Q8) {
+        constexpr int kPieces = kQ8WaveBytes / 1024;
+        if (LOAD && k == 0) q8_scale(load_tile);
+        if (LOAD && k % 4 == 0 && k / 4 < kPieces) q8_dma(load_tile, load_buf, k / 4);
+        if (CONVERT && k == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (CONVERT && k % 4 == 0 && k / 4 < kQ8RowsPerWave) qraw = q8_read(load_buf, k / 4);
+        if (CONVERT && k % 4 == 2 && k / 4 < kQ8RowsPerWave) q8_write(load_buf, k / 4, qraw);
+      } else if (LOAD && k % LOAD_EVERY == 0 && k / LOAD_EVERY < kLoads) {
         if constexpr (TL::PAD) load_embed_piece_padded<D, kWaves>(pb, E, V, lane, k / LOAD_EVERY);
         else load_embed_piece<D, kWaves>(lds, E, V, load_tile, load_buf, wave, lane, k / LOAD_EVERY);
       }
@@ -300,10 +384,11 @@ struct FwdCore {
   // inputs whose logits are mostly large pay the speculation once per kExactRun blocks.
   static constexpr int kExactRun = 16;
   // Returns true when the sums of `prev` came from the series (take_target needs the form).
-  template <bool LOAD>
+  template <bool LOAD, bool CONVERT = false>
   __device__ __forceinline__ bool chain_with_epilogue(int buf, int vb, f32x16 (&a)[NB], const f32x16 (&prev)[NB],
                                                       int vprev, int load_tile = 0, int load_buf = 0) {
     constexpr int NE = NB * 16;
+    static_assert(!CONVERT || Q8, "conversion of staged rows: int8 tiles only");
     if (!FIXED) {   // running maximum (c = 0 or caps above the fixed-shift range)
       if (LOAD)
         for (int i = 0; i < kLoads; ++i) load_embed_piece<D, kWaves>(lds, E, V, load_tile, load_buf, wave, lane, i);
@@ -320,7 +405,7 @@ struct FwdCore {
     // DZ adds a stage: 4 also forms the slope factor, 5 multiplies it by 2^t, 6 stores eight at a time
     constexpr int NST = DZ ? 7 : 6;
     if (exact_left > 0 || (ASYM && !(sc.thr > 0.f))) {
-      pipelined<LOAD, NST>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
+      pipelined<LOAD, NST, CONVERT>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
         const bool neg = ASYM && z < 0.f;
         switch (st) {
           case 0: q[e] = z * (neg ? sc.alpha_n : sc.alpha); break;
@@ -353,7 +438,7 @@ struct FwdCore {
     }
     float u[NE];
     float amax = 0.f;
-    pipelined<LOAD, NST>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
+    pipelined<LOAD, NST, CONVERT>(buf, vb, a, prev, load_tile, load_buf, [&](int st, int e, float z) {
       switch (st) {
         case 0: u[e] = z * z; amax = fmaxf(amax, fabsf(z)); break;
         case 1: {   // asymmetric caps: each side's own coefficients (q0 = log2 e is shared)
@@ -403,7 +488,7 @@ struct FwdCore {
   }
 };
 
-template <int D, bool FIXED, int NB, bool ASYM, bool DZ = false>
+template <int D, bool FIXED, int NB, bool ASYM, bool DZ = false, bool Q8 = false>
 __global__ __launch_bounds__(WaveShape<NB>::kThreads) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
 void fwd_mfma_kernel(FwdParams p) {
   using TL = TileLayout<D>;
@@ -428,10 +513,12 @@ void fwd_mfma_kernel(FwdParams p) {
   const int V = p.V;
   const int64_t tok0 = (int64_t)rt * kRowsPerWG + wave * kTokPerWave;   // first token of this wave
 
-  FwdCore<D, FIXED, NB, ASYM, DZ> core;
+  FwdCore<D, FIXED, NB, ASYM, DZ, Q8> core;
   const lds_char* lds = (const lds_char*)smem;
   core.lds = lds;
   core.E = p.E;
+  core.Eq = p.Eq;
+  core.qscale = p.qscale;
   core.wave = wave;
   core.lane = lane;
   core.h = h;
@@ -442,7 +529,15 @@ void fwd_mfma_kernel(FwdParams p) {
 
   // ---- the first embedding tile goes out first, so that its latency overlaps the prologue
   const int ntiles = t_end - t_begin;
-  if (ntiles > 0) load_embed_tile<D, kFwdWaves>(lds, p.E, V, t_begin, 0, wave, lane);
+  if (ntiles > 0) {
+    if constexpr (Q8) {   // its DMA and scale load now, the conversion after the hidden rows' loads
+      core.q8_scale(t_begin);
+#pragma unroll
+      for (int j = 0; j < core.kQ8WaveBytes / 1024; ++j) core.q8_dma(t_begin, 0, j);
+    } else {
+      load_embed_tile<D, kFwdWaves>(lds, p.E, V, t_begin, 0, wave, lane);
+    }
+  }
 
   // ---- this lane's tokens: hidden row halves into registers (B operands of the MFMA)
   // (token and row indices are recomputed after the main loop, so that they hold no registers)
@@ -470,6 +565,13 @@ void fwd_mfma_kernel(FwdParams p) {
     core.ykey[tb] = (ok && ((y >> 2) & 1) == h) ? y : -1;
     core.ty[tb] = FIXED ? -1.0f : -INFINITY;
   }
+  if constexpr (Q8) {
+    if (ntiles > 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int p8 = 0; p8 < core.kQ8RowsPerWave; ++p8) core.q8_write(0, p8, core.q8_read(0, p8));
+    }
+  }
 
   // ---- main loop. Only the last tile of the vocabulary can be partial; it runs the masked
   //      epilogue. Elsewhere the epilogue of the previous 32-row block is interleaved with the
@@ -487,7 +589,10 @@ void fwd_mfma_kernel(FwdParams p) {
     f32x16 a0[NB];
     // the steady state spreads the next tile's load over the first chain; elsewhere it goes first
     const bool steady = !(last_partial && i + 1 == ntiles) && vprev >= 0;
-    if (next && !steady) load_embed_tile<D, kFwdWaves>(lds, p.E, V, tile + 1, buf ^ 1, wave, lane);
+    if (next && !steady) {
+      if constexpr (Q8) core.q8_load_tile(tile + 1, buf ^ 1);
+      else load_embed_tile<D, kFwdWaves>(lds, p.E, V, tile + 1, buf ^ 1, wave, lane);
+    }
     if (last_partial && i + 1 == ntiles) {
       core.chain(buf, 0, a0);
       if (vprev >= 0) {
@@ -511,7 +616,9 @@ void fwd_mfma_kernel(FwdParams p) {
       if (next) ser = core.template chain_with_epilogue<true>(buf, 0, a0, accp, vprev, tile + 1, buf ^ 1);
       else ser = core.template chain_with_epilogue<false>(buf, 0, a0, accp, vprev);
       core.take_target(accp, vprev, ser);
-      ser = core.template chain_with_epilogue<false>(buf, 1, accp, a0, vb0);
+      // the int8 head: the second chain turns the staged rows into the next tile's buffer
+      if (Q8 && next) ser = core.template chain_with_epilogue<false, Q8>(buf, 1, accp, a0, vb0, tile + 1, buf ^ 1);
+      else ser = core.template chain_with_epilogue<false>(buf, 1, accp, a0, vb0);
       core.take_target(a0, vb0, ser);
       vprev = vb0 + 32;
     }
@@ -850,14 +957,20 @@ hipError_t launch_compact_rows(const uint8_t* mask, int64_t T, char* ws, const F
   return hipGetLastError();
 }
 
-template <int D, bool FIXED, bool ASYM, bool DZ = false>
+template <int D, bool FIXED, bool ASYM, bool DZ = false, bool Q8 = false>
 static void launch_mfma(const FwdParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, FIXED, kFwdTokBlocks, ASYM, DZ>), dim3(grid),
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, FIXED, kFwdTokBlocks, ASYM, DZ, Q8>), dim3(grid),
                      dim3(WaveShape<kFwdTokBlocks>::kThreads), 0, st, p);
 }
 
 template <int D>
 static void launch_mfma_d(const FwdParams& p, int grid, hipStream_t st) {
+  if constexpr (D == 512 && kFwdTokBlocks == 1) {
+    if (p.Eq) {   // the caller checked fwd_reads_q8
+      launch_mfma<D, true, false, false, true>(p, grid, st);
+      return;
+    }
+  }
   if (p.dz) {   // the caller checked fwd_writes_dz
     if (p.sc.asym) launch_mfma<D, true, true, true>(p, grid, st);
     else launch_mfma<D, true, false, true>(p, grid, st);
@@ -875,11 +988,19 @@ bool fwd_writes_dz(int32_t dtype, int32_t D, float cap_pos, float cap_neg) {
   return dtype == 0 && mfma_width(D) && sc.fixed;
 }
 
+bool fwd_reads_q8(int32_t D, float cap) {
+  const Softcap sc = Softcap::make(cap, cap);
+  return D == 512 && kFwdTokBlocks == 1 && sc.fixed && !sc.asym;
+}
+
 hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t* target,
                       const uint8_t* mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
-                      float* nats, float* lse, char* ws, const DeviceInfo& dev, hipStream_t st, uint16_t* dz) {
+                      float* nats, float* lse, char* ws, const DeviceInfo& dev, hipStream_t st, uint16_t* dz,
+                      const int8_t* eq, const float* qscale) {
   if (T == 0) return hipSuccess;
   if (dz && !fwd_writes_dz(dtype, D, cap_pos, cap_neg)) return hipErrorInvalidValue;
+  if (eq && (dz || dtype != 0 || cap_pos != cap_neg || !qscale || !fwd_reads_q8(D, cap_pos)))
+    return hipErrorInvalidValue;
   const FwdWorkspace L = fwd_workspace(T, D, V);
   const Softcap sc = Softcap::make(cap_pos, cap_neg);
   const int32_t* rows = nullptr;
@@ -919,6 +1040,8 @@ hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t
   p.s_target = reinterpret_cast<float*>(ws + L.s_target);
   p.dz = dz;
   p.ldz = (int64_t)p.n_vtiles * kVocabTile;
+  p.Eq = eq;
+  p.qscale = qscale;
 
   const int64_t rt = (T + kRowsPerWG - 1) / kRowsPerWG;
   const int ncu = dev.cu_count > 0 ? (dev.cu_count < 1024 ? dev.cu_count : 1024) : 256;

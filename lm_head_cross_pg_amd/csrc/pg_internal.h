@@ -48,7 +48,10 @@ hipError_t launch_compact_rows(const uint8_t* mask, int64_t T, char* ws, const F
 hipError_t launch_fwd(const void* H, const void* E, int32_t dtype, const int32_t* target,
                       const uint8_t* mask, int64_t T, int32_t D, int32_t V, float cap_pos, float cap_neg,
                       float* nats, float* lse, char* ws, const DeviceInfo& dev, hipStream_t st,
-                      uint16_t* dz = nullptr);
+                      uint16_t* dz = nullptr, const int8_t* eq = nullptr, const float* qscale = nullptr);
+// eq, qscale (nullable): the head is the per-row int8 embedding (q[V, D], scales[V]) read by the
+// forward itself (E is then unused); only where fwd_reads_q8 holds, without dz.
+bool fwd_reads_q8(int32_t D, float cap);
 // The forward can write the unnormalised dZ: bf16 MFMA widths, every side capped within the
 // fixed-shift range (one cap, or two).
 bool fwd_writes_dz(int32_t dtype, int32_t D, float cap_pos, float cap_neg);

@@ -27,12 +27,19 @@ from . import abi
 class SlidingWindowEval:
     def __init__(self, tokens: torch.Tensor, byte_len: torch.Tensor, V: int, D: int, window: int = 2048,
                  stride: int = 64, windows_per_batch: int = 32, softcap: float = 30.0, ttt_lr: float = 0.0,
-                 embed_master: Optional[torch.Tensor] = None, keep_dhidden: bool = False):
+                 embed_master: Optional[torch.Tensor] = None, keep_dhidden: bool = False,
+                 int8_head: bool = False):
         """keep_dhidden: with ttt_lr > 0, also compute the gradient of the hidden states of each
         batch (into self.dH). The embedding step needs only dE, so by default dH is left out and
-        its product is not run."""
+        its product is not run.
+        int8_head: score the per-row int8 form of the tied embedding (pg_quantize_q8) with
+        step_int8, as a model evaluated after quantisation is (README leaderboard, "Mixed Quant +
+        Sliding Window Eval": int8 embeddings); evaluation only, no test-time training."""
         if ttt_lr and embed_master is None:
             raise ValueError("score-first TTT needs float32 master weights of the embedding (embed_master)")
+        if ttt_lr and int8_head:
+            raise ValueError("test-time training updates a bf16 embedding; the int8 head is evaluation only")
+        self.int8_head = bool(int8_head)
         self.tokens, self.byte_len, self.V, self.D = tokens, byte_len, int(V), int(D)
         self.window, self.stride, self.per_batch = int(window), int(stride), int(windows_per_batch)
         self.softcap, self.ttt_lr, self.embed_master = float(softcap), float(ttt_lr), embed_master
@@ -47,7 +54,7 @@ class SlidingWindowEval:
         # running sums (nats, bytes, predictions) and their bits per byte: NaN (0 / 0) until a batch
         # with predictions has been scored, as for a stream too short to predict anything
         self.out = torch.tensor([0.0, 0.0, 0.0, float("nan")], dtype=torch.float64, device=dev)
-        op = abi.PG_OP_FWD_BWD if self.ttt_lr else abi.PG_OP_FWD
+        op = abi.PG_OP_FWD_BWD if self.ttt_lr else (abi.PG_OP_FWD_Q8 if self.int8_head else abi.PG_OP_FWD)
         self.ws = torch.empty(max(abi.workspace_bytes(op, rows, self.D, self.V), 256), dtype=torch.uint8, device=dev)
         self.ws_bpb = torch.empty(max(abi.workspace_bytes(abi.PG_OP_BPB, rows, 1, self.V), 256), dtype=torch.uint8,
                                   device=dev)
@@ -84,6 +91,20 @@ class SlidingWindowEval:
         else:
             abi.pg_lmhead_ce_fwd(hidden, embed, tgt, msk, self.softcap, nats, lse, self.ws)
             abi.pg_bpb_accumulate(nats, tgt, msk, self.byte_len, None, self.V, self.out, self.ws_bpb)
+        return n
+
+    def step_int8(self, hidden: torch.Tensor, embed_q8: torch.Tensor, embed_scale: torch.Tensor,
+                  first_window: int, n_windows: int) -> int:
+        """Score one batch on the int8 head (embed_q8 [V, D] int8, embed_scale [V] float32, from
+        pg_quantize_q8); hidden as for step. Returns the number of predictions the batch scored."""
+        if not self.int8_head:
+            raise ValueError("step_int8 needs a driver built with int8_head=True (its workspace)")
+        rows = n_windows * self.window
+        tgt, msk, nats, lse = self.target[:rows], self.mask[:rows], self.nats[:rows], self.lse[:rows]
+        abi.pg_window_rows(self.tokens, self.window, self.stride, first_window, n_windows, tgt, msk)
+        n = self.scored(first_window, n_windows)
+        abi.pg_lmhead_ce_fwd_q8(hidden, embed_q8, embed_scale, tgt, msk, self.softcap, nats, lse, self.ws)
+        abi.pg_bpb_accumulate(nats, tgt, msk, self.byte_len, None, self.V, self.out, self.ws_bpb)
         return n
 
     def result(self):

@@ -80,9 +80,10 @@ def run_q8(inp, sample_rows=None, mask=None):
     # the same head through the bf16 entry point, with the oracle's dequantised embedding: same bits
     Eb = torch.from_numpy(synth.bf16_bits(Ed.astype(np.float32)).view(np.int16)).cuda()
     ref = torch.empty(T, device="cuda")
-    abi.pg_lmhead_ce_fwd(d["hidden"], Eb, d["target"], mask_t, c, ref, None)
+    ref_lse = torch.full((T,), float("nan"), device="cuda")
+    abi.pg_lmhead_ce_fwd(d["hidden"], Eb, d["target"], mask_t, c, ref, ref_lse)
     torch.cuda.synchronize()
-    assert torch.equal(ref, nats)
+    assert torch.equal(ref, nats) and torch.equal(ref_lse, lse)
     return g, H, Ed
 
 
@@ -97,6 +98,33 @@ def test_quantised_forward_masked_ragged_and_generic(T, D, masked):
     inp = synth.make_inputs(workload("fwd_v8192", T=T, D=D, V=1000, stream=112 + D), 0)
     mask = (np.random.default_rng(T).random(T) < 0.4).astype(np.uint8) if masked else None
     run_q8(inp, mask=mask)
+
+
+@pytest.mark.parametrize("T,V,masked,cap,hscale", [
+    (8192, 8192, False, 30.0, 1.0),    # 32 row tiles: 8 vocabulary splits of 16 tiles, the pipelined conversion
+    (8192, 8192, True, 30.0, 8.0),     # the same with a mask, logits on the exact softcap
+    (20000, 8192, "all", 30.0, 1.0),   # a mask scoring every row: 79 row tiles over the whole vocabulary each
+    (20000, 8192, False, 30.0, 1.0),   # the same rows without a mask: the dequantising pass
+    (2048, 4133, True, 30.0, 1.0),     # ragged vocabulary: the last tile partial
+    (1, 8192, False, 30.0, 1.0),       # one row: every split a single tile
+    (300, 64, False, 30.0, 1.0),       # one tile in all
+    (300, 65, True, 30.0, 1.0),        # one full tile and one row
+    (1000, 8192, False, 50.0, 1.0),    # a cap above the fixed-shift range: the dequantising pass
+    (1000, 1000, False, 0.0, 1.0),     # no cap: the dequantising pass
+])
+def test_q8_on_chip_conversion_same_bits(T, V, masked, cap, hscale):
+    """At D = 512 with one cap in (0, 40] the forward converts each int8 tile into bf16 on chip; the
+    other caps rebuild the bf16 head first. Either way nats and lse are the bits of the bf16 entry
+    point on the dequantised head (torch.equal on every row), and the sampled rows are within the
+    tolerance of the oracle's forward on the quantised head."""
+    inp = synth.make_inputs(workload("fwd_v8192", T=T, V=V, softcap=cap, hidden_scale=hscale, stream=150 + V % 97), 0)
+    mask = (np.random.default_rng(T + V).random(T) < 0.5).astype(np.uint8) if masked else None
+    if masked == "all":
+        mask[:] = 1
+    if mask is not None:
+        mask[0] = 1
+    rows = np.unique(np.concatenate([np.random.default_rng(3).choice(T, min(T, 96), replace=False), [0, T - 1]]))
+    run_q8(inp, sample_rows=rows, mask=mask)
 
 
 def test_quantised_forward_full_size():

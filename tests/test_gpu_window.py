@@ -177,3 +177,43 @@ def test_driver_short_streams(n_tokens):
         assert len(got) == 0 and n == 0 and np.isnan(b) and np.isnan(ref["bpb"])
     else:
         _check(drv, got, ref)
+
+
+def test_driver_int8_head():
+    """Sliding-window evaluation of the int8 head (evaluation after quantisation): the driver's
+    int8 steps against the oracle's loop on the dequantised embedding, and bit for bit the nats and
+    sums of the bf16 driver run on that embedding's bf16 form."""
+    seed, n_tokens, window, stride, D, V, per_batch = 5, 4625, 2048, 64, 512, 8192, 8
+    st = synth.make_stream(seed, n_tokens, V, D=D)
+    tokens, blen = st["tokens"], st["byte_len"]
+    sched = ora.window_schedule(n_tokens, window, stride)
+    E16 = torch.from_numpy(st["embed"].view(np.int16)).cuda().view(torch.bfloat16)
+    q8 = torch.empty((V, D), dtype=torch.int8, device="cuda")
+    sc8 = torch.empty(V, dtype=torch.float32, device="cuda")
+    abi.pg_quantize_q8(E16, q8, sc8)
+    Ed = ora.dequantize_rows_q8(*ora.quantize_rows_q8(synth.bf16_to_f64(st["embed"])))
+    Ed16 = torch.from_numpy(synth.bf16_bits(Ed.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+    t, b = torch.from_numpy(tokens).cuda(), torch.from_numpy(blen).cuda()
+    drv8 = SlidingWindowEval(t, b, V, D, window, stride, per_batch, 30.0, int8_head=True)
+    drv = SlidingWindowEval(t, b, V, D, window, stride, per_batch, 30.0)
+    got = []
+    for w0, nw in drv8.batches():
+        H = np.zeros((nw * window, D), np.uint16)
+        for k in range(nw):
+            w = w0 + k
+            r0 = sched[w][0] - w * stride
+            H[k * window + r0: k * window + r0 + len(sched[w])] = synth.window_hidden(seed, w, len(sched[w]), D)
+        Ht = torch.from_numpy(H.view(np.int16)).cuda().view(torch.bfloat16)
+        print(f"[case] int8 window driver batch w0={w0} nw={nw}", flush=True)
+        n = drv8.step_int8(Ht, q8, sc8, w0, nw)
+        assert drv.step(Ht, Ed16, w0, nw) == n
+        rows = nw * window
+        assert torch.equal(drv8.nats[:rows], drv.nats[:rows])
+        got.append({"n": n, "nats": drv8.nats[:rows][drv8.mask[:rows].bool()].cpu().numpy().astype(np.float64)})
+    torch.cuda.synchronize()
+    assert drv8.result() == drv.result()
+    ref = ora.sliding_window_eval(tokens, blen, lambda w, k: synth.bf16_to_f64(synth.window_hidden(seed, w, k, D)),
+                                  Ed, 30.0, window, stride, per_batch)
+    _check(drv8, got, ref)
+    with pytest.raises(ValueError):
+        drv.step_int8(Ht, q8, sc8, 0, 1)
