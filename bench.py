@@ -34,7 +34,8 @@ PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 F
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_mfma_T65536_D512_V8192_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "lm_head_cross_pg_amd", "csrc", f)
                   for f in ("pg_fwd.hip", "pg_common.h", "pg_tile.h")]
-FWD_KERNEL = "fwd_mfma_kernel<512, true, 1, false, false"   # the symmetric, fixed-shift forward (no dZ)
+# the symmetric, fixed-shift forward on a bf16 head (no dZ, not the int8 head)
+FWD_KERNEL = "fwd_mfma_kernel<512, true, 1, false, false, false"
 COPY_BYTES = 1 << 29          # --calibrate-copy moves 512 MiB each way per launch
 
 
@@ -76,12 +77,25 @@ def _counter_rows(d):
     return rows
 
 
-def _per_dispatch(rows, name_part, counter):
+def _long_dispatches(rows, match):
+    """Dispatch ids of the rows that satisfy match whose duration is at least half the longest of
+    them: the full-size launches of a kernel that also runs on masked batches of the same grid."""
+    dur = {}
+    for r in rows:
+        if match(r):
+            dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    top = max(dur.values(), default=0)
+    return {k for k, v in dur.items() if 2 * v >= top}
+
+
+def _per_dispatch(rows, name_part, counter, long_only=False):
     """Mean over dispatches of kernels whose name contains name_part of one counter (summed over
-    the per-agent rows of a dispatch)."""
+    the per-agent rows of a dispatch); long_only keeps the full-size launches (_long_dispatches)."""
+    match = lambda r: name_part.lower() in r["Kernel_Name"].lower()
+    keep = _long_dispatches(rows, match) if long_only else None
     per = {}
     for r in rows:
-        if name_part.lower() in r["Kernel_Name"].lower() and r["Counter_Name"] == counter:
+        if match(r) and r["Counter_Name"] == counter and (keep is None or r["Dispatch_Id"] in keep):
             per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     return (sum(per.values()) / len(per), len(per)) if per else (None, 0)
 
@@ -94,8 +108,8 @@ def summarize_counters(d):
            "kernel_source_sha256_16": kernel_source_hash()}
     cf, _ = _per_dispatch(_counter_rows(os.path.join(d, "calib_fetch")), "copy", "FETCH_SIZE")
     cw, _ = _per_dispatch(_counter_rows(os.path.join(d, "calib_write")), "copy", "WRITE_SIZE")
-    ff, nf = _per_dispatch(_counter_rows(os.path.join(d, "fetch")), FWD_KERNEL, "FETCH_SIZE")
-    fw, nw = _per_dispatch(_counter_rows(os.path.join(d, "write")), FWD_KERNEL, "WRITE_SIZE")
+    ff, nf = _per_dispatch(_counter_rows(os.path.join(d, "fetch")), FWD_KERNEL, "FETCH_SIZE", long_only=True)
+    fw, nw = _per_dispatch(_counter_rows(os.path.join(d, "write")), FWD_KERNEL, "WRITE_SIZE", long_only=True)
     lines = ["# HBM traffic of the fused forward (T=65536, D=512, V=8192)", ""]
     if None in (cf, cw, ff, fw):
         raise SystemExit("missing counter runs under " + d)
@@ -112,17 +126,18 @@ def summarize_counters(d):
               f"| compulsory (H 64 MiB + E 8 MiB + targets 256 KiB; nats + lse 512 KiB) | 72.25 MiB read, 0.5 MiB written |"]
     mrows = _counter_rows(os.path.join(d, "mfma"))
     if mrows:
-        busy, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_VALU_MFMA_BUSY_CYCLES")
-        gui, _ = _per_dispatch(mrows, FWD_KERNEL, "GRBM_GUI_ACTIVE")
-        mops, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
-        valu, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_INSTS_VALU")
-        lds, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_INSTS_LDS")
-        conf, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_LDS_BANK_CONFLICT")
+        busy, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_VALU_MFMA_BUSY_CYCLES", True)
+        gui, _ = _per_dispatch(mrows, FWD_KERNEL, "GRBM_GUI_ACTIVE", True)
+        mops, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_INSTS_VALU_MFMA_MOPS_BF16", True)
+        valu, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_INSTS_VALU", True)
+        lds, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_INSTS_LDS", True)
+        conf, _ = _per_dispatch(mrows, FWD_KERNEL, "SQ_LDS_BANK_CONFLICT", True)
         if busy and gui:
             # GRBM_GUI_ACTIVE comes back summed over the 8 XCDs; per XCD it is the kernel's cycles
             cyc = gui / 8.0
+            keep = _long_dispatches(mrows, lambda r: FWD_KERNEL in r["Kernel_Name"])
             durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in mrows
-                    if FWD_KERNEL in r["Kernel_Name"] and r["Counter_Name"] == "GRBM_GUI_ACTIVE"]
+                    if r["Dispatch_Id"] in keep and r["Counter_Name"] == "GRBM_GUI_ACTIVE"]
             dur_ns = sum(durs) / len(durs)
             out["mfma_busy_pct"] = 100.0 * busy / (cyc * 1024)
             out["clock_ghz"] = cyc / dur_ns
@@ -140,8 +155,8 @@ def summarize_counters(d):
                 lines.append(f"| {nm} per launch | {v:.4g} |")
     trows = _counter_rows(os.path.join(d, "tcc"))
     if trows:
-        hit, _ = _per_dispatch(trows, FWD_KERNEL, "TCC_HIT_sum")
-        miss, _ = _per_dispatch(trows, FWD_KERNEL, "TCC_MISS_sum")
+        hit, _ = _per_dispatch(trows, FWD_KERNEL, "TCC_HIT_sum", True)
+        miss, _ = _per_dispatch(trows, FWD_KERNEL, "TCC_MISS_sum", True)
         if hit is not None and miss is not None and hit + miss > 0:
             out["l2_hit_pct"] = 100.0 * hit / (hit + miss)
             lines.append(f"| L2 hits / (hits + misses), TCC_HIT_sum and TCC_MISS_sum | {out['l2_hit_pct']:.1f} % "
@@ -154,13 +169,16 @@ def summarize_counters(d):
                         r["Kernel_Name"].startswith("pg::")})
         train_lines = ["", "HBM traffic per launch of each library kernel in the benchmark run with the training "
                            "step (without the sliding-window leg), at each kernel's largest grid (the T = 65536 "
-                           "workloads): FETCH_SIZE x fetch scale, WRITE_SIZE x write scale, MiB.", "",
+                           "workloads; of those, the launches at least half as long as the longest, so that masked "
+                           "batches of the same grid do not mix in): FETCH_SIZE x fetch scale, WRITE_SIZE x write "
+                           "scale, MiB.", "",
                        "| kernel | grid (work-items) | launches | fetched | written |", "|---|---|---|---|---|"]
 
         def at_grid(rows, nm, counter, grid):
+            keep = _long_dispatches(rows, lambda r: r["Kernel_Name"] == nm and int(r["Grid_Size"]) == grid)
             per = {}
             for r in rows:
-                if r["Kernel_Name"] == nm and r["Counter_Name"] == counter and int(r["Grid_Size"]) == grid:
+                if r["Dispatch_Id"] in keep and r["Counter_Name"] == counter:
                     per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
             return (sum(per.values()) / len(per), len(per)) if per else (None, 0)
 
@@ -382,10 +400,11 @@ def summarize_trace(d, steps, warmup):
              "rocprofv3 `--kernel-trace --stats` of the benchmark: per kernel, the number of launches and the",
              f"average / min / max duration. The main forward (`{FWD_KERNEL}>`) runs in the",
              "bench steps, the event-timed launches, the quantised-head launches and the training steps; the",
-             "asymmetric-cap forward (`<512, true, 1, true, false>`) is a kernel of its own; the dZ-writing",
-             "forwards (`..., false, true>`, and `..., true, true>` for asymmetric caps) and the backward kernels",
-             "run once per training step. The kernels run back to back, so the clock falls under the sustained",
-             "load: compare the min column with isolated launches.", "",
+             "asymmetric-cap forward (`<512, true, 1, true, false, false>`) is a kernel of its own, and so is the",
+             "forward on the int8 head (`<512, true, 1, false, false, true>`, masked and small calls); the",
+             "dZ-writing forwards (`..., false, true, false>`, and `..., true, true, false>` for asymmetric caps)",
+             "and the backward kernels run once per training step. The kernels run back to back, so the clock",
+             "falls under the sustained load: compare the min column with isolated launches.", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in stats:
         lines.append(f"| `{r['Name'][:72]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "

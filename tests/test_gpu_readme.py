@@ -38,4 +38,5 @@ def test_readme_examples_run():
     torch.cuda.synchronize()
     assert ns["n_scored"] == ns["tokens"].numel() - 1
     assert ns["bpb"] > 0
+    assert abs(ns["bpb_int8"] - ns["bpb"]) < 1e-2 * ns["bpb"]   # the int8 head scores close to the bf16 one
     assert not torch.equal(ns["embed"], embed0)        # the test-time steps moved the embedding
