@@ -1,21 +1,24 @@
 // bf16 GEMM with float32 accumulation for the two products of the backward, dH = g dZ E and
 // dE = g dZ^T H, on gfx950 (v_mfma_f32_32x32x16_bf16).
 //
-// A workgroup owns a 256 x 256 output tile and runs 8 waves, two per SIMD, in a 2 x 4 grid; each
-// wave accumulates 128 x 64 of the tile in eight 32 x 32 accumulators. k advances in 32-deep
-// chunks; B and A are filled by global_load_lds_dwordx4 into LDS rings of NS and NS + 1 slots.
+// A workgroup owns a 256 x 256 output tile and runs 4 waves, one per SIMD, in a 2 x 2 grid; each
+// wave accumulates 128 x 128 of the tile in sixteen 32 x 32 accumulators, which fill its AGPRs. k
+// advances in 32-deep chunks; B and A are filled by global_load_lds_dwordx4 into LDS rings of NS
+// and NS + AL slots.
 //
 // Why this shape: the operand streams mix a unique stream from HBM (dZ) with a stream that every
-// workgroup shares from L2 (E or H). A CU returns vector-memory data in issue order, so the HBM
-// latency paces the shared stream too. Each stage therefore issues the B loads of stage
-// s + NS - 1 first and the A loads of stage s + NS after them: a B load waits only for A loads
-// issued a stage or more before it, and every load has NS stage periods to land (A needs the extra
-// ring slot). A 256 x 256 tile moves 32 KiB per 4.2 MFLOP chunk, against 40 KiB for 128 x 512, and
-// at T = 65536 it still gives 512 tiles (two full rounds on 256 CUs). The two column tiles of a row
-// tile are launched 8 workgroup ids apart: workgroups are dealt to the 8 XCDs in turn, so the pair
-// runs on one XCD at the same time and its L2 serves the second read of their dZ rows (the HBM
-// fetch stays at one pass over dZ). Two waves per SIMD keep the matrix pipe busy while the other
-// wave of the SIMD is held up issuing a load.
+// workgroup shares from L2 (E or H). A 256 x 256 tile moves 32 KiB per 4.2 MFLOP chunk, against
+// 40 KiB for 128 x 512, and at T = 65536 it still gives 512 tiles (two full rounds on 256 CUs);
+// larger tiles do not fit the register file. The two column tiles of a row tile are launched 8
+// workgroup ids apart: workgroups are dealt to the 8 XCDs in turn, so the pair runs on one XCD at
+// the same time and its L2 serves the second read of their dZ rows (the HBM fetch stays at one
+// pass over dZ). With 128 x 128 per wave, a wave reads 8 KiB of LDS fragments per 16-deep step
+// for 16 MFMAs; two waves of 128 x 64 per SIMD read 6 KiB for 8 MFMAs each, so that fragment reads
+// and DMA writes together needed 128 bytes of LDS bandwidth per clock at the full matrix rate,
+// against 96 here. The lone wave has no partner on its SIMD to cover a wait, so it reads the
+// fragments of the next 16-deep step during the MFMAs of the current one, and the barrier of stage
+// s + 1 sits between the two steps of stage s (all of stage s's fragments are in registers by
+// then): the second step's MFMAs run while the first fragments of stage s + 1 are read.
 //
 // A is dZ in its 32 x 32 block layout (described in pg_internal.h); each stage's A tile is BM / 32
 // whole blocks, i.e. contiguous 2 KiB runs. The other operand (E for dH, H for dE) is k x n
@@ -37,40 +40,30 @@ namespace pg {
 // apart); it is its own inverse.
 __device__ __forceinline__ int a_swz(int c) { return c ^ ((c >> 4) & 1) ^ (((c >> 6) & 1) << 3); }
 
-// Tile shape: each wave accumulates WM x WN blocks of 32 x 32; the 8 waves form a WGM x (8 / WGM)
-// grid, so the workgroup tile is BM x BN = (32 WM WGM) x (32 WN (8 / WGM)).
-template <int WM, int WN, int WGM>
-struct GemmShape {
-  static constexpr int NW = 8, WGN = NW / WGM;
-  static constexpr int BM = 32 * WM * WGM, BN = 32 * WN * WGN, BK = kGemmBK;
-};
-
-template <bool A_TRANS, int WM, int WN, int WGM, int NS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// The loads of each stage are split over the two halves around a barrier: A of stage s + NS + AL - 1
+// before barrier s + 1 (into the slot of stage s - 1), B of stage s + NS after it (into the slot
+// stage s has finished reading). A thus runs AL stages further ahead than B; NS and AL set the
+// depth of the rings (one and two stages ahead measured the same).
+template <bool A_TRANS, int NS, int AL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(GemmParams g) {
-  using S = GemmShape<WM, WN, WGM>;
-  constexpr int BM = S::BM, BN = S::BN, BK = S::BK, NW = S::NW;
+  constexpr int WM = 4, WN = 4, NW = 4, WGN = 2;
+  constexpr int BM = 256, BN = 256, BK = kGemmBK;
   constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;
-  constexpr int A_LOADS = ABYTES / 1024, B_LOADS = BBYTES / 1024;   // 1 KiB load instructions
-  constexpr int APW = A_LOADS / NW, BPW = B_LOADS / NW, LPW = APW + BPW;   // per wave and stage
-  constexpr int RPL = 1024 / (BN * 2);                              // B rows per load (1 or 2)
-  static_assert(BK == 32 && A_LOADS % NW == 0 && B_LOADS % NW == 0 && (RPL == 1 || RPL == 2),
-                "tile shape assumed by the layouts below");
-  // B: ring of NS slots; A: ring of AST slots, one stage deeper, so that each stage's A
-  // loads can be issued after its B loads and a stage earlier
-  constexpr int AST = NS + 1;
-  static_assert(NS * BBYTES + AST * ABYTES <= 160 * 1024, "LDS rings");
+  constexpr int APW = ABYTES / 1024 / NW, BPW = BBYTES / 1024 / NW, LPW = APW + BPW;
+  constexpr int RPL = 1024 / (BN * 2);
+  static_assert(BK == 32 && APW == 4 && BPW == 4 && RPL == 2, "tile shape assumed below");
+  constexpr int AST = NS + AL;   // A is issued AL stages ahead of B
+  static_assert(AL >= 1 && NS * BBYTES + AST * ABYTES <= 160 * 1024, "LDS rings");
   __shared__ __attribute__((aligned(1024))) char smem[NS * BBYTES + AST * ABYTES];
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
-  const int wm = wave / S::WGN, wn = wave % S::WGN;   // this wave's rows wm * 32 WM .., columns wn * 32 WN ..
+  const int wm = wave / WGN, wn = wave % WGN;
 
   const int64_t ndev = g.n_dev ? (int64_t)(*g.n_dev) : 0;
   const int64_t M = g.m_dev ? ndev : g.M;
   const int64_t K = g.k_dev ? ndev : g.K;
-  // Workgroups are dealt to the 8 XCDs in turn; the NT column tiles of one row tile get ids 8 apart,
-  // so they run on the same XCD at the same time and share its L2 copy of their dZ rows.
   const int NT = (int)((g.N + BN - 1) / BN);
   const int64_t wid = blockIdx.x;
   const int64_t mt = (wid / (8 * NT)) * 8 + (wid % 8);
@@ -86,47 +79,70 @@ void gemm_bf16_kernel(GemmParams g) {
   const int64_t nk = kc_end > kc_begin ? kc_end - kc_begin : 0;
   const int64_t kvalid = g.k_dev ? ndev : g.kvalid;
 
-  // ---- the load group of stage kc: this wave's B loads of stage kc (i < BPW: load wave + NW i,
-  //      rows RPL (wave + NW i) ..), then its A loads of stage kc + 1 (i >= BPW: load
-  //      wave + NW (i - BPW), half of an A block). load_one(kc, i) issues the i-th, so that a group
-  //      can be spread over the MFMAs of stage kc - (NS - 1).
-  auto load_one = [&](int64_t kc, int i) {
-    const int64_t rel = kc - kc_begin;
-    if (i >= BPW) {
-      const int q = wave + NW * (i - BPW);
-      char* sA = smem + NS * BBYTES + (int)((rel + 1) % AST) * ABYTES;
-      const int64_t k0 = (kc + 1) * BK;
-      const int bm = q >> 1;             // half (q & 1) of block bm of the stage
-      int64_t bt, bv;
-      if (!A_TRANS) {                    // dH: m = token, k = vocabulary
-        bt = (m0 >> 5) + bm;
-        bt = bt < g.a_mblocks ? bt : g.a_mblocks - 1;
-        bv = k0 >> 5;
-        bv = bv < g.lda ? bv : g.lda - 1;
-      } else {                           // dE: m = vocabulary, k = token
-        bt = k0 >> 5;
-        bt = bt < g.k_blocks ? bt : g.k_blocks - 1;
-        bv = (m0 >> 5) + bm;
-        bv = bv < g.a_mblocks ? bv : g.a_mblocks - 1;
-      }
-      const int chunk = a_swz(64 * (q & 1) + lane);
-      const uint16_t* src = g.A + (bt * g.lda + bv) * 1024 + chunk * 8;
-      lds_dma16(src, (const lds_char*)(sA + q * 1024));
+  // A load i (half i & 1 of block i / 2 of this wave's share) of stage kc into A slot `slot`; B
+  // load i (rows RPL (wave + NW i) ..) of stage kc into B slot `slot`
+  auto load_a = [&](int64_t kc, int slot, int i) {
+    const int q = wave + NW * i;
+    const int64_t k0 = kc * BK;
+    const int bm = q >> 1;
+    int64_t bt, bv;
+    if (!A_TRANS) {
+      bt = (m0 >> 5) + bm;
+      bt = bt < g.a_mblocks ? bt : g.a_mblocks - 1;
+      bv = k0 >> 5;
+      bv = bv < g.lda ? bv : g.lda - 1;
     } else {
-      const int q = wave + NW * i;
-      char* sB = smem + (int)(rel % NS) * BBYTES;
-      const int j = q * RPL + lane / (64 / RPL);    // row of the B tile
-      const int lc = (lane % (64 / RPL)) ^ (4 * (j & 3));
-      int64_t k = kc * BK + j;
-      k = k < kvalid ? k : kvalid - 1;
-      int64_t col = n0 + 8 * lc;
-      col = col <= g.ldb - 8 ? col : g.ldb - 8;
-      lds_dma16(g.B + k * g.ldb + col, (const lds_char*)(sB + q * 1024));
+      bt = k0 >> 5;
+      bt = bt < g.k_blocks ? bt : g.k_blocks - 1;
+      bv = (m0 >> 5) + bm;
+      bv = bv < g.a_mblocks ? bv : g.a_mblocks - 1;
     }
+    const int chunk = a_swz(64 * (q & 1) + lane);
+    lds_dma16(g.A + (bt * g.lda + bv) * 1024 + chunk * 8,
+              (const lds_char*)(smem + NS * BBYTES + slot * ABYTES + q * 1024));
   };
-  auto load_stage = [&](int64_t kc) {
+  auto load_b = [&](int64_t kc, int slot, int i) {
+    const int q = wave + NW * i;
+    const int j = q * RPL + lane / (64 / RPL);
+    const int lc = (lane % (64 / RPL)) ^ (4 * (j & 3));
+    int64_t k = kc * BK + j;
+    k = k < kvalid ? k : kvalid - 1;
+    int64_t col = n0 + 8 * lc;
+    col = col <= g.ldb - 8 ? col : g.ldb - 8;
+    lds_dma16(g.B + k * g.ldb + col, (const lds_char*)(smem + slot * BBYTES + q * 1024));
+  };
+
+  const int grp = lane >> 4, li = lane & 15;
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  // fragment f of a 16-deep step: f < WM is A block f of this wave, f >= WM is B block f - WM
+  auto read_frag = [&](const char* sA, const char* sB, int ks, int f) -> bf16x8 {
+    if (f < WM) {
+      const char* blk = sA + (wm * WM + f) * 2048;
+      if (!A_TRANS)
+        return *(const __attribute__((address_space(3))) bf16x8*)((const lds_char*)blk + a_swz(2 * lane + ks) * 16);
+      i16x4 part[2];
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) load_one(kc, i);
+      for (int half = 0; half < 2; ++half) {
+        const int t = 16 * ks + 8 * (grp >> 1) + 4 * half + (li >> 2);
+        const int cg = li & 3;
+        const int c = 2 * (t + 32 * (cg & 1)) + (grp & 1);
+        part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(blk + a_swz(c) * 16 + 8 * (cg >> 1)));
+      }
+      i16x8 v = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
+      return __builtin_bit_cast(bf16x8, v);
+    }
+    const int cbase = wn * (32 * WN) + (f - WM) * 32;
+    const bool interleaved = !A_TRANS;
+    i16x4 part[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int k = 16 * ks + (interleaved ? 8 * half + 4 * (grp >> 1) : 8 * (grp >> 1) + 4 * half) + (li >> 2);
+      const int c = cbase + 16 * (grp & 1) + 4 * (li & 3);
+      const int addr = k * (BN * 2) + 16 * ((c >> 3) ^ (4 * (k & 3))) + 2 * (c & 7);
+      part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sB + addr));
+    }
+    i16x8 v = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
+    return __builtin_bit_cast(bf16x8, v);
   };
 
   f32x16 acc[WM][WN];
@@ -137,107 +153,77 @@ void gemm_bf16_kernel(GemmParams g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int grp = lane >> 4, li = lane & 15;
-  // transposed read: lanes of group grp take rows k0 + li / 4 and columns cbase + 16 (grp & 1) +
-  // 4 (li & 3) .. + 3, for k0 = 16 ks + 8 (grp >> 1) + 4 half; lane i of the group receives 4
-  // consecutive k of column cbase + 16 (grp & 1) + i
-  // With INTERLEAVED k order, half `half` of lane l's eight values covers rows 16 ks + 8 half +
-  // 4 (l / 32) .. + 3 instead of 16 ks + 8 (l / 32) + 4 half .. + 3 (the order the dZ blocks hold).
-  auto read_tr = [&](const char* tile, int pitch, int ks, int cbase, bool interleaved) -> bf16x8 {
-    i16x4 part[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int k = 16 * ks + (interleaved ? 8 * half + 4 * (grp >> 1) : 8 * (grp >> 1) + 4 * half) + (li >> 2);
-      const int c = cbase + 16 * (grp & 1) + 4 * (li & 3);
-      const int addr = k * pitch + 16 * ((c >> 3) ^ (4 * (k & 3))) + 2 * (c & 7);
-      part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + addr));
-    }
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    i16x8 v = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
-    return __builtin_bit_cast(bf16x8, v);
-  };
-
-  // Fragments of one 16-deep k step: this wave's WM A blocks (all at once) and its WN B blocks
-  // (one at a time).
-  auto load_afrags = [&](const char* sA, int ks, bf16x8 (&af)[WM]) {
-#pragma unroll
-    for (int bm = 0; bm < WM; ++bm) {
-      const char* blk = sA + (wm * WM + bm) * 2048;
-      if (!A_TRANS) {
-        // lane l holds row l % 32 of the block in its own 32 bytes: the 16 at chunk 2 l + ks are
-        // vocabulary rows 16 ks + 8 (j / 4) + 4 (l / 32) + j % 4, j = 0..7
-        af[bm] = *(const __attribute__((address_space(3))) bf16x8*)((const lds_char*)blk + a_swz(2 * lane + ks) * 16);
-      } else {
-        // transposed read: lane l receives vocabulary row l % 32 at tokens 16 ks + 8 (l / 32) + j;
-        // the lanes of a 16-lane group address 4 tokens x 4 runs of 4 vocabulary rows
-        i16x4 part[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int t = 16 * ks + 8 * (grp >> 1) + 4 * half + (li >> 2);
-          const int cg = li & 3;
-          const int c = 2 * (t + 32 * (cg & 1)) + (grp & 1);
-          part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(blk + a_swz(c) * 16 + 8 * (cg >> 1)));
-        }
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
-        i16x8 v = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
-        af[bm] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
-  };
-  auto load_bfrag = [&](const char* sB, int ks, int bn) -> bf16x8 {
-    return read_tr(sB, BN * 2, ks, wn * (32 * WN) + bn * 32, !A_TRANS);
-  };
-
-  // A loads of stage 0, then the groups of stages 0 .. NS - 2; every stage's group is issued (with
-  // clamped addresses past the end), so the waits below are constant
+  constexpr int NF = WM + WN;
+  bf16x8 fa[NF], fb[NF];   // fragments of the first and of the second 16-deep step of a stage
   if (nk > 0) {
+    // A of stages 0 .. AL - 1, then B of stage d and A of stage d + AL for d < NS, A only while
+    // d + AL < NS + AL - 1 (stage d in slot d): the steady state issues A of stage s + NS + AL - 1
+    // before barrier s + 1 and B of stage s + NS after it
 #pragma unroll
-    for (int i = BPW; i < LPW; ++i) load_one(kc_begin - 1, i);
+    for (int d = 0; d < AL; ++d)
 #pragma unroll
-    for (int d = 0; d < NS - 1; ++d) load_stage(kc_begin + d);
-  }
-  for (int64_t it = 0; it < nk; ++it) {
-    // B(it) and A(it) landed: issued after B(it)'s last load are A(it + 1) and the groups of
-    // it + 1 .. it + NS - 2
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APW + (NS - 2) * LPW) : "memory");
-    __builtin_amdgcn_s_barrier();
-    const char* sA = smem + NS * BBYTES + (int)(it % AST) * ABYTES;
-    const char* sB = smem + (int)(it % NS) * BBYTES;
-    // The MFMAs of this stage, one 16-deep step at a time and one B block at a time (the next B
-    // fragment is read while the WM MFMAs of the current one run), with the loads of the group of
-    // it + NS - 1 (into the slots that stage it - 1 used) issued between them. Wave priority drops from 3
-    // to 1 halfway through the stage: the two waves of a SIMD share one matrix pipe, and at equal
-    // priority the older one would run ahead and leave the other to finish the stage alone.
-    constexpr int NMFMA = (BK / 16) * WM * WN;
-    constexpr int MFMA_PER_LOAD = NMFMA / LPW;
-    const int64_t kc_pf = kc_begin + it + (NS - 1);
-    __builtin_amdgcn_s_setprio(3);
+      for (int i = 0; i < APW; ++i) load_a(kc_begin + d, d, i);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[WM], bcur, bnext;
-      load_afrags(sA, ks, af);
-      bcur = load_bfrag(sB, ks, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int d = 0; d < NS; ++d) {
 #pragma unroll
-      for (int bn = 0; bn < WN; ++bn) {
-        if (bn + 1 < WN) bnext = load_bfrag(sB, ks, bn + 1);
+      for (int i = 0; i < BPW; ++i) load_b(kc_begin + d, d, i);
+      if (d + AL < NS + AL - 1)
 #pragma unroll
-        for (int bm = 0; bm < WM; ++bm) {
-          const int mi = (ks * WN + bn) * WM + bm;
-          acc[bm][bn] = mfma32x32x16(af[bm], bcur, acc[bm][bn]);
-          if (mi % MFMA_PER_LOAD == 0 && mi / MFMA_PER_LOAD < LPW) load_one(kc_pf, mi / MFMA_PER_LOAD);
-          if (mi == NMFMA / 2) __builtin_amdgcn_s_setprio(1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        bcur = bnext;
-      }
+        for (int i = 0; i < APW; ++i) load_a(kc_begin + d + AL, d + AL, i);
     }
+    // issued after B of stage 0: the A loads of stages AL .. NS + AL - 2, the B loads of 1 .. NS - 1
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * LPW) : "memory");
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int f = 0; f < NF; ++f) fa[f] = read_frag(smem + NS * BBYTES, smem, 0, f);
   }
-  __builtin_amdgcn_s_setprio(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the clamped loads past the end landed
+  // ring slots of stage it (A and B) and of stage it - 1 (A), kept as counters
+  int sa = 0, sb = 0, sa_prev = AST - 1;
+  for (int64_t it = 0; it < nk; ++it) {
+    const int sa1 = sa + 1 < AST ? sa + 1 : 0, sb1 = sb + 1 < NS ? sb + 1 : 0;
+    const char* sA = smem + NS * BBYTES + sa * ABYTES;
+    const char* sB = smem + sb * BBYTES;
+    const char* sA1 = smem + NS * BBYTES + sa1 * ABYTES;
+    const char* sB1 = smem + sb1 * BBYTES;
+    const int64_t kc_n = kc_begin + it + NS;   // B of this stage and A of stage kc_n + AL - 1 are issued here
+    // first step: MFMAs on fa, the second step's fragments into fb, A loads of stage
+    // it + NS + AL - 1 into the slot of stage it - 1
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int bn = 0; bn < WN; ++bn)
+#pragma unroll
+      for (int bm = 0; bm < WM; ++bm) {
+        const int mi = bn * WM + bm;
+        acc[bm][bn] = mfma32x32x16(fa[bm], fa[WM + bn], acc[bm][bn]);
+        if (mi % 2 == 0) fb[mi / 2] = read_frag(sA, sB, 1, mi / 2);
+        if (mi % 4 == 1) load_a(kc_n + AL - 1, sa_prev, mi / 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    // every fragment of stage it is in registers; stage it + 1 landed: issued after B of stage
+    // it + 1 (A of a stage goes out before its B) are NS - 2 groups of B and A loads and the A loads
+    // above, in the prologue as in the loop. After the last stage the barrier and the reads below
+    // are harmless: nothing is read from what they fetch.
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(APW + (NS - 2) * LPW) : "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // second step: MFMAs on fb, the next stage's first fragments into fa, B loads of stage it + NS
+    // into the slot of stage it
+#pragma unroll
+    for (int bn = 0; bn < WN; ++bn)
+#pragma unroll
+      for (int bm = 0; bm < WM; ++bm) {
+        const int mi = bn * WM + bm;
+        acc[bm][bn] = mfma32x32x16(fb[bm], fb[WM + bn], acc[bm][bn]);
+        if (mi % 2 == 0) fa[mi / 2] = read_frag(sA1, sB1, 0, mi / 2);
+        if (mi % 4 == 1) load_b(kc_n, sb, mi / 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    sa_prev = sa;
+    sa = sa1;
+    sb = sb1;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue: alpha (times the row's scale when given) * acc to C (row-scattered) or to this
-  //      split's partial tile
   float* C = g.C + (int64_t)blockIdx.z * g.split_stride;
 #pragma unroll
   for (int bm = 0; bm < WM; ++bm)
@@ -283,25 +269,23 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* part, int 
   }
 }
 
-// dH: 256 x 256 tiles, 4-slot B ring; dE: 256 x 256 tiles, 3-slot B ring (measured best for each).
-using DhShape = GemmShape<4, 2, 2>;
-using DeShape = GemmShape<4, 2, 2>;
-int gemm_tile_m(bool a_trans) { return a_trans ? DeShape::BM : DhShape::BM; }
-int gemm_tile_n(bool a_trans) { return a_trans ? DeShape::BN : DhShape::BN; }
+constexpr int kGemmBM = 256, kGemmBN = 256;
+int gemm_tile_m(bool) { return kGemmBM; }
+int gemm_tile_n(bool) { return kGemmBN; }
 
-int64_t gemm_grid_x(int64_t M, int64_t N, bool a_trans) {
-  const int64_t bm = gemm_tile_m(a_trans), bn = gemm_tile_n(a_trans);
-  const int64_t mt = (M + bm - 1) / bm, nt = (N + bn - 1) / bn;
+int64_t gemm_grid_x(int64_t M, int64_t N, bool) {
+  const int64_t mt = (M + kGemmBM - 1) / kGemmBM, nt = (N + kGemmBN - 1) / kGemmBN;
   return nt > 1 ? 8 * nt * ((mt + 7) / 8) : mt;   // the id mapping of the kernel
 }
 
+// Both products: 4-slot B ring, A one stage ahead (deeper rings measured the same).
 hipError_t launch_gemm(const GemmParams& g, bool a_trans, int ksplit, hipStream_t st) {
   const int64_t gx = gemm_grid_x(g.M, g.N, a_trans);
   if (gx == 0 || ksplit < 1) return hipSuccess;
   if (gx > kMaxGrid512) return hipErrorInvalidConfiguration;   // the API layer rejects such shapes first
   const dim3 grid((unsigned)gx, 1, (unsigned)ksplit);
-  if (a_trans) hipLaunchKernelGGL((gemm_bf16_kernel<true, 4, 2, 2, 3>), grid, dim3(512), 0, st, g);
-  else hipLaunchKernelGGL((gemm_bf16_kernel<false, 4, 2, 2, 4>), grid, dim3(512), 0, st, g);
+  if (a_trans) hipLaunchKernelGGL((gemm_bf16_kernel<true, 4, 1>), grid, dim3(256), 0, st, g);
+  else hipLaunchKernelGGL((gemm_bf16_kernel<false, 4, 1>), grid, dim3(256), 0, st, g);
   return hipGetLastError();
 }
 

@@ -129,7 +129,8 @@ hipError_t launch_gemm(const GemmParams& g, bool a_trans, int ksplit, hipStream_
 // Output tile of each product (rows x columns).
 int gemm_tile_m(bool a_trans);
 int gemm_tile_n(bool a_trans);
-// Workgroups along x of the launch of an M x N product (512 threads each).
+// Workgroups along x of the launch of an M x N product (256 threads each; the shape checks hold
+// them to kMaxGrid512, which is stricter than the launch limit).
 int64_t gemm_grid_x(int64_t M, int64_t N, bool a_trans);
 // Most workgroups of 512 threads one launch can hold (2^32 - 1 work items).
 constexpr int64_t kMaxGrid512 = ((int64_t)1 << 23) - 1;
