@@ -80,36 +80,43 @@ void gemm_bf16_kernel(GemmParams g) {
   const int64_t kvalid = g.k_dev ? ndev : g.kvalid;
 
   // A load i (half i & 1 of block i / 2 of this wave's share) of stage kc into A slot `slot`; B
-  // load i (rows RPL (wave + NW i) ..) of stage kc into B slot `slot`
-  auto load_a = [&](int64_t kc, int slot, int i) {
+  // load i (rows RPL (wave + NW i) ..) of stage kc into B slot `slot`. The per-lane part of each
+  // address is fixed for the whole k loop; a stage adds a uniform offset (and, for B, clamps the
+  // lane's row to the last one that exists, which only bites in a partial last chunk and in the
+  // stages past the end that the ring issues anyway).
+  const uint16_t* pa[APW];
+  const uint16_t* pb[BPW];
+  int jbo[BPW];   // B load i: element offset of this lane's row within a stage, j ldb
+#pragma unroll
+  for (int i = 0; i < APW; ++i) {
     const int q = wave + NW * i;
-    const int64_t k0 = kc * BK;
-    const int bm = q >> 1;
-    int64_t bt, bv;
-    if (!A_TRANS) {
-      bt = (m0 >> 5) + bm;
-      bt = bt < g.a_mblocks ? bt : g.a_mblocks - 1;
-      bv = k0 >> 5;
-      bv = bv < g.lda ? bv : g.lda - 1;
-    } else {
-      bt = k0 >> 5;
-      bt = bt < g.k_blocks ? bt : g.k_blocks - 1;
-      bv = (m0 >> 5) + bm;
-      bv = bv < g.a_mblocks ? bv : g.a_mblocks - 1;
-    }
-    const int chunk = a_swz(64 * (q & 1) + lane);
-    lds_dma16(g.A + (bt * g.lda + bv) * 1024 + chunk * 8,
-              (const lds_char*)(smem + NS * BBYTES + slot * ABYTES + q * 1024));
-  };
-  auto load_b = [&](int64_t kc, int slot, int i) {
+    int64_t blk = (m0 >> 5) + (q >> 1);            // dH: token block; dE: vocabulary block
+    blk = blk < g.a_mblocks ? blk : g.a_mblocks - 1;
+    pa[i] = g.A + (A_TRANS ? blk : blk * g.lda) * 1024 + a_swz(64 * (q & 1) + lane) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
     const int q = wave + NW * i;
     const int j = q * RPL + lane / (64 / RPL);
     const int lc = (lane % (64 / RPL)) ^ (4 * (j & 3));
-    int64_t k = kc * BK + j;
-    k = k < kvalid ? k : kvalid - 1;
     int64_t col = n0 + 8 * lc;
     col = col <= g.ldb - 8 ? col : g.ldb - 8;
-    lds_dma16(g.B + k * g.ldb + col, (const lds_char*)(smem + slot * BBYTES + q * 1024));
+    pb[i] = g.B + col;
+    jbo[i] = j * (int)g.ldb;
+  }
+  auto load_a = [&](int64_t kc, int slot, int i) {
+    // dH: the stage's vocabulary block kc; dE: its token block kc (clamped to the last block)
+    const int64_t off = A_TRANS ? (kc < g.k_blocks ? kc : g.k_blocks - 1) * g.lda * 1024
+                                : (kc < g.lda ? kc : g.lda - 1) * 1024;
+    lds_dma16(pa[i] + off, (const lds_char*)(smem + NS * BBYTES + slot * ABYTES + (wave + NW * i) * 1024));
+  };
+  auto load_b = [&](int64_t kc, int slot, int i) {
+    const int64_t kcb = kc * BK;
+    int64_t rl = kvalid - 1 - kcb;                  // last row that exists, relative to the stage
+    rl = rl < BK ? rl : BK;
+    const int lim = (int)rl * (int)g.ldb;          // |rl| <= 32 (NS + AL + 1) and ldb <= 512
+    const int r = jbo[i] < lim ? jbo[i] : lim;
+    lds_dma16(pb[i] + kcb * g.ldb + r, (const lds_char*)(smem + slot * BBYTES + (wave + NW * i) * 1024));
   };
 
   const int grp = lane >> 4, li = lane & 15;
