@@ -3,8 +3,8 @@
 //
 // A workgroup owns a 256 x 256 output tile and runs 4 waves, one per SIMD, in a 2 x 2 grid; each
 // wave accumulates 128 x 128 of the tile in sixteen 32 x 32 accumulators, which fill its AGPRs. k
-// advances in 32-deep chunks; B and A are filled by global_load_lds_dwordx4 into LDS rings of NS
-// and NS + AL slots.
+// advances in stages of SPS 32-deep sub-stages (one 32 x 32 dZ block along k each); B and A are
+// filled by global_load_lds_dwordx4 into LDS rings of NS and NS + AL stages.
 //
 // Why this shape: the operand streams mix a unique stream from HBM (dZ) with a stream that every
 // workgroup shares from L2 (E or H). A 256 x 256 tile moves 32 KiB per 4.2 MFLOP chunk, against
@@ -17,8 +17,11 @@
 // and DMA writes together needed 128 bytes of LDS bandwidth per clock at the full matrix rate,
 // against 96 here. The lone wave has no partner on its SIMD to cover a wait, so it reads the
 // fragments of the next 16-deep step during the MFMAs of the current one, and the barrier of stage
-// s + 1 sits between the two steps of stage s (all of stage s's fragments are in registers by
-// then): the second step's MFMAs run while the first fragments of stage s + 1 are read.
+// s + 1 sits before the last step of stage s (all of stage s's fragments are in registers by
+// then): that step's MFMAs run while the first fragments of stage s + 1 are read. The loop issues
+// about 5 other instructions per MFMA, near what a lone wave can issue in an MFMA's 32 cycles, so
+// every instruction in it counts: the per-lane load addresses are formed before the loop, and
+// 64-deep stages (SPS = 2) halve the per-stage work of waits, barrier and ring counters.
 //
 // A is dZ in its 32 x 32 block layout (described in pg_internal.h); each stage's A tile is BM / 32
 // whole blocks, i.e. contiguous 2 KiB runs. The other operand (E for dH, H for dE) is k x n
@@ -40,19 +43,25 @@ namespace pg {
 // apart); it is its own inverse.
 __device__ __forceinline__ int a_swz(int c) { return c ^ ((c >> 4) & 1) ^ (((c >> 6) & 1) << 3); }
 
-// The loads of each stage are split over the two halves around a barrier: A of stage s + NS + AL - 1
-// before barrier s + 1 (into the slot of stage s - 1), B of stage s + NS after it (into the slot
-// stage s has finished reading). A thus runs AL stages further ahead than B; NS and AL set the
-// depth of the rings (one and two stages ahead measured the same).
-template <bool A_TRANS, int NS, int AL>
+// The loads of each stage are split around the barrier: A of stage s + NS + AL - 1 before barrier
+// s + 1 (into the slot of stage s - 1), B of stage s + NS after it (into the slot stage s has
+// finished reading). A thus runs AL stages further ahead than B. With 32-deep stages, rings of
+// 3 + 1, 4 + 1, 4 + 2 and 3 + 3 stages measured the same: the feed's latency does not pace the
+// product, so the 64-deep stages take the smallest rings, 2 + 1 (160 KiB).
+template <bool A_TRANS, int NS, int AL, int SPS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(GemmParams g) {
   constexpr int WM = 4, WN = 4, NW = 4, WGN = 2;
-  constexpr int BM = 256, BN = 256, BK = kGemmBK;
-  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;
-  constexpr int APW = ABYTES / 1024 / NW, BPW = BBYTES / 1024 / NW, LPW = APW + BPW;
+  // a stage is SPS sub-stages of 32 k (one 32 x 32 dZ block along k each), i.e. 2 SPS 16-deep
+  // steps; each sub-stage's A and B tiles take 16 KiB of their stage's ring slot
+  constexpr int BM = 256, BN = 256, BK = kGemmBK * SPS, KS = 2 * SPS;
+  constexpr int SUBA = BM * kGemmBK * 2, SUBB = BN * kGemmBK * 2;
+  constexpr int ABYTES = SUBA * SPS, BBYTES = SUBB * SPS;
+  constexpr int APS = SUBA / 1024 / NW, BPS = SUBB / 1024 / NW;   // loads per wave and sub-stage
+  constexpr int APW = APS * SPS, BPW = BPS * SPS, LPW = APW + BPW;
   constexpr int RPL = 1024 / (BN * 2);
-  static_assert(BK == 32 && APW == 4 && BPW == 4 && RPL == 2, "tile shape assumed below");
+  static_assert(kGemmBK == 32 && APS == 4 && BPS == 4 && RPL == 2 && (SPS == 1 || SPS == 2),
+                "tile shape assumed below");
   constexpr int AST = NS + AL;   // A is issued AL stages ahead of B
   static_assert(AL >= 1 && NS * BBYTES + AST * ABYTES <= 160 * 1024, "LDS rings");
   __shared__ __attribute__((aligned(1024))) char smem[NS * BBYTES + AST * ABYTES];
@@ -84,18 +93,18 @@ void gemm_bf16_kernel(GemmParams g) {
   // address is fixed for the whole k loop; a stage adds a uniform offset (and, for B, clamps the
   // lane's row to the last one that exists, which only bites in a partial last chunk and in the
   // stages past the end that the ring issues anyway).
-  const uint16_t* pa[APW];
-  const uint16_t* pb[BPW];
-  int jbo[BPW];   // B load i: element offset of this lane's row within a stage, j ldb
+  const uint16_t* pa[APS];
+  const uint16_t* pb[BPS];
+  int jbo[BPS];   // B load i: element offset of this lane's row within a sub-stage, j ldb
 #pragma unroll
-  for (int i = 0; i < APW; ++i) {
+  for (int i = 0; i < APS; ++i) {
     const int q = wave + NW * i;
     int64_t blk = (m0 >> 5) + (q >> 1);            // dH: token block; dE: vocabulary block
     blk = blk < g.a_mblocks ? blk : g.a_mblocks - 1;
     pa[i] = g.A + (A_TRANS ? blk : blk * g.lda) * 1024 + a_swz(64 * (q & 1) + lane) * 8;
   }
 #pragma unroll
-  for (int i = 0; i < BPW; ++i) {
+  for (int i = 0; i < BPS; ++i) {
     const int q = wave + NW * i;
     const int j = q * RPL + lane / (64 / RPL);
     const int lc = (lane % (64 / RPL)) ^ (4 * (j & 3));
@@ -104,25 +113,32 @@ void gemm_bf16_kernel(GemmParams g) {
     pb[i] = g.B + col;
     jbo[i] = j * (int)g.ldb;
   }
+  // load i of a stage: sub-stage i / APS (resp. BPS), load i % APS of the sub-stage
   auto load_a = [&](int64_t kc, int slot, int i) {
-    // dH: the stage's vocabulary block kc; dE: its token block kc (clamped to the last block)
-    const int64_t off = A_TRANS ? (kc < g.k_blocks ? kc : g.k_blocks - 1) * g.lda * 1024
-                                : (kc < g.lda ? kc : g.lda - 1) * 1024;
-    lds_dma16(pa[i] + off, (const lds_char*)(smem + NS * BBYTES + slot * ABYTES + (wave + NW * i) * 1024));
+    // dH: vocabulary block SPS kc + sub; dE: token block SPS kc + sub (clamped to the last block)
+    const int64_t kb = SPS * kc + i / APS;
+    const int64_t off = A_TRANS ? (kb < g.k_blocks ? kb : g.k_blocks - 1) * g.lda * 1024
+                                : (kb < g.lda ? kb : g.lda - 1) * 1024;
+    lds_dma16(pa[i % APS] + off, (const lds_char*)(smem + NS * BBYTES + slot * ABYTES + (i / APS) * SUBA +
+                                                   (wave + NW * (i % APS)) * 1024));
   };
-  auto load_b = [&](int64_t kc, int slot, int i) {
-    const int64_t kcb = kc * BK;
+  auto load_b = [&](int64_t kc, int slot, int ib) {
+    const int i = ib % BPS;
+    const int64_t kcb = kc * BK + (ib / BPS) * kGemmBK;
     int64_t rl = kvalid - 1 - kcb;                  // last row that exists, relative to the stage
     rl = rl < BK ? rl : BK;
     const int lim = (int)rl * (int)g.ldb;          // |rl| <= 32 (NS + AL + 1) and ldb <= 512
     const int r = jbo[i] < lim ? jbo[i] : lim;
-    lds_dma16(pb[i] + kcb * g.ldb + r, (const lds_char*)(smem + slot * BBYTES + (wave + NW * i) * 1024));
+    lds_dma16(pb[i] + kcb * g.ldb + r, (const lds_char*)(smem + slot * BBYTES + (ib / BPS) * SUBB + (wave + NW * i) * 1024));
   };
 
   const int grp = lane >> 4, li = lane & 15;
   typedef short i16x8 __attribute__((ext_vector_type(8)));
-  // fragment f of a 16-deep step: f < WM is A block f of this wave, f >= WM is B block f - WM
-  auto read_frag = [&](const char* sA, const char* sB, int ks, int f) -> bf16x8 {
+  // fragment f of 16-deep step ks of a stage: f < WM is A block f of this wave, f >= WM is B block f - WM
+  auto read_frag = [&](const char* sA0, const char* sB0, int kss, int f) -> bf16x8 {
+    const char* sA = sA0 + (kss >> 1) * SUBA;
+    const char* sB = sB0 + (kss >> 1) * SUBB;
+    const int ks = kss & 1;
     if (f < WM) {
       const char* blk = sA + (wm * WM + f) * 2048;
       if (!A_TRANS)
@@ -161,7 +177,7 @@ void gemm_bf16_kernel(GemmParams g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   constexpr int NF = WM + WN;
-  bf16x8 fa[NF], fb[NF];   // fragments of the first and of the second 16-deep step of a stage
+  bf16x8 fa[NF], fb[NF];   // fragments of the even and of the odd 16-deep steps of a stage
   if (nk > 0) {
     // A of stages 0 .. AL - 1, then B of stage d and A of stage d + AL for d < NS, A only while
     // d + AL < NS + AL - 1 (stage d in slot d): the steady state issues A of stage s + NS + AL - 1
@@ -184,6 +200,29 @@ void gemm_bf16_kernel(GemmParams g) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) fa[f] = read_frag(smem + NS * BBYTES, smem, 0, f);
   }
+  // One 16-deep step: the MFMAs on cur, with the fragments of the step after it read into nxt
+  // (from the ring slots rA / rB, step rks) and loads of this stage's group interleaved: counting
+  // MFMAs from gbase (the MFMAs of earlier steps in the same run of loads), load n is issued at
+  // MFMA off + n every (A loads when a_loads, else B loads).
+  auto mstep = [&](const bf16x8 (&cur)[NF], bf16x8 (&nxt)[NF], const char* rA, const char* rB, int rks,
+                   bool a_loads, int gbase, int every, int off, int64_t kc_l, int slot_l) {
+#pragma unroll
+    for (int bn = 0; bn < WN; ++bn)
+#pragma unroll
+      for (int bm = 0; bm < WM; ++bm) {
+        const int mi = bn * WM + bm;
+        acc[bm][bn] = mfma32x32x16(cur[bm], cur[WM + bn], acc[bm][bn]);
+        if (mi % 2 == 0) nxt[mi / 2] = read_frag(rA, rB, rks, mi / 2);
+        const int g = gbase + mi - off;
+        if (g >= 0 && g % every == 0 && g / every < (a_loads ? APW : BPW)) {
+          if (a_loads) load_a(kc_l, slot_l, g / every);
+          else load_b(kc_l, slot_l, g / every);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  // A loads spread over the MFMAs of steps 0 .. KS - 2, B loads over step KS - 1
+  constexpr int AEVERY = (KS - 1) * WM * WN / APW, BEVERY = WM * WN / BPW;
   // ring slots of stage it (A and B) and of stage it - 1 (A), kept as counters
   int sa = 0, sb = 0, sa_prev = AST - 1;
   for (int64_t it = 0; it < nk; ++it) {
@@ -193,19 +232,14 @@ void gemm_bf16_kernel(GemmParams g) {
     const char* sA1 = smem + NS * BBYTES + sa1 * ABYTES;
     const char* sB1 = smem + sb1 * BBYTES;
     const int64_t kc_n = kc_begin + it + NS;   // B of this stage and A of stage kc_n + AL - 1 are issued here
-    // first step: MFMAs on fa, the second step's fragments into fb, A loads of stage
-    // it + NS + AL - 1 into the slot of stage it - 1
+    // steps 0 .. KS - 2 (even steps on fa, odd on fb), with the A loads of stage it + NS + AL - 1
+    // into the slot of stage it - 1
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int bn = 0; bn < WN; ++bn)
-#pragma unroll
-      for (int bm = 0; bm < WM; ++bm) {
-        const int mi = bn * WM + bm;
-        acc[bm][bn] = mfma32x32x16(fa[bm], fa[WM + bn], acc[bm][bn]);
-        if (mi % 2 == 0) fb[mi / 2] = read_frag(sA, sB, 1, mi / 2);
-        if (mi % 4 == 1) load_a(kc_n + AL - 1, sa_prev, mi / 4);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      if (ks % 2 == 0) mstep(fa, fb, sA, sB, ks + 1, true, ks * WM * WN, AEVERY, 1, kc_n + AL - 1, sa_prev);
+      else mstep(fb, fa, sA, sB, ks + 1, true, ks * WM * WN, AEVERY, 1, kc_n + AL - 1, sa_prev);
+    }
     // every fragment of stage it is in registers; stage it + 1 landed: issued after B of stage
     // it + 1 (A of a stage goes out before its B) are NS - 2 groups of B and A loads and the A loads
     // above, in the prologue as in the loop. After the last stage the barrier and the reads below
@@ -213,18 +247,9 @@ void gemm_bf16_kernel(GemmParams g) {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(APW + (NS - 2) * LPW) : "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // second step: MFMAs on fb, the next stage's first fragments into fa, B loads of stage it + NS
+    // last step: MFMAs on fb, the next stage's first fragments into fa, B loads of stage it + NS
     // into the slot of stage it
-#pragma unroll
-    for (int bn = 0; bn < WN; ++bn)
-#pragma unroll
-      for (int bm = 0; bm < WM; ++bm) {
-        const int mi = bn * WM + bm;
-        acc[bm][bn] = mfma32x32x16(fb[bm], fb[WM + bn], acc[bm][bn]);
-        if (mi % 2 == 0) fa[mi / 2] = read_frag(sA1, sB1, 0, mi / 2);
-        if (mi % 4 == 1) load_b(kc_n, sb, mi / 4);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    mstep(fb, fa, sA1, sB1, 0, false, 0, BEVERY, BEVERY > 1 ? 1 : 0, kc_n, sb);
     sa_prev = sa;
     sa = sa1;
     sb = sb1;
@@ -285,14 +310,14 @@ int64_t gemm_grid_x(int64_t M, int64_t N, bool) {
   return nt > 1 ? 8 * nt * ((mt + 7) / 8) : mt;   // the id mapping of the kernel
 }
 
-// Both products: 4-slot B ring, A one stage ahead (deeper rings measured the same).
+// Both products: 64-deep stages, 2-stage B ring, A one stage ahead.
 hipError_t launch_gemm(const GemmParams& g, bool a_trans, int ksplit, hipStream_t st) {
   const int64_t gx = gemm_grid_x(g.M, g.N, a_trans);
   if (gx == 0 || ksplit < 1) return hipSuccess;
   if (gx > kMaxGrid512) return hipErrorInvalidConfiguration;   // the API layer rejects such shapes first
   const dim3 grid((unsigned)gx, 1, (unsigned)ksplit);
-  if (a_trans) hipLaunchKernelGGL((gemm_bf16_kernel<true, 4, 1>), grid, dim3(256), 0, st, g);
-  else hipLaunchKernelGGL((gemm_bf16_kernel<false, 4, 1>), grid, dim3(256), 0, st, g);
+  if (a_trans) hipLaunchKernelGGL((gemm_bf16_kernel<true, 2, 1, 2>), grid, dim3(256), 0, st, g);
+  else hipLaunchKernelGGL((gemm_bf16_kernel<false, 2, 1, 2>), grid, dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
