@@ -211,7 +211,7 @@ void gemm_bf16_kernel(GemmParams g) {
 #pragma unroll
       for (int bm = 0; bm < WM; ++bm) {
         const int mi = bn * WM + bm;
-        acc[bm][bn] = mfma32x32x16(cur[bm], cur[WM + bn], acc[bm][bn]);
+        acc[bm][bn] = mfma32x32x16(cur[WM + bn], cur[bm], acc[bm][bn]);   // transposed block (epilogue)
         if (mi % 2 == 0) nxt[mi / 2] = read_frag(rA, rB, rks, mi / 2);
         const int g = gbase + mi - off;
         if (g >= 0 && g % every == 0 && g / every < (a_loads ? APW : BPW)) {
@@ -256,22 +256,37 @@ void gemm_bf16_kernel(GemmParams g) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  // ---- epilogue: alpha (times the row's scale when given) * acc to C (row-scattered) or to this
+  //      split's partial tile. The MFMAs take the B fragment as their first operand, so each
+  //      accumulator holds its 32 x 32 block transposed: lane l has row l % 32 of the block and,
+  //      in elements 4 k .. 4 k + 3, the four consecutive columns 8 k + 4 (l / 32) .. + 3, i.e. one
+  //      16-byte store each (the untransposed layout took 4-byte stores, 71 us more per dH launch
+  //      at the training shape).
   float* C = g.C + (int64_t)blockIdx.z * g.split_stride;
 #pragma unroll
-  for (int bm = 0; bm < WM; ++bm)
+  for (int bm = 0; bm < WM; ++bm) {
+    const int64_t m = m0 + (wm * WM + bm) * 32 + (lane & 31);
+    if (m < M) {
+      const int64_t crow = g.crows ? (int64_t)g.crows[m] : m;
+      const float f = g.row_scale ? g.alpha * g.row_scale[m] : g.alpha;
+      float* crow_p = C + crow * g.ldc;
 #pragma unroll
-    for (int bn = 0; bn < WN; ++bn) {
-      const int64_t n = n0 + wn * (32 * WN) + bn * 32 + (lane & 31);
+      for (int bn = 0; bn < WN; ++bn)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + (wm * WM + bm) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M && n < g.N) {
-          const int64_t crow = g.crows ? (int64_t)g.crows[m] : m;
-          const float f = g.row_scale ? g.alpha * g.row_scale[m] : g.alpha;
-          C[crow * g.ldc + n] = f * acc[bm][bn][r];
+        for (int k = 0; k < 4; ++k) {
+          const int64_t n = n0 + wn * (32 * WN) + bn * 32 + 8 * k + 4 * h;
+          const f32x4 v = {f * acc[bm][bn][4 * k], f * acc[bm][bn][4 * k + 1], f * acc[bm][bn][4 * k + 2],
+                           f * acc[bm][bn][4 * k + 3]};
+          if (n + 4 <= g.N) {
+            *reinterpret_cast<f32x4*>(crow_p + n) = v;   // ldc and n are multiples of 4, C 16-byte aligned
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < g.N) crow_p[n + e] = v[e];
+          }
         }
-      }
     }
+  }
 }
 
 // out[i] = sum over s of part[s * stride + i], in split order, starting from 0. Four elements per
