@@ -88,8 +88,8 @@ void gemm_bf16_kernel(GemmParams g) {
   const int64_t nk = kc_end > kc_begin ? kc_end - kc_begin : 0;
   const int64_t kvalid = g.k_dev ? ndev : g.kvalid;
 
-  // A load i (half i & 1 of block i / 2 of this wave's share) of stage kc into A slot `slot`; B
-  // load i (rows RPL (wave + NW i) ..) of stage kc into B slot `slot`. The per-lane part of each
+  // A load i of a sub-stage: half q & 1 of its A block q / 2, q = wave + NW i; B load i: its rows
+  // RPL q .. RPL q + RPL - 1. load_a / load_b issue load i of stage kc into ring slot `slot`. The per-lane part of each
   // address is fixed for the whole k loop; a stage adds a uniform offset (and, for B, clamps the
   // lane's row to the last one that exists, which only bites in a partial last chunk and in the
   // stages past the end that the ring issues anyway).
@@ -127,7 +127,7 @@ void gemm_bf16_kernel(GemmParams g) {
     const int64_t kcb = kc * BK + (ib / BPS) * kGemmBK;
     int64_t rl = kvalid - 1 - kcb;                  // last row that exists, relative to the stage
     rl = rl < BK ? rl : BK;
-    const int lim = (int)rl * (int)g.ldb;          // |rl| <= 32 (NS + AL + 1) and ldb <= 512
+    const int lim = (int)rl * (int)g.ldb;          // |rl| <= BK (NS + AL + 1) and ldb <= 512
     const int r = jbo[i] < lim ? jbo[i] : lim;
     lds_dma16(pb[i] + kcb * g.ldb + r, (const lds_char*)(smem + slot * BBYTES + (ib / BPS) * SUBB + (wave + NW * i) * 1024));
   };
