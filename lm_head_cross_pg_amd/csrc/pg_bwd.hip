@@ -113,8 +113,8 @@ __global__ __launch_bounds__(256) void zero_unscored_kernel(const uint8_t* mask,
 //    initialisation scale, 675 us at a trained model's, against 634 and 1005 us for the series
 //    with an exact redo of the blocks it cannot take). dZ goes to the workspace as bf16 in
 //    32 x 32 blocks laid out like the MFMA accumulator (described in pg_internal.h), so that
-//    every lane stores 32 contiguous bytes and each block is one contiguous 2 KiB run; zero in
-//    the padding rows and columns.
+//    each 16-byte store instruction of a wave fills one contiguous KiB and each block is one
+//    contiguous 2 KiB run; zero in the padding rows and columns.
 // 2. The bf16 GEMM of pg_gemm.hip forms the two products from those blocks:
 //      dH = g dZ E      A = dZ blocks, B = E [V][D]
 //      dE = g dZ^T H    A = dZ blocks read transposed, B = H rows (compacted when masked)
@@ -150,7 +150,7 @@ struct DzCore {
   float bias[NB];      // -lse * log2 e of this lane's rows (-inf for padding rows, NaN for a
                        // target outside [0, V): the row's dZ, and with it dH and dE, become NaN)
   int ytok[NB];        // targets of this lane's rows (never matching for padding rows)
-  uint16_t* dzblk[NB]; // this lane's 16 elements of block (token block, vocabulary block 0)
+  uint16_t* dzblk[NB]; // this lane's first 8 elements of block (token block, vocabulary block 0)
 
   __device__ __forceinline__ void chain(int buf, int vb, f32x16 (&acc)[NB]) const {
     logit_blocks<D, NB>(lds, buf, vb, h, col, hf, acc);
@@ -162,7 +162,7 @@ struct DzCore {
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (__bf16)vals[e];
-    *reinterpret_cast<bf16x8*>(dzblk[tb] + (int64_t)(vbase >> 5) * 1024 + 8 * j8) = o;
+    *reinterpret_cast<bf16x8*>(dzblk[tb] + (int64_t)(vbase >> 5) * 1024 + 512 * j8) = o;
   }
 
   // dZ of one block, not pipelined. MODE 1: exact softcap (either cap form), 2: no cap.
@@ -347,7 +347,7 @@ void bwd_dz_kernel(DzParams p) {
     const int y = p.target[grow];
     core.bias[tb] = !valid ? -INFINITY : (y >= 0 && y < V) ? -p.lse[grow] * kLog2e : __builtin_nanf("");
     core.ytok[tb] = valid ? y : -(1 << 30);
-    core.dzblk[tb] = p.dz + ((tok >> 5) * (p.ldz >> 5)) * 1024 + lane * 16;
+    core.dzblk[tb] = p.dz + ((tok >> 5) * (p.ldz >> 5)) * 1024 + lane * 8;
   }
 
   const int ntiles = p.n_vtiles;
@@ -401,15 +401,17 @@ __device__ __forceinline__ void train_prep_row(int64_t i, int lane, const uint16
                                                int D, int V, int64_t nvb, const Softcap& sc, float g, uint16_t* dz,
                                                uint16_t* hs, float* row_scale) {
   uint16_t* zblk = dz + (i >> 5) * nvb * 1024;   // vocabulary block 0 of the row's token block
-  const int l0 = (int)(i & 31);                  // the row's two 16-element runs: lanes l0, l0 + 32
+  const int l0 = (int)(i & 31);                  // the row's elements: those of lanes l0 and l0 + 32
   if (i >= n) {
     bf16x8 zero;
 #pragma unroll
     for (int e = 0; e < 8; ++e) zero[e] = (__bf16)0.f;
     for (int64_t bv = lane; bv < nvb; bv += 64) {
-      bf16x8* a = reinterpret_cast<bf16x8*>(zblk + bv * 1024 + 16 * l0);
-      bf16x8* b = reinterpret_cast<bf16x8*>(zblk + bv * 1024 + 16 * (l0 + 32));
-      a[0] = zero; a[1] = zero; b[0] = zero; b[1] = zero;
+      uint16_t* blk = zblk + bv * 1024;
+      *reinterpret_cast<bf16x8*>(blk + 8 * l0) = zero;
+      *reinterpret_cast<bf16x8*>(blk + 512 + 8 * l0) = zero;
+      *reinterpret_cast<bf16x8*>(blk + 8 * (l0 + 32)) = zero;
+      *reinterpret_cast<bf16x8*>(blk + 512 + 8 * (l0 + 32)) = zero;
     }
     return;
   }
@@ -436,7 +438,8 @@ __device__ __forceinline__ void train_prep_row(int64_t i, int lane, const uint16
     if ((float)stored != 0.f) f = g * val / (float)stored;
     if (lane == 0) {
       const int L = l0 + 32 * ((y >> 2) & 1);
-      zblk[(int64_t)(y >> 5) * 1024 + 16 * L + 4 * ((y & 31) >> 3) + (y & 3)] = __builtin_bit_cast(uint16_t, stored);
+      const int r = 4 * ((y & 31) >> 3) + (y & 3);   // the accumulator register that holds row y
+      zblk[(int64_t)(y >> 5) * 1024 + 512 * (r >> 3) + 8 * L + (r & 7)] = __builtin_bit_cast(uint16_t, stored);
     }
   } else {
     f = __builtin_nanf("");   // a target outside [0, V) poisons the row: NaN dH row, NaN dE

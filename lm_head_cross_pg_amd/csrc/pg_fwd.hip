@@ -115,7 +115,7 @@ struct FwdCore {
   float mrun[NB];
   int exact_left;   // blocks still to take the exact form before the series is tried again (uniform)
   uint16_t* dzblk[NB];   // DZ: block (its token block, vocabulary block 0); wave-uniform
-  int dzlane;            // DZ: this lane's 16 elements in a block (element offset lane * 16)
+  int dzlane;            // DZ: this lane's elements in a block (offsets lane * 8 and 512 + lane * 8)
   // The target logit is taken from the accumulators the log-sum-exp sums, so that the two share
   // every rounding: ykey is the target id when this lane holds its logit (lane half h holds rows
   // with ((v >> 2) & 1) == h of every 32-row block), else -1. ty is, with the fixed shift, the very
@@ -172,7 +172,7 @@ struct FwdCore {
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (__bf16)vals[e];
-    *reinterpret_cast<bf16x8*>(dzblk[tb] + (int64_t)(vbase >> 5) * 1024 + dzlane + 8 * j8) = o;
+    *reinterpret_cast<bf16x8*>(dzblk[tb] + (int64_t)(vbase >> 5) * 1024 + dzlane + 512 * j8) = o;
   }
 
   // DZ: the slope factor of the stored gradient from the exponent t = s log2 e - M: t (t - K) for
@@ -546,7 +546,7 @@ void fwd_mfma_kernel(FwdParams p) {
     const int64_t ic = t < n ? t : n - 1;
     return p.rows ? (int64_t)p.rows[ic] : ic;
   };
-  core.dzlane = lane * 16;
+  core.dzlane = lane * 8;
 #pragma unroll
   for (int tb = 0; tb < NB; ++tb) {
     core.lsum[tb] = 0.f;

@@ -38,10 +38,12 @@ namespace pg {
 // phase hit 16 different 16-byte bank groups:
 //   A: BM / 32 dZ blocks of 2 KiB; chunk c of a block stored at chunk a_swz(c)
 //   B: [32 k][BN n], rows of 2 BN bytes; chunk c of row k stored at c ^ (4 (k & 3))
-// a_swz flips chunk bit 0 when bit 4 is set (the plain 16-byte reads of dH, which stride two
-// chunks per lane) and bit 3 when bit 6 is set (the transposed reads of dE, which pair chunks 64
-// apart); it is its own inverse.
-__device__ __forceinline__ int a_swz(int c) { return c ^ ((c >> 4) & 1) ^ (((c >> 6) & 1) << 3); }
+// In the dZ block layout, chunk 64 j + L holds registers 8 j .. 8 j + 7 of lane L. The plain
+// 16-byte reads of dH take chunks 64 ks + lane, 16 consecutive ones per read phase; the
+// transposed reads of dE pair chunks 32 apart, so a_swz flips chunk bit 3 when bit 5 is set (a
+// permutation within each aligned run of 16 chunks, which leaves the dH reads alone); it is its
+// own inverse.
+__device__ __forceinline__ int a_swz(int c) { return c ^ (((c >> 5) & 1) << 3); }
 
 // The loads of each stage are split around the barrier: A of stage s + NS + AL - 1 before barrier
 // s + 1 (into the slot of stage s - 1), B of stage s + NS after it (into the slot stage s has
@@ -141,14 +143,16 @@ void gemm_bf16_kernel(GemmParams g) {
     const int ks = kss & 1;
     if (f < WM) {
       const char* blk = sA + (wm * WM + f) * 2048;
+      // dH: lane l takes row l % 32 of the block, registers 8 ks .. 8 ks + 7 of lane l: vocabulary
+      // rows 16 ks + 8 (j / 4) + 4 (l / 32) + j % 4, j = 0..7
       if (!A_TRANS)
-        return *(const __attribute__((address_space(3))) bf16x8*)((const lds_char*)blk + a_swz(2 * lane + ks) * 16);
+        return *(const __attribute__((address_space(3))) bf16x8*)((const lds_char*)blk + a_swz(64 * ks + lane) * 16);
       i16x4 part[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int t = 16 * ks + 8 * (grp >> 1) + 4 * half + (li >> 2);
         const int cg = li & 3;
-        const int c = 2 * (t + 32 * (cg & 1)) + (grp & 1);
+        const int c = 64 * (grp & 1) + t + 32 * (cg & 1);   // registers 8 (grp & 1) .. of lane t + 32 (cg & 1)
         part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(blk + a_swz(c) * 16 + 8 * (cg >> 1)));
       }
       i16x8 v = {part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};

@@ -98,9 +98,11 @@ hipError_t launch_sgd_step(float* master, const float* grad, float lr, int64_t n
 // dZ block layout (the backward's workspace). dZ[t][v] is stored in 32 x 32 blocks laid out like
 // the accumulator of v_mfma_f32_32x32x16_bf16: block (bt, bv) holds tokens 32 bt .. 32 bt + 31 and
 // vocabulary rows 32 bv .. 32 bv + 31 as 1024 bf16 at offset (bt * nvb + bv) * 1024, nvb = number
-// of vocabulary blocks; inside a block, element (t, v) sits at 16 L + r with
+// of vocabulary blocks; inside a block, element (t, v) sits at 512 (r >> 3) + 8 L + (r & 7) with
 //   L = t + 32 ((v >> 2) & 1)   (the lane that computed it),  r = 4 (v >> 3) + (v & 3).
-// Each lane of the dZ kernel thus writes 32 contiguous bytes and each block is one 2 KiB run.
+// The writers store a lane's accumulator registers 8 j .. 8 j + 7 as 16 bytes at 512 j + 8 L, so
+// each 16-byte store instruction of a wave fills one contiguous KiB (the first half of the block,
+// then the second), and each block is one 2 KiB run.
 
 // C = alpha * A B in bf16 with float32 accumulation (pg_gemm.hip), k in 32-deep chunks.
 constexpr int kGemmBK = 32;
