@@ -39,11 +39,12 @@ namespace pg {
 //   A: BM / 32 dZ blocks of 2 KiB; chunk c of a block stored at chunk a_swz(c)
 //   B: [32 k][BN n], rows of 2 BN bytes; chunk c of row k stored at c ^ (4 (k & 3))
 // In the dZ block layout, chunk 64 j + L holds registers 8 j .. 8 j + 7 of lane L. The plain
-// 16-byte reads of dH take chunks 64 ks + lane, 16 consecutive ones per read phase; the
-// transposed reads of dE pair chunks 32 apart, so a_swz flips chunk bit 3 when bit 5 is set (a
-// permutation within each aligned run of 16 chunks, which leaves the dH reads alone); it is its
-// own inverse.
-__device__ __forceinline__ int a_swz(int c) { return c ^ (((c >> 5) & 1) << 3); }
+// 16-byte reads of dH take chunks 64 ks + lane, 16 consecutive ones per read phase. A 32-lane
+// phase of the transposed 8-byte reads of dE takes four runs of 4 chunks at offsets 0, 32, 64
+// and 96, which fall on the same banks, so a_swz XORs chunk bits 2-3 with bits 5-6: the four runs
+// land on four different quarters of the 64 banks. Within an aligned run of 16 chunks this only
+// permutes, so the dH reads stay conflict-free; it is its own inverse.
+__device__ __forceinline__ int a_swz(int c) { return c ^ (((c >> 5) & 3) << 2); }
 
 // The loads of each stage are split around the barrier: A of stage s + NS + AL - 1 before barrier
 // s + 1 (into the slot of stage s - 1), B of stage s + NS after it (into the slot stage s has
