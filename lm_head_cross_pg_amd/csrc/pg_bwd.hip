@@ -662,8 +662,8 @@ hipError_t launch_train(const void* H, const void* E, int32_t dtype, const int32
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // dH = f dZ' E, row by row (left out when the caller takes no dH)
+  GemmParams a{};
   if (dH) {
-    GemmParams a{};
     a.A = dz; a.lda = ldz / 32;
     a.a_mblocks = rblk * (kRowsPerWG / 32);
     a.B = (const uint16_t*)E; a.ldb = D;
@@ -671,7 +671,6 @@ hipError_t launch_train(const void* H, const void* E, int32_t dtype, const int32
     a.M = T; a.N = D; a.K = V; a.kvalid = V;
     a.alpha = 1.f;
     a.C = dH; a.ldc = D; a.crows = rows; a.split_stride = 0; a.row_scale = row_scale;
-    if ((e = launch_gemm(a, false, 1, st)) != hipSuccess) return e;
   }
 
   // dE = dZ'^T (f H): the row factors sit in the scaled hidden rows
@@ -690,7 +689,9 @@ hipError_t launch_train(const void* H, const void* E, int32_t dtype, const int32
   b.M = V; b.N = D; b.K = T; b.kvalid = T;
   b.alpha = 1.f;
   b.C = ks > 1 ? part : dE; b.ldc = D; b.crows = nullptr; b.split_stride = (int64_t)V * D;
-  if ((e = launch_gemm(b, true, (int)ks, st)) != hipSuccess || ks == 1) return e;
+  // both products in one launch when dH is taken (dE's workgroups fill the CUs dH's last ones leave)
+  e = dH ? launch_gemm_pair(a, b, (int)ks, st) : launch_gemm(b, true, (int)ks, st);
+  if (e != hipSuccess || ks == 1) return e;
   return launch_sum_splits(part, (int)ks, (int64_t)V * D, (int64_t)V * D, dE, st);
 }
 

@@ -51,9 +51,10 @@ __device__ __forceinline__ int a_swz(int c) { return c ^ (((c >> 5) & 3) << 2); 
 // finished reading). A thus runs AL stages further ahead than B. With 32-deep stages, rings of
 // 3 + 1, 4 + 1, 4 + 2 and 3 + 3 stages measured the same: the feed's latency does not pace the
 // product, so the 64-deep stages take the smallest rings, 2 + 1 (160 KiB).
+// The product of one workgroup: wid is its index along x (the output tile), zsplit its k split
+// of nsplit; smem is the kernel's LDS (NS stages of B and NS + AL of A).
 template <bool A_TRANS, int NS, int AL, int SPS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_bf16_kernel(GemmParams g) {
+__device__ __forceinline__ void gemm_body(const GemmParams& g, int64_t wid, int zsplit, int nsplit, lds_char* smem) {
   constexpr int WM = 4, WN = 4, NW = 4, WGN = 2;
   // a stage is SPS sub-stages of 32 k (one 32 x 32 dZ block along k each), i.e. 2 SPS 16-deep
   // steps; each sub-stage's A and B tiles take 16 KiB of their stage's ring slot
@@ -67,7 +68,6 @@ void gemm_bf16_kernel(GemmParams g) {
                 "tile shape assumed below");
   constexpr int AST = NS + AL;   // A is issued AL stages ahead of B
   static_assert(AL >= 1 && NS * BBYTES + AST * ABYTES <= 160 * 1024, "LDS rings");
-  __shared__ __attribute__((aligned(1024))) char smem[NS * BBYTES + AST * ABYTES];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5;
@@ -77,16 +77,14 @@ void gemm_bf16_kernel(GemmParams g) {
   const int64_t M = g.m_dev ? ndev : g.M;
   const int64_t K = g.k_dev ? ndev : g.K;
   const int NT = (int)((g.N + BN - 1) / BN);
-  const int64_t wid = blockIdx.x;
   const int64_t mt = (wid / (8 * NT)) * 8 + (wid % 8);
   const int nt = (int)((wid / 8) % NT);
   const int64_t m0 = mt * BM;
   const int64_t n0 = (int64_t)nt * BN;
   if (m0 >= M) return;
   const int64_t kchunks = (K + BK - 1) / BK;
-  const int nsplit = gridDim.z;
   const int64_t cps = (kchunks + nsplit - 1) / nsplit;
-  const int64_t kc_begin = (int64_t)blockIdx.z * cps;
+  const int64_t kc_begin = (int64_t)zsplit * cps;
   const int64_t kc_end = kc_begin + cps < kchunks ? kc_begin + cps : kchunks;
   const int64_t nk = kc_end > kc_begin ? kc_end - kc_begin : 0;
   const int64_t kvalid = g.k_dev ? ndev : g.kvalid;
@@ -122,7 +120,7 @@ void gemm_bf16_kernel(GemmParams g) {
     const int64_t kb = SPS * kc + i / APS;
     const int64_t off = A_TRANS ? (kb < g.k_blocks ? kb : g.k_blocks - 1) * g.lda * 1024
                                 : (kb < g.lda ? kb : g.lda - 1) * 1024;
-    lds_dma16(pa[i % APS] + off, (const lds_char*)(smem + NS * BBYTES + slot * ABYTES + (i / APS) * SUBA +
+    lds_dma16(pa[i % APS] + off, (smem + NS * BBYTES + slot * ABYTES + (i / APS) * SUBA +
                                                    (wave + NW * (i % APS)) * 1024));
   };
   auto load_b = [&](int64_t kc, int slot, int ib) {
@@ -132,22 +130,22 @@ void gemm_bf16_kernel(GemmParams g) {
     rl = rl < BK ? rl : BK;
     const int lim = (int)rl * (int)g.ldb;          // |rl| <= BK (NS + AL + 1) and ldb <= 512
     const int r = jbo[i] < lim ? jbo[i] : lim;
-    lds_dma16(pb[i] + kcb * g.ldb + r, (const lds_char*)(smem + slot * BBYTES + (ib / BPS) * SUBB + (wave + NW * i) * 1024));
+    lds_dma16(pb[i] + kcb * g.ldb + r, (smem + slot * BBYTES + (ib / BPS) * SUBB + (wave + NW * i) * 1024));
   };
 
   const int grp = lane >> 4, li = lane & 15;
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   // fragment f of 16-deep step ks of a stage: f < WM is A block f of this wave, f >= WM is B block f - WM
-  auto read_frag = [&](const char* sA0, const char* sB0, int kss, int f) -> bf16x8 {
-    const char* sA = sA0 + (kss >> 1) * SUBA;
-    const char* sB = sB0 + (kss >> 1) * SUBB;
+  auto read_frag = [&](const lds_char* sA0, const lds_char* sB0, int kss, int f) -> bf16x8 {
+    const lds_char* sA = sA0 + (kss >> 1) * SUBA;
+    const lds_char* sB = sB0 + (kss >> 1) * SUBB;
     const int ks = kss & 1;
     if (f < WM) {
-      const char* blk = sA + (wm * WM + f) * 2048;
+      const lds_char* blk = sA + (wm * WM + f) * 2048;
       // dH: lane l takes row l % 32 of the block, registers 8 ks .. 8 ks + 7 of lane l: vocabulary
       // rows 16 ks + 8 (j / 4) + 4 (l / 32) + j % 4, j = 0..7
       if (!A_TRANS)
-        return *(const __attribute__((address_space(3))) bf16x8*)((const lds_char*)blk + a_swz(64 * ks + lane) * 16);
+        return *(const __attribute__((address_space(3))) bf16x8*)(blk + a_swz(64 * ks + lane) * 16);
       i16x4 part[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -209,7 +207,7 @@ void gemm_bf16_kernel(GemmParams g) {
   // (from the ring slots rA / rB, step rks) and loads of this stage's group interleaved: counting
   // MFMAs from gbase (the MFMAs of earlier steps in the same run of loads), load n is issued at
   // MFMA off + n every (A loads when a_loads, else B loads).
-  auto mstep = [&](const bf16x8 (&cur)[NF], bf16x8 (&nxt)[NF], const char* rA, const char* rB, int rks,
+  auto mstep = [&](const bf16x8 (&cur)[NF], bf16x8 (&nxt)[NF], const lds_char* rA, const lds_char* rB, int rks,
                    bool a_loads, int gbase, int every, int off, int64_t kc_l, int slot_l) {
 #pragma unroll
     for (int bn = 0; bn < WN; ++bn)
@@ -232,10 +230,10 @@ void gemm_bf16_kernel(GemmParams g) {
   int sa = 0, sb = 0, sa_prev = AST - 1;
   for (int64_t it = 0; it < nk; ++it) {
     const int sa1 = sa + 1 < AST ? sa + 1 : 0, sb1 = sb + 1 < NS ? sb + 1 : 0;
-    const char* sA = smem + NS * BBYTES + sa * ABYTES;
-    const char* sB = smem + sb * BBYTES;
-    const char* sA1 = smem + NS * BBYTES + sa1 * ABYTES;
-    const char* sB1 = smem + sb1 * BBYTES;
+    const lds_char* sA = smem + NS * BBYTES + sa * ABYTES;
+    const lds_char* sB = smem + sb * BBYTES;
+    const lds_char* sA1 = smem + NS * BBYTES + sa1 * ABYTES;
+    const lds_char* sB1 = smem + sb1 * BBYTES;
     const int64_t kc_n = kc_begin + it + NS;   // B of this stage and A of stage kc_n + AL - 1 are issued here
     // steps 0 .. KS - 2 (even steps on fa, odd on fb), with the A loads of stage it + NS + AL - 1
     // into the slot of stage it - 1
@@ -267,7 +265,7 @@ void gemm_bf16_kernel(GemmParams g) {
   //      in elements 4 k .. 4 k + 3, the four consecutive columns 8 k + 4 (l / 32) .. + 3, i.e. one
   //      16-byte store each (the untransposed layout took 4-byte stores, 71 us more per dH launch
   //      at the training shape).
-  float* C = g.C + (int64_t)blockIdx.z * g.split_stride;
+  float* C = g.C + (int64_t)zsplit * g.split_stride;
 #pragma unroll
   for (int bm = 0; bm < WM; ++bm) {
     const int64_t m = m0 + (wm * WM + bm) * 32 + (lane & 31);
@@ -292,6 +290,29 @@ void gemm_bf16_kernel(GemmParams g) {
         }
     }
   }
+}
+
+// Both products' tiles are 256 x 256, with 64-deep stages, a 2-stage B ring and A one stage ahead.
+constexpr int kGemmNS = 2, kGemmAL = 1, kGemmSPS = 2;
+constexpr size_t kGemmLds = (size_t)(kGemmNS + kGemmNS + kGemmAL) * 256 * kGemmBK * kGemmSPS * 2;
+
+template <bool A_TRANS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_kernel(GemmParams g) {
+  __shared__ __attribute__((aligned(1024))) char smem[kGemmLds];
+  gemm_body<A_TRANS, kGemmNS, kGemmAL, kGemmSPS>(g, blockIdx.x, blockIdx.z, gridDim.z, (lds_char*)smem);
+}
+
+// dH and dE in one launch: workgroups 0 .. gxa - 1 take dH's tiles, the rest dE's (ksb k splits of
+// gxb tiles each). A CU that finishes its last dH tile picks up dE work at once, instead of idling
+// until the slowest dH tile ends. gxa and gxb are multiples of 8, so every workgroup keeps the XCD
+// its own product's id mapping gives it.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_pair_kernel(GemmParams a, GemmParams b, int64_t gxa, int64_t gxb, int ksb) {
+  __shared__ __attribute__((aligned(1024))) char smem[kGemmLds];
+  const int64_t w = blockIdx.x;
+  if (w < gxa) gemm_body<false, kGemmNS, kGemmAL, kGemmSPS>(a, w, 0, 1, (lds_char*)smem);
+  else gemm_body<true, kGemmNS, kGemmAL, kGemmSPS>(b, (w - gxa) % gxb, (int)((w - gxa) / gxb), ksb, (lds_char*)smem);
 }
 
 // out[i] = sum over s of part[s * stride + i], in split order, starting from 0. Four elements per
@@ -330,14 +351,25 @@ int64_t gemm_grid_x(int64_t M, int64_t N, bool) {
   return nt > 1 ? 8 * nt * ((mt + 7) / 8) : mt;   // the id mapping of the kernel
 }
 
-// Both products: 64-deep stages, 2-stage B ring, A one stage ahead.
 hipError_t launch_gemm(const GemmParams& g, bool a_trans, int ksplit, hipStream_t st) {
   const int64_t gx = gemm_grid_x(g.M, g.N, a_trans);
   if (gx == 0 || ksplit < 1) return hipSuccess;
   if (gx > kMaxGrid512) return hipErrorInvalidConfiguration;   // the API layer rejects such shapes first
   const dim3 grid((unsigned)gx, 1, (unsigned)ksplit);
-  if (a_trans) hipLaunchKernelGGL((gemm_bf16_kernel<true, 2, 1, 2>), grid, dim3(256), 0, st, g);
-  else hipLaunchKernelGGL((gemm_bf16_kernel<false, 2, 1, 2>), grid, dim3(256), 0, st, g);
+  if (a_trans) hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, dim3(256), 0, st, g);
+  else hipLaunchKernelGGL(gemm_bf16_kernel<false>, grid, dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_pair(const GemmParams& a, const GemmParams& b, int ksb, hipStream_t st) {
+  const int64_t gxa = gemm_grid_x(a.M, a.N, false), gxb = gemm_grid_x(b.M, b.N, true);
+  if (ksb < 1 || gxa % 8 != 0 || gxb % 8 != 0) {   // the id mapping needs whole groups of 8
+    hipError_t e = launch_gemm(a, false, 1, st);
+    return e != hipSuccess ? e : launch_gemm(b, true, ksb, st);
+  }
+  const int64_t n = gxa + gxb * ksb;
+  if (n > kMaxGrid512) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(gemm_pair_kernel, dim3((unsigned)n), dim3(256), 0, st, a, b, gxa, gxb, ksb);
   return hipGetLastError();
 }
 

@@ -128,6 +128,9 @@ struct GemmParams {
 // output tile; with several splits, C receives one partial output per split at split_stride.
 // M and N are the host bounds that size the grid.
 hipError_t launch_gemm(const GemmParams& g, bool a_trans, int ksplit, hipStream_t st);
+// dH (a, not transposed, one split) and dE (b, transposed, ksb splits) in one launch; the same
+// results as the two launch_gemm calls.
+hipError_t launch_gemm_pair(const GemmParams& a, const GemmParams& b, int ksb, hipStream_t st);
 // Output tile of each product (rows x columns).
 int gemm_tile_m(bool a_trans);
 int gemm_tile_n(bool a_trans);
