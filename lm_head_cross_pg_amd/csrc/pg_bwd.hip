@@ -525,6 +525,7 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
   }
   uint16_t* dz = reinterpret_cast<uint16_t*>(ws + L.dz);
   if (dtype == 0 && mfma_width(D)) {
+    GemmParams a{};
     if (T > 0) {
       DzParams q{};
       q.H = (const uint16_t*)H;
@@ -550,9 +551,8 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
 
-      // dH = g dZ E (left out when the caller takes no dH)
+      // dH = g dZ E (left out when the caller takes no dH), launched with dE below
       if (dH) {
-        GemmParams a{};
         a.A = dz; a.lda = q.ldz / 32;
         a.a_mblocks = (int64_t)rblk * (kRowsPerWG / 32);   // token blocks of the padded dZ rows
         a.B = (const uint16_t*)E; a.ldb = D;
@@ -560,8 +560,6 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
         a.M = T; a.N = D; a.K = V; a.kvalid = V;
         a.alpha = grad_scale;
         a.C = dH; a.ldc = D; a.crows = rows; a.split_stride = 0;
-        e = launch_gemm(a, false, 1, st);
-        if (e != hipSuccess) return e;
       }
     }
     // dE = g dZ^T H, k split over workgroups when the output has few tiles
@@ -588,7 +586,8 @@ hipError_t launch_bwd(const void* H, const void* E, int32_t dtype, const int32_t
     b.M = V; b.N = D; b.K = T; b.kvalid = T;
     b.alpha = grad_scale;
     b.C = ks > 1 ? part : dE; b.ldc = D; b.crows = nullptr; b.split_stride = (int64_t)V * D;
-    hipError_t e = launch_gemm(b, true, (int)ks, st);
+    // both products in one launch when dH is taken (T > 0 here)
+    hipError_t e = dH ? launch_gemm_pair(a, b, (int)ks, st) : launch_gemm(b, true, (int)ks, st);
     if (e != hipSuccess || ks == 1) return e;
     return launch_sum_splits(part, (int)ks, (int64_t)V * D, (int64_t)V * D, dE, st);
   }
